@@ -1,0 +1,80 @@
+"""The oracle against what the pages and the mathematics fix (CPU only)."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import pins
+
+
+def test_layout_bruteforce():
+    pins.pin_layout_bruteforce()
+
+
+def test_bf16_rounding_vs_torch():
+    pins.pin_bf16_vs_torch()
+
+
+@pytest.mark.slow
+def test_bf16_rounding_exhaustive():
+    """All 2^32 binary32 patterns, in chunks (about a minute)."""
+    step = 1 << 26
+    for start in range(0, 1 << 32, step):
+        pats = np.arange(start, start + step, dtype=np.uint64).astype(np.uint32)
+        pins.pin_bf16_vs_torch(patterns=pats)
+
+
+def test_adamw_vs_torch_binary64():
+    pins.pin_adamw_vs_torch64()
+
+
+def test_step_scalars():
+    pins.pin_scalars()
+
+
+def test_sharded_equals_unsharded():
+    pins.pin_sharded_equals_unsharded()
+
+
+def test_rank_local_equals_global():
+    pins.pin_rank_local_equals_global()
+
+
+def test_toy():
+    pins.pin_toy()
+
+
+def test_norm_and_clip():
+    pins.pin_norm()
+
+
+def test_ledger_values_printed_on_pages():
+    pins.pin_ledger()
+
+
+def test_bf16_special_values():
+    x = np.array([0.0, -0.0, np.inf, -np.inf, 1.0, -1.0, 3.4028235e38, 1e-45, -1e-45], np.float32)
+    got = oracle.bf16(x)
+    want = np.array([0x0000, 0x8000, 0x7F80, 0xFF80, 0x3F80, 0xBF80, 0x7F80, 0x0000, 0x8000], np.uint16)
+    assert np.array_equal(got, want), [hex(v) for v in got]
+
+
+def test_padding_stays_positive_zero():
+    """Padding with zero gradient and zero state stays +0 through any number
+    of steps: g = 0 gives m = v = 0, update 0 / eps = 0, w = 0 * decay - 0."""
+    n, numel = 4, [5]
+    L = oracle.Layout(n, numel)
+    gs = [np.zeros(L.total_padded, np.uint16) for _ in range(n)]
+    for g in gs:
+        g[:5] = oracle.bf16(np.ones(5, np.float32) * 1e-3)
+    master = np.zeros(L.total_padded, np.float32)
+    master[:5] = 0.5
+    m = np.zeros_like(master)
+    v = np.zeros_like(master)
+    out = np.zeros(L.total_padded, np.uint16)
+    for t in range(1, 30):
+        oracle.zero_step_all(n, numel, gs, divisor=4.0, clip=1.0, master=master, m=m, v=v, out=out,
+                             t=t, lr=0.01, b1=0.9, b2=0.95, eps=1e-8, wd=0.1)
+    assert np.all(master[5:].view(np.uint32) == 0) and np.all(out[5:] == 0)
+    assert np.all(m[5:].view(np.uint32) == 0) and np.all(v[5:].view(np.uint32) == 0)
