@@ -1,0 +1,268 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused ZeRO sharded optimizer step on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload gpt2l|gpt2l_block|llama8b_z3|llama8b_z3_clip]
+
+A step is one call of the whole hot path over one batch of synthetic input:
+for the default workload (a GPT-2-Large-sized model, 36 units, 774,090,240
+parameters, N = 8 simulated ranks) every rank's shard is reduced over the 8
+bf16 gradient buffers, averaged, stepped with AdamW on the fp32 master / m / v
+and cast to bf16 into the all-gather slots.  The clipped workload adds the
+two-stage norm pass and steps from the reduced gradient it writes.
+
+Prints ONE JSON line: throughput in shard elements per second (value), the
+achieved HBM bandwidth of the dominant kernel against MI355X's 8 TB/s
+(roofline), and the serial CPU oracle on a bounded sample (cpu_baseline).
+Inputs are resident in HBM before the timed region; gradients are generated
+once and reused by every timed step (their values do not change the work).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+KERNEL_SOURCES = ["fsdp_sharded_optimizer_flat_amd/csrc/step_kernels.hip",
+                  "fsdp_sharded_optimizer_flat_amd/csrc/norm_kernels.hip",
+                  "fsdp_sharded_optimizer_flat_amd/csrc/device_common.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gpt2l")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="wall-clock budget of the CPU oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain device copy of known size (PMC calibration)")
+    return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain copy of 4 GiB (2 GiB read + 2 GiB written): the reference the
+    FETCH_SIZE / WRITE_SIZE counters are scaled by."""
+    import torch
+    n = 1 << 29  # fp32 elements = 2 GiB
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "dispatches": 3}))
+
+
+def cpu_baseline(wl, seconds: float):
+    """The oracle as it stands (serial C, one thread) on a bounded sample of
+    the workload: a one-unit layout of 2^22 elements with the workload's rank
+    count, gradient type and distributions, stepped until the budget is
+    spent.  Returns elements per second."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from fsdp_sharded_optimizer_flat_amd import synth
+
+    n = wl.n_ranks
+    P = 1 << 22 if n <= 8 else 1 << 19
+    numel = [P * n] if wl.rank >= 0 else [P]
+    K = P                                    # elements one oracle step processes
+    grads = []
+    for r in range(n):
+        g = torch.empty(K, dtype=torch.bfloat16)
+        synth.fill_grad_(g, wl.grad_dist, wl.grad_scale, synth.seed_of(wl.seed, synth.TAG_GRAD, 1, r))
+        grads.append(np.ascontiguousarray(g.view(torch.int16).numpy().view(np.uint16)))
+    w = torch.empty(K, dtype=torch.float32)
+    synth.fill_normal_(w, wl.master_std, synth.seed_of(wl.seed, synth.TAG_MASTER))
+    w = w.numpy().copy()
+    m, v = np.zeros(K, np.float32), np.zeros(K, np.float32)
+    out = np.zeros(K, np.uint16)
+    h = wl.hyper
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        if wl.rank >= 0:
+            oracle.zero_step_rank(n, numel, 0, grads, grad_local=True, divisor=float(n), clip=1.0,
+                                  master=w, m=m, v=v, state_global=False, out=out, out_gather=False,
+                                  t=steps + 1, **h)
+        else:
+            oracle.zero_step_all(n, numel, grads, divisor=float(n), clip=1.0, master=w, m=m, v=v,
+                                 out=out, t=steps + 1, **h)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": steps * K / el, "unit": "elements/s", "cores": 1, "kind": "oracle",
+            "sample": f"{steps} oracle steps over a {K}-element one-unit sample of the workload "
+                      f"(N={n}, {wl.grad_dist} bf16 gradients), serial C, {el:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the sharded step for N "
+              "ranks runs here as N simulated ranks' buffers in one GPU's memory", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import numpy as np
+    import torch
+
+    import fsdp_sharded_optimizer_flat_amd as z
+    from fsdp_sharded_optimizer_flat_amd import synth
+    from fsdp_sharded_optimizer_flat_amd.workloads import WORKLOADS
+
+    wl = WORKLOADS[args.workload]
+    n, h = wl.n_ranks, wl.hyper
+    dev = torch.device("cuda:0")
+    L = z.zero_pack(n, wl.unit_numel)
+    G, Lc = z.ZERO_GLOBAL, z.ZERO_LOCAL
+    gidx = G if wl.grad_index == "global" else Lc
+    sidx = G if wl.rank < 0 else Lc
+    oidx = G if wl.out_index == "global" else Lc
+    ge = L.padded if gidx == G else L.shard
+    se = L.padded if sidx == G else L.shard
+    oe = L.padded if oidx == G else L.shard
+    clip = wl.clip_max_norm is not None
+
+    # -- inputs, resident before the timed region --------------------------------------
+    master = torch.empty(se, dtype=torch.float32, device=dev)
+    synth.fill_normal_(master, wl.master_std, synth.seed_of(wl.seed, synth.TAG_MASTER))
+    m, v = torch.zeros_like(master), torch.zeros_like(master)
+    out = torch.zeros(oe, dtype=torch.int16, device=dev)
+    grads = torch.empty(n, ge, dtype=torch.bfloat16, device=dev)
+    for r in range(n):
+        synth.fill_grad_(grads[r], wl.grad_dist, wl.grad_scale, synth.seed_of(wl.seed, synth.TAG_GRAD, 1, r))
+    gp = z.grad_pointer_array(list(grads))
+    if clip:
+        g_red = torch.empty(se, dtype=torch.float32, device=dev)
+        ws = torch.zeros(z.zero_gradnorm_workspace_bytes(L, wl.rank) // 8, dtype=torch.float64, device=dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    sc = z.zero_adamw_scalars_for(1, h["lr"], h["b1"], h["b2"], h["eps"], h["wd"], 1.0)
+
+    def one_step(t, ev=None):
+        nonlocal sc
+        sc = z.zero_adamw_scalars_for(t, h["lr"], h["b1"], h["b2"], h["eps"], h["wd"], 1.0) \
+            if t == 1 else z.zero_adamw_scalars_next(sc)
+        if clip:
+            ss = z.zero_gradnorm(L, wl.rank, list(grads), gidx, float(n), g_red, sidx, ws, stream)
+            sc.clip_coef = z.zero_clip_coef(ss, wl.clip_max_norm)
+            if ev:
+                ev[0].record(stream)
+            z.zero_step(L, wl.rank, [g_red], sidx, 1.0, master, m, v, sidx, out, oidx, sc, stream)
+        else:
+            if ev:
+                ev[0].record(stream)
+            z.zero_step(L, wl.rank, None, gidx, float(n), master, m, v, sidx, out, oidx, sc, stream,
+                        grad_ptrs=gp)
+        if ev:
+            ev[1].record(stream)
+
+    t = 0
+    for _ in range(args.warmup):
+        t += 1
+        one_step(t)
+    torch.cuda.synchronize()
+
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        t += 1
+        one_step(t, events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    launch_ms = [a.elapsed_time(b) for a, b in events]
+    avg_launch_s = float(np.mean(launch_ms)) / 1e3
+    elements = se if wl.rank < 0 else L.shard
+    if clip:
+        step_bytes, _ = z.zero_step_traffic(L, wl.rank, 1, z.ZERO_F32, True)
+        norm_bytes, _ = z.zero_gradnorm_traffic(L, wl.rank, n, z.ZERO_BF16, True)
+        job_bytes = step_bytes + norm_bytes
+    else:
+        step_bytes, _ = z.zero_step_traffic(L, wl.rank, n, z.ZERO_BF16, True)
+        job_bytes = step_bytes
+    achieved = step_bytes / avg_launch_s / 1e9
+    ms_per_step = wall / args.steps * 1e3
+    value = elements * args.steps / wall
+
+    traffic = None
+    if os.path.exists(PMC_SUMMARY):
+        with open(PMC_SUMMARY) as f:
+            pmc = json.load(f)
+        ent = pmc.get("workloads", {}).get(args.workload)
+        if ent and pmc.get("kernel_source_hash") == kernel_source_hash():
+            traffic = ent["traffic_bytes_per_launch"]
+
+    result = {
+        "metric": "optimizer-step shard elements/sec and achieved HBM GB/s (% of MI355X peak)",
+        "value": value,
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name,
+            "description": wl.description,
+            "simulated_ranks": n,
+            "units": len(wl.unit_numel),
+            "params": int(L.numel),
+            "elements_per_step": int(elements),
+            "grad_dtype": "bf16",
+            "state_dtype": "f32",
+            "out_dtype": "bf16",
+            "clip_max_norm": wl.clip_max_norm,
+            "algorithmic_bytes_per_step": job_bytes,
+            "bytes_per_element": job_bytes / elements,
+            "hbm_GBps_whole_step": job_bytes / (wall / args.steps) / 1e9,
+            "pct_of_peak_whole_step": 100.0 * job_bytes / (wall / args.steps) / 1e9 / PEAK_HBM_GBPS,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "step_vec_kernel (fused rank-sum + AdamW + bf16 cast)",
+            "achieved": achieved,
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBPS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": step_bytes,
+            "avg_launch_ms": avg_launch_s * 1e3,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        del grads, master, m, v, out
+        torch.cuda.empty_cache()
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,381 @@
+"""Python binding of libzero.so, the MI355X ZeRO sharded optimizer step.
+
+Argument marshalling only: every entry point here forwards to the C function
+of the same name declared in ``include/zero.h``; all step arithmetic runs in
+the library's HIP kernels.  torch tensors supply device memory (``data_ptr``)
+and streams (``torch.cuda.current_stream().cuda_stream``).  There is no CPU
+fallback: importing this package raises if the built library is missing.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Sequence
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libzero.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m fsdp_sharded_optimizer_flat_amd._build` "
+        "(there is no CPU fallback for the sharded step)")
+
+_lib = C.CDLL(LIB_PATH)
+
+# -- constants mirrored from zero.h -------------------------------------------
+ZERO_OK, ZERO_EINVAL, ZERO_ERANGE, ZERO_EALIGN, ZERO_ENOSPC, ZERO_EHIP = 0, -1, -2, -3, -4, -5
+ZERO_F32, ZERO_BF16 = 0, 1
+ZERO_GLOBAL, ZERO_LOCAL = 0, 1
+ZERO_MAX_RANKS = 256
+ZERO_LAYOUT_MAGIC = 0x5A45524F
+ZERO_ABI_VERSION = 1
+
+i32, i64, f32, f64, vp, sz = C.c_int32, C.c_int64, C.c_float, C.c_double, C.c_void_p, C.c_size_t
+
+
+class ZeroUnit(C.Structure):
+    _fields_ = [("numel", i64), ("padded", i64), ("shard", i64), ("offset", i64),
+                ("local_offset", i64)]
+
+
+class ZeroLayoutHeader(C.Structure):
+    _fields_ = [("magic", C.c_uint32), ("n_ranks", i32), ("n_units", i32), ("reserved", i32),
+                ("numel", i64), ("padded", i64), ("shard", i64)]
+
+
+class ZeroAdamwScalars(C.Structure):
+    _fields_ = [("t", i32), ("lr", f32), ("b1", f32), ("b2", f32), ("eps", f32), ("wd", f32),
+                ("one_minus_b1", f32), ("one_minus_b2", f32), ("pow1", f32), ("pow2", f32),
+                ("bc1", f32), ("bc2", f32), ("step_size", f32), ("decay", f32),
+                ("clip_coef", f32)]
+
+    def as_dict(self):
+        return {k: getattr(self, k) for k, _ in self._fields_}
+
+
+class ZeroLedgerOut(C.Structure):
+    _fields_ = [("params_bytes", f64), ("grads_bytes", f64), ("optim_bytes", f64),
+                ("model_state_bytes", f64), ("comm_elements", f64),
+                ("comm_elements_ring", f64), ("optimizer_floats_per_rank", f64)]
+
+    def as_dict(self):
+        return {k: getattr(self, k) for k, _ in self._fields_}
+
+
+def _sig(name, res, *args):
+    fn = getattr(_lib, name)
+    fn.restype = res
+    fn.argtypes = list(args)
+    return fn
+
+
+_zero_layout_bytes = _sig("zero_layout_bytes", sz, i32)
+_zero_pack = _sig("zero_pack", i32, i32, i32, vp, vp, sz, C.POINTER(sz))
+_zero_global_index = _sig("zero_global_index", i32, vp, i32, i64, C.POINTER(i64))
+_zero_owner = _sig("zero_owner", i32, vp, i64, C.POINTER(i32), C.POINTER(i64))
+_zero_pack_copy = _sig("zero_pack_copy", i32, vp, i32, i32, vp, vp, vp, i32, vp, i32, vp)
+_zero_unpack_copy = _sig("zero_unpack_copy", i32, vp, i32, vp, i32, i32, vp, vp, vp, i32, vp)
+_zero_adamw_scalars_for = _sig("zero_adamw_scalars_for", i32, i32, f32, f32, f32, f32, f32, f32,
+                               C.POINTER(ZeroAdamwScalars))
+_zero_adamw_scalars_next = _sig("zero_adamw_scalars_next", i32, C.POINTER(ZeroAdamwScalars),
+                                C.POINTER(ZeroAdamwScalars))
+_zero_step = _sig("zero_step", i32, vp, i32, vp, i32, i32, i32, f32, vp, vp, vp, i32, vp, i32,
+                  C.POINTER(ZeroAdamwScalars), vp)
+_zero_gradnorm_workspace_bytes = _sig("zero_gradnorm_workspace_bytes", i32, vp, i32,
+                                      C.POINTER(sz))
+_zero_gradnorm = _sig("zero_gradnorm", i32, vp, i32, vp, i32, i32, i32, f32, vp, i32, vp, sz,
+                      C.POINTER(f64), vp)
+_zero_clip_coef = _sig("zero_clip_coef", i32, f64, f64, C.POINTER(f32))
+_zero_ledger = _sig("zero_ledger", i32, f64, i32, i32, i32, C.POINTER(ZeroLedgerOut))
+_zero_gather_buffer_bytes = _sig("zero_gather_buffer_bytes", i32, vp, i32, C.POINTER(f64))
+_zero_step_traffic = _sig("zero_step_traffic", i32, vp, i32, i32, i32, i32, C.POINTER(f64),
+                          C.POINTER(i64))
+_zero_gradnorm_traffic = _sig("zero_gradnorm_traffic", i32, vp, i32, i32, i32, i32,
+                              C.POINTER(f64), C.POINTER(i64))
+_zero_strerror = _sig("zero_strerror", C.c_char_p, i32)
+_zero_last_hip_error = _sig("zero_last_hip_error", C.c_char_p)
+_zero_abi_version = _sig("zero_abi_version", i32)
+
+EXPORTED = ["zero_layout_bytes", "zero_pack", "zero_global_index", "zero_owner", "zero_pack_copy",
+            "zero_unpack_copy", "zero_adamw_scalars_for", "zero_adamw_scalars_next", "zero_step",
+            "zero_gradnorm_workspace_bytes", "zero_gradnorm", "zero_clip_coef", "zero_ledger",
+            "zero_gather_buffer_bytes", "zero_step_traffic", "zero_gradnorm_traffic",
+            "zero_strerror", "zero_last_hip_error", "zero_abi_version"]
+
+
+class ZeroError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = _zero_strerror(status).decode()
+        if status == ZERO_EHIP:
+            msg += ": " + _zero_last_hip_error().decode()
+        super().__init__(f"{where}: {msg} ({status})")
+        self.status = status
+
+
+def _check(status: int, where: str):
+    if status != ZERO_OK:
+        raise ZeroError(status, where)
+
+
+# -- tensor marshalling ---------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dev_ptr(t, what: str) -> int:
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a device tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return t.data_ptr()
+
+
+def _grad_dtype(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return ZERO_BF16
+    if t.dtype == torch.float32:
+        return ZERO_F32
+    raise TypeError(f"gradient dtype must be bfloat16 or float32, got {t.dtype}")
+
+
+def _f32_ptr(t, what):
+    torch = _torch()
+    if t.dtype != torch.float32:
+        raise TypeError(f"{what} must be float32")
+    return _dev_ptr(t, what)
+
+
+def _bf16_ptr(t, what):
+    torch = _torch()
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"{what} must hold bf16 bits (bfloat16, int16 or uint16)")
+    return _dev_ptr(t, what)
+
+
+def _stream(stream):
+    if stream is None:
+        return _torch().cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# -- layout -------------------------------------------------------------------------
+
+class Layout:
+    """A filled ``zero_layout`` in host memory (the library's own copy)."""
+
+    def __init__(self, buf: C.Array):
+        self._buf = buf
+        self.header = ZeroLayoutHeader.from_buffer(buf)
+        n = self.header.n_units
+        self.units = (ZeroUnit * n).from_buffer(buf, C.sizeof(ZeroLayoutHeader))
+
+    @property
+    def ptr(self) -> int:
+        return C.addressof(self._buf)
+
+    n_ranks = property(lambda s: s.header.n_ranks)
+    n_units = property(lambda s: s.header.n_units)
+    numel = property(lambda s: s.header.numel)
+    padded = property(lambda s: s.header.padded)
+    shard = property(lambda s: s.header.shard)
+
+    def unit_table(self) -> np.ndarray:
+        """(U, 5) int64: numel, padded, shard, offset, local_offset."""
+        return np.array([[u.numel, u.padded, u.shard, u.offset, u.local_offset]
+                         for u in self.units], dtype=np.int64).reshape(-1, 5)
+
+
+def zero_layout_bytes(n_units: int) -> int:
+    return int(_zero_layout_bytes(n_units))
+
+
+def zero_pack(n_ranks: int, unit_numel: Sequence[int]) -> Layout:
+    numel = np.ascontiguousarray(unit_numel, dtype=np.int64)
+    need = sz()
+    _check(_zero_pack(n_ranks, len(numel), numel.ctypes.data if len(numel) else None, None, 0,
+                      C.byref(need)), "zero_pack")
+    buf = (C.c_char * need.value)()
+    _check(_zero_pack(n_ranks, len(numel), numel.ctypes.data if len(numel) else None,
+                      C.addressof(buf), need.value, None), "zero_pack")
+    return Layout(buf)
+
+
+def zero_global_index(layout: Layout, rank: int, k: int) -> int:
+    j = i64()
+    _check(_zero_global_index(layout.ptr, rank, k, C.byref(j)), "zero_global_index")
+    return j.value
+
+
+def zero_owner(layout: Layout, j: int):
+    r, k = i32(), i64()
+    _check(_zero_owner(layout.ptr, j, C.byref(r), C.byref(k)), "zero_owner")
+    return r.value, k.value
+
+
+def _param_arrays(params, units):
+    torch = _torch()
+    n = len(params)
+    ptrs = (vp * max(n, 1))(*[_dev_ptr(p, "param") for p in params])
+    numel = np.ascontiguousarray([p.numel() for p in params], dtype=np.int64)
+    unit = np.ascontiguousarray(units, dtype=np.int32)
+    if len(unit) != n:
+        raise ValueError("one unit id per parameter")
+    dt = {torch.float32: ZERO_F32, torch.bfloat16: ZERO_BF16}
+    dts = {dt.get(p.dtype, -1) for p in params}
+    if len(dts) > 1 or -1 in dts:
+        raise TypeError("parameters must all be float32 or all bfloat16")
+    return ptrs, numel, unit, (dts.pop() if dts else ZERO_F32)
+
+
+def _flat_dtype(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return ZERO_F32
+    if t.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return ZERO_BF16
+    raise TypeError("flat buffer must be float32 or bf16")
+
+
+def zero_pack_copy(layout: Layout, rank: int, params, units, dst, stream=None):
+    ptrs, numel, unit, sdt = _param_arrays(params, units)
+    _check(_zero_pack_copy(layout.ptr, rank, len(params), C.addressof(ptrs), numel.ctypes.data,
+                           unit.ctypes.data, sdt, _dev_ptr(dst, "dst"), _flat_dtype(dst),
+                           _stream(stream)), "zero_pack_copy")
+
+
+def zero_unpack_copy(layout: Layout, rank: int, src, params, units, stream=None):
+    ptrs, numel, unit, ddt = _param_arrays(params, units)
+    _check(_zero_unpack_copy(layout.ptr, rank, _dev_ptr(src, "src"), _flat_dtype(src),
+                             len(params), C.addressof(ptrs), numel.ctypes.data, unit.ctypes.data,
+                             ddt, _stream(stream)), "zero_unpack_copy")
+
+
+# -- scalars ------------------------------------------------------------------------------
+
+def zero_adamw_scalars_for(t: int, lr: float, b1: float, b2: float, eps: float, wd: float,
+                           clip_coef: float = 1.0) -> ZeroAdamwScalars:
+    s = ZeroAdamwScalars()
+    _check(_zero_adamw_scalars_for(t, lr, b1, b2, eps, wd, clip_coef, C.byref(s)),
+           "zero_adamw_scalars_for")
+    return s
+
+
+def zero_adamw_scalars_next(prev: ZeroAdamwScalars) -> ZeroAdamwScalars:
+    s = ZeroAdamwScalars()
+    _check(_zero_adamw_scalars_next(C.byref(prev), C.byref(s)), "zero_adamw_scalars_next")
+    return s
+
+
+def zero_clip_coef(sumsq: float, max_norm: float) -> float:
+    c = f32()
+    _check(_zero_clip_coef(sumsq, max_norm, C.byref(c)), "zero_clip_coef")
+    return c.value
+
+
+# -- the step and the norm -------------------------------------------------------------
+
+def _grad_ptrs(grads):
+    if len(grads) < 1:
+        raise ValueError("at least one gradient buffer")
+    gdt = {_grad_dtype(g) for g in grads}
+    if len(gdt) != 1:
+        raise TypeError("all gradient buffers must share one dtype")
+    arr = (vp * len(grads))(*[_dev_ptr(g, "grad") for g in grads])
+    return arr, gdt.pop()
+
+
+def zero_step(layout: Layout, rank: int, grads, grad_index: int, divisor: float,
+              master, exp_avg, exp_avg_sq, state_index: int, out, out_index: int,
+              scalars: ZeroAdamwScalars, stream=None, *, grad_ptrs=None):
+    """Enqueue the fused step.  ``grads``: list of device tensors (bf16 or
+    fp32), summed in list order.  ``grad_ptrs`` (a prepared ``(array, dtype)``
+    from :func:`grad_pointer_array`) skips re-marshalling in timed loops."""
+    arr, gdt = grad_ptrs if grad_ptrs is not None else _grad_ptrs(grads)
+    _check(_zero_step(layout.ptr, rank, C.addressof(arr), len(arr), gdt, grad_index, divisor,
+                      _f32_ptr(master, "master"), _f32_ptr(exp_avg, "exp_avg"),
+                      _f32_ptr(exp_avg_sq, "exp_avg_sq"), state_index,
+                      _bf16_ptr(out, "out") if out is not None else None, out_index,
+                      C.byref(scalars), _stream(stream)), "zero_step")
+
+
+def grad_pointer_array(grads):
+    return _grad_ptrs(grads)
+
+
+def zero_gradnorm_workspace_bytes(layout: Layout, rank: int) -> int:
+    b = sz()
+    _check(_zero_gradnorm_workspace_bytes(layout.ptr, rank, C.byref(b)),
+           "zero_gradnorm_workspace_bytes")
+    return b.value
+
+
+def zero_gradnorm(layout: Layout, rank: int, grads, grad_index: int, divisor: float,
+                  g_out, g_index: int, workspace, stream=None) -> float:
+    """Sum of squares (binary64) of the averaged gradient; optionally writes
+    the averaged gradient (fp32) into ``g_out``.  Synchronizes the stream."""
+    arr, gdt = _grad_ptrs(grads)
+    res = f64()
+    _check(_zero_gradnorm(layout.ptr, rank, C.addressof(arr), len(arr), gdt, grad_index, divisor,
+                          _f32_ptr(g_out, "g_out") if g_out is not None else None, g_index,
+                          _dev_ptr(workspace, "workspace"),
+                          workspace.numel() * workspace.element_size(), C.byref(res),
+                          _stream(stream)), "zero_gradnorm")
+    return res.value
+
+
+# -- ledger -------------------------------------------------------------------------------
+
+def zero_ledger(psi: float, n_ranks: int, stage: int, grads_transient: bool = False) -> dict:
+    o = ZeroLedgerOut()
+    _check(_zero_ledger(psi, n_ranks, stage, int(grads_transient), C.byref(o)), "zero_ledger")
+    return o.as_dict()
+
+
+def zero_gather_buffer_bytes(layout: Layout, units_in_flight: int = 2) -> float:
+    b = f64()
+    _check(_zero_gather_buffer_bytes(layout.ptr, units_in_flight, C.byref(b)),
+           "zero_gather_buffer_bytes")
+    return b.value
+
+
+def zero_step_traffic(layout: Layout, rank: int, n_grads: int, grad_dtype: int,
+                      with_out: bool = True):
+    b, e = f64(), i64()
+    _check(_zero_step_traffic(layout.ptr, rank, n_grads, grad_dtype, int(with_out), C.byref(b),
+                              C.byref(e)), "zero_step_traffic")
+    return b.value, e.value
+
+
+def zero_gradnorm_traffic(layout: Layout, rank: int, n_grads: int, grad_dtype: int,
+                          with_g_out: bool = True):
+    b, e = f64(), i64()
+    _check(_zero_gradnorm_traffic(layout.ptr, rank, n_grads, grad_dtype, int(with_g_out),
+                                  C.byref(b), C.byref(e)), "zero_gradnorm_traffic")
+    return b.value, e.value
+
+
+def zero_strerror(status: int) -> str:
+    return _zero_strerror(status).decode()
+
+
+def zero_last_hip_error() -> str:
+    return _zero_last_hip_error().decode()
+
+
+def zero_abi_version() -> int:
+    return int(_zero_abi_version())
+
+
+def raw_library():
+    """The ctypes handle (for tests that call the C ABI with raw pointers)."""
+    return _lib

@@ -1,0 +1,92 @@
+"""Build libzero.so (the HIP kernels and the C ABI) in-tree with hipcc for gfx950.
+
+    python -m fsdp_sharded_optimizer_flat_amd._build
+
+Floating-point flags are part of the contract: -ffp-contract=off (no FMA
+contraction), IEEE binary32 denormals (-fno-gpu-flush-denormals-to-zero),
+correctly rounded division and square root, and no packed-fp32 instructions.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libzero.so")
+
+SOURCES = ["layout.cpp", "scalars.cpp", "ledger.cpp", "capi.cpp",
+           "step_kernels.hip", "norm_kernels.hip", "pack_kernels.hip"]
+
+ARCH = "gfx950"
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    "-ffp-contract=off", "-fno-fast-math",
+    "-fno-gpu-flush-denormals-to-zero", "-fhip-fp32-correctly-rounded-divide-sqrt",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-command-line-argument",
+    f"-I{INCLUDE}", f"-I{CSRC}",
+]
+
+
+def hipcc() -> str:
+    p = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(p):
+        raise RuntimeError("hipcc not found; the library needs ROCm's hipcc to build")
+    return p
+
+
+def _compile(src: str) -> str:
+    obj = os.path.join(BUILD, src + ".o")
+    cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{res.stderr}")
+    return obj
+
+
+def build(jobs: int | None = None) -> str:
+    """Compile every source and link libzero.so next to this file."""
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = jobs or min(len(SOURCES), os.cpu_count() or 4, 16)
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed:\n{res.stderr}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def device_ir(src: str = "step_kernels.hip") -> str:
+    """Device LLVM IR of one source, for the flag checks in the tests."""
+    os.makedirs(BUILD, exist_ok=True)
+    out = os.path.join(BUILD, src + ".ll")
+    cmd = [hipcc(), *FLAGS, "--cuda-device-only", "-S", "-emit-llvm",
+           os.path.join(CSRC, src), "-o", out]
+    subprocess.run(cmd, check=True, capture_output=True)
+    with open(out) as f:
+        return f.read()
+
+
+def device_asm(src: str = "step_kernels.hip") -> str:
+    """gfx950 assembly of one source (resource usage, instruction checks)."""
+    os.makedirs(BUILD, exist_ok=True)
+    out = os.path.join(BUILD, src + ".s")
+    cmd = [hipcc(), *FLAGS, "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", out]
+    subprocess.run(cmd, check=True, capture_output=True)
+    with open(out) as f:
+        return f.read()
+
+
+if __name__ == "__main__":
+    print(build())
+    sys.exit(0)

@@ -1,0 +1,433 @@
+// capi.cpp -- the exported entry points: argument validation, aliasing
+// checks, the per-piece launch loop of the step and the norm, the packer's
+// copies, and diagnostics.  Every check runs before any device work.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "zero_internal.h"
+
+namespace zero {
+
+namespace {
+thread_local std::string t_last_hip_error;
+
+bool dtype_ok(int32_t d) { return d == ZERO_F32 || d == ZERO_BF16; }
+bool index_ok(int32_t x) { return x == ZERO_GLOBAL || x == ZERO_LOCAL; }
+int dsize(int32_t d) { return d == ZERO_BF16 ? 2 : 4; }
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int64_t extent(const zero_layout *L, int32_t index)
+{
+    return index == ZERO_GLOBAL ? L->padded : L->shard;
+}
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+Range range_of(const void *p, int64_t elems, int elem_size)
+{
+    const uintptr_t lo = (uintptr_t)p;
+    return {lo, lo + (uintptr_t)elems * (uintptr_t)elem_size};
+}
+bool overlap(Range a, Range b)
+{
+    if (a.lo == a.hi || b.lo == b.hi)
+        return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+// The checks zero_step and zero_gradnorm share: selection, gradients and
+// divisor.
+zero_status check_grads(const zero_layout *L, int32_t rank, const void *const *grads,
+                        int32_t n_grads, int32_t grad_dtype, int32_t grad_index, float divisor)
+{
+    if (!layout_ok(L) || rank >= L->n_ranks || !dtype_ok(grad_dtype) || !index_ok(grad_index))
+        return ZERO_EINVAL;
+    if (!grads)
+        return ZERO_EINVAL;
+    if (n_grads < 1 || n_grads > ZERO_MAX_RANKS)
+        return ZERO_ERANGE;
+    if (!(divisor > 0.0f) || !std::isfinite(divisor))
+        return ZERO_EINVAL;
+    for (int q = 0; q < n_grads; ++q) {
+        if (!grads[q])
+            return ZERO_EINVAL;
+        if (!aligned(grads[q], (size_t)dsize(grad_dtype)))
+            return ZERO_EALIGN;
+    }
+    return ZERO_OK;
+}
+
+StepConsts make_consts(const zero_adamw_scalars *sc, float divisor)
+{
+    StepConsts c{};
+    if (sc) {
+        c.b1 = sc->b1;
+        c.b2 = sc->b2;
+        c.omb1 = sc->one_minus_b1;
+        c.omb2 = sc->one_minus_b2;
+        c.bc2 = sc->bc2;
+        c.eps = sc->eps;
+        c.step_size = sc->step_size;
+        c.decay = sc->decay;
+        c.clip = sc->clip_coef;
+    }
+    c.divisor = divisor;
+    float inv = 0.0f;
+    c.div_pow2 = is_pow2_float(divisor, &inv) ? 1 : 0;
+    c.inv_divisor = inv;
+    return c;
+}
+
+std::vector<const void *> offset_grads(const void *const *grads, int n, int64_t off, int gsize)
+{
+    std::vector<const void *> v((size_t)n);
+    for (int q = 0; q < n; ++q)
+        v[(size_t)q] = (const char *)grads[q] + off * gsize;
+    return v;
+}
+
+}  // namespace
+
+bool is_pow2_float(float x, float *inv)
+{
+    // Powers of two in [2^-126, 2^126], whose reciprocal is exact and normal.
+    if (!(x >= 0x1p-126f && x <= 0x1p126f))
+        return false;
+    int e = 0;
+    const float mant = std::frexp(x, &e);
+    if (mant != 0.5f)
+        return false;
+    *inv = std::ldexp(1.0f, 1 - e);
+    return true;
+}
+
+int device_cu_count()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return -1;
+    static std::mutex mu;
+    static std::vector<int> cache;
+    std::lock_guard<std::mutex> lock(mu);
+    if ((size_t)dev >= cache.size())
+        cache.resize((size_t)dev + 1, 0);
+    if (cache[(size_t)dev] == 0) {
+        int cu = 0;
+        if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return -1;
+        cache[(size_t)dev] = cu;
+    }
+    return cache[(size_t)dev];
+}
+
+zero_status hip_fail(int err, const char *where)
+{
+    char buf[256];
+    std::snprintf(buf, sizeof buf, "%s: %s (%d)", where,
+                  hipGetErrorString(static_cast<hipError_t>(err)), err);
+    t_last_hip_error = buf;
+    return ZERO_EHIP;
+}
+
+}  // namespace zero
+
+using namespace zero;
+
+extern "C" zero_status zero_step(const zero_layout *L, int32_t rank, const void *const *grads,
+                                 int32_t n_grads, int32_t grad_dtype, int32_t grad_index,
+                                 float divisor, float *master, float *exp_avg, float *exp_avg_sq,
+                                 int32_t state_index, uint16_t *out, int32_t out_index,
+                                 const zero_adamw_scalars *sc, void *stream)
+{
+    zero_status st = check_grads(L, rank, grads, n_grads, grad_dtype, grad_index, divisor);
+    if (st != ZERO_OK)
+        return st;
+    if (!index_ok(state_index) || !index_ok(out_index) || !master || !exp_avg || !exp_avg_sq ||
+        !sc || sc->t < 1)
+        return ZERO_EINVAL;
+    if (rank < 0 && (grad_index != ZERO_GLOBAL || state_index != ZERO_GLOBAL ||
+                     out_index != ZERO_GLOBAL))
+        return ZERO_EINVAL;
+    if (!aligned(master, 4) || !aligned(exp_avg, 4) || !aligned(exp_avg_sq, 4) ||
+        (out && !aligned(out, 2)))
+        return ZERO_EALIGN;
+
+    // Aliasing: gradients are read-only and may alias each other; nothing
+    // written may overlap a gradient or another written buffer.
+    const int gsize = dsize(grad_dtype);
+    const int64_t ge = extent(L, grad_index), se = extent(L, state_index),
+                  oe = extent(L, out_index);
+    const Range w = range_of(master, se, 4), m = range_of(exp_avg, se, 4),
+                v = range_of(exp_avg_sq, se, 4),
+                o = out ? range_of(out, oe, 2) : Range{0, 0};
+    if (overlap(w, m) || overlap(w, v) || overlap(m, v) || overlap(w, o) || overlap(m, o) ||
+        overlap(v, o))
+        return ZERO_EINVAL;
+    for (int q = 0; q < n_grads; ++q) {
+        const Range g = range_of(grads[q], ge, gsize);
+        if (overlap(g, w) || overlap(g, m) || overlap(g, v) || overlap(g, o))
+            return ZERO_EINVAL;
+    }
+
+    const StepConsts c = make_consts(sc, divisor);
+    Request rq{};
+    rq.layout = L;
+    rq.rank = rank;
+    rq.grads = grads;
+    rq.n_grads = n_grads;
+    rq.grad_dtype = grad_dtype;
+    rq.grad_index = grad_index;
+    rq.divisor = divisor;
+    rq.state_index = state_index;
+    rq.out_index = out_index;
+    rq.state_ptrs[0] = master;
+    rq.state_ptrs[1] = exp_avg;
+    rq.state_ptrs[2] = exp_avg_sq;
+    rq.n_state_ptrs = 3;
+    rq.out_ptr = out;
+    const std::vector<Piece> pieces =
+        build_pieces(build_segments(L, rank, grad_index, state_index, out_index), rq);
+    for (const Piece &pc : pieces) {
+        const std::vector<const void *> gp = offset_grads(grads, n_grads, pc.g_off, gsize);
+        const int err = launch_step_piece(pc, gp.data(), n_grads, grad_dtype, master + pc.s_off,
+                                          exp_avg + pc.s_off, exp_avg_sq + pc.s_off,
+                                          out ? out + pc.o_off : nullptr, c, stream);
+        if (err != hipSuccess)
+            return hip_fail(err, "zero_step launch");
+    }
+    return ZERO_OK;
+}
+
+extern "C" zero_status zero_gradnorm_workspace_bytes(const zero_layout *L, int32_t rank,
+                                                     size_t *bytes)
+{
+    if (!layout_ok(L) || !bytes || rank >= L->n_ranks)
+        return ZERO_EINVAL;
+    *bytes = (size_t)(norm_partials_bound(L, rank) + 1) * sizeof(double);
+    return ZERO_OK;
+}
+
+extern "C" zero_status zero_gradnorm(const zero_layout *L, int32_t rank,
+                                     const void *const *grads, int32_t n_grads,
+                                     int32_t grad_dtype, int32_t grad_index, float divisor,
+                                     float *g_out, int32_t g_index, void *workspace,
+                                     size_t workspace_bytes, double *sumsq, void *stream)
+{
+    zero_status st = check_grads(L, rank, grads, n_grads, grad_dtype, grad_index, divisor);
+    if (st != ZERO_OK)
+        return st;
+    if (!sumsq || !workspace || !index_ok(g_index))
+        return ZERO_EINVAL;
+    if (rank < 0 && (grad_index != ZERO_GLOBAL || g_index != ZERO_GLOBAL))
+        return ZERO_EINVAL;
+    if (!aligned(workspace, 8) || (g_out && !aligned(g_out, 4)))
+        return ZERO_EALIGN;
+    size_t need = 0;
+    zero_gradnorm_workspace_bytes(L, rank, &need);
+    if (workspace_bytes < need)
+        return ZERO_ENOSPC;
+    const int gsize = dsize(grad_dtype);
+    const Range ws = range_of(workspace, (int64_t)need, 1);
+    const Range go = g_out ? range_of(g_out, extent(L, g_index), 4) : Range{0, 0};
+    if (overlap(ws, go))
+        return ZERO_EINVAL;
+    for (int q = 0; q < n_grads; ++q) {
+        const Range g = range_of(grads[q], extent(L, grad_index), gsize);
+        if (overlap(g, ws) || overlap(g, go))
+            return ZERO_EINVAL;
+    }
+
+    const StepConsts c = make_consts(nullptr, divisor);
+    Request rq{};
+    rq.layout = L;
+    rq.rank = rank;
+    rq.grads = grads;
+    rq.n_grads = n_grads;
+    rq.grad_dtype = grad_dtype;
+    rq.grad_index = grad_index;
+    rq.divisor = divisor;
+    rq.state_index = g_index;
+    rq.out_index = ZERO_LOCAL;
+    rq.state_ptrs[0] = g_out;
+    rq.n_state_ptrs = g_out ? 1 : 0;
+    rq.out_ptr = nullptr;
+    const std::vector<Piece> pieces =
+        build_pieces(build_segments(L, rank, grad_index, g_index, ZERO_LOCAL), rq);
+    double *partials = static_cast<double *>(workspace);
+    double *result = partials + norm_partials_bound(L, rank);
+    int total = 0;
+    for (const Piece &pc : pieces) {
+        const std::vector<const void *> gp = offset_grads(grads, n_grads, pc.g_off, gsize);
+        int np = 0;
+        const int err = launch_norm_piece(pc, gp.data(), n_grads, grad_dtype,
+                                          g_out ? g_out + pc.s_off : nullptr, c, partials + total,
+                                          &np, stream);
+        if (err != hipSuccess)
+            return hip_fail(err, "zero_gradnorm stage 1");
+        total += np;
+    }
+    if (total == 0) {
+        *sumsq = 0.0;
+        return ZERO_OK;
+    }
+    int err = launch_norm_final(partials, total, result, stream);
+    if (err != hipSuccess)
+        return hip_fail(err, "zero_gradnorm stage 2");
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    double host = 0.0;
+    err = hipMemcpyAsync(&host, result, sizeof(double), hipMemcpyDeviceToHost, hs);
+    if (err != hipSuccess)
+        return hip_fail(err, "zero_gradnorm readback");
+    err = hipStreamSynchronize(hs);
+    if (err != hipSuccess)
+        return hip_fail(err, "zero_gradnorm synchronize");
+    *sumsq = host;
+    return ZERO_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Packer copies.
+// ---------------------------------------------------------------------------
+
+namespace {
+
+struct ParamPlace {
+    int64_t start;  // global index of the parameter's first element
+    int64_t numel;
+};
+
+// Validate the parameter list against the layout and place every parameter
+// in the flat buffer (in list order within each unit).
+zero_status place_params(const zero_layout *L, int32_t n_params, const void *const *ptrs,
+                         const int64_t *numel, const int32_t *unit, int32_t dtype,
+                         std::vector<ParamPlace> &place)
+{
+    if (n_params < 0 || (n_params > 0 && (!ptrs || !numel || !unit)) || !dtype_ok(dtype))
+        return ZERO_EINVAL;
+    std::vector<int64_t> fill((size_t)L->n_units, 0);
+    place.resize((size_t)n_params);
+    for (int32_t p = 0; p < n_params; ++p) {
+        if (unit[p] < 0 || unit[p] >= L->n_units || numel[p] < 0 || (numel[p] > 0 && !ptrs[p]))
+            return ZERO_EINVAL;
+        if (ptrs[p] && !aligned(ptrs[p], (size_t)dsize(dtype)))
+            return ZERO_EALIGN;
+        const zero_unit &x = L->unit[unit[p]];
+        place[(size_t)p] = {x.offset + fill[(size_t)unit[p]], numel[p]};
+        fill[(size_t)unit[p]] += numel[p];
+        if (fill[(size_t)unit[p]] > x.numel)
+            return ZERO_EINVAL;
+    }
+    for (int32_t u = 0; u < L->n_units; ++u)
+        if (fill[(size_t)u] != L->unit[u].numel)
+            return ZERO_EINVAL;
+    return ZERO_OK;
+}
+
+// Where global range [lo, hi) lands in the flat buffer of the copy: the
+// global index itself (rank < 0) or rank r's local index.  Returns false if
+// none of it belongs to rank r; otherwise clips [lo, hi) to rank r's slice.
+bool to_flat(const zero_layout *L, int32_t rank, int32_t u, int64_t &lo, int64_t &hi,
+             int64_t &flat_lo)
+{
+    const zero_unit &x = L->unit[u];
+    if (rank < 0) {
+        flat_lo = lo;
+        return lo < hi;
+    }
+    const int64_t a = x.offset + (int64_t)rank * x.shard, b = a + x.shard;
+    lo = lo > a ? lo : a;
+    hi = hi < b ? hi : b;
+    if (lo >= hi)
+        return false;
+    flat_lo = x.local_offset + (lo - a);
+    return true;
+}
+
+zero_status pack_like(const zero_layout *L, int32_t rank, int32_t n_params,
+                      const void *const *params, const int64_t *numel, const int32_t *unit,
+                      int32_t param_dtype, void *flat, int32_t flat_dtype, void *stream, bool pack)
+{
+    if (!layout_ok(L) || rank >= L->n_ranks || !flat || !dtype_ok(flat_dtype))
+        return ZERO_EINVAL;
+    if (!aligned(flat, (size_t)dsize(flat_dtype)))
+        return ZERO_EALIGN;
+    std::vector<ParamPlace> place;
+    zero_status st = place_params(L, n_params, params, numel, unit, param_dtype, place);
+    if (st != ZERO_OK)
+        return st;
+    const Range fr = range_of(flat, rank < 0 ? L->padded : L->shard, dsize(flat_dtype));
+    for (int32_t p = 0; p < n_params; ++p)
+        if (params[p] && overlap(fr, range_of(params[p], numel[p], dsize(param_dtype))))
+            return ZERO_EINVAL;
+    char *fb = static_cast<char *>(flat);
+    const int fs = dsize(flat_dtype), ps = dsize(param_dtype);
+    for (int32_t p = 0; p < n_params; ++p) {
+        int64_t lo = place[(size_t)p].start, hi = lo + place[(size_t)p].numel, flo = 0;
+        if (!to_flat(L, rank, unit[p], lo, hi, flo))
+            continue;
+        char *pp = (char *)params[p] + (lo - place[(size_t)p].start) * ps;
+        int err = pack ? launch_convert(pp, param_dtype, fb + flo * fs, flat_dtype, hi - lo, stream)
+                       : launch_convert(fb + flo * fs, flat_dtype, pp, param_dtype, hi - lo, stream);
+        if (err != hipSuccess)
+            return hip_fail(err, pack ? "zero_pack_copy" : "zero_unpack_copy");
+    }
+    if (pack) {  // zero the padding of every unit
+        for (int32_t u = 0; u < L->n_units; ++u) {
+            const zero_unit &x = L->unit[u];
+            int64_t lo = x.offset + x.numel, hi = x.offset + x.padded, flo = 0;
+            if (!to_flat(L, rank, u, lo, hi, flo))
+                continue;
+            int err = launch_fill_zero(fb + flo * fs, flat_dtype, hi - lo, stream);
+            if (err != hipSuccess)
+                return hip_fail(err, "zero_pack_copy padding");
+        }
+    }
+    return ZERO_OK;
+}
+
+}  // namespace
+
+extern "C" zero_status zero_pack_copy(const zero_layout *L, int32_t rank, int32_t n_params,
+                                      const void *const *params, const int64_t *src_numel,
+                                      const int32_t *src_unit, int32_t src_dtype, void *dst,
+                                      int32_t dst_dtype, void *stream)
+{
+    return pack_like(L, rank, n_params, params, src_numel, src_unit, src_dtype, dst, dst_dtype,
+                     stream, true);
+}
+
+extern "C" zero_status zero_unpack_copy(const zero_layout *L, int32_t rank, const void *src,
+                                        int32_t src_dtype, int32_t n_params,
+                                        void *const *params, const int64_t *dst_numel,
+                                        const int32_t *dst_unit, int32_t dst_dtype, void *stream)
+{
+    return pack_like(L, rank, n_params, (const void *const *)params, dst_numel, dst_unit,
+                     dst_dtype, const_cast<void *>(src), src_dtype, stream, false);
+}
+
+// ---------------------------------------------------------------------------
+// Diagnostics.
+// ---------------------------------------------------------------------------
+
+extern "C" const char *zero_strerror(zero_status s)
+{
+    switch (s) {
+    case ZERO_OK: return "ok";
+    case ZERO_EINVAL: return "invalid argument";
+    case ZERO_ERANGE: return "size or rank count out of range";
+    case ZERO_EALIGN: return "pointer not aligned to its element size";
+    case ZERO_ENOSPC: return "caller buffer too small";
+    case ZERO_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+extern "C" const char *zero_last_hip_error(void) { return t_last_hip_error.c_str(); }
+
+extern "C" int32_t zero_abi_version(void) { return ZERO_ABI_VERSION; }

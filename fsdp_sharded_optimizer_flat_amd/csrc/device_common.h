@@ -1,0 +1,214 @@
+// device_common.h -- device helpers shared by the step and norm kernels:
+// the rank-ordered gradient sum over a chunk, the average, the AdamW element
+// update and the bf16 packing.  gfx950 only.
+//
+// Bit-exactness rests on three things the build guarantees: no FMA
+// contraction (-ffp-contract=off), IEEE binary32 denormals, and correctly
+// rounded '/' and sqrtf (HIP's defaults for gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "zero_internal.h"
+
+namespace zero {
+namespace dev {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Gradient base pointers, passed by value in the kernel arguments so the
+// rank loop reads them with scalar loads.  CAP is the compile-time rank
+// count, or ZERO_MAX_RANKS for the runtime-count kernels.
+template <int CAP>
+struct GradSet {
+    const void *p[CAP];
+};
+
+// Streaming loads / stores: every byte is touched once per step, so they
+// bypass the caches' reuse policy.
+template <typename T>
+__device__ __forceinline__ T ld_stream(const T *p)
+{
+    return __builtin_nontemporal_load(p);
+}
+template <typename T>
+__device__ __forceinline__ void st_stream(T v, T *p)
+{
+    __builtin_nontemporal_store(v, p);
+}
+
+// binary32 value of the low / high bf16 of a packed pair (exact widening).
+__device__ __forceinline__ float bf_lo(unsigned x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf_hi(unsigned x) { return __uint_as_float(x & 0xffff0000u); }
+
+// Unpack one 16-byte load of 8 bf16 gradients; FIRST: s = G, else s = s + G.
+template <bool FIRST>
+__device__ __forceinline__ void acc_bf16x8(float s[8], u32x4 r)
+{
+    const float e[8] = {bf_lo(r.x), bf_hi(r.x), bf_lo(r.y), bf_hi(r.y),
+                        bf_lo(r.z), bf_hi(r.z), bf_lo(r.w), bf_hi(r.w)};
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        s[k] = FIRST ? e[k] : s[k] + e[k];
+}
+
+template <bool FIRST>
+__device__ __forceinline__ void acc_f32x8(float s[8], f32x4 a, f32x4 b)
+{
+    const float e[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        s[k] = FIRST ? e[k] : s[k] + e[k];
+}
+
+// Loads of chunk i (8 elements) of gradient buffer q.
+struct Bf16Chunk {
+    u32x4 r;
+    __device__ __forceinline__ void load(const void *base, int64_t i)
+    {
+        r = ld_stream(reinterpret_cast<const u32x4 *>(base) + i);
+    }
+    template <bool FIRST>
+    __device__ __forceinline__ void add_to(float s[8]) const { acc_bf16x8<FIRST>(s, r); }
+};
+struct F32Chunk {
+    f32x4 a, b;
+    __device__ __forceinline__ void load(const void *base, int64_t i)
+    {
+        const f32x4 *p = reinterpret_cast<const f32x4 *>(base) + 2 * i;
+        a = ld_stream(p);
+        b = ld_stream(p + 1);
+    }
+    template <bool FIRST>
+    __device__ __forceinline__ void add_to(float s[8]) const { acc_f32x8<FIRST>(s, a, b); }
+};
+
+// s[k] = G_0[k] + G_1[k] + ... + G_{n-1}[k], left to right in rank order.
+// Loads are issued in batches ahead of the adds; the adds keep rank order.
+template <int NR, int CAP, typename CH>
+__device__ __forceinline__ void rank_sum(const GradSet<CAP> &gs, int n, int64_t i, float s[8])
+{
+    if constexpr (NR > 0) {
+        constexpr int B = NR < 16 ? NR : 16;
+#pragma unroll
+        for (int q0 = 0; q0 < NR; q0 += B) {
+            CH c[B];
+#pragma unroll
+            for (int b = 0; b < B; ++b)
+                c[b].load(gs.p[q0 + b], i);
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                if (q0 + b == 0)
+                    c[b].template add_to<true>(s);
+                else
+                    c[b].template add_to<false>(s);
+            }
+        }
+    } else {
+        {
+            CH c0;
+            c0.load(gs.p[0], i);
+            c0.template add_to<true>(s);
+        }
+        int q = 1;
+        for (; q + 8 <= n; q += 8) {
+            CH c[8];
+#pragma unroll
+            for (int b = 0; b < 8; ++b)
+                c[b].load(gs.p[q + b], i);
+#pragma unroll
+            for (int b = 0; b < 8; ++b)
+                c[b].template add_to<false>(s);
+        }
+        for (; q < n; ++q) {
+            CH c;
+            c.load(gs.p[q], i);
+            c.template add_to<false>(s);
+        }
+    }
+}
+
+// One element's gradient, scalar path.
+template <typename GT>
+__device__ __forceinline__ float grad_at(const void *base, int64_t i);
+template <>
+__device__ __forceinline__ float grad_at<uint16_t>(const void *base, int64_t i)
+{
+    return __uint_as_float((unsigned)reinterpret_cast<const uint16_t *>(base)[i] << 16);
+}
+template <>
+__device__ __forceinline__ float grad_at<float>(const void *base, int64_t i)
+{
+    return reinterpret_cast<const float *>(base)[i];
+}
+
+// The average s / divisor.  For a power-of-two divisor, s * (1/divisor) is
+// the same correctly rounded value (both round the same real number), and
+// costs one multiply instead of a division sequence.
+template <bool POW2>
+__device__ __forceinline__ float average(float s, const StepConsts &c)
+{
+    if constexpr (POW2)
+        return s * c.inv_divisor;
+    else
+        return s / c.divisor;
+}
+
+// AdamW on one element ("ZeRO and FSDP sharding", Code), one rounding per
+// operation in this order:
+//   m = b1*m + (1-b1)*g
+//   v = b2*v + ((1-b2)*g)*g
+//   w = w*decay - (step_size*m) / (sqrt(v)/bc2 + eps)
+__device__ __forceinline__ void adamw(float g, float &w, float &m, float &v, const StepConsts &c)
+{
+    const float m_dec = c.b1 * m;
+    const float m_inc = c.omb1 * g;
+    m = m_dec + m_inc;
+    const float v_dec = c.b2 * v;
+    const float v_inc = (c.omb2 * g) * g;
+    v = v_dec + v_inc;
+    const float den = sqrtf(v) / c.bc2 + c.eps;
+    const float upd = (c.step_size * m) / den;
+    const float w_dec = w * c.decay;
+    w = w_dec - upd;
+}
+
+// Round-to-nearest-even bf16 of a pair, packed low-first (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi)
+{
+    const f32x2 f = {lo, hi};
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(f, bf16x2));
+}
+
+__device__ __forceinline__ uint16_t to_bf16(float x)
+{
+    return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+// Sum of a double over a 256-thread workgroup in a fixed order; valid in
+// thread 0.  Wave64 butterfly, then the four wave totals in wave order.
+__device__ __forceinline__ double block_sum(double x)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        x = x + __shfl_xor(x, off, 64);
+    __shared__ double wave_tot[kBlock / 64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0)
+        wave_tot[wave] = x;
+    __syncthreads();
+    double t = 0.0;
+    if (threadIdx.x == 0) {
+        t = wave_tot[0];
+#pragma unroll
+        for (int w = 1; w < kBlock / 64; ++w)
+            t = t + wave_tot[w];
+    }
+    return t;
+}
+
+}  // namespace dev
+}  // namespace zero

@@ -1,0 +1,96 @@
+// zero_internal.h -- declarations shared by the library's translation units
+// (host plan builder, launchers, error state).  Not part of the public ABI.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <vector>
+
+#include "zero.h"
+
+namespace zero {
+
+// Elements per vector chunk: 8 bf16 gradients are one 16-byte load, 8 fp32
+// state values are two.
+constexpr int kChunk = 8;
+constexpr int kBlock = 256;          // threads per workgroup (4 wave64s)
+constexpr int kNormMaxBlocks = 1024; // fixed partition of the norm's first stage
+
+// One contiguous run of elements whose gradient, state and output indices all
+// advance together.  Offsets are element offsets into the respective buffers.
+struct Segment {
+    int64_t g_off, s_off, o_off, len;
+};
+
+// A piece of a segment handed to one kernel launch: either a vector body
+// (len is a multiple of kChunk and every buffer is 16-byte aligned at its
+// start) or a scalar piece (any alignment).
+struct Piece {
+    int64_t g_off, s_off, o_off, len;
+    bool vec;
+};
+
+// Validated step / norm request, pointers already checked.
+struct Request {
+    const zero_layout *layout;
+    int32_t rank;
+    const void *const *grads;
+    int32_t n_grads;
+    int32_t grad_dtype, grad_index;
+    float divisor;
+    int32_t state_index;  // for the norm: the g_out index space
+    int32_t out_index;
+    // base pointers used for alignment decisions (may be null)
+    const void *state_ptrs[3];
+    int n_state_ptrs;
+    const void *out_ptr;
+};
+
+// Segments of the elements a (layout, rank, index spaces) selection touches,
+// with contiguous neighbours merged.
+std::vector<Segment> build_segments(const zero_layout *L, int32_t rank, int32_t grad_index,
+                                    int32_t state_index, int32_t out_index);
+
+// Split segments into vector bodies and scalar heads / tails, given the
+// actual buffer addresses (every gradient, every fp32 state buffer, output).
+std::vector<Piece> build_pieces(const std::vector<Segment> &segs, const Request &rq);
+
+// Number of elements the selection processes.
+int64_t selected_elements(const zero_layout *L, int32_t rank);
+
+// Upper bound on the norm's first-stage partial count for a selection.
+int64_t norm_partials_bound(const zero_layout *L, int32_t rank);
+
+// Layout sanity (magic, counts, internal consistency of the totals).
+bool layout_ok(const zero_layout *L);
+
+// Compute units of the current device (cached per device).  <= 0 on error.
+int device_cu_count();
+
+// Record a HIP error code for zero_last_hip_error(); returns ZERO_EHIP.
+zero_status hip_fail(int hip_error, const char *where);
+
+// Uniform per-launch constants of the fused step.
+struct StepConsts {
+    float b1, b2, omb1, omb2, bc2, eps, step_size, decay, clip;
+    float divisor, inv_divisor;
+    int32_t div_pow2;  // 1: multiply by inv_divisor (exactly the same value)
+};
+
+bool is_pow2_float(float x, float *inv);
+
+// Launchers (defined in the .hip files).  Pointers are already offset to the
+// piece's first element.  Return a hipError_t value.
+int launch_step_piece(const Piece &pc, const void *const *grads, int n_grads, int grad_dtype,
+                      float *w, float *m, float *v, uint16_t *out, const StepConsts &c,
+                      void *stream);
+int launch_norm_piece(const Piece &pc, const void *const *grads, int n_grads, int grad_dtype,
+                      float *g_out, const StepConsts &c, double *partials, int *n_partials,
+                      void *stream);
+int norm_piece_blocks(const Piece &pc);
+int launch_norm_final(const double *partials, int n_partials, double *result, void *stream);
+int launch_convert(const void *src, int src_dtype, void *dst, int dst_dtype, int64_t n,
+                   void *stream);
+int launch_fill_zero(void *dst, int dtype, int64_t n, void *stream);
+
+}  // namespace zero

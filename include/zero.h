@@ -1,0 +1,319 @@
+/*
+ * zero.h -- C ABI of the ZeRO sharded optimizer step for AMD Instinct MI355X
+ * (gfx950), built as libzero.so.
+ *
+ * The library runs one GPU's share of the data-parallel optimizer step of
+ * ZeRO stages 1-3 / FSDP, with N ranks' gradient buffers resident in that
+ * GPU's memory: for every element of a rank's shard it sums the N ranks'
+ * gradients in rank order (the reduction half of reduce-scatter), divides by
+ * N, optionally scales by a global-norm clip coefficient, runs AdamW on the
+ * fp32 master / first-moment / second-moment slice and writes the bf16 copy of
+ * the updated master into its all-gather output slot.
+ *
+ * Pages cited below:
+ *   [p1] "ZeRO and FSDP sharding" (tirogla.com): How it works; Code;
+ *        Implementation notes; Pitfalls.
+ *   [p3] "ZeRO: Three Ledgers, Zero Redundancy" (dominator-index.github.io):
+ *        sections 1, 2 and 4.
+ *   [p4] "Learn: ZeRO & FSDP" (gunjandhanuka.github.io): sections 3 and 4.
+ *
+ * Conventions for every entry point:
+ *   - Returns zero_status: ZERO_OK (0) or a negative error code.  Nothing
+ *     prints, throws or exits.
+ *   - Validation happens before any device work: on an error return before a
+ *     launch, no device memory has been written.
+ *   - Device pointers are plain HIP device addresses (e.g. from hipMalloc or a
+ *     torch tensor's data_ptr()).  The caller owns every buffer; the library
+ *     allocates no device memory and keeps no pointer after a call returns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls marked "async" only enqueue work on it.
+ *   - The library is reentrant; its only global state is a per-device cache
+ *     of the compute-unit count and a thread-local last-HIP-error string.
+ *
+ * Floating point: the device code is compiled without FMA contraction, with
+ * IEEE binary32 denormals and correctly rounded division and square root, so
+ * that every element's result is the same bit pattern as a serial binary32
+ * evaluation of the same operations in the same order.
+ */
+#ifndef ZERO_H
+#define ZERO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ZERO_ABI_VERSION 1
+
+typedef int32_t zero_status;
+#define ZERO_OK 0
+#define ZERO_EINVAL (-1)  /* bad argument: NULL, negative size, bad enum, aliasing, N < 1 */
+#define ZERO_ERANGE (-2)  /* a size or index overflows, or N > ZERO_MAX_RANKS */
+#define ZERO_EALIGN (-3)  /* a pointer is not aligned to its element size */
+#define ZERO_ENOSPC (-4)  /* a caller-provided buffer is too small */
+#define ZERO_EHIP (-5)    /* a HIP runtime call or kernel launch failed; see zero_last_hip_error() */
+
+#define ZERO_MAX_RANKS 256   /* largest N accepted by zero_step / zero_gradnorm */
+#define ZERO_MAX_UNITS (1 << 20)
+
+/* Element types. */
+#define ZERO_F32 0
+#define ZERO_BF16 1
+
+/* Index spaces of a buffer (see the layout below).
+ *   ZERO_GLOBAL: indexed by the global index j of the padded flat buffer
+ *                (length P^).  For gradients this is a rank's full gradient;
+ *                for the bf16 output it is the all-gather output buffer, and
+ *                rank r's values land in rank r's slots.
+ *   ZERO_LOCAL:  indexed by the local index k of one rank's shard (length S).
+ *                For gradients this is the chunk every rank sends to this rank
+ *                in the reduce-scatter; for the output it is the bf16 shard
+ *                ZeRO-3 keeps. */
+#define ZERO_GLOBAL 0
+#define ZERO_LOCAL 1
+
+/* ------------------------------------------------------------------------
+ * Layout -- [p1 How it works]: each unit's parameters are flattened into one
+ * buffer padded to a multiple of N and rank r owns slice r; [p1 Pitfalls]:
+ * the flat numel must divide by N or the last rank's slice is corrupted.
+ *
+ * For unit u with numel P_u (the sum of its parameters' numels, in the
+ * caller's order):
+ *   padded_u  = ceil(P_u / N) * N          shard_u = padded_u / N
+ *   offset_u  = sum of padded_{u'} over u' < u   (start in the flat buffer)
+ *   local_u   = sum of shard_{u'}  over u' < u   (start inside a rank's shard)
+ * Rank r's slice of unit u is global [offset_u + r*shard_u, +shard_u); its
+ * local index k in [local_u, local_u + shard_u) maps to global index
+ * j = offset_u + r*shard_u + (k - local_u).  P^ = sum padded_u, S = sum shard_u.
+ * ------------------------------------------------------------------------ */
+
+typedef struct zero_unit {
+    int64_t numel;         /* P_u */
+    int64_t padded;        /* padded_u */
+    int64_t shard;         /* shard_u */
+    int64_t offset;        /* offset_u */
+    int64_t local_offset;  /* local_u */
+} zero_unit;
+
+typedef struct zero_layout {
+    uint32_t magic;        /* ZERO_LAYOUT_MAGIC once filled by zero_pack */
+    int32_t n_ranks;       /* N */
+    int32_t n_units;       /* U */
+    int32_t reserved;
+    int64_t numel;         /* sum P_u */
+    int64_t padded;        /* P^ */
+    int64_t shard;         /* S */
+    zero_unit unit[];      /* U entries */
+} zero_layout;
+
+#define ZERO_LAYOUT_MAGIC 0x5a45524fu /* "ZERO" */
+
+/* Bytes a layout of n_units units occupies. */
+size_t zero_layout_bytes(int32_t n_units);
+
+/* Fill a caller-owned layout.  Host only.
+ *   n_ranks    N >= 1 (any value up to 2^31-1; zero_step itself caps N).
+ *   unit_numel U non-negative numels (host array).
+ *   layout     caller memory of layout_bytes bytes, or NULL to query the size.
+ *   bytes_needed (may be NULL) receives zero_layout_bytes(n_units).
+ * Errors: EINVAL (bad N, U < 0, negative numel, NULL unit_numel with U > 0),
+ *         ERANGE (a padded size overflows int64), ENOSPC (layout_bytes short;
+ *         bytes_needed is still filled). */
+zero_status zero_pack(int32_t n_ranks, int32_t n_units, const int64_t *unit_numel,
+                      zero_layout *layout, size_t layout_bytes, size_t *bytes_needed);
+
+/* Index maps of the layout (host only).  zero_global_index: global j of rank
+ * r's local k (EINVAL unless 0 <= r < N and 0 <= k < S).  zero_owner: owning
+ * rank and local index of global j (EINVAL unless 0 <= j < P^). */
+zero_status zero_global_index(const zero_layout *layout, int32_t rank, int64_t k, int64_t *j);
+zero_status zero_owner(const zero_layout *layout, int64_t j, int32_t *rank, int64_t *k);
+
+/* Pack parameters into a flat buffer on the device (async) -- [p1 How it
+ * works] flattening, with the padding zero-filled.
+ *   params: n_params device pointers; param p has src_numel[p] elements of
+ *     src_dtype and belongs to unit src_unit[p].  Within a unit, parameters
+ *     are laid out in the order they appear in this list; the numels of each
+ *     unit's parameters must add up to that unit's numel.
+ *   rank < 0: dst is the whole padded flat buffer (ZERO_GLOBAL, P^ elements).
+ *   rank r:   dst is rank r's shard (ZERO_LOCAL, S elements): only the
+ *             elements rank r owns are copied.
+ *   dst_dtype: ZERO_F32 or ZERO_BF16 (F32 -> BF16 rounds to nearest even;
+ *     BF16 -> F32 widens exactly).
+ * Errors: EINVAL (bad arguments, unit numels do not add up, dst overlaps a
+ *   source), EALIGN, EHIP. */
+zero_status zero_pack_copy(const zero_layout *layout, int32_t rank, int32_t n_params,
+                           const void *const *params, const int64_t *src_numel,
+                           const int32_t *src_unit, int32_t src_dtype,
+                           void *dst, int32_t dst_dtype, void *stream);
+
+/* Inverse of zero_pack_copy: copy each parameter's elements out of a flat
+ * buffer (rank < 0: GLOBAL P^ buffer; rank r: rank r's LOCAL shard, only the
+ * elements rank r owns are written).  Async. */
+zero_status zero_unpack_copy(const zero_layout *layout, int32_t rank, const void *src,
+                             int32_t src_dtype, int32_t n_params, void *const *params,
+                             const int64_t *dst_numel, const int32_t *dst_unit,
+                             int32_t dst_dtype, void *stream);
+
+/* ------------------------------------------------------------------------
+ * AdamW step scalars -- [p1 Code]: AdamW with b1, b2, eps, decoupled weight
+ * decay wd, a step counter t that is 1 at the first step, and bias
+ * corrections 1 - b1^t and sqrt(1 - b2^t).
+ *
+ * Computed on the host in binary32, one rounding per operation:
+ *   one_minus_b1 = 1 - b1, one_minus_b2 = 1 - b2 (from the binary32 betas);
+ *   pow1 = b1^t, pow2 = b2^t as running products (p_t = p_{t-1} * b, p_0 = 1);
+ *   bc1 = 1 - pow1;  bc2 = sqrtf(1 - pow2);
+ *   step_size = lr / bc1;  decay = 1 - lr * wd.
+ * clip_coef multiplies the averaged gradient (1 = no clipping).
+ * ------------------------------------------------------------------------ */
+
+typedef struct zero_adamw_scalars {
+    int32_t t;
+    float lr, b1, b2, eps, wd;
+    float one_minus_b1, one_minus_b2;
+    float pow1, pow2;
+    float bc1, bc2;
+    float step_size;
+    float decay;
+    float clip_coef;
+} zero_adamw_scalars;
+
+/* Scalars of step t >= 1 (O(t) host work).  EINVAL: t < 1, NULL out, or a
+ * hyperparameter that is NaN. */
+zero_status zero_adamw_scalars_for(int32_t t, float lr, float b1, float b2, float eps, float wd,
+                                   float clip_coef, zero_adamw_scalars *out);
+
+/* Scalars of step prev->t + 1 from those of step prev->t (O(1); equal to
+ * zero_adamw_scalars_for(prev->t + 1, ...)).  clip_coef is copied. */
+zero_status zero_adamw_scalars_next(const zero_adamw_scalars *prev, zero_adamw_scalars *out);
+
+/* ------------------------------------------------------------------------
+ * The fused step -- [p1 Code] reduce-scatter, divide by N, AdamW on the
+ * local slice, all-gather; [p1 How it works] the updated fp32 master is
+ * cast to a bf16 copy for the gather; [p3 section 1] the update is
+ * elementwise, so any partition of the elements gives the same result.
+ *
+ * For every processed element, with G_q the binary32 value of gradient q:
+ *   s = G_0 + G_1 + ... + G_{n_grads-1}   (left to right, binary32)
+ *   g = s / divisor  (a multiply by 1/divisor when divisor is a power of two,
+ *                     which is the same correctly rounded value)
+ *   g = g * clip_coef
+ *   m = b1*m + (1-b1)*g
+ *   v = b2*v + ((1-b2)*g)*g
+ *   w = w*decay - (step_size*m) / (sqrt(v)/bc2 + eps)
+ *   out = bf16(w), rounded to nearest even
+ *
+ *   rank < 0:  every shard of every unit -- all N simulated ranks' steps at
+ *              once.  grads, state and out must all be ZERO_GLOBAL.
+ *   rank r:    rank r's shard only (S elements).
+ *   grads:     host array of n_grads device pointers (1 <= n_grads <=
+ *              ZERO_MAX_RANKS), summed in array order; each of grad_dtype and
+ *              in the grad_index space.  n_grads is normally N; pass 1 with
+ *              divisor 1 for a gradient that is already reduced.
+ *   divisor:   > 0 and finite (normally N).
+ *   master, exp_avg, exp_avg_sq: fp32 state in the state_index space, updated
+ *              in place.
+ *   out:       bf16 bits in the out_index space, or NULL.
+ *   sc:        the step's scalars.
+ * Async on `stream`.  Errors: EINVAL (NULL, bad enum, rank >= N, rank < 0 with
+ *   a LOCAL index, divisor not > 0, gradient range overlapping state or out,
+ *   state/out ranges overlapping each other), ERANGE (n_grads out of range),
+ *   EALIGN (pointer not aligned to its element size), EHIP (launch failed). */
+zero_status zero_step(const zero_layout *layout, int32_t rank,
+                      const void *const *grads, int32_t n_grads, int32_t grad_dtype,
+                      int32_t grad_index, float divisor,
+                      float *master, float *exp_avg, float *exp_avg_sq, int32_t state_index,
+                      uint16_t *out, int32_t out_index,
+                      const zero_adamw_scalars *sc, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Global gradient norm -- [p1 Implementation notes]: clipping needs the
+ * global norm, the sum of the shards' squared norms (all-reduced across
+ * ranks); [p3 section 2] a norm is a decomposable sum of squares.
+ *
+ * Sum of squares, accumulated in binary64, of g = (rank-ordered binary32 sum
+ * of the gradients) / divisor over the processed elements (same selection and
+ * index rules as zero_step).  Two kernels: each workgroup of the first reduces
+ * a fixed grid-stride partition to one binary64 partial; a single workgroup of
+ * the second sums the partials in a fixed order.  The partition depends only
+ * on the layout and rank, so the result is bitwise reproducible.
+ *   g_out:      if not NULL, g is also written (fp32, g_index space), so the
+ *               step can read one reduced gradient instead of N.
+ *   workspace:  caller device memory of at least zero_gradnorm_workspace_bytes.
+ *   sumsq:      host pointer; receives the binary64 sum.
+ * Synchronizes `stream` (the host needs the value to form the clip
+ * coefficient).  Errors as zero_step, plus ENOSPC for a short workspace. */
+zero_status zero_gradnorm_workspace_bytes(const zero_layout *layout, int32_t rank,
+                                          size_t *bytes);
+zero_status zero_gradnorm(const zero_layout *layout, int32_t rank,
+                          const void *const *grads, int32_t n_grads, int32_t grad_dtype,
+                          int32_t grad_index, float divisor,
+                          float *g_out, int32_t g_index,
+                          void *workspace, size_t workspace_bytes,
+                          double *sumsq, void *stream);
+
+/* Clip coefficient from a sum of squares (host): norm = sqrt(sumsq) and
+ * coef = min(1, max_norm / (norm + 1e-6)) in binary64, rounded once to
+ * binary32 -- the convention of the clip_grad_norm_ routine [p1
+ * Implementation notes] names.  EINVAL: sumsq < 0 or NaN, max_norm <= 0. */
+zero_status zero_clip_coef(double sumsq, double max_norm, float *coef);
+
+/* ------------------------------------------------------------------------
+ * Ledger -- [p4 section 3]: model state is (2 + 2 + K) psi bytes with K = 12
+ * (bf16 params 2, bf16 grads 2, fp32 master + m + v 12); [p4 section 4]:
+ * stage 1 shards the optimizer state, stage 2 also the gradients, stage 3
+ * also the parameters; communication per step is 2 psi elements for stages
+ * 0-2 and 3 psi for stage 3, times (N-1)/N for ring collectives [p3 section
+ * 2]; [p3 section 4]: with bucketed reduce-scatter the gradients are
+ * transient and drop out of the resident ledger; [p1 Complexity and
+ * constants]: ZeRO-3 needs about two units of gathered bf16 weights.
+ * ------------------------------------------------------------------------ */
+
+typedef struct zero_ledger_out {
+    double params_bytes;        /* bf16 working parameters held per GPU */
+    double grads_bytes;         /* bf16 gradients held per GPU (0 if transient) */
+    double optim_bytes;         /* fp32 master + m + v held per GPU */
+    double model_state_bytes;   /* the sum of the three */
+    double comm_elements;       /* 2 psi (stages 0-2) or 3 psi (stage 3) */
+    double comm_elements_ring;  /* the same times (N-1)/N */
+    double optimizer_floats_per_rank;  /* 3 psi / N floats (master, m, v) for stages >= 1, 3 psi for 0 */
+} zero_ledger_out;
+
+/* EINVAL: psi < 0, N < 1, stage outside 0..3, NULL out. */
+zero_status zero_ledger(double psi, int32_t n_ranks, int32_t stage, int32_t grads_transient,
+                        zero_ledger_out *out);
+
+/* ZeRO-3 gather working set: `units_in_flight` units of bf16 weights of the
+ * largest unit of the layout (bytes). */
+zero_status zero_gather_buffer_bytes(const zero_layout *layout, int32_t units_in_flight,
+                                     double *bytes);
+
+/* Algorithmic HBM bytes one zero_step call moves, and the elements it
+ * processes: n_grads * grad_size (reads) + 12 (master, m, v reads) + 12
+ * (writes) + 2 (bf16 out, if with_out) per processed element. */
+zero_status zero_step_traffic(const zero_layout *layout, int32_t rank, int32_t n_grads,
+                              int32_t grad_dtype, int32_t with_out,
+                              double *bytes, int64_t *elements);
+
+/* Algorithmic bytes of one zero_gradnorm call: n_grads * grad_size reads per
+ * element plus 4 bytes written per element when g_out is requested. */
+zero_status zero_gradnorm_traffic(const zero_layout *layout, int32_t rank, int32_t n_grads,
+                                  int32_t grad_dtype, int32_t with_g_out,
+                                  double *bytes, int64_t *elements);
+
+/* ------------------------------------------------------------------------
+ * Diagnostics.
+ * ------------------------------------------------------------------------ */
+
+const char *zero_strerror(zero_status status);
+/* Text of the last HIP error seen by this thread ("" if none). */
+const char *zero_last_hip_error(void);
+int32_t zero_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZERO_H */

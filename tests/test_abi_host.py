@@ -1,0 +1,296 @@
+"""The C ABI on the host: the library loads, exports every declared symbol,
+and its host-side parts (layout, index maps, step scalars, clip coefficient,
+ledger, traffic counts, argument validation) agree with the oracle and the
+pages.  No GPU needed: nothing here launches a kernel."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import pins
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "zero.h")
+
+z = pytest.importorskip("fsdp_sharded_optimizer_flat_amd")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(zero_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 19, names
+    lib = z.raw_library()
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in zero.h but not exported"
+    assert set(names) == set(z.EXPORTED)
+    assert z.zero_abi_version() == z.ZERO_ABI_VERSION == 1
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    for name in ["ZERO_OK", "ZERO_EINVAL", "ZERO_ERANGE", "ZERO_EALIGN", "ZERO_ENOSPC", "ZERO_EHIP",
+                 "ZERO_F32", "ZERO_BF16", "ZERO_GLOBAL", "ZERO_LOCAL", "ZERO_MAX_RANKS"]:
+        m = re.search(rf"#define {name} \(?(-?\d+)\)?", text)
+        assert m and int(m.group(1)) == getattr(z, name), name
+    assert C.sizeof(z.ZeroLayoutHeader) == 40 and C.sizeof(z.ZeroUnit) == 40
+    assert z.zero_layout_bytes(36) == 40 + 36 * 40
+
+
+# -- layout ---------------------------------------------------------------------
+
+def test_layout_matches_oracle_and_bruteforce():
+    rng = np.random.default_rng(3)
+    cases = [(n, [p]) for n in range(1, 10) for p in range(0, 30)]
+    cases += [(int(rng.integers(1, 10)), [int(x) for x in rng.integers(0, 65, rng.integers(1, 5))])
+              for _ in range(300)]
+    for n, numel in cases:
+        L = z.zero_pack(n, numel)
+        O = oracle.Layout(n, numel)
+        t = L.unit_table()
+        assert L.padded == O.total_padded and L.shard == O.total_shard and L.numel == sum(numel)
+        assert np.array_equal(t[:, 1], O.padded) and np.array_equal(t[:, 2], O.shard)
+        assert np.array_equal(t[:, 3], O.offset) and np.array_equal(t[:, 4], O.local_offset)
+        flat, _starts, local = pins.brute_layout(n, numel)
+        for r in range(n):
+            for k, j in enumerate(local[r]):
+                assert z.zero_global_index(L, r, k) == j
+                assert z.zero_owner(L, j) == (r, k)
+
+
+def test_layout_of_the_workloads():
+    from fsdp_sharded_optimizer_flat_amd.workloads import WORKLOADS
+    want = {"toy": (1000, 250), "gpt2l_block": (19_677_440, 2_459_680),
+            "gpt2l": (774_090_240, 96_761_280), "llama8b_z3": (8_030_261_248, 125_472_832)}
+    for name, (ph, s) in want.items():
+        w = WORKLOADS[name]
+        L = z.zero_pack(w.n_ranks, w.unit_numel)
+        assert (L.padded, L.shard) == (ph, s), name
+
+
+def test_pack_errors():
+    with pytest.raises(z.ZeroError) as e:
+        z.zero_pack(0, [10])
+    assert e.value.status == z.ZERO_EINVAL
+    with pytest.raises(z.ZeroError) as e:
+        z.zero_pack(4, [-1])
+    assert e.value.status == z.ZERO_EINVAL
+    with pytest.raises(z.ZeroError) as e:
+        z.zero_pack(4, [2 ** 63 - 2])
+    assert e.value.status == z.ZERO_ERANGE
+    lib = z.raw_library()
+    numel = np.array([10], np.int64)
+    buf = (C.c_char * 8)()
+    need = C.c_size_t()
+    assert lib.zero_pack(4, 1, numel.ctypes.data, C.addressof(buf), 8, C.byref(need)) == z.ZERO_ENOSPC
+    assert need.value == 80
+    L = z.zero_pack(4, [10])
+    with pytest.raises(z.ZeroError):
+        z.zero_global_index(L, 4, 0)
+    with pytest.raises(z.ZeroError):
+        z.zero_owner(L, 12)
+
+
+def test_empty_layout():
+    L = z.zero_pack(8, [])
+    assert (L.padded, L.shard, L.n_units) == (0, 0, 0)
+    L = z.zero_pack(8, [0, 0])
+    assert (L.padded, L.shard) == (0, 0)
+
+
+# -- scalars --------------------------------------------------------------------------
+
+def test_scalars_match_oracle_bitwise():
+    for (lr, b1, b2, eps, wd) in pins.HYPER_SETS:
+        prev = None
+        for t in range(1, 3001):
+            s = z.zero_adamw_scalars_for(t, lr, b1, b2, eps, wd) if t <= 40 or t % 97 == 0 else None
+            nxt = z.zero_adamw_scalars_next(prev) if prev is not None else z.zero_adamw_scalars_for(1, lr, b1, b2, eps, wd)
+            if s is not None:
+                o = oracle.adamw_scalars(t, lr, b1, b2, wd)
+                got = np.array([s.one_minus_b1, s.one_minus_b2, s.pow1, s.pow2, s.bc1, s.bc2,
+                                s.step_size, s.decay], np.float32)
+                assert np.array_equal(got.view(np.uint32), o["_raw"].view(np.uint32)), (t, lr)
+                assert s.as_dict() == nxt.as_dict(), t
+            prev = nxt
+
+
+def test_scalars_survey_hex_pins():
+    """bc1, bc2, lr/bc1 and 1 - lr*wd for t = 1..3 as binary32 bit patterns
+    (independent of how b^t is formed, since b^t is exact-rounded for t <= 3)."""
+    want = {
+        0.01: dict(bc1=[0x3dccccd0, 0x3e428f60, 0x3e8ac086], bc2=[0x3e64f930, 0x3e9fdf39, 0x3ec15c4c],
+                   step=[0x3dccccc9, 0x3d579431, 0x3d1724d4], decay=0x3f7fbe77),
+        3e-4: dict(bc1=[0x3dccccd0, 0x3e428f60, 0x3e8ac086], bc2=[0x3e64f930, 0x3e9fdf39, 0x3ec15c4c],
+                   step=[0x3b449ba3, 0x3acef4ab, 0x3a91191e], decay=0x3f7ffe09),
+    }
+    u = lambda x: int(np.float32(x).view(np.uint32))
+    for lr, w in want.items():
+        for t in (1, 2, 3):
+            s = z.zero_adamw_scalars_for(t, lr, 0.9, 0.95, 1e-8, 0.1)
+            assert (u(s.bc1), u(s.bc2), u(s.step_size), u(s.decay)) == \
+                (w["bc1"][t - 1], w["bc2"][t - 1], w["step"][t - 1], w["decay"])
+
+
+def test_scalar_errors():
+    with pytest.raises(z.ZeroError):
+        z.zero_adamw_scalars_for(0, 1e-3, 0.9, 0.95, 1e-8, 0.1)
+    with pytest.raises(z.ZeroError):
+        z.zero_adamw_scalars_for(1, float("nan"), 0.9, 0.95, 1e-8, 0.1)
+
+
+def test_clip_coef_matches_oracle():
+    rng = np.random.default_rng(5)
+    for s in list(10.0 ** rng.uniform(-12, 8, 2000)) + [0.0, 1.0, 1e-12]:
+        for mx in (1.0, 0.5, 3.0):
+            assert z.zero_clip_coef(float(s), mx) == oracle.clip_coef(float(s), mx)
+    with pytest.raises(z.ZeroError):
+        z.zero_clip_coef(-1.0, 1.0)
+    with pytest.raises(z.ZeroError):
+        z.zero_clip_coef(1.0, 0.0)
+
+
+# -- ledger -------------------------------------------------------------------------------
+
+def test_ledger_matches_oracle_and_pages():
+    for psi in (1.0, 0.774e9, 7.5e9, 70e9):
+        for n in (1, 2, 8, 64):
+            for stage in range(4):
+                for tr in (False, True):
+                    led = z.zero_ledger(psi, n, stage, tr)
+                    assert led["model_state_bytes"] == pytest.approx(oracle.ledger_bytes(psi, n, stage, tr), rel=1e-15)
+                    assert led["comm_elements"] == oracle.comm_elements(psi, n, stage)
+                    assert led["comm_elements_ring"] == pytest.approx(oracle.comm_elements(psi, n, stage, True), rel=1e-15)
+    gold = pins.golden("ledger_worked_values.json")
+    for case in gold["memory"]:
+        unit = 1e9 if case["unit"] == "GB" else float(1 << 30)
+        for stage, val in case["stage_values"].items():
+            got = z.zero_ledger(case["psi"], case["n"], int(stage), case["grads_transient"])
+            assert abs(got["model_state_bytes"] / unit - val) <= case["tol"], (case["cite"], stage)
+    toy = pins.golden("toy_printed.json")
+    assert z.zero_ledger(toy["P"], toy["n"], 1)["optimizer_floats_per_rank"] == toy["optimizer_floats_per_rank"]
+    assert z.zero_ledger(toy["P"], toy["n"], 0)["optimizer_floats_per_rank"] == toy["optimizer_floats_unsharded"]
+    gb = gold["zero3_gather_buffer"]
+    per_unit = gb["psi"] / gb["units"]
+    L = z.zero_pack(64, [int(per_unit)] * 4)
+    assert abs(z.zero_gather_buffer_bytes(L, 1) / 1e9 - gb["GB_per_unit"]) <= gb["tol"]
+
+
+def test_traffic_counts():
+    L = z.zero_pack(8, [774_090_240])
+    b, e = z.zero_step_traffic(L, -1, 8, z.ZERO_BF16, True)
+    assert e == 774_090_240 and b == (2 * 8 + 26) * e
+    L = z.zero_pack(64, [8_030_261_248])
+    b, e = z.zero_step_traffic(L, 0, 64, z.ZERO_BF16, True)
+    assert e == 125_472_832 and b == (2 * 64 + 26) * e
+    b, e = z.zero_gradnorm_traffic(L, 0, 64, z.ZERO_BF16, True)
+    assert b == (2 * 64 + 4) * e
+    b, e = z.zero_step_traffic(z.zero_pack(4, [1000]), -1, 4, z.ZERO_F32, True)
+    assert b == (4 * 4 + 26) * 1000
+
+
+# -- argument validation (rejected before any device work) -------------------------------
+# These calls pass made-up device addresses that validation must reject; they
+# are skipped where a GPU is visible so that a validation bug can never turn
+# into a launch on fake pointers.
+
+def _no_gpu():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("host-validation test with made-up addresses; runs only without a GPU")
+
+
+def _raw_step(L, rank=-1, grads=(0x1000,), n_grads=None, gdt=1, gidx=0, div=1.0,
+              w=0x10000000, m=0x20000000, v=0x30000000, sidx=0, out=0x40000000, oidx=0, sc=True):
+    lib = z.raw_library()
+    arr = (C.c_void_p * max(len(grads), 1))(*grads) if grads is not None else None
+    s = z.zero_adamw_scalars_for(1, 1e-3, 0.9, 0.95, 1e-8, 0.1) if sc else None
+    if n_grads is None:
+        n_grads = len(grads) if grads is not None else 1
+    return lib.zero_step(L.ptr, rank, C.addressof(arr) if arr is not None else None,
+                         n_grads, gdt, gidx, div, w, m, v, sidx,
+                         out, oidx, C.byref(s) if s is not None else None, None)
+
+
+def test_step_argument_errors():
+    _no_gpu()
+    L = z.zero_pack(4, [1000])
+    assert _raw_step(L, rank=4) == z.ZERO_EINVAL                       # rank >= N
+    assert _raw_step(L, rank=-1, sidx=1) == z.ZERO_EINVAL              # all-ranks needs GLOBAL
+    assert _raw_step(L, grads=None) == z.ZERO_EINVAL
+    assert _raw_step(L, n_grads=0) == z.ZERO_ERANGE
+    assert _raw_step(L, grads=(0x1000,) * 257) == z.ZERO_ERANGE
+    assert _raw_step(L, grads=(0,)) == z.ZERO_EINVAL                    # NULL gradient
+    assert _raw_step(L, div=0.0) == z.ZERO_EINVAL
+    assert _raw_step(L, div=float("inf")) == z.ZERO_EINVAL
+    assert _raw_step(L, gdt=7) == z.ZERO_EINVAL
+    assert _raw_step(L, gidx=5) == z.ZERO_EINVAL
+    assert _raw_step(L, w=0) == z.ZERO_EINVAL
+    assert _raw_step(L, sc=False) == z.ZERO_EINVAL
+    assert _raw_step(L, grads=(0x1001,)) == z.ZERO_EALIGN              # bf16 needs 2-byte alignment
+    assert _raw_step(L, gdt=0, grads=(0x1002,)) == z.ZERO_EALIGN       # f32 needs 4
+    assert _raw_step(L, w=0x10000002) == z.ZERO_EALIGN
+    assert _raw_step(L, out=0x40000001) == z.ZERO_EALIGN
+    # aliasing: a written buffer inside a gradient, or two written buffers overlapping
+    assert _raw_step(L, grads=(0x10000000 - 100,)) == z.ZERO_EINVAL
+    assert _raw_step(L, m=0x10000000 + 3996) == z.ZERO_EINVAL
+    assert _raw_step(L, out=0x30000000 + 8) == z.ZERO_EINVAL
+    bad = z.zero_pack(4, [1000])
+    bad.header.magic = 0
+    assert _raw_step(bad) == z.ZERO_EINVAL
+    bad = z.zero_pack(4, [1000])
+    bad.units[0].shard = 7                                               # inconsistent layout
+    assert _raw_step(bad) == z.ZERO_EINVAL
+
+
+def test_gradnorm_argument_errors():
+    _no_gpu()
+    L = z.zero_pack(4, [1000])
+    lib = z.raw_library()
+    need = z.zero_gradnorm_workspace_bytes(L, -1)
+    assert need == 8 * (1 + 1026)
+    arr = (C.c_void_p * 1)(0x1000)
+    res = C.c_double()
+    # short workspace
+    assert lib.zero_gradnorm(L.ptr, -1, C.addressof(arr), 1, 1, 0, 1.0, None, 0, 0x20000000,
+                             need - 8, C.byref(res), None) == z.ZERO_ENOSPC
+    # NULL result
+    assert lib.zero_gradnorm(L.ptr, -1, C.addressof(arr), 1, 1, 0, 1.0, None, 0, 0x20000000,
+                             need, None, None) == z.ZERO_EINVAL
+    # workspace misaligned / overlapping the gradient
+    assert lib.zero_gradnorm(L.ptr, -1, C.addressof(arr), 1, 1, 0, 1.0, None, 0, 0x20000004,
+                             need, C.byref(res), None) == z.ZERO_EALIGN
+    assert lib.zero_gradnorm(L.ptr, -1, C.addressof(arr), 1, 1, 0, 1.0, None, 0, 0x1000 + 8,
+                             need, C.byref(res), None) == z.ZERO_EINVAL
+
+
+def test_strerror():
+    for s in (0, -1, -2, -3, -4, -5):
+        assert z.zero_strerror(s) and z.zero_strerror(s) != "unknown status"
+    assert z.zero_last_hip_error() == ""
+
+
+# -- build flags --------------------------------------------------------------------------------
+
+def test_device_code_has_no_contraction_or_flush():
+    """The device IR carries no fast-math flags that could fuse or reassociate
+    (contract / reassoc / afn / fast) and no denormal flushing; the gfx950
+    assembly has no packed-fp32 arithmetic and no scratch spills."""
+    from fsdp_sharded_optimizer_flat_amd import _build
+    for src in ("step_kernels.hip", "norm_kernels.hip"):
+        ir = _build.device_ir(src)
+        for flag in (" contract ", " reassoc ", " afn ", " fast ", " nnan ", " ninf "):
+            assert flag not in ir, (src, flag)
+        assert '"denormal-fp-math-f32"="preserve-sign' not in ir
+        asm = _build.device_asm(src)
+        assert not re.search(r"v_pk_(fma|mul|add)_f32", asm), src
+        assert ".amdhsa_float_denorm_mode_32 3" in asm
+        for m in re.finditer(r"\.private_segment_fixed_size:\s+(\d+)", asm):
+            assert int(m.group(1)) == 0, (src, "scratch use")

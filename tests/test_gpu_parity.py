@@ -1,0 +1,467 @@
+"""GPU parity: the HIP step and norm, called through the C ABI, against the
+oracle, element by element.  Floating-point state (master, m, v) and the bf16
+output must match bit for bit (NaN compared as NaN-ness); the binary64 sum of
+squares must match to a relative 1e-12 (its summation order differs).
+
+Sizes: small enough for the oracle to finish in seconds yet spanning many
+workgroup tiles and ragged tails, plus the full workload sizes with sampled
+elements the oracle computes one by one."""
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import oracle  # noqa: E402
+import fsdp_sharded_optimizer_flat_amd as z  # noqa: E402
+from fsdp_sharded_optimizer_flat_amd import synth  # noqa: E402
+from fsdp_sharded_optimizer_flat_amd.workloads import WORKLOADS, GPT_HYPER, TOY_HYPER  # noqa: E402
+from gpu_common import (DEV, assert_same_bf16, assert_same_f32, dev_buffer, extent,  # noqa: E402
+                        gather_np, hyper_args, oracle_on_samples, sampled_indices, scalars,
+                        to_np)
+
+G, Lc = z.ZERO_GLOBAL, z.ZERO_LOCAL
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# The pages' toy, 50 steps, bit-exact (fp32 gradients w - t_r).
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,P", [(4, 1000), (4, 1001), (3, 1000), (8, 13)])
+def test_toy_bitexact(n, P):
+    log(f"toy n={n} P={P}")
+    h = TOY_HYPER
+    L = z.zero_pack(n, [P])
+    Ph = L.padded
+    tgt = torch.tensor([[(i * 7 + r * 13) % 11 for i in range(P)] for r in range(n)],
+                       dtype=torch.float32, device=DEV)
+    w = torch.zeros(Ph, dtype=torch.float32, device=DEV)
+    m = torch.zeros_like(w)
+    v = torch.zeros_like(w)
+    out = torch.zeros(Ph, dtype=torch.int16, device=DEV)
+    grads = [torch.zeros(Ph, dtype=torch.float32, device=DEV) for _ in range(n)]
+    steps = 50
+    for t in range(1, steps + 1):
+        for r in range(n):
+            torch.sub(w[:P], tgt[r], out=grads[r][:P])   # rank r's local gradient; padding stays 0
+        z.zero_step(L, -1, grads, G, float(n), w, m, v, G, out, G, scalars(t, h))
+    torch.cuda.synchronize()
+    ws, wu, ob, _ = oracle.toy(n, P, steps, h["lr"])
+    assert_same_f32(to_np(w)[:P], ws, "toy master vs oracle")
+    assert_same_f32(to_np(w)[:P], wu, "toy master vs unsharded AdamW")
+    assert_same_bf16(to_np(out)[:P], ob, "toy bf16 out")
+    assert np.all(to_np(w)[P:].view(np.uint32) == 0), "padding must stay +0"
+
+
+# ---------------------------------------------------------------------------
+# One GPT-2 Large block, N = 8, all shards, 10 steps: full comparison.
+# ---------------------------------------------------------------------------
+
+def test_gpt2l_block_full_10_steps():
+    wl = WORKLOADS["gpt2l_block"]
+    log(f"gpt2l_block P={sum(wl.unit_numel)}")
+    n, h = wl.n_ranks, wl.hyper
+    L = z.zero_pack(n, wl.unit_numel)
+    Ph = L.padded
+    master = torch.empty(Ph, dtype=torch.float32, device=DEV)
+    synth.fill_normal_(master, wl.master_std, synth.seed_of(wl.seed, synth.TAG_MASTER))
+    m, v = torch.zeros_like(master), torch.zeros_like(master)
+    out = torch.zeros(Ph, dtype=torch.int16, device=DEV)
+    grads = torch.empty(n, Ph, dtype=torch.bfloat16, device=DEV)
+    om = to_np(master).copy()
+    omm, ov = np.zeros_like(om), np.zeros_like(om)
+    oout = np.zeros(Ph, np.uint16)
+    for t in range(1, wl.steps + 1):
+        for r in range(n):
+            synth.fill_grad_(grads[r], wl.grad_dist, wl.grad_scale, synth.seed_of(wl.seed, synth.TAG_GRAD, t, r))
+        z.zero_step(L, -1, list(grads), G, float(n), master, m, v, G, out, G, scalars(t, h))
+        gnp = [np.ascontiguousarray(to_np(grads[r])) for r in range(n)]
+        oracle.zero_step_all(n, list(wl.unit_numel), gnp, divisor=float(n), clip=1.0, master=om,
+                             m=omm, v=ov, out=oout, t=t, **hyper_args(h))
+    torch.cuda.synchronize()
+    assert_same_f32(to_np(master), om, "master")
+    assert_same_f32(to_np(m), omm, "m")
+    assert_same_f32(to_np(v), ov, "v")
+    assert_same_bf16(to_np(out), oout, "bf16 out")
+
+
+# ---------------------------------------------------------------------------
+# Every index mode, rank, dtype, rank count and pointer alignment on tiny
+# layouts (brute force), against the oracle's rank step.
+# ---------------------------------------------------------------------------
+
+def _run_case(rng, n, numel, rank, gdt, gidx, sidx, oidx, shift, steps=2, with_out=True, n_grads=None):
+    h = dict(lr=1e-3, b1=0.9, b2=0.95, eps=1e-8, wd=0.1)
+    L = z.zero_pack(n, numel)
+    O = oracle.Layout(n, numel)
+    ng = n if n_grads is None else n_grads
+    tdt = torch.bfloat16 if gdt == z.ZERO_BF16 else torch.float32
+    ge, se, oe = extent(L, gidx), extent(L, sidx), extent(L, oidx)
+    grads = [dev_buffer(ge, tdt, shift=(shift * (q + 1)) % 8) for q in range(ng)]
+    master = dev_buffer(se, torch.float32, shift=shift)
+    m = dev_buffer(se, torch.float32, shift=shift)
+    v = dev_buffer(se, torch.float32, shift=shift)
+    out = dev_buffer(oe, torch.int16, shift=(shift * 3) % 8) if with_out else None
+    init = rng.normal(0, 0.02, se).astype(np.float32)
+    master.copy_(torch.from_numpy(init))
+    om, omm, ov = init.copy(), np.zeros(se, np.float32), np.zeros(se, np.float32)
+    oout = np.zeros(oe, np.uint16)
+    for t in range(1, steps + 1):
+        for g in grads:
+            vals = (rng.standard_normal(ge) * 1e-3).astype(np.float32)
+            g.copy_(torch.from_numpy(vals).to(tdt))
+        gnp = [np.ascontiguousarray(to_np(g)) for g in grads]
+        z.zero_step(L, rank, grads, gidx, float(n), master, m, v, sidx, out, oidx, scalars(t, h))
+        if rank < 0:
+            oracle.zero_step_all(n, numel, gnp, divisor=float(n), clip=1.0, master=om, m=omm, v=ov,
+                                 out=oout if with_out else None, t=t, **hyper_args(h))
+        else:
+            oracle.zero_step_rank(n, numel, rank, gnp, grad_local=(gidx == Lc), divisor=float(n),
+                                  clip=1.0, master=om, m=omm, v=ov, state_global=(sidx == G),
+                                  out=oout if with_out else None, out_gather=(oidx == G), t=t,
+                                  **hyper_args(h))
+    torch.cuda.synchronize()
+    tag = f"n={n} numel={numel} rank={rank} gdt={gdt} idx={gidx}{sidx}{oidx} shift={shift}"
+    # compare only the elements the selection owns (others stay as initialised)
+    if rank < 0:
+        sel_s = np.arange(se)
+        sel_o = np.arange(oe)
+    else:
+        ks = np.arange(L.shard)
+        js = np.array([O.global_of_local(rank, int(k)) for k in ks], np.int64)
+        sel_s = js if sidx == G else ks
+        sel_o = js if oidx == G else ks
+    assert_same_f32(to_np(master)[sel_s], om[sel_s], "master " + tag)
+    assert_same_f32(to_np(m)[sel_s], omm[sel_s], "m " + tag)
+    assert_same_f32(to_np(v)[sel_s], ov[sel_s], "v " + tag)
+    if with_out:
+        assert_same_bf16(to_np(out)[sel_o], oout[sel_o], "out " + tag)
+        untouched = np.setdiff1d(np.arange(oe), sel_o)
+        assert np.all(to_np(out)[untouched] == 0), "elements outside the selection were written"
+
+
+def test_index_modes_bruteforce():
+    rng = np.random.default_rng(11)
+    cases = 0
+    for n in (1, 2, 3, 4, 8):
+        for numel in ([37], [64, 5, 0, 19], [8 * n + 3, 16 * n]):
+            for gdt in (z.ZERO_BF16, z.ZERO_F32):
+                ranks = [-1] + sorted(set([0, n - 1, n // 2]))
+                for rank in ranks:
+                    modes = [(G, G, G)] if rank < 0 else [(gi, si, oi) for gi in (G, Lc) for si in (G, Lc) for oi in (G, Lc)]
+                    for gidx, sidx, oidx in modes:
+                        shift = int(rng.integers(0, 8))
+                        _run_case(rng, n, numel, rank, gdt, gidx, sidx, oidx, shift)
+                        cases += 1
+    log(f"index-mode cases: {cases}")
+
+
+@pytest.mark.parametrize("n", [5, 7, 16, 32, 64, 100, 256])
+def test_rank_counts(n):
+    """Compile-time and runtime rank-count kernels, power-of-two and other
+    divisors, multi-tile sizes with ragged tails."""
+    rng = np.random.default_rng(n)
+    numel = [n * 2048 + 11, 3 * n + 1] if n <= 64 else [n * 64 + 5]
+    _run_case(rng, n, numel, -1, z.ZERO_BF16, G, G, G, shift=0)
+    _run_case(rng, n, numel, n - 1, z.ZERO_BF16, Lc, Lc, Lc, shift=0)
+    _run_case(rng, n, numel, 0, z.ZERO_BF16, G, Lc, G, shift=2)
+
+
+def test_ragged_multitile_and_no_out():
+    rng = np.random.default_rng(5)
+    numel = [1_000_003, 77, 12_293, 0, 4096 * 8 + 3]
+    _run_case(rng, 8, numel, -1, z.ZERO_BF16, G, G, G, shift=0)
+    _run_case(rng, 8, numel, 3, z.ZERO_BF16, G, Lc, G, shift=0)
+    _run_case(rng, 8, numel, 5, z.ZERO_BF16, Lc, Lc, Lc, shift=1, with_out=False)
+
+
+def test_reduced_gradient_input():
+    """n_grads = 1 with divisor 1: the step on an already-reduced fp32
+    gradient (how the clipped step consumes the norm pass's output)."""
+    rng = np.random.default_rng(6)
+    _run_case(rng, 8, [4096 + 3], 2, z.ZERO_F32, Lc, Lc, Lc, shift=0, n_grads=1)
+
+
+def test_rank_by_rank_equals_all_at_once_and_unsharded():
+    """The pages' invariant on the GPU: every rank stepping its own shard
+    (LOCAL state) reproduces the all-ranks step and plain AdamW."""
+    n, numel = 8, [100_003, 4097]
+    h = GPT_HYPER
+    L = z.zero_pack(n, numel)
+    O = oracle.Layout(n, numel)
+    rng = np.random.default_rng(7)
+    w0 = rng.normal(0, 0.02, L.padded).astype(np.float32)
+    for u in range(len(numel)):
+        w0[O.offset[u] + numel[u]:O.offset[u] + O.padded[u]] = 0
+    g = (rng.standard_normal((n, L.padded)) * 1e-3).astype(np.float32)
+    for u in range(len(numel)):
+        g[:, O.offset[u] + numel[u]:O.offset[u] + O.padded[u]] = 0
+    grads = torch.from_numpy(g).to(DEV).to(torch.bfloat16)
+    W = torch.from_numpy(w0).to(DEV)
+    M, V = torch.zeros_like(W), torch.zeros_like(W)
+    out_all = torch.zeros(L.padded, dtype=torch.int16, device=DEV)
+    out_rank = torch.zeros(L.padded, dtype=torch.int16, device=DEV)
+    idx = [torch.tensor([O.global_of_local(r, k) for k in range(L.shard)], device=DEV) for r in range(n)]
+    ws = [W.index_select(0, idx[r]).contiguous() for r in range(n)]
+    ms = [torch.zeros(L.shard, device=DEV) for _ in range(n)]
+    vs = [torch.zeros(L.shard, device=DEV) for _ in range(n)]
+    for t in (1, 2, 3):
+        sc = scalars(t, h)
+        z.zero_step(L, -1, list(grads), G, float(n), W, M, V, G, out_all, G, sc)
+        for r in range(n):
+            z.zero_step(L, r, list(grads), G, float(n), ws[r], ms[r], vs[r], Lc, out_rank, G, sc)
+    torch.cuda.synchronize()
+    Wr = torch.zeros_like(W)
+    for r in range(n):
+        Wr.index_copy_(0, idx[r], ws[r])
+    assert_same_f32(to_np(Wr), to_np(W), "rank-by-rank vs all-at-once")
+    assert_same_bf16(to_np(out_rank), to_np(out_all), "gathered bf16")
+    # plain AdamW on the averaged gradient, unpadded
+    gu = [np.ascontiguousarray(np.concatenate([to_np(grads[q])[O.offset[u]:O.offset[u] + numel[u]]
+                                               for u in range(len(numel))])) for q in range(n)]
+    wu = np.concatenate([w0[O.offset[u]:O.offset[u] + numel[u]] for u in range(len(numel))])
+    mu, vu = np.zeros_like(wu), np.zeros_like(wu)
+    for t in (1, 2, 3):
+        oracle.adamw_unsharded(gu, divisor=float(n), clip=1.0, w=wu, m=mu, v=vu, t=t, **hyper_args(h))
+    Wn = to_np(W)
+    got = np.concatenate([Wn[O.offset[u]:O.offset[u] + numel[u]] for u in range(len(numel))])
+    assert_same_f32(got, wu, "sharded GPU vs unsharded AdamW")
+
+
+# ---------------------------------------------------------------------------
+# Edge cases.
+# ---------------------------------------------------------------------------
+
+def test_empty_layouts_are_noops():
+    for numel in ([], [0], [0, 0]):
+        L = z.zero_pack(4, numel)
+        dummy = torch.zeros(8, device=DEV)
+        g = torch.zeros(8, dtype=torch.bfloat16, device=DEV)
+        z.zero_step(L, -1, [g], G, 4.0, dummy, dummy.clone(), dummy.clone(), G, None, G,
+                    scalars(1, GPT_HYPER))
+        ws = torch.zeros(z.zero_gradnorm_workspace_bytes(L, -1) // 8, dtype=torch.float64, device=DEV)
+        assert z.zero_gradnorm(L, -1, [g], G, 4.0, None, G, ws) == 0.0
+    torch.cuda.synchronize()
+
+
+def test_all_padding_shards():
+    """P = 1 over N = 8: ranks 1..7 own nothing but padding; it stays +0."""
+    rng = np.random.default_rng(8)
+    for rank in range(8):
+        _run_case(rng, 8, [1], rank, z.ZERO_BF16, G, Lc, G, shift=0)
+
+
+def test_nan_and_inf_propagate_like_the_oracle():
+    n, P = 4, 4096 + 5
+    h = GPT_HYPER
+    L = z.zero_pack(n, [P])
+    rng = np.random.default_rng(9)
+    g = (rng.standard_normal((n, L.padded)) * 1e-3).astype(np.float32)
+    g[0, 10] = np.nan
+    g[1, 20] = np.inf
+    g[2, 20] = -np.inf          # inf + -inf = NaN
+    g[3, 30] = np.inf
+    g[0, 4000] = 3e38
+    g[1, 4000] = 3e38           # overflow in the sum
+    w0 = rng.normal(0, 0.02, L.padded).astype(np.float32)
+    w0[40] = np.nan
+    w0[41] = np.inf
+    gb = torch.from_numpy(g).to(torch.bfloat16).to(DEV)
+    W = torch.from_numpy(w0).to(DEV)
+    M, V = torch.zeros_like(W), torch.zeros_like(W)
+    out = torch.zeros(L.padded, dtype=torch.int16, device=DEV)
+    gnp = [np.ascontiguousarray(to_np(gb[q])) for q in range(n)]
+    om, omm, ov, oo = w0.copy(), np.zeros_like(w0), np.zeros_like(w0), np.zeros(L.padded, np.uint16)
+    for t in (1, 2):
+        z.zero_step(L, -1, list(gb), G, float(n), W, M, V, G, out, G, scalars(t, h))
+        oracle.zero_step_all(n, [P], gnp, divisor=float(n), clip=1.0, master=om, m=omm, v=ov, out=oo,
+                             t=t, **hyper_args(h))
+    torch.cuda.synchronize()
+    assert_same_f32(to_np(W), om, "master with NaN/Inf")
+    assert_same_f32(to_np(M), omm, "m with NaN/Inf")
+    assert_same_f32(to_np(V), ov, "v with NaN/Inf")
+    assert_same_bf16(to_np(out), oo, "out with NaN/Inf")
+
+
+def test_resume_equals_uninterrupted():
+    """10 steps == 5 steps, copy the state out and back, 5 more steps."""
+    n, numel = 8, [50_001]
+    h = GPT_HYPER
+    L = z.zero_pack(n, numel)
+    rng = np.random.default_rng(10)
+    w0 = rng.normal(0, 0.02, L.padded).astype(np.float32)
+    w0[numel[0]:] = 0
+    gsteps = []
+    for _ in range(10):
+        g = (rng.standard_normal((n, L.padded)) * 1e-3).astype(np.float32)
+        g[:, numel[0]:] = 0
+        gsteps.append(torch.from_numpy(g).to(torch.bfloat16).to(DEV))
+
+    def run(W, M, V, t0, t1):
+        for t in range(t0, t1):
+            z.zero_step(L, -1, list(gsteps[t - 1]), G, float(n), W, M, V, G, None, G, scalars(t, h))
+
+    A = [torch.from_numpy(w0).to(DEV), torch.zeros(L.padded, device=DEV), torch.zeros(L.padded, device=DEV)]
+    run(*A, 1, 11)
+    B = [torch.from_numpy(w0).to(DEV), torch.zeros(L.padded, device=DEV), torch.zeros(L.padded, device=DEV)]
+    run(*B, 1, 6)
+    saved = [to_np(x).copy() for x in B]
+    C = [torch.from_numpy(s).to(DEV) for s in saved]
+    run(*C, 6, 11)
+    torch.cuda.synchronize()
+    for a, c, name in zip(A, C, "wmv"):
+        assert_same_f32(to_np(c), to_np(a), "resume " + name)
+
+
+def test_bf16_cast_on_all_exponents():
+    """With lr = 0 the update is exactly zero and decay exactly one, so the
+    step writes bf16(master): every upper half-word with the low half-words
+    that decide rounding, plus random patterns, against the oracle's cast."""
+    import pins
+    pats = pins.bf16_probe_patterns(seed=1, n_random=1 << 22)
+    P = pats.size
+    L = z.zero_pack(1, [P])
+    W = torch.from_numpy(pats.view(np.float32).copy()).to(DEV)
+    M, V = torch.zeros_like(W), torch.zeros_like(W)
+    g = torch.zeros(P, dtype=torch.bfloat16, device=DEV)
+    out = torch.zeros(P, dtype=torch.int16, device=DEV)
+    sc = z.zero_adamw_scalars_for(1, 0.0, 0.9, 0.95, 1e-8, 0.1)
+    assert sc.step_size == 0.0 and sc.decay == 1.0
+    z.zero_step(L, -1, [g], G, 1.0, W, M, V, G, out, G, sc)
+    torch.cuda.synchronize()
+    x = pats.view(np.float32)
+    assert_same_f32(to_np(W), x, "master unchanged at lr = 0")
+    assert_same_bf16(to_np(out), oracle.bf16(x), "bf16 cast")
+
+
+# ---------------------------------------------------------------------------
+# Norm: full oracle comparison at moderate size, closed form, determinism.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,numel,rank,gidx,gdt", [
+    (64, [64 * 30_000 + 64, 64 * 777], 0, Lc, z.ZERO_BF16),
+    (8, [1_000_003, 77], -1, G, z.ZERO_BF16),
+    (8, [1_000_003, 77], 5, G, z.ZERO_BF16),
+    (3, [10_001], 1, Lc, z.ZERO_F32),
+])
+def test_norm_and_clipped_step_vs_oracle(n, numel, rank, gidx, gdt):
+    log(f"norm n={n} numel={numel} rank={rank}")
+    rng = np.random.default_rng(12)
+    L = z.zero_pack(n, numel)
+    O = oracle.Layout(n, numel)
+    ge = extent(L, gidx)
+    gidx_state = G if rank < 0 else Lc
+    se = extent(L, gidx_state)
+    tdt = torch.bfloat16 if gdt == z.ZERO_BF16 else torch.float32
+    vals = (rng.standard_t(3, (n, ge)) * 1e-3 * 40).astype(np.float32)
+    if gidx == G:
+        for u in range(len(numel)):
+            vals[:, O.offset[u] + numel[u]:O.offset[u] + O.padded[u]] = 0
+    grads = torch.from_numpy(vals).to(tdt).to(DEV)
+    gnp = [np.ascontiguousarray(to_np(grads[q])) for q in range(n)]
+    ws = torch.zeros(z.zero_gradnorm_workspace_bytes(L, rank) // 8, dtype=torch.float64, device=DEV)
+    g_out = torch.zeros(se, dtype=torch.float32, device=DEV)
+    s1 = z.zero_gradnorm(L, rank, list(grads), gidx, float(n), g_out, gidx_state, ws)
+    s2 = z.zero_gradnorm(L, rank, list(grads), gidx, float(n), None, gidx_state, ws)
+    assert s1 == s2, "norm must be bitwise reproducible"
+    # oracle: reduced gradient over the selection, then sum of squares
+    if rank < 0:
+        og = np.zeros(se, np.float32)
+        for r in range(n):
+            ks = oracle.reduced_grad(n, numel, r, gnp, grad_local=False, divisor=float(n))
+            js = [O.global_of_local(r, k) for k in range(L.shard)]
+            og[js] = ks
+        sel = np.arange(se)
+    else:
+        og = oracle.reduced_grad(n, numel, rank, gnp, grad_local=(gidx == Lc), divisor=float(n))
+        sel = np.arange(se)
+    assert_same_f32(to_np(g_out)[sel], og[sel], "reduced gradient written by the norm pass")
+    osum = oracle.sumsq(og)
+    assert abs(s1 - osum) <= 1e-12 * osum, (s1, osum)
+    coef_gpu = z.zero_clip_coef(s1, 1.0)
+    coef_orc = oracle.clip_coef(osum, 1.0)
+    assert coef_gpu == coef_orc
+    assert coef_gpu < 1.0, "the test data should make clipping active"
+    # the clipped step reading the reduced gradient (n_grads = 1, divisor 1)
+    h = GPT_HYPER
+    w0 = rng.normal(0, 0.02, se).astype(np.float32)
+    W = torch.from_numpy(w0).to(DEV)
+    M, V = torch.zeros_like(W), torch.zeros_like(W)
+    out = torch.zeros(se, dtype=torch.int16, device=DEV)
+    sc = scalars(1, h, clip=coef_gpu)
+    if rank < 0:
+        z.zero_step(L, -1, [g_out], G, 1.0, W, M, V, G, out, G, sc)
+    else:
+        z.zero_step(L, rank, [g_out], Lc, 1.0, W, M, V, Lc, out, Lc, sc)
+    # and the same step straight from the N gradients
+    W2 = torch.from_numpy(w0).to(DEV)
+    M2, V2 = torch.zeros_like(W2), torch.zeros_like(W2)
+    z.zero_step(L, rank, list(grads), gidx, float(n), W2, M2, V2, gidx_state, None, gidx_state, sc)
+    torch.cuda.synchronize()
+    om, omm, ov, oo = w0.copy(), np.zeros(se, np.float32), np.zeros(se, np.float32), np.zeros(se, np.uint16)
+    oracle.zero_step_rank(1, [se], 0, [og], grad_local=True, divisor=1.0, clip=coef_orc, master=om,
+                          m=omm, v=ov, state_global=False, out=oo, out_gather=False, t=1, **hyper_args(h))
+    assert_same_f32(to_np(W), om, "clipped master")
+    assert_same_f32(to_np(V), ov, "clipped v")
+    assert_same_bf16(to_np(out), oo, "clipped out")
+    assert_same_f32(to_np(W2), om, "clipped master from N gradients")
+
+
+def test_norm_closed_form():
+    """Every rank's gradient equal to c: the average is c exactly and the sum
+    of squares is (elements) * c^2 exactly in binary64."""
+    n, P = 64, 64 * 100_000
+    L = z.zero_pack(n, [P])
+    c = 0.375
+    grads = [torch.full((L.shard,), c, dtype=torch.bfloat16, device=DEV) for _ in range(n)]
+    ws = torch.zeros(z.zero_gradnorm_workspace_bytes(L, 3) // 8, dtype=torch.float64, device=DEV)
+    s = z.zero_gradnorm(L, 3, grads, Lc, float(n), None, Lc, ws)
+    assert s == L.shard * c * c
+
+
+# ---------------------------------------------------------------------------
+# Packer copies.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("src_dt,dst_dt", [(torch.float32, torch.float32), (torch.float32, torch.bfloat16),
+                                           (torch.bfloat16, torch.float32), (torch.bfloat16, torch.bfloat16)])
+def test_pack_and_unpack(src_dt, dst_dt):
+    from fsdp_sharded_optimizer_flat_amd.workloads import gpt2_block, numel_of
+    rng = np.random.default_rng(13)
+    n = 8
+    shapes = [s for _, s in gpt2_block(64)] + [(13,), (5, 3)]
+    units = [0] * 12 + [1, 1]
+    params = [torch.from_numpy(rng.standard_normal(numel_of(s)).astype(np.float32)).to(src_dt).to(DEV)
+              for s in shapes]
+    unit_numel = [sum(numel_of(s) for s, u in zip(shapes, units) if u == k) for k in (0, 1)]
+    L = z.zero_pack(n, unit_numel)
+    O = oracle.Layout(n, unit_numel)
+    flat = torch.full((L.padded,), 7, dtype=dst_dt, device=DEV)
+    z.zero_pack_copy(L, -1, params, units, flat)
+    # expected flat buffer, built on the host from the oracle's layout
+    exp = np.zeros(L.padded, np.float32)
+    pos = [0, 0]
+    for p, u in zip(params, units):
+        a = O.offset[u] + pos[u]
+        exp[a:a + p.numel()] = p.float().cpu().numpy()
+        pos[u] += p.numel()
+    got = flat.float().cpu().numpy()
+    want = torch.from_numpy(exp).to(dst_dt).float().numpy()
+    assert_same_f32(got, want, "packed flat buffer (padding zero)")
+    for r in (0, 5, n - 1):
+        shard = torch.full((L.shard,), 7, dtype=dst_dt, device=DEV)
+        z.zero_pack_copy(L, r, params, units, shard)
+        js = [O.global_of_local(r, k) for k in range(L.shard)]
+        assert_same_f32(shard.float().cpu().numpy(), want[js], f"rank {r} shard")
+    back = [torch.zeros_like(p) for p in params]
+    z.zero_unpack_copy(L, -1, flat, back, units)
+    torch.cuda.synchronize()
+    for p, b in zip(params, back):
+        assert_same_f32(b.float().cpu().numpy(), p.to(dst_dt).to(src_dt).float().cpu().numpy(), "unpack")
