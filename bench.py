@@ -246,7 +246,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "step_vec_kernel (fused rank-sum + AdamW + bf16 cast)",
+            "kernel": "step_quad_kernel (fused rank-sum + AdamW + bf16 cast)",
             "achieved": achieved,
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",

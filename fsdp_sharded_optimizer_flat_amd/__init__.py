@@ -14,6 +14,12 @@ from typing import Sequence
 
 import numpy as np
 
+# torch carries its own HIP runtime (SONAME libamdhip64.so.7, the same as
+# ROCm's).  Loading torch first makes libzero.so's dependency resolve to that
+# already-loaded runtime; loading libzero.so first would map a second HIP
+# runtime into the process, and whichever initialises second sees no device.
+import torch  # noqa: F401  (must precede the CDLL below)
+
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libzero.so")
 
@@ -374,6 +380,17 @@ def zero_last_hip_error() -> str:
 
 def zero_abi_version() -> int:
     return int(_zero_abi_version())
+
+
+def hip_runtimes_mapped() -> list[str]:
+    """Paths of every HIP runtime library mapped into this process (there
+    must be exactly one)."""
+    paths = set()
+    with open("/proc/self/maps") as f:
+        for line in f:
+            if "libamdhip64" in line:
+                paths.add(line.split()[-1])
+    return sorted(paths)
 
 
 def raw_library():

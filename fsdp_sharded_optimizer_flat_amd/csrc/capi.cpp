@@ -257,20 +257,18 @@ extern "C" zero_status zero_gradnorm(const zero_layout *L, int32_t rank,
     rq.state_ptrs[0] = g_out;
     rq.n_state_ptrs = g_out ? 1 : 0;
     rq.out_ptr = nullptr;
-    const std::vector<Piece> pieces =
-        build_pieces(build_segments(L, rank, grad_index, g_index, ZERO_LOCAL), rq);
+    const std::vector<Segment> segs = build_segments(L, rank, grad_index, g_index, ZERO_LOCAL);
     double *partials = static_cast<double *>(workspace);
     double *result = partials + norm_partials_bound(L, rank);
-    int total = 0;
-    for (const Piece &pc : pieces) {
-        const std::vector<const void *> gp = offset_grads(grads, n_grads, pc.g_off, gsize);
-        int np = 0;
-        const int err = launch_norm_piece(pc, gp.data(), n_grads, grad_dtype,
-                                          g_out ? g_out + pc.s_off : nullptr, c, partials + total,
-                                          &np, stream);
+    int64_t total = 0;
+    for (const Segment &sg : segs) {
+        const std::vector<const void *> gp = offset_grads(grads, n_grads, sg.g_off, gsize);
+        const int err = launch_norm_segment(sg.len, segment_vec_aligned(sg, rq), gp.data(), n_grads,
+                                            grad_dtype, g_out ? g_out + sg.s_off : nullptr, c,
+                                            partials + total, stream);
         if (err != hipSuccess)
             return hip_fail(err, "zero_gradnorm stage 1");
-        total += np;
+        total += norm_segment_blocks(sg.len);
     }
     if (total == 0) {
         *sumsq = 0.0;

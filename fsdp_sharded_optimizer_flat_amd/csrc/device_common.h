@@ -15,6 +15,7 @@ namespace zero {
 namespace dev {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -44,58 +45,52 @@ __device__ __forceinline__ void st_stream(T v, T *p)
 __device__ __forceinline__ float bf_lo(unsigned x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bf_hi(unsigned x) { return __uint_as_float(x & 0xffff0000u); }
 
-// Unpack one 16-byte load of 8 bf16 gradients; FIRST: s = G, else s = s + G.
-template <bool FIRST>
-__device__ __forceinline__ void acc_bf16x8(float s[8], u32x4 r)
-{
-    const float e[8] = {bf_lo(r.x), bf_hi(r.x), bf_lo(r.y), bf_hi(r.y),
-                        bf_lo(r.z), bf_hi(r.z), bf_lo(r.w), bf_hi(r.w)};
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-        s[k] = FIRST ? e[k] : s[k] + e[k];
-}
-
-template <bool FIRST>
-__device__ __forceinline__ void acc_f32x8(float s[8], f32x4 a, f32x4 b)
-{
-    const float e[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-        s[k] = FIRST ? e[k] : s[k] + e[k];
-}
-
-// Loads of chunk i (8 elements) of gradient buffer q.
-struct Bf16Chunk {
-    u32x4 r;
+// Loads of quad i (elements 4i .. 4i+3) of one gradient buffer: 8 bytes of
+// bf16 or 16 bytes of fp32 per lane.  Lane l of a wave reads quad
+// (tile * 64 + l), so each wave instruction covers one contiguous span.
+struct Bf16Quad {
+    u32x2 r;
     __device__ __forceinline__ void load(const void *base, int64_t i)
     {
-        r = ld_stream(reinterpret_cast<const u32x4 *>(base) + i);
+        r = ld_stream(reinterpret_cast<const u32x2 *>(base) + i);
     }
     template <bool FIRST>
-    __device__ __forceinline__ void add_to(float s[8]) const { acc_bf16x8<FIRST>(s, r); }
+    __device__ __forceinline__ void add_to(float s[4]) const
+    {
+        const float e[4] = {bf_lo(r.x), bf_hi(r.x), bf_lo(r.y), bf_hi(r.y)};
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            s[k] = FIRST ? e[k] : s[k] + e[k];
+    }
 };
-struct F32Chunk {
-    f32x4 a, b;
+struct F32Quad {
+    f32x4 a;
     __device__ __forceinline__ void load(const void *base, int64_t i)
     {
-        const f32x4 *p = reinterpret_cast<const f32x4 *>(base) + 2 * i;
-        a = ld_stream(p);
-        b = ld_stream(p + 1);
+        a = ld_stream(reinterpret_cast<const f32x4 *>(base) + i);
     }
     template <bool FIRST>
-    __device__ __forceinline__ void add_to(float s[8]) const { acc_f32x8<FIRST>(s, a, b); }
+    __device__ __forceinline__ void add_to(float s[4]) const
+    {
+        const float e[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            s[k] = FIRST ? e[k] : s[k] + e[k];
+    }
 };
 
-// s[k] = G_0[k] + G_1[k] + ... + G_{n-1}[k], left to right in rank order.
-// Loads are issued in batches ahead of the adds; the adds keep rank order.
-template <int NR, int CAP, typename CH>
-__device__ __forceinline__ void rank_sum(const GradSet<CAP> &gs, int n, int64_t i, float s[8])
+// s[k] = G_0[k] + G_1[k] + ... + G_{n-1}[k] over quad i, left to right in
+// rank order.  Loads are issued in batches ahead of the adds (at most 16
+// ranks in flight per lane, to bound register use at large N); the adds keep
+// rank order.
+template <int NR, int CAP, typename QD>
+__device__ __forceinline__ void rank_sum(const GradSet<CAP> &gs, int n, int64_t i, float s[4])
 {
     if constexpr (NR > 0) {
         constexpr int B = NR < 16 ? NR : 16;
 #pragma unroll
         for (int q0 = 0; q0 < NR; q0 += B) {
-            CH c[B];
+            QD c[B];
 #pragma unroll
             for (int b = 0; b < B; ++b)
                 c[b].load(gs.p[q0 + b], i);
@@ -109,13 +104,13 @@ __device__ __forceinline__ void rank_sum(const GradSet<CAP> &gs, int n, int64_t 
         }
     } else {
         {
-            CH c0;
+            QD c0;
             c0.load(gs.p[0], i);
             c0.template add_to<true>(s);
         }
         int q = 1;
         for (; q + 8 <= n; q += 8) {
-            CH c[8];
+            QD c[8];
 #pragma unroll
             for (int b = 0; b < 8; ++b)
                 c[b].load(gs.p[q + b], i);
@@ -124,7 +119,7 @@ __device__ __forceinline__ void rank_sum(const GradSet<CAP> &gs, int n, int64_t 
                 c[b].template add_to<false>(s);
         }
         for (; q < n; ++q) {
-            CH c;
+            QD c;
             c.load(gs.p[q], i);
             c.template add_to<false>(s);
         }
@@ -188,13 +183,21 @@ __device__ __forceinline__ uint16_t to_bf16(float x)
     return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
 
-// Sum of a double over a 256-thread workgroup in a fixed order; valid in
-// thread 0.  Wave64 butterfly, then the four wave totals in wave order.
-__device__ __forceinline__ double block_sum(double x)
+// Sum of a double over one wave64 in a fixed order (butterfly); every lane
+// ends with the same bits.
+__device__ __forceinline__ double wave_sum(double x)
 {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1)
         x = x + __shfl_xor(x, off, 64);
+    return x;
+}
+
+// Sum of a double over a kBlock-thread workgroup in a fixed order; valid in
+// thread 0.  Wave butterflies, then the wave totals in wave order.
+__device__ __forceinline__ double block_sum(double x)
+{
+    x = wave_sum(x);
     __shared__ double wave_tot[kBlock / 64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     if (lane == 0)

@@ -77,25 +77,33 @@ static inline int64_t need_mod(const void *p, int elem, int64_t off, int mult)
     return (mult - r) % mult;
 }
 
+// Quad accesses need 16 bytes of alignment for fp32 buffers and 8 bytes for
+// bf16 buffers; either way a multiple of kQuad elements from a suitably
+// aligned address.
+static inline int64_t quad_need(const void *p, int elem, int64_t off)
+{
+    const int bytes = elem == 4 ? 16 : 8;
+    const int mult = bytes / elem;  // elements per aligned unit: 4 in both cases
+    return need_mod(p, elem, off, mult);
+}
+
 std::vector<Piece> build_pieces(const std::vector<Segment> &segs, const Request &rq)
 {
     std::vector<Piece> pieces;
     const int gsize = rq.grad_dtype == ZERO_BF16 ? 2 : 4;
-    const int gmult = gsize == 2 ? 8 : 4;  // elements per 16 bytes
     for (const Segment &s : segs) {
-        // Find the head length h in [0, 8) that puts every buffer on a
-        // 16-byte boundary; h must also make the body start chunk-aligned
-        // for each buffer type, so test the candidates directly.
+        // The head h in [0, kQuad) after which every buffer is quad-aligned;
+        // none exists when the buffers' phases disagree.
         int64_t head = -1;
-        for (int64_t h = 0; h < kChunk && head < 0; ++h) {
+        for (int64_t h = 0; h < kQuad && head < 0; ++h) {
             bool ok = true;
             for (int q = 0; q < rq.n_grads && ok; ++q)
-                ok = (need_mod(rq.grads[q], gsize, s.g_off, gmult) == h % gmult);
+                ok = quad_need(rq.grads[q], gsize, s.g_off) == h;
             for (int i = 0; i < rq.n_state_ptrs && ok; ++i)
                 if (rq.state_ptrs[i])
-                    ok = (need_mod(rq.state_ptrs[i], 4, s.s_off, 4) == h % 4);
+                    ok = quad_need(rq.state_ptrs[i], 4, s.s_off) == h;
             if (ok && rq.out_ptr)
-                ok = (need_mod(rq.out_ptr, 2, s.o_off, 8) == h % 8);
+                ok = quad_need(rq.out_ptr, 2, s.o_off) == h;
             if (ok)
                 head = h;
         }
@@ -103,7 +111,7 @@ std::vector<Piece> build_pieces(const std::vector<Segment> &segs, const Request 
             pieces.push_back({s.g_off, s.s_off, s.o_off, s.len, false});
             continue;
         }
-        const int64_t body = (s.len - head) / kChunk * kChunk;
+        const int64_t body = (s.len - head) / kQuad * kQuad;
         if (head > 0)
             pieces.push_back({s.g_off, s.s_off, s.o_off, head, false});
         if (body > 0)
@@ -116,13 +124,24 @@ std::vector<Piece> build_pieces(const std::vector<Segment> &segs, const Request 
     return pieces;
 }
 
+bool segment_vec_aligned(const Segment &s, const Request &rq)
+{
+    const int gsize = rq.grad_dtype == ZERO_BF16 ? 2 : 4;
+    for (int q = 0; q < rq.n_grads; ++q)
+        if (quad_need(rq.grads[q], gsize, s.g_off) != 0)
+            return false;
+    for (int i = 0; i < rq.n_state_ptrs; ++i)
+        if (rq.state_ptrs[i] && quad_need(rq.state_ptrs[i], 4, s.s_off) != 0)
+            return false;
+    return true;
+}
+
 int64_t norm_partials_bound(const zero_layout *L, int32_t rank)
 {
-    // At most one segment per unit (one in total for rank < 0); each yields a
-    // body of at most kNormMaxBlocks partials and two one-block scalar pieces,
-    // or a single scalar piece of at most kNormMaxBlocks partials.
-    int64_t segs = rank < 0 ? 1 : (L->n_units > 0 ? L->n_units : 1);
-    return segs * (kNormMaxBlocks + 2);
+    // One partial per started kNormSpan elements of each segment; at most one
+    // segment per unit (one in total for rank < 0).
+    const int64_t segs = rank < 0 ? 1 : (L->n_units > 0 ? L->n_units : 1);
+    return selected_elements(L, rank) / kNormSpan + segs;
 }
 
 }  // namespace zero

@@ -10,11 +10,16 @@
 
 namespace zero {
 
-// Elements per vector chunk: 8 bf16 gradients are one 16-byte load, 8 fp32
-// state values are two.
-constexpr int kChunk = 8;
-constexpr int kBlock = 256;          // threads per workgroup (4 wave64s)
-constexpr int kNormMaxBlocks = 1024; // fixed partition of the norm's first stage
+// The vector kernels give each lane one quad of 4 consecutive elements (8
+// bytes of bf16, 16 bytes of fp32) and each wave64 one tile of 64 quads, so
+// every wave-wide load or store covers one contiguous span.
+constexpr int kQuad = 4;
+constexpr int kWave = 64;
+constexpr int kTile = kQuad * kWave;       // 256 elements per wave
+constexpr int kBlock = 256;                // threads of the grid-stride / final kernels
+constexpr int kNormTilesPerWave = 8;       // norm: one partial per 2048 elements
+constexpr int kNormSpan = kTile * kNormTilesPerWave;
+constexpr int64_t kMaxQuadsPerLaunch = int64_t(1) << 30;  // 32-bit dispatch grid size
 
 // One contiguous run of elements whose gradient, state and output indices all
 // advance together.  Offsets are element offsets into the respective buffers.
@@ -22,9 +27,10 @@ struct Segment {
     int64_t g_off, s_off, o_off, len;
 };
 
-// A piece of a segment handed to one kernel launch: either a vector body
-// (len is a multiple of kChunk and every buffer is 16-byte aligned at its
-// start) or a scalar piece (any alignment).
+// A piece of a segment handed to the kernels: either a vector body (len is a
+// multiple of kQuad and every buffer is aligned for quad accesses at its
+// start: 16 bytes for fp32, 8 bytes for bf16) or a scalar piece (any
+// alignment).
 struct Piece {
     int64_t g_off, s_off, o_off, len;
     bool vec;
@@ -84,11 +90,16 @@ bool is_pow2_float(float x, float *inv);
 int launch_step_piece(const Piece &pc, const void *const *grads, int n_grads, int grad_dtype,
                       float *w, float *m, float *v, uint16_t *out, const StepConsts &c,
                       void *stream);
-int launch_norm_piece(const Piece &pc, const void *const *grads, int n_grads, int grad_dtype,
-                      float *g_out, const StepConsts &c, double *partials, int *n_partials,
-                      void *stream);
-int norm_piece_blocks(const Piece &pc);
-int launch_norm_final(const double *partials, int n_partials, double *result, void *stream);
+int launch_norm_segment(int64_t len, bool vec, const void *const *grads, int n_grads,
+                        int grad_dtype, float *g_out, const StepConsts &c, double *partials,
+                        void *stream);
+int64_t norm_segment_blocks(int64_t len);
+
+// True if every gradient (at element g_off) and g_out (at s_off, if given)
+// is aligned for quad accesses, so the norm can use vector accesses on a
+// segment.
+bool segment_vec_aligned(const Segment &s, const Request &rq);
+int launch_norm_final(const double *partials, int64_t n_partials, double *result, void *stream);
 int launch_convert(const void *src, int src_dtype, void *dst, int dst_dtype, int64_t n,
                    void *stream);
 int launch_fill_zero(void *dst, int dtype, int64_t n, void *stream);

@@ -236,9 +236,11 @@ zero_status zero_step(const zero_layout *layout, int32_t rank,
  * Sum of squares, accumulated in binary64, of g = (rank-ordered binary32 sum
  * of the gradients) / divisor over the processed elements (same selection and
  * index rules as zero_step).  Two kernels: each workgroup of the first reduces
- * a fixed grid-stride partition to one binary64 partial; a single workgroup of
- * the second sums the partials in a fixed order.  The partition depends only
- * on the layout and rank, so the result is bitwise reproducible.
+ * a fixed grid-stride partition of 8-element chunks to one binary64 partial; a
+ * single workgroup of the second sums the partials in a fixed order.  The
+ * partition depends only on the layout, the rank and the index spaces (not on
+ * the device, pointer alignment or whether g_out is written), so the result is
+ * bitwise reproducible.
  *   g_out:      if not NULL, g is also written (fp32, g_index space), so the
  *               step can read one reduced gradient instead of N.
  *   workspace:  caller device memory of at least zero_gradnorm_workspace_bytes.

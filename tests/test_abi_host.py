@@ -255,7 +255,7 @@ def test_gradnorm_argument_errors():
     L = z.zero_pack(4, [1000])
     lib = z.raw_library()
     need = z.zero_gradnorm_workspace_bytes(L, -1)
-    assert need == 8 * (1 + 1026)
+    assert need == 8 * (1000 // 2048 + 1 + 1)   # partials (one per 2048 elements and segment) + result
     arr = (C.c_void_p * 1)(0x1000)
     res = C.c_double()
     # short workspace

@@ -30,6 +30,13 @@ def log(msg):
     print(msg, flush=True)
 
 
+def test_one_hip_runtime():
+    """The library and torch share one HIP runtime in the process."""
+    torch.zeros(1, device=DEV)
+    maps = z.hip_runtimes_mapped()
+    assert len(maps) == 1, maps
+
+
 # ---------------------------------------------------------------------------
 # The pages' toy, 50 steps, bit-exact (fp32 gradients w - t_r).
 # ---------------------------------------------------------------------------
@@ -183,8 +190,8 @@ def test_ragged_multitile_and_no_out():
 
 
 def test_reduced_gradient_input():
-    """n_grads = 1 with divisor 1: the step on an already-reduced fp32
-    gradient (how the clipped step consumes the norm pass's output)."""
+    """n_grads = 1: the step on an already-reduced fp32 gradient, the way the
+    clipped step consumes the norm pass's output."""
     rng = np.random.default_rng(6)
     _run_case(rng, 8, [4096 + 3], 2, z.ZERO_F32, Lc, Lc, Lc, shift=0, n_grads=1)
 
