@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -126,6 +127,76 @@ int device_cu_count()
     return cache[(size_t)dev];
 }
 
+namespace {
+struct DeviceLds {
+    int per_cu = 0, per_block = 0;
+};
+DeviceLds device_lds()
+{
+    static std::mutex mu;
+    static std::vector<DeviceLds> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return {};
+    std::lock_guard<std::mutex> lock(mu);
+    if ((size_t)dev >= cache.size())
+        cache.resize((size_t)dev + 1);
+    DeviceLds &d = cache[(size_t)dev];
+    if (d.per_cu == 0) {
+        int cu = 0, blk = 0;
+        if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+                hipSuccess ||
+            hipDeviceGetAttribute(&blk, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
+                hipSuccess)
+            return {};
+        d.per_cu = cu;
+        d.per_block = blk;
+    }
+    return d;
+}
+
+int env_int(const char *name, int dflt, int lo, int hi)
+{
+    if (const char *e = std::getenv(name)) {
+        const int x = std::atoi(e);
+        if (x >= lo && x <= hi)
+            return x;
+    }
+    return dflt;
+}
+}  // namespace
+
+size_t occupancy_cap_lds(int waves_per_cu)
+{
+    if (waves_per_cu <= 0)
+        return 0;
+    const DeviceLds d = device_lds();
+    if (d.per_cu <= 0 || d.per_block <= 0)
+        return 0;
+    size_t lds = (size_t)d.per_cu / (size_t)waves_per_cu;
+    lds = lds / 512 * 512;  // whole allocation granules, rounding the cap up
+    if (lds > (size_t)d.per_block)
+        lds = (size_t)d.per_block;
+    return lds;
+}
+
+int step_waves_per_cu(int n_grads)
+{
+    // 8 resident one-wave workgroups per CU (2 per SIMD): with every wave
+    // streaming 2N + 3 reads and 4 writes, a smaller window of tiles in
+    // flight keeps fewer DRAM rows competing per bank.
+    static const int v = env_int("ZERO_STEP_WAVES_PER_CU", -1, 0, 64);
+    (void)n_grads;
+    return v >= 0 ? v : 8;
+}
+
+int norm_waves_per_cu(int n_grads)
+{
+    static const int v = env_int("ZERO_NORM_WAVES_PER_CU", -1, 0, 64);
+    (void)n_grads;
+    return v >= 0 ? v : 0;
+}
+
 zero_status hip_fail(int err, const char *where)
 {
     char buf[256];
@@ -209,7 +280,8 @@ extern "C" zero_status zero_gradnorm_workspace_bytes(const zero_layout *L, int32
 {
     if (!layout_ok(L) || !bytes || rank >= L->n_ranks)
         return ZERO_EINVAL;
-    *bytes = (size_t)(norm_partials_bound(L, rank) + 1) * sizeof(double);
+    const int64_t np = norm_partials_bound(L, rank);
+    *bytes = (size_t)(np + 1 + norm_tree_scratch(np)) * sizeof(double);
     return ZERO_OK;
 }
 
@@ -274,7 +346,8 @@ extern "C" zero_status zero_gradnorm(const zero_layout *L, int32_t rank,
         *sumsq = 0.0;
         return ZERO_OK;
     }
-    int err = launch_norm_final(partials, total, result, stream);
+    // result sits right after the partials; the tree's intermediate levels after it
+    int err = launch_norm_tree(partials, total, result + 1, result, stream);
     if (err != hipSuccess)
         return hip_fail(err, "zero_gradnorm stage 2");
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);

@@ -144,6 +144,17 @@ int64_t norm_partials_bound(const zero_layout *L, int32_t rank)
     return selected_elements(L, rank) / kNormSpan + segs;
 }
 
+int64_t norm_tree_scratch(int64_t n)
+{
+    // sum over the levels of ceil(n / kNormFanIn^k), k >= 1, until one value
+    int64_t total = 0;
+    while (n > 1) {
+        n = (n + kNormFanIn - 1) / kNormFanIn;
+        total += n;
+    }
+    return total;
+}
+
 }  // namespace zero
 
 using namespace zero;

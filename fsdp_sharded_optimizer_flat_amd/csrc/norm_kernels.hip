@@ -6,11 +6,11 @@
 // reduction costing O(1) scalars per rank.
 //
 // Stage 1 fuses the reduction half of the reduce-scatter with the sum of
-// squares: each lane forms g = (rank-ordered sum) / divisor for its quads,
+// squares: each lane forms g = (rank-ordered sum) / divisor for its quad,
 // optionally writes g (fp32) so the step can read one reduced gradient instead
 // of N, and accumulates g^2 in binary64.  Each wave reduces its lanes in a
-// fixed order to one partial per 2048 elements.  Stage 2 is one workgroup
-// summing the partials in a fixed order.
+// fixed order to one partial per 256-element tile.  Stage 2 sums the partials
+// in a fixed-order tree of 1024-way workgroups.
 // The partition (segments, grid size, chunk assignment) depends only on the
 // layout, the rank and the index spaces -- never on the device, the pointers'
 // alignment or whether g is written -- so the result is bitwise reproducible.
@@ -22,17 +22,17 @@ namespace {
 using namespace dev;
 
 // Stage 1 over one segment of `len` elements.  The elements form logical
-// quads (4 consecutive elements; the last quad may be partial) and spans of
-// kNormSpan elements; workgroup b (one wave64) owns span b, lane l the quads
-// (b * kNormTilesPerWave + t) * 64 + l for t = 0 .. kNormTilesPerWave-1.  Each
-// lane adds its quads' squares in that order (element order inside a quad),
-// the wave sums its lanes by a fixed butterfly, and lane 0 writes the span's
-// partial.  Absent elements of a partial quad contribute +0.0, which leaves a
-// binary64 sum unchanged.  VEC selects quad-wide loads / stores (every buffer
-// aligned at the segment start); without it the same quads are read element
-// by element.  Either way every value and every addition happen in the same
+// quads (4 consecutive elements; the last quad may be partial) and tiles of
+// 64 quads; workgroup b (one wave64) owns tile b and lane l its quad
+// b * 64 + l.  The lane adds its quad's squares in element order, the wave
+// sums its lanes by a fixed butterfly, and lane 0 writes the tile's partial.
+// Absent elements of a partial quad contribute +0.0, which leaves a binary64
+// sum unchanged.  VEC selects quad-wide loads / stores (every buffer aligned
+// at the segment start); without it the same quads are read element by
+// element.  Either way every value and every addition happen in the same
 // order, so the result depends on neither pointer alignment nor on whether
-// g_out is written.
+// g_out is written.  One tile per workgroup (a non-persistent grid) keeps the
+// tiles in flight in one compact window, as in the step kernel.
 template <int NR, int CAP, typename GT, typename QD, bool POW2, bool VEC>
 __global__ __launch_bounds__(kWave) void norm_kernel(GradSet<CAP> gs, int n,
                                                     float *__restrict__ G, int64_t len,
@@ -40,12 +40,9 @@ __global__ __launch_bounds__(kWave) void norm_kernel(GradSet<CAP> gs, int n,
                                                     double *__restrict__ partials)
 {
     const int64_t nquads = (len + kQuad - 1) / kQuad;
+    const int64_t i = (int64_t)blockIdx.x * kWave + threadIdx.x;
     double acc = 0.0;
-#pragma unroll 1
-    for (int t = 0; t < kNormTilesPerWave; ++t) {
-        const int64_t i = ((int64_t)blockIdx.x * kNormTilesPerWave + t) * kWave + threadIdx.x;
-        if (i >= nquads)
-            break;
+    if (i < nquads) {
         const int64_t e0 = i * kQuad;
         const int cnt = len - e0 >= kQuad ? kQuad : (int)(len - e0);
         float g[4];
@@ -82,15 +79,22 @@ __global__ __launch_bounds__(kWave) void norm_kernel(GradSet<CAP> gs, int n,
         partials[blockIdx.x] = t;
 }
 
-__global__ __launch_bounds__(kBlock) void norm_final_kernel(const double *__restrict__ partials,
+// One level of the fixed-order reduction of the partials: workgroup b sums
+// in[b * kNormFanIn .. min(n, (b + 1) * kNormFanIn)) -- thread t takes the
+// four consecutive values at b * kNormFanIn + 4t, in order, then the
+// workgroup sums its threads in a fixed order -- and writes out[b].
+__global__ __launch_bounds__(kBlock) void norm_level_kernel(const double *__restrict__ in,
                                                            int64_t n, double *__restrict__ out)
 {
+    const int64_t base = (int64_t)blockIdx.x * kNormFanIn + 4 * (int64_t)threadIdx.x;
     double acc = 0.0;
-    for (int64_t i = threadIdx.x; i < n; i += kBlock)
-        acc = acc + partials[i];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        if (base + k < n)
+            acc = acc + in[base + k];
     const double t = block_sum(acc);
     if (threadIdx.x == 0)
-        *out = t;
+        out[blockIdx.x] = t;
 }
 
 template <int NR, typename GT, typename QD, bool POW2, bool VEC>
@@ -101,8 +105,9 @@ hipError_t launch_nr(const void *const *grads, int n, float *G, int64_t len, con
     GradSet<CAP> gs{};
     for (int q = 0; q < n; ++q)
         gs.p[q] = grads[q];
+    const size_t lds = occupancy_cap_lds(norm_waves_per_cu(n));
     hipLaunchKernelGGL((norm_kernel<NR, CAP, GT, QD, POW2, VEC>), dim3((unsigned)blocks),
-                       dim3(kWave), 0, st, gs, n, G, len, c, partials);
+                       dim3(kWave), lds, st, gs, n, G, len, c, partials);
     return hipGetLastError();
 }
 
@@ -156,12 +161,29 @@ int launch_norm_segment(int64_t len, bool vec, const void *const *grads, int n_g
               : launch_nr<0, float, F32Quad, false, false>(grads, n_grads, g_out, len, c, partials, blocks, st);
 }
 
-int launch_norm_final(const double *partials, int64_t n_partials, double *result, void *stream)
+int launch_norm_tree(const double *partials, int64_t n_partials, double *scratch, double *result,
+                     void *stream)
 {
+    // Levels of kNormFanIn-way sums until one value remains; the last level
+    // writes *result.  A single partial still passes through one level, so the
+    // result is always produced the same way.
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    hipLaunchKernelGGL(norm_final_kernel, dim3(1), dim3(kBlock), 0, st, partials, n_partials,
-                       result);
-    return hipGetLastError();
+    const double *in = partials;
+    int64_t n = n_partials;
+    double *out = scratch;
+    do {
+        const int64_t blocks = (n + kNormFanIn - 1) / kNormFanIn;
+        double *dst = blocks == 1 ? result : out;
+        hipLaunchKernelGGL(norm_level_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, st, in, n,
+                           dst);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+        in = dst;
+        n = blocks;
+        out += blocks;
+    } while (n > 1);
+    return hipSuccess;
 }
 
 }  // namespace zero

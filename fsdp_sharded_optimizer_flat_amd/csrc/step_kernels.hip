@@ -15,8 +15,9 @@
 // and written back whole.  The grid is not persistent: one tile per
 // workgroup, so the tiles in flight form one compact window that sweeps the
 // buffers in address order.  Loads and stores carry the nontemporal hint.
-#include <cstdlib>
-
+// The number of resident waves is capped (8 per CU by default, through a
+// dynamic LDS reservation the kernel never touches): fewer tiles in flight
+// keep fewer DRAM rows competing per bank across the 2N + 7 streams.
 #include "device_common.h"
 
 namespace zero {
@@ -107,13 +108,14 @@ hipError_t launch_quads_nr(const void *const *grads, int n, int gsize_quad, floa
                            hipStream_t st)
 {
     constexpr int CAP = NR > 0 ? NR : ZERO_MAX_RANKS;
+    const size_t lds = occupancy_cap_lds(step_waves_per_cu(n));
     for (int64_t q0 = 0; q0 < nquads; q0 += kMaxQuadsPerLaunch) {
         const int64_t nq = nquads - q0 < kMaxQuadsPerLaunch ? nquads - q0 : kMaxQuadsPerLaunch;
         GradSet<CAP> gs{};
         for (int q = 0; q < n; ++q)
             gs.p[q] = static_cast<const char *>(grads[q]) + q0 * gsize_quad;
         const unsigned blocks = (unsigned)((nq + kWave - 1) / kWave);
-        hipLaunchKernelGGL((step_quad_kernel<NR, CAP, QD, POW2>), dim3(blocks), dim3(kWave), 0, st,
+        hipLaunchKernelGGL((step_quad_kernel<NR, CAP, QD, POW2>), dim3(blocks), dim3(kWave), lds, st,
                            gs, n, w + q0 * kQuad, m + q0 * kQuad, v + q0 * kQuad,
                            o ? o + q0 * kQuad : nullptr, nq, c);
         const hipError_t e = hipGetLastError();

@@ -17,8 +17,8 @@ constexpr int kQuad = 4;
 constexpr int kWave = 64;
 constexpr int kTile = kQuad * kWave;       // 256 elements per wave
 constexpr int kBlock = 256;                // threads of the grid-stride / final kernels
-constexpr int kNormTilesPerWave = 8;       // norm: one partial per 2048 elements
-constexpr int kNormSpan = kTile * kNormTilesPerWave;
+constexpr int kNormSpan = kTile;           // norm: one partial per 256-element tile
+constexpr int kNormFanIn = 1024;           // partials one reduction workgroup combines
 constexpr int64_t kMaxQuadsPerLaunch = int64_t(1) << 30;  // 32-bit dispatch grid size
 
 // One contiguous run of elements whose gradient, state and output indices all
@@ -73,6 +73,18 @@ bool layout_ok(const zero_layout *L);
 // Compute units of the current device (cached per device).  <= 0 on error.
 int device_cu_count();
 
+// Dynamic LDS bytes to reserve per one-wave workgroup so that at most
+// `waves_per_cu` such workgroups are resident on a compute unit of the
+// current device (0 = no cap).  The kernels never touch this LDS: it only
+// bounds how many waves stream at once.  Cached per device.
+size_t occupancy_cap_lds(int waves_per_cu);
+
+// Target resident waves per CU of the step and norm kernels.  Defaults were
+// measured on MI355X; ZERO_STEP_WAVES_PER_CU / ZERO_NORM_WAVES_PER_CU
+// override them for launch-shape sweeps (0 disables the cap).
+int step_waves_per_cu(int n_grads);
+int norm_waves_per_cu(int n_grads);
+
 // Record a HIP error code for zero_last_hip_error(); returns ZERO_EHIP.
 zero_status hip_fail(int hip_error, const char *where);
 
@@ -99,7 +111,12 @@ int64_t norm_segment_blocks(int64_t len);
 // is aligned for quad accesses, so the norm can use vector accesses on a
 // segment.
 bool segment_vec_aligned(const Segment &s, const Request &rq);
-int launch_norm_final(const double *partials, int64_t n_partials, double *result, void *stream);
+// Reduce n_partials partials to one value at *result (fixed order, several
+// levels of kNormFanIn-way workgroups); scratch holds the intermediate
+// levels (norm_tree_scratch(n_partials) doubles).
+int launch_norm_tree(const double *partials, int64_t n_partials, double *scratch, double *result,
+                     void *stream);
+int64_t norm_tree_scratch(int64_t n_partials);
 int launch_convert(const void *src, int src_dtype, void *dst, int dst_dtype, int64_t n,
                    void *stream);
 int launch_fill_zero(void *dst, int dtype, int64_t n, void *stream);
