@@ -93,6 +93,8 @@ _zero_gradnorm_workspace_bytes = _sig("zero_gradnorm_workspace_bytes", i32, vp, 
                                       C.POINTER(sz))
 _zero_gradnorm = _sig("zero_gradnorm", i32, vp, i32, vp, i32, i32, i32, f32, vp, i32, vp, sz,
                       C.POINTER(f64), vp)
+_zero_gradnorm_async = _sig("zero_gradnorm_async", i32, vp, i32, vp, i32, i32, i32, f32, vp, i32, vp,
+                            sz, vp, vp)
 _zero_clip_coef = _sig("zero_clip_coef", i32, f64, f64, C.POINTER(f32))
 _zero_ledger = _sig("zero_ledger", i32, f64, i32, i32, i32, C.POINTER(ZeroLedgerOut))
 _zero_gather_buffer_bytes = _sig("zero_gather_buffer_bytes", i32, vp, i32, C.POINTER(f64))
@@ -106,7 +108,8 @@ _zero_abi_version = _sig("zero_abi_version", i32)
 
 EXPORTED = ["zero_layout_bytes", "zero_pack", "zero_global_index", "zero_owner", "zero_pack_copy",
             "zero_unpack_copy", "zero_adamw_scalars_for", "zero_adamw_scalars_next", "zero_step",
-            "zero_gradnorm_workspace_bytes", "zero_gradnorm", "zero_clip_coef", "zero_ledger",
+            "zero_gradnorm_workspace_bytes", "zero_gradnorm", "zero_gradnorm_async",
+            "zero_clip_coef", "zero_ledger",
             "zero_gather_buffer_bytes", "zero_step_traffic", "zero_gradnorm_traffic",
             "zero_strerror", "zero_last_hip_error", "zero_abi_version"]
 
@@ -337,6 +340,22 @@ def zero_gradnorm(layout: Layout, rank: int, grads, grad_index: int, divisor: fl
                           workspace.numel() * workspace.element_size(), C.byref(res),
                           _stream(stream)), "zero_gradnorm")
     return res.value
+
+
+def zero_gradnorm_async(layout: Layout, rank: int, grads, grad_index: int, divisor: float,
+                        g_out, g_index: int, workspace, sumsq_dev, stream=None):
+    """Enqueue the norm pass; the binary64 sum of squares lands in
+    ``sumsq_dev`` (a float64 device tensor) without synchronizing."""
+    torch = _torch()
+    if sumsq_dev.dtype != torch.float64:
+        raise TypeError("sumsq_dev must be a float64 device tensor")
+    arr, gdt = _grad_ptrs(grads)
+    _check(_zero_gradnorm_async(layout.ptr, rank, C.addressof(arr), len(arr), gdt, grad_index,
+                                divisor, _f32_ptr(g_out, "g_out") if g_out is not None else None,
+                                g_index, _dev_ptr(workspace, "workspace"),
+                                workspace.numel() * workspace.element_size(),
+                                _dev_ptr(sumsq_dev, "sumsq_dev"), _stream(stream)),
+           "zero_gradnorm_async")
 
 
 # -- ledger -------------------------------------------------------------------------------

@@ -285,20 +285,25 @@ extern "C" zero_status zero_gradnorm_workspace_bytes(const zero_layout *L, int32
     return ZERO_OK;
 }
 
-extern "C" zero_status zero_gradnorm(const zero_layout *L, int32_t rank,
-                                     const void *const *grads, int32_t n_grads,
-                                     int32_t grad_dtype, int32_t grad_index, float divisor,
-                                     float *g_out, int32_t g_index, void *workspace,
-                                     size_t workspace_bytes, double *sumsq, void *stream)
+namespace {
+
+// The norm pass up to the device-side result: validation, stage 1 over the
+// segments, the fixed-order tree.  *n_partials = 0 means nothing was selected
+// (no launch; the caller reports 0).
+zero_status gradnorm_launch(const zero_layout *L, int32_t rank, const void *const *grads,
+                            int32_t n_grads, int32_t grad_dtype, int32_t grad_index,
+                            float divisor, float *g_out, int32_t g_index, void *workspace,
+                            size_t workspace_bytes, double *result, void *stream,
+                            int64_t *n_partials)
 {
     zero_status st = check_grads(L, rank, grads, n_grads, grad_dtype, grad_index, divisor);
     if (st != ZERO_OK)
         return st;
-    if (!sumsq || !workspace || !index_ok(g_index))
+    if (!workspace || !index_ok(g_index) || !result)
         return ZERO_EINVAL;
     if (rank < 0 && (grad_index != ZERO_GLOBAL || g_index != ZERO_GLOBAL))
         return ZERO_EINVAL;
-    if (!aligned(workspace, 8) || (g_out && !aligned(g_out, 4)))
+    if (!aligned(workspace, 8) || (g_out && !aligned(g_out, 4)) || !aligned(result, 8))
         return ZERO_EALIGN;
     size_t need = 0;
     zero_gradnorm_workspace_bytes(L, rank, &need);
@@ -307,11 +312,14 @@ extern "C" zero_status zero_gradnorm(const zero_layout *L, int32_t rank,
     const int gsize = dsize(grad_dtype);
     const Range ws = range_of(workspace, (int64_t)need, 1);
     const Range go = g_out ? range_of(g_out, extent(L, g_index), 4) : Range{0, 0};
-    if (overlap(ws, go))
+    const Range rs = range_of(result, 1, 8);
+    if (overlap(ws, go) || overlap(rs, go) || (result != static_cast<double *>(workspace) +
+                                                          norm_partials_bound(L, rank) &&
+                                               overlap(rs, ws)))
         return ZERO_EINVAL;
     for (int q = 0; q < n_grads; ++q) {
         const Range g = range_of(grads[q], extent(L, grad_index), gsize);
-        if (overlap(g, ws) || overlap(g, go))
+        if (overlap(g, ws) || overlap(g, go) || overlap(g, rs))
             return ZERO_EINVAL;
     }
 
@@ -329,9 +337,10 @@ extern "C" zero_status zero_gradnorm(const zero_layout *L, int32_t rank,
     rq.state_ptrs[0] = g_out;
     rq.n_state_ptrs = g_out ? 1 : 0;
     rq.out_ptr = nullptr;
-    const std::vector<Segment> segs = build_segments(L, rank, grad_index, g_index, ZERO_LOCAL);
+    // workspace: [partials | result slot | tree levels]
     double *partials = static_cast<double *>(workspace);
-    double *result = partials + norm_partials_bound(L, rank);
+    double *tree = partials + norm_partials_bound(L, rank) + 1;
+    const std::vector<Segment> segs = build_segments(L, rank, grad_index, g_index, ZERO_LOCAL);
     int64_t total = 0;
     for (const Segment &sg : segs) {
         const std::vector<const void *> gp = offset_grads(grads, n_grads, sg.g_off, gsize);
@@ -342,17 +351,43 @@ extern "C" zero_status zero_gradnorm(const zero_layout *L, int32_t rank,
             return hip_fail(err, "zero_gradnorm stage 1");
         total += norm_segment_blocks(sg.len);
     }
-    if (total == 0) {
+    *n_partials = total;
+    if (total == 0)
+        return ZERO_OK;
+    const int err = launch_norm_tree(partials, total, tree, result, stream);
+    if (err != hipSuccess)
+        return hip_fail(err, "zero_gradnorm stage 2");
+    return ZERO_OK;
+}
+
+}  // namespace
+
+extern "C" zero_status zero_gradnorm(const zero_layout *L, int32_t rank,
+                                     const void *const *grads, int32_t n_grads,
+                                     int32_t grad_dtype, int32_t grad_index, float divisor,
+                                     float *g_out, int32_t g_index, void *workspace,
+                                     size_t workspace_bytes, double *sumsq, void *stream)
+{
+    if (!sumsq)
+        return ZERO_EINVAL;
+    if (!layout_ok(L) || rank >= L->n_ranks)
+        return ZERO_EINVAL;
+    // the result lives in the workspace's result slot
+    double *result = workspace ? static_cast<double *>(workspace) + norm_partials_bound(L, rank)
+                               : nullptr;
+    int64_t np = 0;
+    zero_status st = gradnorm_launch(L, rank, grads, n_grads, grad_dtype, grad_index, divisor,
+                                     g_out, g_index, workspace, workspace_bytes, result, stream,
+                                     &np);
+    if (st != ZERO_OK)
+        return st;
+    if (np == 0) {
         *sumsq = 0.0;
         return ZERO_OK;
     }
-    // result sits right after the partials; the tree's intermediate levels after it
-    int err = launch_norm_tree(partials, total, result + 1, result, stream);
-    if (err != hipSuccess)
-        return hip_fail(err, "zero_gradnorm stage 2");
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     double host = 0.0;
-    err = hipMemcpyAsync(&host, result, sizeof(double), hipMemcpyDeviceToHost, hs);
+    int err = hipMemcpyAsync(&host, result, sizeof(double), hipMemcpyDeviceToHost, hs);
     if (err != hipSuccess)
         return hip_fail(err, "zero_gradnorm readback");
     err = hipStreamSynchronize(hs);
@@ -360,6 +395,27 @@ extern "C" zero_status zero_gradnorm(const zero_layout *L, int32_t rank,
         return hip_fail(err, "zero_gradnorm synchronize");
     *sumsq = host;
     return ZERO_OK;
+}
+
+extern "C" zero_status zero_gradnorm_async(const zero_layout *L, int32_t rank,
+                                           const void *const *grads, int32_t n_grads,
+                                           int32_t grad_dtype, int32_t grad_index, float divisor,
+                                           float *g_out, int32_t g_index, void *workspace,
+                                           size_t workspace_bytes, double *sumsq_dev,
+                                           void *stream)
+{
+    if (!sumsq_dev)
+        return ZERO_EINVAL;
+    int64_t np = 0;
+    zero_status st = gradnorm_launch(L, rank, grads, n_grads, grad_dtype, grad_index, divisor,
+                                     g_out, g_index, workspace, workspace_bytes, sumsq_dev, stream,
+                                     &np);
+    if (st != ZERO_OK || np > 0)
+        return st;
+    // nothing selected: the sum is 0 (written by a kernel, not a memset, so
+    // the call may sit in a captured graph)
+    const int err = launch_fill_zero(sumsq_dev, ZERO_F32, 2, stream);
+    return err == hipSuccess ? ZERO_OK : hip_fail(err, "zero_gradnorm_async");
 }
 
 // ---------------------------------------------------------------------------

@@ -256,6 +256,18 @@ zero_status zero_gradnorm(const zero_layout *layout, int32_t rank,
                           void *workspace, size_t workspace_bytes,
                           double *sumsq, void *stream);
 
+/* The same pass without the host synchronization (async): the binary64 sum
+ * of squares is written to the device pointer sumsq_dev (8-byte aligned,
+ * outside the workspace), bitwise equal to what zero_gradnorm returns.  For
+ * callers that keep the norm on the stream (a later kernel, a graph, an
+ * all-reduce of the per-rank sums) or time it with events. */
+zero_status zero_gradnorm_async(const zero_layout *layout, int32_t rank,
+                                const void *const *grads, int32_t n_grads, int32_t grad_dtype,
+                                int32_t grad_index, float divisor,
+                                float *g_out, int32_t g_index,
+                                void *workspace, size_t workspace_bytes,
+                                double *sumsq_dev, void *stream);
+
 /* Clip coefficient from a sum of squares (host): norm = sqrt(sumsq) and
  * coef = min(1, max_norm / (norm + 1e-6)) in binary64, rounded once to
  * binary32 -- the convention of the clip_grad_norm_ routine [p1

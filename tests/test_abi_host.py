@@ -271,6 +271,13 @@ def test_gradnorm_argument_errors():
                              need, C.byref(res), None) == z.ZERO_EALIGN
     assert lib.zero_gradnorm(L.ptr, -1, C.addressof(arr), 1, 1, 0, 1.0, None, 0, 0x1000 + 8,
                              need, C.byref(res), None) == z.ZERO_EINVAL
+    # async: NULL / misaligned result, result inside a gradient
+    assert lib.zero_gradnorm_async(L.ptr, -1, C.addressof(arr), 1, 1, 0, 1.0, None, 0, 0x20000000,
+                                   need, None, None) == z.ZERO_EINVAL
+    assert lib.zero_gradnorm_async(L.ptr, -1, C.addressof(arr), 1, 1, 0, 1.0, None, 0, 0x20000000,
+                                   need, 0x30000004, None) == z.ZERO_EALIGN
+    assert lib.zero_gradnorm_async(L.ptr, -1, C.addressof(arr), 1, 1, 0, 1.0, None, 0, 0x20000000,
+                                   need, 0x1000 + 16, None) == z.ZERO_EINVAL
 
 
 def test_strerror():

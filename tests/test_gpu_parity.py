@@ -421,6 +421,33 @@ def test_norm_and_clipped_step_vs_oracle(n, numel, rank, gidx, gdt):
     assert_same_f32(to_np(W2), om, "clipped master from N gradients")
 
 
+def test_norm_async_equals_sync():
+    """The async pass leaves the same bits on the device as the synchronous
+    call returns, for vector and unaligned pieces and an empty selection."""
+    rng = np.random.default_rng(14)
+    for n, numel, rank, gidx in [(8, [100_003, 5], -1, G), (8, [100_003, 5], 3, G), (16, [16 * 999], 2, Lc)]:
+        L = z.zero_pack(n, numel)
+        ge = extent(L, gidx)
+        se = extent(L, G if rank < 0 else Lc)
+        grads = [dev_buffer(ge, torch.bfloat16, shift=q % 3) for q in range(n)]
+        for g in grads:
+            g.copy_(torch.from_numpy((rng.standard_normal(ge) * 1e-2).astype(np.float32)).to(torch.bfloat16))
+        ws = torch.zeros(z.zero_gradnorm_workspace_bytes(L, rank) // 8, dtype=torch.float64, device=DEV)
+        sidx = G if rank < 0 else Lc
+        want = z.zero_gradnorm(L, rank, grads, gidx, float(n), None, sidx, ws)
+        res = torch.full((1,), -1.0, dtype=torch.float64, device=DEV)
+        z.zero_gradnorm_async(L, rank, grads, gidx, float(n), None, sidx, ws, res)
+        torch.cuda.synchronize()
+        assert res.item() == want
+    L = z.zero_pack(4, [0])
+    g = torch.zeros(8, dtype=torch.bfloat16, device=DEV)
+    ws = torch.zeros(z.zero_gradnorm_workspace_bytes(L, -1) // 8, dtype=torch.float64, device=DEV)
+    res = torch.full((1,), -1.0, dtype=torch.float64, device=DEV)
+    z.zero_gradnorm_async(L, -1, [g], G, 4.0, None, G, ws, res)
+    torch.cuda.synchronize()
+    assert res.item() == 0.0 and not torch.signbit(res).item()
+
+
 def test_norm_closed_form():
     """Every rank's gradient equal to c: the average is c exactly and the sum
     of squares is (elements) * c^2 exactly in binary64."""
