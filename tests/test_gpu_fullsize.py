@@ -114,3 +114,36 @@ def test_llama8b_z3_norm_full_size():
     coef = z.zero_clip_coef(s1, wl.clip_max_norm)
     log(f"norm: sumsq={s1:.6e} norm={np.sqrt(s1):.4f} clip coef={coef:.6f}")
     assert 0.0 < coef < 1.0, "Student-t(3) x 1e-3 gradients over 125M elements must trigger clipping"
+
+
+def test_step_beyond_one_launch():
+    """2^32 + 17 elements at N = 1: more quads than one dispatch addresses
+    (2^30), so the step runs as two vector launches plus a scalar tail.  The
+    oracle checks elements around both launch boundaries and random ones."""
+    n, P = 1, (1 << 32) + 17
+    h = WORKLOADS["gpt2l"].hyper
+    L = z.zero_pack(n, [P])
+    log(f"max-size: P={P} ({P * 18 / 1e9:.1f} GB of device buffers)")
+    g = torch.empty(P, dtype=torch.bfloat16, device=DEV)
+    synth.fill_normal_(g, 1e-3, 99)
+    master = torch.empty(P, dtype=torch.float32, device=DEV)
+    synth.fill_normal_(master, 0.02, 98)
+    m, v = torch.zeros_like(master), torch.zeros_like(master)
+    out = torch.zeros(P, dtype=torch.int16, device=DEV)
+    rng = np.random.default_rng(5)
+    edge = (1 << 30) * 4                   # first element of the second launch
+    picks = set(int(x) for x in rng.integers(0, P, 4096))
+    picks.update(range(0, 8))
+    picks.update(range(edge - 8, edge + 8))
+    picks.update(range(P - 24, P))
+    idx = np.array(sorted(picks), np.int64)
+    idx_t = torch.from_numpy(idx).to(DEV)
+    master0 = gather_np(master, idx_t)
+    gs = [[gather_np(g, idx_t)]]
+    z.zero_step(L, -1, [g], G, 1.0, master, m, v, G, out, G, scalars(1, h))
+    torch.cuda.synchronize()
+    w, mm, vv, oo = oracle_on_samples(1, gs, master0, 1, h, divisor=1.0)
+    assert_same_f32(gather_np(master, idx_t), w, "max-size master")
+    assert_same_f32(gather_np(v, idx_t), vv, "max-size v")
+    assert_same_bf16(gather_np(out, idx_t), oo, "max-size out")
+    del g, master, m, v, out
