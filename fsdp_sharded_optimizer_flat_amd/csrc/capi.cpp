@@ -182,12 +182,14 @@ size_t occupancy_cap_lds(int waves_per_cu)
 
 int step_waves_per_cu(int n_grads)
 {
-    // 8 resident one-wave workgroups per CU (2 per SIMD): with every wave
-    // streaming 2N + 3 reads and 4 writes, a smaller window of tiles in
-    // flight keeps fewer DRAM rows competing per bank.
+    // 7 resident one-wave workgroups per CU (under 2 per SIMD): with every
+    // wave streaming 2N + 3 reads and 4 writes, a smaller window of tiles in
+    // flight keeps fewer DRAM rows competing per bank.  Measured on MI355X
+    // for N = 8 and N = 64: 6 starves the memory pipeline, 7 is best, 8 / 9 /
+    // 12 / uncapped lose 1 / 2 / 4 / 6 points of the 8 TB/s peak.
     static const int v = env_int("ZERO_STEP_WAVES_PER_CU", -1, 0, 64);
     (void)n_grads;
-    return v >= 0 ? v : 8;
+    return v >= 0 ? v : 7;
 }
 
 int norm_waves_per_cu(int n_grads)

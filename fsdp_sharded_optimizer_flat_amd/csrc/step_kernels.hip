@@ -7,7 +7,7 @@
 // ("ZeRO and FSDP sharding", How it works and Code).
 //
 // The work is elementwise and streams every byte once, so the kernel is bound
-// by HBM bandwidth: no MFMA, no LDS.  Mapping: each workgroup is one wave64
+// by HBM bandwidth: no MFMA, and no LDS traffic.  Mapping: each workgroup is one wave64
 // and owns one tile of 256 consecutive elements; lane l owns the quad
 // 4l .. 4l+3 of the tile.  Every wave-wide access is therefore one contiguous
 // span -- 512 bytes per rank's bf16 gradients and per bf16 output, 1 KiB per
@@ -15,7 +15,7 @@
 // and written back whole.  The grid is not persistent: one tile per
 // workgroup, so the tiles in flight form one compact window that sweeps the
 // buffers in address order.  Loads and stores carry the nontemporal hint.
-// The number of resident waves is capped (8 per CU by default, through a
+// The number of resident waves is capped (7 per CU by default, through a
 // dynamic LDS reservation the kernel never touches): fewer tiles in flight
 // keep fewer DRAM rows competing per bank across the 2N + 7 streams.
 #include "device_common.h"
