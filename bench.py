@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of known size (PMC calibration)")
+    ap.add_argument("--host-step", action="store_true",
+                    help="time the offload step on host cores (zero_step_host) instead of the GPU")
+    ap.add_argument("--threads", type=int, default=0, help="host-step worker threads (0: all)")
     return ap.parse_args()
 
 
@@ -112,8 +115,64 @@ def cpu_baseline(wl, seconds: float):
                       f"(N={n}, {wl.grad_dist} bf16 gradients), serial C, {el:.1f} s"}
 
 
+def host_step_bench(args):
+    """The ZeRO-Offload step on host cores: the workload's rank count and
+    distributions on host memory, every element of one rank's shard (or of
+    all shards) per step.  Prints one JSON line."""
+    import numpy as np
+    import torch
+
+    import fsdp_sharded_optimizer_flat_amd as z
+    from fsdp_sharded_optimizer_flat_amd import synth
+    from fsdp_sharded_optimizer_flat_amd.workloads import WORKLOADS
+
+    wl = WORKLOADS[args.workload]
+    n, h = wl.n_ranks, wl.hyper
+    L = z.zero_pack(n, wl.unit_numel)
+    G, Lc = z.ZERO_GLOBAL, z.ZERO_LOCAL
+    gidx = G if wl.grad_index == "global" else Lc
+    sidx = G if wl.rank < 0 else Lc
+    oidx = G if wl.out_index == "global" else Lc
+    ge = L.padded if gidx == G else L.shard
+    se = L.padded if sidx == G else L.shard
+    oe = L.padded if oidx == G else L.shard
+    master = torch.empty(se, dtype=torch.float32)
+    synth.fill_normal_(master, wl.master_std, synth.seed_of(wl.seed, synth.TAG_MASTER))
+    m, v = torch.zeros_like(master), torch.zeros_like(master)
+    out = torch.zeros(oe, dtype=torch.int16)
+    grads = torch.empty(n, ge, dtype=torch.bfloat16)
+    for r in range(n):
+        synth.fill_grad_(grads[r], wl.grad_dist, wl.grad_scale, synth.seed_of(wl.seed, synth.TAG_GRAD, 1, r))
+    gl = list(grads)
+    sc = z.zero_adamw_scalars_for(1, h["lr"], h["b1"], h["b2"], h["eps"], h["wd"], 1.0)
+    for _ in range(args.warmup):
+        z.zero_step_host(L, wl.rank, gl, gidx, float(n), master, m, v, sidx, out, oidx, sc, args.threads)
+        sc = z.zero_adamw_scalars_next(sc)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        z.zero_step_host(L, wl.rank, gl, gidx, float(n), master, m, v, sidx, out, oidx, sc, args.threads)
+        sc = z.zero_adamw_scalars_next(sc)
+    wall = time.perf_counter() - t0
+    elements = se if wl.rank < 0 else L.shard
+    step_bytes, _ = z.zero_step_traffic(L, wl.rank, n, z.ZERO_BF16, True)
+    threads = args.threads if args.threads > 0 else os.cpu_count()
+    res = {"metric": "offload (host-core) optimizer-step shard elements/sec", "value": elements * args.steps / wall,
+           "unit": "elements/s", "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True, "dtype": "f32",
+           "data": "synthetic",
+           "config": {"workload": wl.name, "simulated_ranks": n, "elements_per_step": int(elements),
+                      "threads": threads, "host_GBps": step_bytes * args.steps / wall / 1e9},
+           "cpu_baseline": None}
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(res))
+
+
 def main():
     args = parse()
+    if args.host_step:
+        host_step_bench(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the sharded step for N "
               "ranks runs here as N simulated ranks' buffers in one GPU's memory", file=sys.stderr)

@@ -89,6 +89,8 @@ _zero_adamw_scalars_next = _sig("zero_adamw_scalars_next", i32, C.POINTER(ZeroAd
                                 C.POINTER(ZeroAdamwScalars))
 _zero_step = _sig("zero_step", i32, vp, i32, vp, i32, i32, i32, f32, vp, vp, vp, i32, vp, i32,
                   C.POINTER(ZeroAdamwScalars), vp)
+_zero_step_host = _sig("zero_step_host", i32, vp, i32, vp, i32, i32, i32, f32, vp, vp, vp, i32, vp,
+                       i32, C.POINTER(ZeroAdamwScalars), i32)
 _zero_gradnorm_workspace_bytes = _sig("zero_gradnorm_workspace_bytes", i32, vp, i32,
                                       C.POINTER(sz))
 _zero_gradnorm = _sig("zero_gradnorm", i32, vp, i32, vp, i32, i32, i32, f32, vp, i32, vp, sz,
@@ -108,6 +110,7 @@ _zero_abi_version = _sig("zero_abi_version", i32)
 
 EXPORTED = ["zero_layout_bytes", "zero_pack", "zero_global_index", "zero_owner", "zero_pack_copy",
             "zero_unpack_copy", "zero_adamw_scalars_for", "zero_adamw_scalars_next", "zero_step",
+            "zero_step_host",
             "zero_gradnorm_workspace_bytes", "zero_gradnorm", "zero_gradnorm_async",
             "zero_clip_coef", "zero_ledger",
             "zero_gather_buffer_bytes", "zero_step_traffic", "zero_gradnorm_traffic",
@@ -315,6 +318,51 @@ def zero_step(layout: Layout, rank: int, grads, grad_index: int, divisor: float,
                       _f32_ptr(exp_avg_sq, "exp_avg_sq"), state_index,
                       _bf16_ptr(out, "out") if out is not None else None, out_index,
                       C.byref(scalars), _stream(stream)), "zero_step")
+
+
+def _host_ptr(a, what: str, kind: str):
+    """Address of a host buffer: a numpy array or a CPU torch tensor
+    (C-contiguous).  kind: 'f32', 'bf16' (uint16 / int16 / bfloat16 bits) or
+    'grad' (either)."""
+    torch = _torch()
+    if isinstance(a, torch.Tensor):
+        if a.is_cuda:
+            raise ValueError(f"{what} must be in host memory")
+        if not a.is_contiguous():
+            raise ValueError(f"{what} must be contiguous")
+        dt = {torch.float32: "f32", torch.bfloat16: "bf16", torch.int16: "bf16",
+              torch.uint16: "bf16"}.get(a.dtype)
+        ptr = a.data_ptr()
+    else:
+        if not isinstance(a, np.ndarray) or not a.flags["C_CONTIGUOUS"]:
+            raise ValueError(f"{what} must be a C-contiguous numpy array or CPU tensor")
+        dt = {np.dtype(np.float32): "f32", np.dtype(np.uint16): "bf16",
+              np.dtype(np.int16): "bf16"}.get(a.dtype)
+        ptr = a.ctypes.data
+    if dt is None or (kind != "grad" and dt != kind):
+        raise TypeError(f"{what}: unexpected dtype")
+    return ptr, dt
+
+
+def zero_step_host(layout: Layout, rank: int, grads, grad_index: int, divisor: float,
+                   master, exp_avg, exp_avg_sq, state_index: int, out, out_index: int,
+                   scalars: ZeroAdamwScalars, n_threads: int = 0):
+    """The step on host cores (ZeRO-Offload): same arguments as zero_step on
+    host buffers (numpy arrays or CPU tensors); synchronous."""
+    if len(grads) < 1:
+        raise ValueError("at least one gradient buffer")
+    gp = [_host_ptr(g, "grad", "grad") for g in grads]
+    kinds = {k for _, k in gp}
+    if len(kinds) != 1:
+        raise TypeError("all gradient buffers must share one dtype")
+    gdt = ZERO_BF16 if kinds.pop() == "bf16" else ZERO_F32
+    arr = (vp * len(gp))(*[p for p, _ in gp])
+    _check(_zero_step_host(layout.ptr, rank, C.addressof(arr), len(gp), gdt, grad_index, divisor,
+                           _host_ptr(master, "master", "f32")[0],
+                           _host_ptr(exp_avg, "exp_avg", "f32")[0],
+                           _host_ptr(exp_avg_sq, "exp_avg_sq", "f32")[0], state_index,
+                           _host_ptr(out, "out", "bf16")[0] if out is not None else None,
+                           out_index, C.byref(scalars), n_threads), "zero_step_host")
 
 
 def grad_pointer_array(grads):

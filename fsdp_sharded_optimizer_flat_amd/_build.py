@@ -23,6 +23,11 @@ LIB = os.path.join(PKG, "libzero.so")
 
 SOURCES = ["layout.cpp", "scalars.cpp", "ledger.cpp", "capi.cpp",
            "step_kernels.hip", "norm_kernels.hip", "pack_kernels.hip"]
+# Host-only C++ built with g++: the offload step's AVX2 code (no FMA, no
+# fast-math, so every operation rounds once, as on the GPU).
+HOST_SOURCES = ["host_step.cpp"]
+HOST_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-mavx2", "-mno-fma", "-ffp-contract=off",
+              "-fno-fast-math", "-pthread", "-Wall"]
 
 ARCH = "gfx950"
 FLAGS = [
@@ -44,7 +49,11 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, src + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    if src in HOST_SOURCES:
+        cmd = ["g++", *HOST_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-c", os.path.join(CSRC, src),
+               "-o", obj]
+    else:
+        cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{res.stderr}")
@@ -54,11 +63,12 @@ def _compile(src: str) -> str:
 def build(jobs: int | None = None) -> str:
     """Compile every source and link libzero.so next to this file."""
     os.makedirs(BUILD, exist_ok=True)
-    jobs = jobs or min(len(SOURCES), os.cpu_count() or 4, 16)
+    srcs = SOURCES + HOST_SOURCES
+    jobs = jobs or min(len(srcs), os.cpu_count() or 4, 16)
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        objs = list(ex.map(_compile, srcs))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stderr}")

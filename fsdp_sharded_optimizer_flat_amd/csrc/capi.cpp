@@ -64,7 +64,17 @@ zero_status check_grads(const zero_layout *L, int32_t rank, const void *const *g
     return ZERO_OK;
 }
 
-StepConsts make_consts(const zero_adamw_scalars *sc, float divisor)
+std::vector<const void *> offset_grads(const void *const *grads, int n, int64_t off, int gsize)
+{
+    std::vector<const void *> v((size_t)n);
+    for (int q = 0; q < n; ++q)
+        v[(size_t)q] = (const char *)grads[q] + off * gsize;
+    return v;
+}
+
+}  // namespace
+
+StepConsts make_step_consts(const zero_adamw_scalars *sc, float divisor)
 {
     StepConsts c{};
     if (sc) {
@@ -84,16 +94,6 @@ StepConsts make_consts(const zero_adamw_scalars *sc, float divisor)
     c.inv_divisor = inv;
     return c;
 }
-
-std::vector<const void *> offset_grads(const void *const *grads, int n, int64_t off, int gsize)
-{
-    std::vector<const void *> v((size_t)n);
-    for (int q = 0; q < n; ++q)
-        v[(size_t)q] = (const char *)grads[q] + off * gsize;
-    return v;
-}
-
-}  // namespace
 
 bool is_pow2_float(float x, float *inv)
 {
@@ -212,11 +212,11 @@ zero_status hip_fail(int err, const char *where)
 
 using namespace zero;
 
-extern "C" zero_status zero_step(const zero_layout *L, int32_t rank, const void *const *grads,
-                                 int32_t n_grads, int32_t grad_dtype, int32_t grad_index,
-                                 float divisor, float *master, float *exp_avg, float *exp_avg_sq,
-                                 int32_t state_index, uint16_t *out, int32_t out_index,
-                                 const zero_adamw_scalars *sc, void *stream)
+zero_status zero::validate_step(const zero_layout *L, int32_t rank, const void *const *grads,
+                               int32_t n_grads, int32_t grad_dtype, int32_t grad_index,
+                               float divisor, const float *master, const float *exp_avg,
+                               const float *exp_avg_sq, int32_t state_index, const uint16_t *out,
+                               int32_t out_index, const zero_adamw_scalars *sc)
 {
     zero_status st = check_grads(L, rank, grads, n_grads, grad_dtype, grad_index, divisor);
     if (st != ZERO_OK)
@@ -247,8 +247,21 @@ extern "C" zero_status zero_step(const zero_layout *L, int32_t rank, const void 
         if (overlap(g, w) || overlap(g, m) || overlap(g, v) || overlap(g, o))
             return ZERO_EINVAL;
     }
+    return ZERO_OK;
+}
 
-    const StepConsts c = make_consts(sc, divisor);
+extern "C" zero_status zero_step(const zero_layout *L, int32_t rank, const void *const *grads,
+                                 int32_t n_grads, int32_t grad_dtype, int32_t grad_index,
+                                 float divisor, float *master, float *exp_avg, float *exp_avg_sq,
+                                 int32_t state_index, uint16_t *out, int32_t out_index,
+                                 const zero_adamw_scalars *sc, void *stream)
+{
+    zero_status st = validate_step(L, rank, grads, n_grads, grad_dtype, grad_index, divisor,
+                                   master, exp_avg, exp_avg_sq, state_index, out, out_index, sc);
+    if (st != ZERO_OK)
+        return st;
+    const int gsize = dsize(grad_dtype);
+    const StepConsts c = make_step_consts(sc, divisor);
     Request rq{};
     rq.layout = L;
     rq.rank = rank;
@@ -325,7 +338,7 @@ zero_status gradnorm_launch(const zero_layout *L, int32_t rank, const void *cons
             return ZERO_EINVAL;
     }
 
-    const StepConsts c = make_consts(nullptr, divisor);
+    const StepConsts c = make_step_consts(nullptr, divisor);
     Request rq{};
     rq.layout = L;
     rq.rank = rank;

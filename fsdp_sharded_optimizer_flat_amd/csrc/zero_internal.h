@@ -97,6 +97,17 @@ struct StepConsts {
 
 bool is_pow2_float(float x, float *inv);
 
+// The step's constants from the host scalars (sc may be null: divisor only).
+StepConsts make_step_consts(const zero_adamw_scalars *sc, float divisor);
+
+// Every check zero_step makes before device work (selection, enums, NULLs,
+// alignment, aliasing of written buffers); shared by the host step.
+zero_status validate_step(const zero_layout *L, int32_t rank, const void *const *grads,
+                          int32_t n_grads, int32_t grad_dtype, int32_t grad_index, float divisor,
+                          const float *master, const float *exp_avg, const float *exp_avg_sq,
+                          int32_t state_index, const uint16_t *out, int32_t out_index,
+                          const zero_adamw_scalars *sc);
+
 // Launchers (defined in the .hip files).  Pointers are already offset to the
 // piece's first element.  Return a hipError_t value.
 int launch_step_piece(const Piece &pc, const void *const *grads, int n_grads, int grad_dtype,

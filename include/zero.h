@@ -229,6 +229,25 @@ zero_status zero_step(const zero_layout *layout, int32_t rank,
                       const zero_adamw_scalars *sc, void *stream);
 
 /* ------------------------------------------------------------------------
+ * The step on host cores, for ZeRO-Offload -- [p4 section 6]: the optimizer
+ * state and the fp32 step live in CPU memory; gradients come down from the
+ * GPU and updated parameters go back; [p1 Implementation notes]: offload
+ * trades PCIe bandwidth for capacity.
+ *
+ * Same selection, index rules, validation and arithmetic as zero_step (every
+ * element bit-identical to it), on host pointers, by n_threads worker threads
+ * (<= 0: all hardware threads; fewer are used for small selections).  The
+ * result does not depend on the thread count.  Synchronous: returns when the
+ * step is done.  Errors as zero_step (EHIP cannot occur).
+ * ------------------------------------------------------------------------ */
+zero_status zero_step_host(const zero_layout *layout, int32_t rank,
+                           const void *const *grads, int32_t n_grads, int32_t grad_dtype,
+                           int32_t grad_index, float divisor,
+                           float *master, float *exp_avg, float *exp_avg_sq, int32_t state_index,
+                           uint16_t *out, int32_t out_index,
+                           const zero_adamw_scalars *sc, int32_t n_threads);
+
+/* ------------------------------------------------------------------------
  * Global gradient norm -- [p1 Implementation notes]: clipping needs the
  * global norm, the sum of the shards' squared norms (all-reduced across
  * ranks); [p3 section 2] a norm is a decomposable sum of squares.

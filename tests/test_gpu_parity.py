@@ -499,3 +499,27 @@ def test_pack_and_unpack(src_dt, dst_dt):
     torch.cuda.synchronize()
     for p, b in zip(params, back):
         assert_same_f32(b.float().cpu().numpy(), p.to(dst_dt).to(src_dt).float().cpu().numpy(), "unpack")
+
+
+def test_host_step_equals_gpu_step():
+    """The offload (host) step and the GPU step give the same bits."""
+    rng = np.random.default_rng(31)
+    n, numel = 8, [200_003, 4097]
+    L = z.zero_pack(n, numel)
+    h = GPT_HYPER
+    g = (rng.standard_normal((n, L.shard)) * 1e-3).astype(np.float32)
+    gb = torch.from_numpy(g).to(torch.bfloat16)
+    w0 = rng.normal(0, 0.02, L.shard).astype(np.float32)
+    W, M, V = torch.from_numpy(w0).to(DEV), torch.zeros(L.shard, device=DEV), torch.zeros(L.shard, device=DEV)
+    O = torch.zeros(L.shard, dtype=torch.int16, device=DEV)
+    gd = gb.to(DEV)
+    hw, hm, hv = w0.copy(), np.zeros_like(w0), np.zeros_like(w0)
+    ho = np.zeros(L.shard, np.uint16)
+    hg = [np.ascontiguousarray(gb[q].view(torch.int16).numpy().view(np.uint16)) for q in range(n)]
+    for t in (1, 2, 3):
+        z.zero_step(L, 4, list(gd), Lc, float(n), W, M, V, Lc, O, Lc, scalars(t, h))
+        z.zero_step_host(L, 4, hg, Lc, float(n), hw, hm, hv, Lc, ho, Lc, scalars(t, h), 0)
+    torch.cuda.synchronize()
+    assert_same_f32(to_np(W), hw, "host vs GPU master")
+    assert_same_f32(to_np(V), hv, "host vs GPU v")
+    assert_same_bf16(to_np(O), ho, "host vs GPU out")
