@@ -55,6 +55,10 @@ def parse():
     ap.add_argument("--host-step", action="store_true",
                     help="time the offload step on host cores (zero_step_host) instead of the GPU")
     ap.add_argument("--threads", type=int, default=0, help="host-step worker threads (0: all)")
+    ap.add_argument("--offload", action="store_true",
+                    help="time the ZeRO-Offload step: norm pass on the GPU, reduced gradient "
+                         "down over PCIe, host step, bf16 parameters up (one rank's shard)")
+    ap.add_argument("--chunk", type=int, default=1 << 22, help="offload pipeline chunk (elements)")
     return ap.parse_args()
 
 
@@ -168,8 +172,78 @@ def host_step_bench(args):
     print(json.dumps(res))
 
 
+def offload_bench(args):
+    """One rank's ZeRO-Offload step: the GPU reduces the N ranks' gradients
+    (norm pass, fp32 reduced gradient in HBM), the pipelined offload step
+    brings it down, steps the host-resident state and sends the bf16
+    parameters back.  Prints one JSON line."""
+    import numpy as np
+    import torch
+
+    import fsdp_sharded_optimizer_flat_amd as z
+    from fsdp_sharded_optimizer_flat_amd import synth
+    from fsdp_sharded_optimizer_flat_amd.workloads import WORKLOADS
+
+    wl = WORKLOADS[args.workload]
+    if wl.rank < 0:
+        raise SystemExit("--offload needs a one-rank workload (llama8b_z3, llama8b_z3_clip)")
+    n, h = wl.n_ranks, wl.hyper
+    dev = torch.device("cuda:0")
+    L = z.zero_pack(n, wl.unit_numel)
+    G, Lc = z.ZERO_GLOBAL, z.ZERO_LOCAL
+    S = L.shard
+    grads = torch.empty(n, S, dtype=torch.bfloat16, device=dev)
+    for r in range(n):
+        synth.fill_grad_(grads[r], wl.grad_dist, wl.grad_scale, synth.seed_of(wl.seed, synth.TAG_GRAD, 1, r))
+    g_red = torch.empty(S, dtype=torch.float32, device=dev)
+    ws = torch.zeros(z.zero_gradnorm_workspace_bytes(L, wl.rank) // 8, dtype=torch.float64, device=dev)
+    master = torch.empty(S, dtype=torch.float32)
+    synth.fill_normal_(master, wl.master_std, synth.seed_of(wl.seed, synth.TAG_MASTER))
+    m, v = torch.zeros_like(master), torch.zeros_like(master)
+    chunk = args.chunk
+    gst = torch.zeros(2 * chunk, dtype=torch.float32, pin_memory=True)
+    ost = torch.zeros(2 * chunk, dtype=torch.int16, pin_memory=True)
+    d_out = torch.zeros(S, dtype=torch.int16, device=dev)
+    s_down, s_up = torch.cuda.Stream(), torch.cuda.Stream()
+    gl = list(grads)
+    sc = z.zero_adamw_scalars_for(1, h["lr"], h["b1"], h["b2"], h["eps"], h["wd"], 1.0)
+
+    def step():
+        nonlocal sc
+        ss = z.zero_gradnorm(L, wl.rank, gl, Lc, float(n), g_red, Lc, ws)
+        sc.clip_coef = z.zero_clip_coef(ss, wl.clip_max_norm) if wl.clip_max_norm else 1.0
+        t0 = time.perf_counter()
+        z.zero_offload_step(L, wl.rank, g_red, gst, master, m, v, ost, d_out, chunk, sc,
+                            args.threads, s_down, s_up)
+        dt = time.perf_counter() - t0
+        sc = z.zero_adamw_scalars_next(sc)
+        return dt
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    off = [step() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    off_s = float(np.mean(off))
+    res = {"metric": "offload optimizer-step shard elements/sec (GPU reduce + PCIe + host step)",
+           "value": S * args.steps / wall, "unit": "elements/s", "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True,
+           "dtype": "f32", "data": "synthetic",
+           "config": {"workload": wl.name, "simulated_ranks": n, "elements_per_step": int(S),
+                      "chunk": chunk, "threads": args.threads if args.threads > 0 else os.cpu_count(),
+                      "offload_ms": off_s * 1e3,
+                      "pcie_GBps": 6.0 * S / off_s / 1e9,
+                      "host_GBps": 30.0 * S / off_s / 1e9}}
+    print(json.dumps(res))
+
+
 def main():
     args = parse()
+    if args.offload:
+        offload_bench(args)
+        return
     if args.host_step:
         host_step_bench(args)
         return

@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(_PKG, "libzero.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m fsdp_sharded_optimizer_flat_amd._build` "
+        f"{LIB_PATH} is missing: build it with `python fsdp_sharded_optimizer_flat_amd/_build.py` "
         "(there is no CPU fallback for the sharded step)")
 
 _lib = C.CDLL(LIB_PATH)
@@ -91,6 +91,8 @@ _zero_step = _sig("zero_step", i32, vp, i32, vp, i32, i32, i32, f32, vp, vp, vp,
                   C.POINTER(ZeroAdamwScalars), vp)
 _zero_step_host = _sig("zero_step_host", i32, vp, i32, vp, i32, i32, i32, f32, vp, vp, vp, i32, vp,
                        i32, C.POINTER(ZeroAdamwScalars), i32)
+_zero_offload_step = _sig("zero_offload_step", i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, i64,
+                          C.POINTER(ZeroAdamwScalars), i32, vp, vp)
 _zero_gradnorm_workspace_bytes = _sig("zero_gradnorm_workspace_bytes", i32, vp, i32,
                                       C.POINTER(sz))
 _zero_gradnorm = _sig("zero_gradnorm", i32, vp, i32, vp, i32, i32, i32, f32, vp, i32, vp, sz,
@@ -110,7 +112,7 @@ _zero_abi_version = _sig("zero_abi_version", i32)
 
 EXPORTED = ["zero_layout_bytes", "zero_pack", "zero_global_index", "zero_owner", "zero_pack_copy",
             "zero_unpack_copy", "zero_adamw_scalars_for", "zero_adamw_scalars_next", "zero_step",
-            "zero_step_host",
+            "zero_step_host", "zero_offload_step",
             "zero_gradnorm_workspace_bytes", "zero_gradnorm", "zero_gradnorm_async",
             "zero_clip_coef", "zero_ledger",
             "zero_gather_buffer_bytes", "zero_step_traffic", "zero_gradnorm_traffic",
@@ -363,6 +365,28 @@ def zero_step_host(layout: Layout, rank: int, grads, grad_index: int, divisor: f
                            _host_ptr(exp_avg_sq, "exp_avg_sq", "f32")[0], state_index,
                            _host_ptr(out, "out", "bf16")[0] if out is not None else None,
                            out_index, C.byref(scalars), n_threads), "zero_step_host")
+
+
+def zero_offload_step(layout: Layout, rank: int, d_grad, h_grad_stage, master, exp_avg,
+                      exp_avg_sq, h_out_stage, d_out, chunk: int, scalars: ZeroAdamwScalars,
+                      n_threads: int = 0, stream_down=None, stream_up=None):
+    """The pipelined offload step: d_grad / d_out are device tensors, the
+    staging slots pinned CPU tensors (2 * chunk elements each), the state CPU
+    tensors or numpy arrays.  Synchronous."""
+    torch = _torch()
+    for t, what in ((h_grad_stage, "h_grad_stage"), (h_out_stage, "h_out_stage")):
+        if not (isinstance(t, torch.Tensor) and t.is_pinned()):
+            raise ValueError(f"{what} must be a pinned CPU tensor")
+        if t.numel() < 2 * chunk:
+            raise ValueError(f"{what} needs 2 * chunk elements")
+    _check(_zero_offload_step(layout.ptr, rank, _f32_ptr(d_grad, "d_grad"),
+                              _host_ptr(h_grad_stage, "h_grad_stage", "f32")[0],
+                              _host_ptr(master, "master", "f32")[0],
+                              _host_ptr(exp_avg, "exp_avg", "f32")[0],
+                              _host_ptr(exp_avg_sq, "exp_avg_sq", "f32")[0],
+                              _host_ptr(h_out_stage, "h_out_stage", "bf16")[0],
+                              _bf16_ptr(d_out, "d_out"), chunk, C.byref(scalars), n_threads,
+                              _stream(stream_down), _stream(stream_up)), "zero_offload_step")
 
 
 def grad_pointer_array(grads):

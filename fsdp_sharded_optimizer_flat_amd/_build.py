@@ -1,6 +1,9 @@
 """Build libzero.so (the HIP kernels and the C ABI) in-tree with hipcc for gfx950.
 
-    python -m fsdp_sharded_optimizer_flat_amd._build
+    python fsdp_sharded_optimizer_flat_amd/_build.py
+
+(run as a file: importing it through the package would load the library it
+is about to rebuild).
 
 Floating-point flags are part of the contract: -ffp-contract=off (no FMA
 contraction), IEEE binary32 denormals (-fno-gpu-flush-denormals-to-zero),
@@ -21,7 +24,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libzero.so")
 
-SOURCES = ["layout.cpp", "scalars.cpp", "ledger.cpp", "capi.cpp",
+SOURCES = ["layout.cpp", "scalars.cpp", "ledger.cpp", "capi.cpp", "offload.cpp",
            "step_kernels.hip", "norm_kernels.hip", "pack_kernels.hip"]
 # Host-only C++ built with g++: the offload step's AVX2 code (no FMA, no
 # fast-math, so every operation rounds once, as on the GPU).

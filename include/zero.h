@@ -247,6 +247,28 @@ zero_status zero_step_host(const zero_layout *layout, int32_t rank,
                            uint16_t *out, int32_t out_index,
                            const zero_adamw_scalars *sc, int32_t n_threads);
 
+/* The offload step with its PCIe transfers, pipelined -- [p4 section 6]: the
+ * reduced gradient comes down, the host steps the fp32 state, the bf16
+ * parameters go back up; the PCIe link is the bottleneck.
+ *
+ * For rank r's shard (S = layout->shard elements, LOCAL indexing): d_grad is
+ * the reduced fp32 gradient on the device (e.g. written by the norm pass),
+ * already averaged and, if clipping, to be scaled by sc->clip_coef; master,
+ * exp_avg, exp_avg_sq are host arrays of S floats; d_out receives the S bf16
+ * parameters on the device.  The shard moves in chunks of `chunk` elements
+ * through two staging slots the caller provides in pinned host memory
+ * (h_grad_stage: 2 * chunk floats; h_out_stage: 2 * chunk bf16): the copy
+ * down of chunk c + 1 (stream_down), the host step of chunk c and the copy up
+ * of chunk c - 1 (stream_up) overlap.  Every element is bit-identical to
+ * zero_step with one fp32 gradient and divisor 1.  Synchronous: returns when
+ * the last chunk is on the device.  Errors: EINVAL, EALIGN, EHIP. */
+zero_status zero_offload_step(const zero_layout *layout, int32_t rank,
+                              const float *d_grad, float *h_grad_stage,
+                              float *master, float *exp_avg, float *exp_avg_sq,
+                              uint16_t *h_out_stage, uint16_t *d_out,
+                              int64_t chunk, const zero_adamw_scalars *sc, int32_t n_threads,
+                              void *stream_down, void *stream_up);
+
 /* ------------------------------------------------------------------------
  * Global gradient norm -- [p1 Implementation notes]: clipping needs the
  * global norm, the sum of the shards' squared norms (all-reduced across

@@ -523,3 +523,34 @@ def test_host_step_equals_gpu_step():
     assert_same_f32(to_np(W), hw, "host vs GPU master")
     assert_same_f32(to_np(V), hv, "host vs GPU v")
     assert_same_bf16(to_np(O), ho, "host vs GPU out")
+
+
+@pytest.mark.parametrize("chunk", [1 << 16, 100_003, 1 << 22])
+def test_offload_step_equals_gpu_step(chunk):
+    """The pipelined offload step (reduced gradient down over PCIe, host step,
+    bf16 parameters up) against the GPU step on the same reduced gradient."""
+    rng = np.random.default_rng(32)
+    n, numel = 8, [8 * 300_007, 8 * 77]
+    L = z.zero_pack(n, numel)
+    h = GPT_HYPER
+    S = L.shard
+    g = torch.from_numpy((rng.standard_normal(S) * 1e-3).astype(np.float32)).to(DEV)
+    w0 = rng.normal(0, 0.02, S).astype(np.float32)
+    W, M, V = torch.from_numpy(w0).to(DEV), torch.zeros(S, device=DEV), torch.zeros(S, device=DEV)
+    O = torch.zeros(S, dtype=torch.int16, device=DEV)
+    hw = torch.from_numpy(w0.copy())
+    hm, hv = torch.zeros(S), torch.zeros(S)
+    gst = torch.zeros(2 * chunk, dtype=torch.float32, pin_memory=True)
+    ost = torch.zeros(2 * chunk, dtype=torch.int16, pin_memory=True)
+    dO = torch.zeros(S, dtype=torch.int16, device=DEV)
+    s_down, s_up = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for t in (1, 2):
+        sc = scalars(t, h, clip=0.75)
+        z.zero_step(L, 2, [g], Lc, 1.0, W, M, V, Lc, O, Lc, sc)
+        torch.cuda.synchronize()
+        z.zero_offload_step(L, 2, g, gst, hw, hm, hv, ost, dO, chunk, sc, 0, s_down, s_up)
+    torch.cuda.synchronize()
+    assert_same_f32(hw.numpy(), to_np(W), "offload master")
+    assert_same_f32(hv.numpy(), to_np(V), "offload v")
+    assert_same_bf16(to_np(dO), to_np(O), "offload bf16 params on the device")
