@@ -288,6 +288,7 @@ def main():
         g_red = torch.empty(se, dtype=torch.float32, device=dev)
         ws = torch.zeros(z.zero_gradnorm_workspace_bytes(L, wl.rank) // 8, dtype=torch.float64, device=dev)
         ss_dev = torch.zeros(1, dtype=torch.float64, device=dev)
+        coef_dev = torch.zeros(1, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
@@ -300,13 +301,16 @@ def main():
         sc = z.zero_adamw_scalars_for(t, h["lr"], h["b1"], h["b2"], h["eps"], h["wd"], 1.0) \
             if t == 1 else z.zero_adamw_scalars_next(sc)
         if clip:
+            # norm pass -> coefficient on the device -> step reading it: no
+            # host round trip inside the step
             if ev:
                 ev[0].record(stream)
             z.zero_gradnorm_async(L, wl.rank, list(grads), gidx, float(n), g_red, sidx, ws, ss_dev, stream)
             if ev:
                 ev[1].record(stream)
-            sc.clip_coef = z.zero_clip_coef(ss_dev.item(), wl.clip_max_norm)  # host reads the sum
-            z.zero_step(L, wl.rank, [g_red], sidx, 1.0, master, m, v, sidx, out, oidx, sc, stream)
+            z.zero_clip_coef_async(ss_dev, wl.clip_max_norm, coef_dev, stream)
+            z.zero_step_device_clip(L, wl.rank, [g_red], sidx, 1.0, master, m, v, sidx, out, oidx, sc,
+                                    coef_dev, stream)
         else:
             if ev:
                 ev[0].record(stream)

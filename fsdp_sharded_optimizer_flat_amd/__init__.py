@@ -61,6 +61,14 @@ class ZeroAdamwScalars(C.Structure):
         return {k: getattr(self, k) for k, _ in self._fields_}
 
 
+class ZeroOverlapOut(C.Structure):
+    _fields_ = [("gather_bytes", f64), ("gather_s", f64), ("compute_flops", f64),
+                ("compute_s", f64), ("ratio", f64), ("hidden", i32), ("reserved", i32)]
+
+    def as_dict(self):
+        return {k: getattr(self, k) for k, _ in self._fields_ if k != "reserved"}
+
+
 class ZeroLedgerOut(C.Structure):
     _fields_ = [("params_bytes", f64), ("grads_bytes", f64), ("optim_bytes", f64),
                 ("model_state_bytes", f64), ("comm_elements", f64),
@@ -89,6 +97,10 @@ _zero_adamw_scalars_next = _sig("zero_adamw_scalars_next", i32, C.POINTER(ZeroAd
                                 C.POINTER(ZeroAdamwScalars))
 _zero_step = _sig("zero_step", i32, vp, i32, vp, i32, i32, i32, f32, vp, vp, vp, i32, vp, i32,
                   C.POINTER(ZeroAdamwScalars), vp)
+_zero_step_device_clip = _sig("zero_step_device_clip", i32, vp, i32, vp, i32, i32, i32, f32, vp, vp,
+                              vp, i32, vp, i32, C.POINTER(ZeroAdamwScalars), vp, vp)
+_zero_clip_coef_async = _sig("zero_clip_coef_async", i32, vp, f64, vp, vp)
+_zero_overlap = _sig("zero_overlap", i32, f64, i32, f64, f64, f64, C.POINTER(ZeroOverlapOut))
 _zero_step_host = _sig("zero_step_host", i32, vp, i32, vp, i32, i32, i32, f32, vp, vp, vp, i32, vp,
                        i32, C.POINTER(ZeroAdamwScalars), i32)
 _zero_offload_step = _sig("zero_offload_step", i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, i64,
@@ -112,7 +124,8 @@ _zero_abi_version = _sig("zero_abi_version", i32)
 
 EXPORTED = ["zero_layout_bytes", "zero_pack", "zero_global_index", "zero_owner", "zero_pack_copy",
             "zero_unpack_copy", "zero_adamw_scalars_for", "zero_adamw_scalars_next", "zero_step",
-            "zero_step_host", "zero_offload_step",
+            "zero_step_host", "zero_offload_step", "zero_step_device_clip",
+            "zero_clip_coef_async", "zero_overlap",
             "zero_gradnorm_workspace_bytes", "zero_gradnorm", "zero_gradnorm_async",
             "zero_clip_coef", "zero_ledger",
             "zero_gather_buffer_bytes", "zero_step_traffic", "zero_gradnorm_traffic",
@@ -387,6 +400,38 @@ def zero_offload_step(layout: Layout, rank: int, d_grad, h_grad_stage, master, e
                               _host_ptr(h_out_stage, "h_out_stage", "bf16")[0],
                               _bf16_ptr(d_out, "d_out"), chunk, C.byref(scalars), n_threads,
                               _stream(stream_down), _stream(stream_up)), "zero_offload_step")
+
+
+def zero_step_device_clip(layout: Layout, rank: int, grads, grad_index: int, divisor: float,
+                          master, exp_avg, exp_avg_sq, state_index: int, out, out_index: int,
+                          scalars: ZeroAdamwScalars, clip_coef_dev, stream=None, *, grad_ptrs=None):
+    """zero_step with the clip multiplier read from the float32 device tensor
+    ``clip_coef_dev`` (e.g. filled by zero_clip_coef_async)."""
+    arr, gdt = grad_ptrs if grad_ptrs is not None else _grad_ptrs(grads)
+    _check(_zero_step_device_clip(layout.ptr, rank, C.addressof(arr), len(arr), gdt, grad_index,
+                                  divisor, _f32_ptr(master, "master"), _f32_ptr(exp_avg, "exp_avg"),
+                                  _f32_ptr(exp_avg_sq, "exp_avg_sq"), state_index,
+                                  _bf16_ptr(out, "out") if out is not None else None, out_index,
+                                  C.byref(scalars), _f32_ptr(clip_coef_dev, "clip_coef_dev"),
+                                  _stream(stream)), "zero_step_device_clip")
+
+
+def zero_clip_coef_async(sumsq_dev, max_norm: float, coef_dev, stream=None):
+    """The clip coefficient on the device: float64 tensor in, float32 out."""
+    torch = _torch()
+    if sumsq_dev.dtype != torch.float64:
+        raise TypeError("sumsq_dev must be float64")
+    _check(_zero_clip_coef_async(_dev_ptr(sumsq_dev, "sumsq_dev"), max_norm,
+                                 _f32_ptr(coef_dev, "coef_dev"), _stream(stream)),
+           "zero_clip_coef_async")
+
+
+def zero_overlap(psi_unit: float, n_ranks: int, busbw_bytes_per_s: float, tokens_per_gpu: float,
+                 flops_per_s: float) -> dict:
+    o = ZeroOverlapOut()
+    _check(_zero_overlap(psi_unit, n_ranks, busbw_bytes_per_s, tokens_per_gpu, flops_per_s,
+                         C.byref(o)), "zero_overlap")
+    return o.as_dict()
 
 
 def grad_pointer_array(grads):

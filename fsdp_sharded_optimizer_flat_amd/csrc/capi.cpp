@@ -250,18 +250,20 @@ zero_status zero::validate_step(const zero_layout *L, int32_t rank, const void *
     return ZERO_OK;
 }
 
-extern "C" zero_status zero_step(const zero_layout *L, int32_t rank, const void *const *grads,
+static zero_status step_impl(const zero_layout *L, int32_t rank, const void *const *grads,
                                  int32_t n_grads, int32_t grad_dtype, int32_t grad_index,
                                  float divisor, float *master, float *exp_avg, float *exp_avg_sq,
                                  int32_t state_index, uint16_t *out, int32_t out_index,
-                                 const zero_adamw_scalars *sc, void *stream)
+                                 const zero_adamw_scalars *sc, const float *clip_dev,
+                                 void *stream)
 {
     zero_status st = validate_step(L, rank, grads, n_grads, grad_dtype, grad_index, divisor,
                                    master, exp_avg, exp_avg_sq, state_index, out, out_index, sc);
     if (st != ZERO_OK)
         return st;
     const int gsize = dsize(grad_dtype);
-    const StepConsts c = make_step_consts(sc, divisor);
+    StepConsts c = make_step_consts(sc, divisor);
+    c.clip_dev = clip_dev;
     Request rq{};
     rq.layout = L;
     rq.rank = rank;
@@ -288,6 +290,52 @@ extern "C" zero_status zero_step(const zero_layout *L, int32_t rank, const void 
             return hip_fail(err, "zero_step launch");
     }
     return ZERO_OK;
+}
+
+extern "C" zero_status zero_step(const zero_layout *L, int32_t rank, const void *const *grads,
+                                 int32_t n_grads, int32_t grad_dtype, int32_t grad_index,
+                                 float divisor, float *master, float *exp_avg, float *exp_avg_sq,
+                                 int32_t state_index, uint16_t *out, int32_t out_index,
+                                 const zero_adamw_scalars *sc, void *stream)
+{
+    return step_impl(L, rank, grads, n_grads, grad_dtype, grad_index, divisor, master, exp_avg,
+                     exp_avg_sq, state_index, out, out_index, sc, nullptr, stream);
+}
+
+extern "C" zero_status zero_step_device_clip(const zero_layout *L, int32_t rank,
+                                             const void *const *grads, int32_t n_grads,
+                                             int32_t grad_dtype, int32_t grad_index,
+                                             float divisor, float *master, float *exp_avg,
+                                             float *exp_avg_sq, int32_t state_index,
+                                             uint16_t *out, int32_t out_index,
+                                             const zero_adamw_scalars *sc,
+                                             const float *clip_coef_dev, void *stream)
+{
+    if (!clip_coef_dev)
+        return ZERO_EINVAL;
+    if (!aligned(clip_coef_dev, 4))
+        return ZERO_EALIGN;
+    if (layout_ok(L) && index_ok(state_index) && index_ok(out_index)) {
+        // the multiplier is read while the step writes: it must not alias
+        const Range cr = range_of(clip_coef_dev, 1, 4);
+        const int64_t se = extent(L, state_index), oe = extent(L, out_index);
+        if (overlap(cr, range_of(master, se, 4)) || overlap(cr, range_of(exp_avg, se, 4)) ||
+            overlap(cr, range_of(exp_avg_sq, se, 4)) || (out && overlap(cr, range_of(out, oe, 2))))
+            return ZERO_EINVAL;
+    }
+    return step_impl(L, rank, grads, n_grads, grad_dtype, grad_index, divisor, master, exp_avg,
+                     exp_avg_sq, state_index, out, out_index, sc, clip_coef_dev, stream);
+}
+
+extern "C" zero_status zero_clip_coef_async(const double *sumsq_dev, double max_norm,
+                                            float *coef_dev, void *stream)
+{
+    if (!sumsq_dev || !coef_dev || !(max_norm > 0.0))
+        return ZERO_EINVAL;
+    if (!aligned(sumsq_dev, 8) || !aligned(coef_dev, 4))
+        return ZERO_EALIGN;
+    const int err = launch_clip_coef(sumsq_dev, max_norm, coef_dev, stream);
+    return err == hipSuccess ? ZERO_OK : hip_fail(err, "zero_clip_coef_async");
 }
 
 extern "C" zero_status zero_gradnorm_workspace_bytes(const zero_layout *L, int32_t rank,

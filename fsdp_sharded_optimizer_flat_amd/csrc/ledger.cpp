@@ -11,6 +11,8 @@
 // gradients transient (stage 1 = stage 2 in resident memory).
 // "ZeRO and FSDP sharding", Complexity and constants: ZeRO-3's extra memory is
 // about two units of gathered bf16 weights (current and prefetched).
+#include <cmath>
+
 #include "zero_internal.h"
 
 namespace {
@@ -76,5 +78,27 @@ extern "C" zero_status zero_gradnorm_traffic(const zero_layout *L, int32_t rank,
     const double gsize = grad_dtype == ZERO_BF16 ? 2.0 : 4.0;
     *elements = e;
     *bytes = (n_grads * gsize + (with_g_out ? 4.0 : 0.0)) * (double)e;
+    return ZERO_OK;
+}
+
+// "ZeRO and FSDP sharding", Complexity and constants: a unit's all-gather
+// (2 psi_unit (N-1)/N bytes of bf16 weights per rank) is hidden when it takes
+// no longer than the unit's compute (6 psi_unit flops per token).
+extern "C" zero_status zero_overlap(double psi_unit, int32_t n_ranks, double busbw_bytes_per_s,
+                                    double tokens_per_gpu, double flops_per_s,
+                                    zero_overlap_out *out)
+{
+    if (!out || !(psi_unit >= 0.0) || n_ranks < 1 || !(busbw_bytes_per_s > 0.0) ||
+        !(tokens_per_gpu >= 0.0) || !(flops_per_s > 0.0))
+        return ZERO_EINVAL;
+    const double n = (double)n_ranks;
+    zero_overlap_out o{};
+    o.gather_bytes = kParamBytes * psi_unit * (n - 1.0) / n;
+    o.gather_s = o.gather_bytes / busbw_bytes_per_s;
+    o.compute_flops = 6.0 * psi_unit * tokens_per_gpu;
+    o.compute_s = o.compute_flops / flops_per_s;
+    o.ratio = o.compute_s > 0.0 ? o.gather_s / o.compute_s : (o.gather_s > 0.0 ? INFINITY : 0.0);
+    o.hidden = o.gather_s <= o.compute_s ? 1 : 0;
+    *out = o;
     return ZERO_OK;
 }

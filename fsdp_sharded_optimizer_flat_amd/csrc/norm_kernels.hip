@@ -97,6 +97,22 @@ __global__ __launch_bounds__(kBlock) void norm_level_kernel(const double *__rest
         out[blockIdx.x] = t;
 }
 
+// The clip coefficient on the device, with the host formula: norm =
+// sqrt(sumsq), c = max_norm / (norm + 1e-6) in binary64 (correctly rounded
+// sqrt and division), capped at 1, rounded once to binary32 -- the same bits
+// as zero_clip_coef computes on the host.  One thread.
+__global__ void clip_coef_kernel(const double *__restrict__ sumsq, double max_norm,
+                                 float *__restrict__ coef)
+{
+    if (threadIdx.x != 0 || blockIdx.x != 0)
+        return;
+    const double norm = sqrt(*sumsq);
+    double c = max_norm / (norm + 1e-6);
+    if (c > 1.0)
+        c = 1.0;
+    *coef = (float)c;
+}
+
 template <int NR, typename GT, typename QD, bool POW2, bool VEC>
 hipError_t launch_nr(const void *const *grads, int n, float *G, int64_t len, const StepConsts &c,
                      double *partials, int64_t blocks, hipStream_t st)
@@ -159,6 +175,13 @@ int launch_norm_segment(int64_t len, bool vec, const void *const *grads, int n_g
                   : launch_nr<0, float, F32Quad, false, true>(grads, n_grads, g_out, len, c, partials, blocks, st);
     return p2 ? launch_nr<0, float, F32Quad, true, false>(grads, n_grads, g_out, len, c, partials, blocks, st)
               : launch_nr<0, float, F32Quad, false, false>(grads, n_grads, g_out, len, c, partials, blocks, st);
+}
+
+int launch_clip_coef(const double *sumsq, double max_norm, float *coef, void *stream)
+{
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    hipLaunchKernelGGL(clip_coef_kernel, dim3(1), dim3(kWave), 0, st, sumsq, max_norm, coef);
+    return hipGetLastError();
 }
 
 int launch_norm_tree(const double *partials, int64_t n_partials, double *scratch, double *result,

@@ -43,6 +43,7 @@ __global__ __launch_bounds__(kWave) void step_quad_kernel(GradSet<CAP> gs, int n
     float s[4];
     rank_sum<NR, CAP, QD>(gs, n, i, s);
     const f32x4 wq = ld_stream(w4), mq = ld_stream(m4), vq = ld_stream(v4);
+    const float clip = c.clip_dev ? *c.clip_dev : c.clip;  // uniform: one scalar load
 
     float w[4] = {wq.x, wq.y, wq.z, wq.w};
     float m[4] = {mq.x, mq.y, mq.z, mq.w};
@@ -50,7 +51,7 @@ __global__ __launch_bounds__(kWave) void step_quad_kernel(GradSet<CAP> gs, int n
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         float g = average<POW2>(s[k], c);
-        g = g * c.clip;
+        g = g * clip;
         adamw(g, w[k], m[k], v[k], c);
     }
     st_stream(f32x4{w[0], w[1], w[2], w[3]}, w4);
@@ -72,12 +73,13 @@ __global__ __launch_bounds__(kBlock) void step_scalar_kernel(GradSet<ZERO_MAX_RA
                                                             int64_t len, StepConsts c)
 {
     const int64_t stride = (int64_t)gridDim.x * kBlock;
+    const float clip = c.clip_dev ? *c.clip_dev : c.clip;
     for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < len; i += stride) {
         float s = grad_at<GT>(gs.p[0], i);
         for (int q = 1; q < n; ++q)
             s = s + grad_at<GT>(gs.p[q], i);
         float g = average<POW2>(s, c);
-        g = g * c.clip;
+        g = g * clip;
         float w = W[i], m = M[i], v = V[i];
         adamw(g, w, m, v, c);
         W[i] = w;

@@ -92,7 +92,8 @@ zero_status hip_fail(int hip_error, const char *where);
 struct StepConsts {
     float b1, b2, omb1, omb2, bc2, eps, step_size, decay, clip;
     float divisor, inv_divisor;
-    int32_t div_pow2;  // 1: multiply by inv_divisor (exactly the same value)
+    int32_t div_pow2;        // 1: multiply by inv_divisor (exactly the same value)
+    const float *clip_dev;   // if set, the clip multiplier is read from device memory
 };
 
 bool is_pow2_float(float x, float *inv);
@@ -125,6 +126,7 @@ bool segment_vec_aligned(const Segment &s, const Request &rq);
 // Reduce n_partials partials to one value at *result (fixed order, several
 // levels of kNormFanIn-way workgroups); scratch holds the intermediate
 // levels (norm_tree_scratch(n_partials) doubles).
+int launch_clip_coef(const double *sumsq, double max_norm, float *coef, void *stream);
 int launch_norm_tree(const double *partials, int64_t n_partials, double *scratch, double *result,
                      void *stream);
 int64_t norm_tree_scratch(int64_t n_partials);

@@ -228,6 +228,20 @@ zero_status zero_step(const zero_layout *layout, int32_t rank,
                       uint16_t *out, int32_t out_index,
                       const zero_adamw_scalars *sc, void *stream);
 
+/* zero_step with the clip multiplier read from device memory (a float the
+ * stream has produced, e.g. by zero_clip_coef_async) instead of
+ * sc->clip_coef.  With zero_gradnorm_async and zero_clip_coef_async this
+ * makes the whole clipped step free of host synchronization, so it can be
+ * enqueued ahead or captured in a graph.  clip_coef_dev must not overlap any
+ * buffer the step writes (EINVAL).  Otherwise as zero_step. */
+zero_status zero_step_device_clip(const zero_layout *layout, int32_t rank,
+                                  const void *const *grads, int32_t n_grads, int32_t grad_dtype,
+                                  int32_t grad_index, float divisor,
+                                  float *master, float *exp_avg, float *exp_avg_sq,
+                                  int32_t state_index, uint16_t *out, int32_t out_index,
+                                  const zero_adamw_scalars *sc, const float *clip_coef_dev,
+                                  void *stream);
+
 /* ------------------------------------------------------------------------
  * The step on host cores, for ZeRO-Offload -- [p4 section 6]: the optimizer
  * state and the fp32 step live in CPU memory; gradients come down from the
@@ -315,6 +329,13 @@ zero_status zero_gradnorm_async(const zero_layout *layout, int32_t rank,
  * Implementation notes] names.  EINVAL: sumsq < 0 or NaN, max_norm <= 0. */
 zero_status zero_clip_coef(double sumsq, double max_norm, float *coef);
 
+/* The same coefficient on the device (async): reads the binary64 sum of
+ * squares at sumsq_dev (8-byte aligned) and writes the binary32 coefficient
+ * to coef_dev (4-byte aligned) -- bitwise equal to zero_clip_coef.  EINVAL:
+ * NULL pointers or max_norm <= 0. */
+zero_status zero_clip_coef_async(const double *sumsq_dev, double max_norm, float *coef_dev,
+                                 void *stream);
+
 /* ------------------------------------------------------------------------
  * Ledger -- [p4 section 3]: model state is (2 + 2 + K) psi bytes with K = 12
  * (bf16 params 2, bf16 grads 2, fp32 master + m + v 12); [p4 section 4]:
@@ -339,6 +360,25 @@ typedef struct zero_ledger_out {
 /* EINVAL: psi < 0, N < 1, stage outside 0..3, NULL out. */
 zero_status zero_ledger(double psi, int32_t n_ranks, int32_t stage, int32_t grads_transient,
                         zero_ledger_out *out);
+
+/* Overlap condition of one FSDP unit -- [p1 Complexity and constants]: the
+ * unit's all-gather, 2 psi_unit (N-1)/N bytes of bf16 weights received per
+ * rank, takes gather_bytes / busbw; it is hidden behind the unit's compute,
+ * 6 psi_unit flops per token (forward + backward) for tokens_per_gpu tokens at
+ * flops_per_s, when gather_s <= compute_s.  EINVAL: negative or zero rates,
+ * N < 1, NULL out. */
+typedef struct zero_overlap_out {
+    double gather_bytes;
+    double gather_s;
+    double compute_flops;
+    double compute_s;
+    double ratio;      /* gather_s / compute_s */
+    int32_t hidden;    /* 1 if gather_s <= compute_s */
+    int32_t reserved;
+} zero_overlap_out;
+
+zero_status zero_overlap(double psi_unit, int32_t n_ranks, double busbw_bytes_per_s,
+                         double tokens_per_gpu, double flops_per_s, zero_overlap_out *out);
 
 /* ZeRO-3 gather working set: `units_in_flight` units of bf16 weights of the
  * largest unit of the layout (bytes). */

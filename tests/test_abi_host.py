@@ -303,3 +303,20 @@ def test_device_code_has_no_contraction_or_flush():
         assert ".amdhsa_float_denorm_mode_32 3" in asm
         for m in re.finditer(r"\.private_segment_fixed_size:\s+(\d+)", asm):
             assert int(m.group(1)) == 0, (src, "scratch use")
+
+
+def test_overlap_condition_worked_numbers():
+    """The overlap condition against the numbers the pages work out."""
+    o = pins.golden("ledger_worked_values.json")["overlap"]
+    for key in ("intra_node", "cross_node"):
+        c = o[key]
+        r = z.zero_overlap(o["psi_unit"], c["n"], c["busbw"], o["tokens"], o["implied_flops_per_s"])
+        assert abs(r["gather_s"] * 1e3 - c["gather_ms"]) <= c["tol_rel"] * c["gather_ms"], (key, r)
+        assert abs(r["compute_flops"] / 1e12 - o["compute_tflop"]) <= o["compute_tol_rel"] * o["compute_tflop"]
+        assert abs(r["compute_s"] * 1e3 - o["compute_ms"]) <= 0.05 * o["compute_ms"]
+        assert r["hidden"] == 1 and r["ratio"] < 1
+    # a tiny batch cannot hide the gather (the page's caveat)
+    r = z.zero_overlap(o["psi_unit"], 64, 50e9, 64, o["implied_flops_per_s"])
+    assert r["hidden"] == 0
+    with pytest.raises(z.ZeroError):
+        z.zero_overlap(1e9, 8, 0.0, 1.0, 1.0)

@@ -554,3 +554,79 @@ def test_offload_step_equals_gpu_step(chunk):
     assert_same_f32(hw.numpy(), to_np(W), "offload master")
     assert_same_f32(hv.numpy(), to_np(V), "offload v")
     assert_same_bf16(to_np(dO), to_np(O), "offload bf16 params on the device")
+
+
+def test_device_clip_coefficient_equals_host():
+    """zero_clip_coef_async forms the same binary32 coefficient as the host."""
+    rng = np.random.default_rng(33)
+    vals = np.concatenate([10.0 ** rng.uniform(-14, 10, 20000), [0.0, 1.0, 0.999999e0, 4.0, 1e-12]])
+    res = torch.empty(1, dtype=torch.float32, device=DEV)
+    d = torch.from_numpy(vals).to(DEV)
+    for i in range(0, vals.size, 997):   # spread over the range; one launch per value
+        for mx in (1.0, 0.5):
+            z.zero_clip_coef_async(d[i:i + 1], mx, res)
+            assert res.item() == z.zero_clip_coef(float(vals[i]), mx), (vals[i], mx)
+
+
+def test_clipped_step_without_host_sync_and_in_a_graph():
+    """norm (async) -> coefficient (device) -> step reading it: equal to the
+    host-synchronized clipped step, eagerly and replayed from a HIP graph."""
+    rng = np.random.default_rng(34)
+    n, numel = 16, [16 * 40_000 + 16, 16 * 77]
+    L = z.zero_pack(n, numel)
+    h = GPT_HYPER
+    grads = torch.from_numpy((rng.standard_t(3, (n, L.shard)) * 4e-2).astype(np.float32)).to(torch.bfloat16).to(DEV)
+    gl = list(grads)
+    ws = torch.zeros(z.zero_gradnorm_workspace_bytes(L, 1) // 8, dtype=torch.float64, device=DEV)
+    g_red = torch.empty(L.shard, device=DEV)
+    ssd = torch.zeros(1, dtype=torch.float64, device=DEV)
+    coef = torch.zeros(1, dtype=torch.float32, device=DEV)
+    w0 = rng.normal(0, 0.02, L.shard).astype(np.float32)
+
+    def fresh():
+        return (torch.from_numpy(w0).to(DEV), torch.zeros(L.shard, device=DEV), torch.zeros(L.shard, device=DEV),
+                torch.zeros(L.shard, dtype=torch.int16, device=DEV))
+
+    # reference: host round trip
+    W, M, V, O = fresh()
+    for t in (1, 2, 3):
+        ss = z.zero_gradnorm(L, 1, gl, Lc, float(n), None, Lc, ws)
+        z.zero_step(L, 1, gl, Lc, float(n), W, M, V, Lc, O, Lc, scalars(t, h, clip=z.zero_clip_coef(ss, 1.0)))
+    torch.cuda.synchronize()
+    assert z.zero_clip_coef(ss, 1.0) < 1.0
+
+    def device_chain(t, W2, M2, V2, O2, stream=None):
+        z.zero_gradnorm_async(L, 1, gl, Lc, float(n), g_red, Lc, ws, ssd, stream)
+        z.zero_clip_coef_async(ssd, 1.0, coef, stream)
+        z.zero_step_device_clip(L, 1, [g_red], Lc, 1.0, W2, M2, V2, Lc, O2, Lc, scalars(t, h), coef, stream)
+
+    W2, M2, V2, O2 = fresh()
+    for t in (1, 2, 3):
+        device_chain(t, W2, M2, V2, O2)
+    torch.cuda.synchronize()
+    assert_same_f32(to_np(W2), to_np(W), "device-clip chain master")
+    assert_same_bf16(to_np(O2), to_np(O), "device-clip chain out")
+
+    # the same chain captured once per step count and replayed, with eager work
+    # and synchronizations between the replays; every replay checked
+    W3, M3, V3, O3 = fresh()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graphs = []
+    for t in (1, 2, 3):
+        gph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gph, stream=s):
+            device_chain(t, W3, M3, V3, O3, s)
+        graphs.append(gph)
+    torch.cuda.synchronize()
+    W3.copy_(torch.from_numpy(w0).to(DEV)); M3.zero_(); V3.zero_(); O3.zero_()
+    Wr, Mr, Vr, Or = fresh()
+    for t in (1, 2, 3):
+        graphs[t - 1].replay()
+        torch.cuda.synchronize()
+        device_chain(t, Wr, Mr, Vr, Or)          # eager, between replays
+        torch.cuda.synchronize()
+        assert_same_f32(to_np(W3), to_np(Wr), f"graph replay {t} master")
+        assert_same_f32(to_np(V3), to_np(Vr), f"graph replay {t} v")
+        assert_same_bf16(to_np(O3), to_np(Or), f"graph replay {t} out")
+    assert_same_f32(to_np(W3), to_np(W), "graph chain vs host-synchronized step")
