@@ -113,6 +113,10 @@ def _declare(lib):
     lib.orc_ledger_bytes.restype = f64
     lib.orc_comm_elements.argtypes = [f64, i32, i32, i32]
     lib.orc_comm_elements.restype = f64
+    lib.orc_layout_rows.argtypes = [i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.orc_layout_rows.restype = C.c_int
+    lib.orc_reshard.argtypes = [i32, vp, i32, vp, vp, i32, vp, i32, vp, i32, vp, i32]
+    lib.orc_reshard.restype = C.c_int
 
 
 def _ptr(a: np.ndarray) -> int:
@@ -132,23 +136,31 @@ HYPER = dict(lr=3e-4, b1=0.9, b2=0.95, eps=1e-8, wd=0.1)
 
 
 class Layout:
-    """The oracle's own layout of units padded to a multiple of n."""
+    """The oracle's own layout: units padded to a multiple of n elements
+    (row_len None), or to a multiple of n whole rows of row_len[u] elements."""
 
-    def __init__(self, n: int, numel, lib=None):
+    def __init__(self, n: int, numel, lib=None, row_len=None):
         self.lib = lib or load()
         self.n = int(n)
         self.numel = np.ascontiguousarray(numel, dtype=np.int64)
         U = len(self.numel)
+        self.row_len = None if row_len is None else np.ascontiguousarray(row_len, dtype=np.int64)
+        if self.row_len is not None and len(self.row_len) != U:
+            raise ValueError("one row length per unit")
         self.padded = np.zeros(max(U, 1), np.int64)
         self.shard = np.zeros(max(U, 1), np.int64)
         self.offset = np.zeros(max(U, 1), np.int64)
         self.local_offset = np.zeros(max(U, 1), np.int64)
         tp, ts = i64(), i64()
-        rc = self.lib.orc_layout(self.n, U, _ptr(self.numel) if U else None,
-                                 _ptr(self.padded), _ptr(self.shard), _ptr(self.offset),
-                                 _ptr(self.local_offset), C.byref(tp), C.byref(ts))
+        outs = (_ptr(self.padded), _ptr(self.shard), _ptr(self.offset), _ptr(self.local_offset),
+                C.byref(tp), C.byref(ts))
+        if self.row_len is None:
+            rc = self.lib.orc_layout(self.n, U, _ptr(self.numel) if U else None, *outs)
+        else:
+            rc = self.lib.orc_layout_rows(self.n, U, _ptr(self.numel) if U else None,
+                                          _ptr(self.row_len) if U else None, *outs)
         if rc != 0:
-            raise ValueError(f"orc_layout rc={rc}")
+            raise ValueError(f"oracle layout rc={rc}")
         self.padded, self.shard = self.padded[:U], self.shard[:U]
         self.offset, self.local_offset = self.offset[:U], self.local_offset[:U]
         self.total_padded, self.total_shard = tp.value, ts.value
@@ -165,6 +177,31 @@ class Layout:
         if rc != 0:
             raise ValueError(j)
         return r.value, k.value
+
+
+def reshard(numel, n_a, src, n_b, dst_rank, *, row_a=None, row_b=None, numel_b=None) -> np.ndarray:
+    """Rank dst_rank's local shard under layout B (units numel_b, default
+    numel; n_b ranks; row lengths row_b or flat), built from the local shards
+    src[q] of every rank q under layout A (units numel, n_a ranks, row_a).
+    src: n_a arrays of one dtype (4-byte or 2-byte elements)."""
+    lib = load()
+    na = np.ascontiguousarray(numel, dtype=np.int64)
+    nb = na if numel_b is None else np.ascontiguousarray(numel_b, dtype=np.int64)
+    src = [np.ascontiguousarray(a) for a in src]
+    if len(src) != n_a or len({a.dtype for a in src}) != 1:
+        raise ValueError("one source shard per rank of layout A, one dtype")
+    dt = src[0].dtype
+    B = Layout(n_b, nb, row_len=row_b)
+    dst = np.zeros(B.total_shard, dt)
+    ra = None if row_a is None else np.ascontiguousarray(row_a, dtype=np.int64)
+    rb = None if row_b is None else np.ascontiguousarray(row_b, dtype=np.int64)
+    keep = _ptr_array(src)
+    opt = lambda a: _ptr(a) if a is not None and len(a) else None
+    rc = lib.orc_reshard(len(na), opt(na), n_a, opt(ra), keep, len(nb), opt(nb), n_b, opt(rb),
+                         dst_rank, _ptr(dst) if len(dst) else None, dt.itemsize)
+    if rc != 0:
+        raise ValueError(f"orc_reshard rc={rc}")
+    return dst
 
 
 def bf16(x) -> np.ndarray:

@@ -114,6 +114,41 @@ int orc_owner_of_global(int32_t n, int32_t n_units, const int64_t *shard,
     return ORC_EINVAL;
 }
 
+/* Row-aligned layout: p4 section 5, "FSDP1 vs FSDP2" (FSDP2 keeps each
+ * parameter as its own tensor, chunked along dim 0); p3's note after its
+ * section 5 names this row-aligned sharding.  Unit u is one parameter
+ * of rows[u] = numel[u] / row_len[u] rows; torch.chunk over the rows gives
+ * every rank ceil(rows / n) rows (the last ranks fewer, or none), and FSDP2
+ * pads each rank's piece to that many rows.  So the unit is padded one whole
+ * row at a time until the row count divides by n, and rank r's slice is rows
+ * [r c, (r + 1) c), c = padded rows / n.  The outputs mean what they mean in
+ * orc_layout; row_len[u] must divide numel[u]. */
+int orc_layout_rows(int32_t n, int32_t n_units, const int64_t *numel,
+                    const int64_t *row_len, int64_t *padded, int64_t *shard,
+                    int64_t *offset, int64_t *local_offset,
+                    int64_t *total_padded, int64_t *total_shard)
+{
+    if (n < 1 || n_units < 0)
+        return ORC_EINVAL;
+    int64_t next_offset = 0, next_local = 0;
+    for (int32_t u = 0; u < n_units; ++u) {
+        if (numel[u] < 0 || row_len[u] < 1 || numel[u] % row_len[u] != 0)
+            return ORC_EINVAL;
+        int64_t rows = numel[u] / row_len[u];
+        while (rows % n != 0)   /* pad one row at a time */
+            rows += 1;
+        padded[u] = rows * row_len[u];
+        shard[u] = padded[u] / n;
+        offset[u] = next_offset;
+        local_offset[u] = next_local;
+        next_offset += padded[u];
+        next_local += shard[u];
+    }
+    *total_padded = next_offset;
+    *total_shard = next_local;
+    return ORC_OK;
+}
+
 /* ------------------------------------------------------------------------ */
 /* bfloat16 rounding (p1 "How it works": the updated master is cast to bf16). */
 /* ------------------------------------------------------------------------ */
@@ -301,6 +336,89 @@ static void lay_free(orc_lay *L)
     free(L->shard);
     free(L->offset);
     free(L->local_offset);
+}
+
+/* Either layout: row_len == NULL gives the flat layout (orc_layout). */
+static int lay_make_any(int32_t n, int32_t n_units, const int64_t *numel,
+                        const int64_t *row_len, orc_lay *L)
+{
+    if (!row_len)
+        return lay_make(n, n_units, numel, L);
+    L->n = n;
+    L->n_units = n_units;
+    size_t bytes = sizeof(int64_t) * (size_t)(n_units > 0 ? n_units : 1);
+    L->padded = malloc(bytes);
+    L->shard = malloc(bytes);
+    L->offset = malloc(bytes);
+    L->local_offset = malloc(bytes);
+    if (!L->padded || !L->shard || !L->offset || !L->local_offset)
+        return ORC_ENOMEM;
+    return orc_layout_rows(n, n_units, numel, row_len, L->padded, L->shard,
+                           L->offset, L->local_offset, &L->total_padded,
+                           &L->total_shard);
+}
+
+/* Reshard: p1 "Implementation notes" (a checkpoint saved as per-rank shards
+ * is resharded when loaded under a different N) and p4 section 5, "FSDP1 vs
+ * FSDP2" (checkpoints carry over between the flat and per-parameter
+ * layouts).  An element is named by its stream position: its index in all
+ * units' unpadded elements laid end to end.  Layout A has units numel_a,
+ * n_a ranks and row lengths row_a (NULL: flat); layout B likewise; both hold
+ * the same number of elements.  src[q] is rank q's local shard in A; dst
+ * receives rank dst_rank's local shard in B.  Element by element: local index
+ * k of B -> B's global index -> (unit, position in the unit); a position at or
+ * past the unit's numel is padding and becomes zero, any other gives a stream
+ * position, which gives A's unit and position, A's global index and its owner
+ * (rank, local index), read from src.  elem: bytes per element. */
+int orc_reshard(int32_t units_a, const int64_t *numel_a, int32_t n_a,
+                const int64_t *row_a, const void *const *src, int32_t units_b,
+                const int64_t *numel_b, int32_t n_b, const int64_t *row_b,
+                int32_t dst_rank, void *dst, int32_t elem)
+{
+    if (dst_rank < 0 || dst_rank >= n_b || (elem != 2 && elem != 4))
+        return ORC_EINVAL;
+    int64_t total_a = 0, total_b = 0;
+    for (int32_t u = 0; u < units_a; ++u)
+        total_a += numel_a[u];
+    for (int32_t u = 0; u < units_b; ++u)
+        total_b += numel_b[u];
+    if (total_a != total_b)
+        return ORC_EINVAL;
+    orc_lay A = {0}, B = {0};
+    int st = lay_make_any(n_a, units_a, numel_a, row_a, &A);
+    if (st == ORC_OK)
+        st = lay_make_any(n_b, units_b, numel_b, row_b, &B);
+    for (int64_t k = 0; st == ORC_OK && k < B.total_shard; ++k) {
+        int64_t j = orc_global_of_local(units_b, B.shard, B.offset,
+                                        B.local_offset, dst_rank, k);
+        int32_t u = 0;
+        int64_t stream = 0;
+        while (!(j >= B.offset[u] && j < B.offset[u] + B.padded[u])) {
+            stream += numel_b[u];
+            ++u;
+        }
+        int64_t pos = j - B.offset[u];
+        char *d = (char *)dst + k * elem;
+        if (pos >= numel_b[u]) {
+            memset(d, 0, (size_t)elem);
+            continue;
+        }
+        stream += pos;
+        int32_t w = 0;                       /* A's unit holding the position */
+        while (stream >= numel_a[w]) {
+            stream -= numel_a[w];
+            ++w;
+        }
+        int32_t q;
+        int64_t ka;
+        st = orc_owner_of_global(n_a, units_a, A.shard, A.offset,
+                                 A.local_offset, A.offset[w] + stream, &q, &ka);
+        if (st == ORC_OK)
+            memcpy(d, (const char *)src[q] + ka * elem, (size_t)elem);
+    }
+    lay_free(&A);
+    lay_free(&B);
+    return st;
 }
 
 /* One rank's step.

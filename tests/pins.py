@@ -88,6 +88,147 @@ def pin_layout_bruteforce(seed=0, cases=400):
 
 
 # ---------------------------------------------------------------------------
+# Row-aligned layout: FSDP2 chunks each parameter on dim 0 with torch.chunk
+# and pads every rank's piece to the first chunk's row count ("Learn: ZeRO &
+# FSDP", section 5, FSDP1 vs FSDP2).  Reshard: a checkpoint saved as per-rank
+# shards is re-cut for another N ("ZeRO and FSDP sharding", Implementation
+# notes).  Both are pinned to explicit constructions that share nothing with
+# the oracle's index maps.
+# ---------------------------------------------------------------------------
+
+def fsdp2_local_shards(params, n):
+    """Rank r's local shard as FSDP2 lays it out: for each parameter in order,
+    torch.chunk(param, n, dim=0)[r] (empty where chunk returns fewer pieces),
+    zero-padded to the first chunk's row count, flattened; concatenated."""
+    import torch
+    shards = []
+    for r in range(n):
+        parts = []
+        for p in params:
+            chunks = torch.chunk(p, n, dim=0)
+            c = chunks[0].shape[0] if p.shape[0] else 0
+            piece = chunks[r] if r < len(chunks) and p.shape[0] else p[:0]
+            pad = torch.zeros((c - piece.shape[0],) + tuple(p.shape[1:]), dtype=p.dtype)
+            parts.append(torch.cat([piece, pad]).reshape(-1))
+        shards.append(torch.cat(parts).numpy() if parts else np.zeros(0))
+    return shards
+
+
+def flat_local_shards(params, n, groups=None):
+    """Rank r's local shard of the flat layout, from brute_layout's listing.
+    groups: how many consecutive parameters each unit holds (default one)."""
+    vals = [np.asarray(p).reshape(-1) for p in params]
+    groups = groups or [1] * len(vals)
+    units, at = [], 0
+    for g in groups:
+        units.append(np.concatenate(vals[at:at + g]) if g else np.zeros(0))
+        at += g
+    flat, _, local = brute_layout(n, [len(v) for v in units])
+    dt = vals[0].dtype if vals else np.float64
+    return [np.array([0 if flat[j] is None else units[flat[j][0]][flat[j][1]] for j in local[r]],
+                     dtype=dt) for r in range(n)]
+
+
+def random_groups(rng, U):
+    """A random split of U parameters into consecutive units (FSDP1-style
+    blocks), empty units included now and then."""
+    groups, left = [], U
+    while left:
+        g = int(rng.integers(0, left + 1))
+        groups.append(g)
+        left -= g
+    return groups
+
+
+def layout_case(rng, params, numel, row_len, n):
+    """A random layout of the parameters: per-parameter rows (FSDP2),
+    per-parameter flat, or flat blocks of several parameters (FSDP1).
+    Returns (shards by explicit construction, unit numels, row lengths)."""
+    kind = int(rng.integers(0, 3))
+    if kind == 0:
+        return fsdp2_local_shards(params, n), numel, row_len
+    if kind == 1:
+        return flat_local_shards(params, n), numel, None
+    groups = random_groups(rng, len(params))
+    units, at = [], 0
+    for g in groups:
+        units.append(sum(numel[at:at + g]))
+        at += g
+    return flat_local_shards(params, n, groups), units, None
+
+
+def random_params(rng, U, max_rows=13, max_cols=5):
+    """U parameters with unique nonzero values (so zero marks padding only):
+    2-D (rows, cols), or 1-D (row length 1); rows may be 0."""
+    import torch
+    shapes = []
+    for _ in range(U):
+        rows = int(rng.integers(0, max_rows + 1))
+        shapes.append((rows,) if rng.random() < 0.3 else (rows, int(rng.integers(1, max_cols + 1))))
+    total = sum(int(np.prod(s)) for s in shapes)
+    vals = torch.arange(1, total + 1, dtype=torch.float64)
+    params, at = [], 0
+    for s in shapes:
+        k = int(np.prod(s))
+        params.append(vals[at:at + k].reshape(s))
+        at += k
+    row_len = [int(np.prod(s[1:])) if len(s) > 1 else 1 for s in shapes]
+    return params, [int(np.prod(s)) for s in shapes], row_len
+
+
+def shards_from_layout(L, params, n):
+    """Every rank's local shard read through the oracle's own index maps."""
+    vals = [np.asarray(p).reshape(-1) for p in params]
+    out = []
+    for r in range(n):
+        v = np.zeros(L.total_shard)
+        for k in range(L.total_shard):
+            j = L.global_of_local(r, k)
+            u = next(u for u in range(L.n_units) if L.offset[u] <= j < L.offset[u] + L.padded[u])
+            pos = j - L.offset[u]
+            if pos < L.numel[u]:
+                v[k] = vals[u][pos]
+        out.append(v)
+    return out
+
+
+def pin_rows_vs_torch_chunk(seed=0, cases=150):
+    rng = np.random.default_rng(seed)
+    for case in range(cases):
+        n = int(rng.integers(1, 10))
+        params, numel, row_len = random_params(rng, int(rng.integers(1, 5)))
+        L = oracle.Layout(n, numel, row_len=row_len)
+        want = fsdp2_local_shards(params, n)
+        assert L.total_shard == len(want[0]), (case, n, numel, row_len)
+        assert L.total_padded == n * L.total_shard
+        got = shards_from_layout(L, params, n)
+        for r in range(n):
+            assert np.array_equal(got[r], want[r]), (case, n, numel, row_len, r)
+
+
+def pin_reshard(seed=0, cases=80):
+    """Reshard between random layouts (rows, flat, flat blocks; any N) equals
+    the destination layout's explicit construction, for 4- and 2-byte
+    elements; resharding to one flat rank gives the parameters themselves."""
+    rng = np.random.default_rng(seed)
+    for case in range(cases):
+        params, numel, row_len = random_params(rng, int(rng.integers(1, 6)))
+        n_a, n_b = int(rng.integers(1, 9)), int(rng.integers(1, 9))
+        src, units_a, row_a = layout_case(rng, params, numel, row_len, n_a)
+        want, units_b, row_b = layout_case(rng, params, numel, row_len, n_b)
+        dt = np.float32 if case % 2 == 0 else np.uint16
+        src = [x.astype(dt) for x in src]
+        for r in range(n_b):
+            got = oracle.reshard(units_a, n_a, src, n_b, r, row_a=row_a, row_b=row_b,
+                                 numel_b=units_b)
+            assert got.dtype == dt and np.array_equal(got, want[r].astype(dt)), \
+                (case, n_a, n_b, units_a, units_b, row_a, row_b, r)
+        whole = oracle.reshard(units_a, n_a, src, 1, 0, row_a=row_a, numel_b=[sum(numel)])
+        cat = np.concatenate([np.asarray(p).reshape(-1) for p in params]).astype(dt)
+        assert np.array_equal(whole, cat), (case, "gather to one rank")
+
+
+# ---------------------------------------------------------------------------
 # bf16 rounding: torch's float32 -> bfloat16 conversion rounds to nearest even.
 # ---------------------------------------------------------------------------
 
@@ -365,4 +506,5 @@ def pin_ledger():
 
 
 ALL_PINS = [pin_layout_bruteforce, pin_bf16_vs_torch, pin_adamw_vs_torch64, pin_scalars,
-            pin_sharded_equals_unsharded, pin_rank_local_equals_global, pin_toy, pin_norm, pin_ledger]
+            pin_sharded_equals_unsharded, pin_rank_local_equals_global, pin_toy, pin_norm, pin_ledger,
+            pin_rows_vs_torch_chunk, pin_reshard]

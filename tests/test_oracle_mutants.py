@@ -38,6 +38,14 @@ MUTANTS = [
      "float acc = 0.0f;\n    for (int64_t i = 0; i < n; ++i) {\n        float x = g[i];"),
     ("ledger stage 2 forgets the gradients", "if (stage >= 2)\n        grads = grads / n;", ""),
     ("ledger stage 3 communication 2 psi", "double passes = (stage >= 3) ? 3.0 : 2.0;", "double passes = 2.0;"),
+    ("rows padded by elements", "while (rows % n != 0)   /* pad one row at a time */",
+     "while ((rows * row_len[u]) % n != 0)   /* pad one row at a time */"),
+    ("reshard reads the destination layout's offset", "A.local_offset, A.offset[w] + stream, &q, &ka);",
+     "A.local_offset, B.offset[w] + stream, &q, &ka);"),
+    ("reshard ignores the unit's stream start", "stream += numel_b[u];\n            ++u;",
+     "++u;"),
+    ("reshard reads the destination rank's shard", "memcpy(d, (const char *)src[q] + ka * elem",
+     "memcpy(d, (const char *)src[dst_rank < n_a ? dst_rank : 0] + ka * elem"),
 ]
 
 

@@ -78,3 +78,36 @@ def test_padding_stays_positive_zero():
                              t=t, lr=0.01, b1=0.9, b2=0.95, eps=1e-8, wd=0.1)
     assert np.all(master[5:].view(np.uint32) == 0) and np.all(out[5:] == 0)
     assert np.all(m[5:].view(np.uint32) == 0) and np.all(v[5:].view(np.uint32) == 0)
+
+
+def test_row_layout_vs_torch_chunk():
+    pins.pin_rows_vs_torch_chunk()
+
+
+def test_reshard_vs_explicit_layouts():
+    pins.pin_reshard()
+
+
+def test_reshard_round_trip_and_edges():
+    """A -> B -> A gives A back; empty units and single-rank layouts pass
+    through; mismatched arguments are refused."""
+    rng = np.random.default_rng(7)
+    for case in range(20):
+        params, numel, row_len = pins.random_params(rng, int(rng.integers(1, 6)))
+        n_a, n_b = int(rng.integers(1, 9)), int(rng.integers(1, 9))
+        groups = pins.random_groups(rng, len(numel))
+        units = [sum(numel[sum(groups[:i]):sum(groups[:i + 1])]) for i in range(len(groups))]
+        src = pins.flat_local_shards(params, n_a, groups)
+        src = [s.astype(np.float32) for s in src]
+        mid = [oracle.reshard(units, n_a, src, n_b, r, row_b=row_len, numel_b=numel)
+               for r in range(n_b)]
+        back = [oracle.reshard(numel, n_b, mid, n_a, r, row_a=row_len, numel_b=units)
+                for r in range(n_a)]
+        for r in range(n_a):
+            assert np.array_equal(back[r], src[r]), (case, r)
+    with pytest.raises(ValueError):
+        oracle.reshard([4], 2, [np.zeros(2, np.float32)] * 2, 2, 2)   # no rank 2
+    with pytest.raises(ValueError):                                    # 4 vs 5 elements
+        oracle.reshard([4], 2, [np.zeros(2, np.float32)] * 2, 2, 0, numel_b=[5])
+    with pytest.raises(ValueError):
+        oracle.Layout(2, [5], row_len=[2])                              # 2 does not divide 5
