@@ -59,6 +59,10 @@ def parse():
                     help="time the ZeRO-Offload step: norm pass on the GPU, reduced gradient "
                          "down over PCIe, host step, bf16 parameters up (one rank's shard)")
     ap.add_argument("--chunk", type=int, default=1 << 22, help="offload pipeline chunk (elements)")
+    ap.add_argument("--reshard", default=None, metavar="NAME",
+                    help="time a checkpoint reshard (gpt2l_reshard, llama8b_reshard) instead of "
+                         "the step: one destination rank's fp32 shard from flat block units to "
+                         "row-aligned per-parameter units at another N")
     return ap.parse_args()
 
 
@@ -239,8 +243,112 @@ def offload_bench(args):
     print(json.dumps(res))
 
 
+def reshard_layouts(R, z, workloads):
+    units = [list(u) for u in R.units]
+    A = z.zero_pack(R.from_ranks, workloads.unit_numels(units))
+    shapes = workloads.param_shapes(units)
+    numel = [workloads.numel_of(sh) for sh in shapes]
+    row_len = workloads.row_lengths(shapes)
+    B = z.zero_pack_rows(R.to_ranks, numel, row_len)
+    return A, B, workloads.unit_numels(units), numel, row_len
+
+
+def reshard_cpu_baseline(R, seconds: float):
+    """The oracle's reshard (serial C) on contiguous spans of the same
+    destination shard, from the same source layout, until the budget is
+    spent.  Returns destination elements per second."""
+    import numpy as np
+
+    import oracle
+    import fsdp_sharded_optimizer_flat_amd as z
+    from fsdp_sharded_optimizer_flat_amd import workloads
+
+    A, B, units_a, numel, row_len = reshard_layouts(R, z, workloads)
+    # the oracle reads only the source elements the spans need; the rest of
+    # each source shard may hold anything, so the sources are views of one
+    # shared array (the oracle's inputs are host memory)
+    shared = np.random.default_rng(R.seed).standard_normal(A.shard).astype(np.float32)
+    src = [shared] * R.from_ranks
+    span = 1 << 14
+    done, k0, t0 = 0, 0, time.perf_counter()
+    while True:
+        k1 = min(k0 + span, B.shard)
+        oracle.reshard_span(units_a, R.from_ranks, src, R.to_ranks, R.dst_rank, k0, k1,
+                            row_b=row_len, numel_b=numel)
+        done += k1 - k0
+        k0 = (k0 + 7919 * span) % max(B.shard - span, 1)
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": done / el, "unit": "elements/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} destination elements in {span}-element spans spread over the "
+                      f"{B.shard}-element shard, serial C, {el:.1f} s"}
+
+
+def reshard_bench(args):
+    """One destination rank's fp32 state shard resharded on the device from
+    the flat block layout to the row-aligned per-parameter layout; the
+    sources are every source rank's shard, resident in HBM."""
+    import numpy as np
+    import torch
+
+    import fsdp_sharded_optimizer_flat_amd as z
+    from fsdp_sharded_optimizer_flat_amd import synth, workloads
+
+    R = workloads.RESHARDS[args.reshard]
+    dev = torch.device("cuda:0")
+    A, B, units_a, numel, row_len = reshard_layouts(R, z, workloads)
+    src = []
+    for q in range(R.from_ranks):
+        t = torch.empty(A.shard, dtype=torch.float32, device=dev)
+        synth.fill_normal_(t, 0.02, synth.seed_of(R.seed, synth.TAG_MASTER, 0, q))
+        src.append(t)
+    dst = torch.empty(B.shard, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        z.zero_reshard(A, src, B, R.dst_rank, dst, stream)
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in events:
+        a.record(stream)
+        z.zero_reshard(A, src, B, R.dst_rank, dst, stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    call_s = float(np.mean([a.elapsed_time(b) for a, b in events])) / 1e3
+    nbytes, elements = z.zero_reshard_traffic(A, B, R.dst_rank, z.ZERO_F32)
+    achieved = nbytes / call_s / 1e9
+    result = {
+        "metric": "checkpoint reshard destination elements/sec and achieved HBM GB/s",
+        "value": elements * args.steps / wall, "unit": "elements/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": R.name, "description": R.description,
+                   "from": f"{len(units_a)} flat units, N={R.from_ranks}",
+                   "to": f"{len(numel)} row-aligned units, N={R.to_ranks}",
+                   "dst_rank": R.dst_rank, "elements_per_step": int(elements),
+                   "algorithmic_bytes_per_step": nbytes},
+        "roofline": {"bound": "hbm", "kernel": "copy_batch_kernel (all launches of one reshard)",
+                     "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": None,
+                     "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": call_s * 1e3},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        del src, dst
+        torch.cuda.empty_cache()
+        result["cpu_baseline"] = reshard_cpu_baseline(R, args.cpu_seconds)
+    print(json.dumps(result))
+
+
 def main():
     args = parse()
+    if args.reshard:
+        reshard_bench(args)
+        return
     if args.offload:
         offload_bench(args)
         return

@@ -36,14 +36,14 @@ ZERO_F32, ZERO_BF16 = 0, 1
 ZERO_GLOBAL, ZERO_LOCAL = 0, 1
 ZERO_MAX_RANKS = 256
 ZERO_LAYOUT_MAGIC = 0x5A45524F
-ZERO_ABI_VERSION = 1
+ZERO_ABI_VERSION = 2
 
 i32, i64, f32, f64, vp, sz = C.c_int32, C.c_int64, C.c_float, C.c_double, C.c_void_p, C.c_size_t
 
 
 class ZeroUnit(C.Structure):
     _fields_ = [("numel", i64), ("padded", i64), ("shard", i64), ("offset", i64),
-                ("local_offset", i64)]
+                ("local_offset", i64), ("granule", i64)]
 
 
 class ZeroLayoutHeader(C.Structure):
@@ -87,6 +87,11 @@ def _sig(name, res, *args):
 
 _zero_layout_bytes = _sig("zero_layout_bytes", sz, i32)
 _zero_pack = _sig("zero_pack", i32, i32, i32, vp, vp, sz, C.POINTER(sz))
+_zero_pack_rows = _sig("zero_pack_rows", i32, i32, i32, vp, vp, vp, sz, C.POINTER(sz))
+_zero_reshard = _sig("zero_reshard", i32, vp, vp, vp, i32, vp, i32, vp)
+_zero_reshard_host = _sig("zero_reshard_host", i32, vp, vp, vp, i32, vp, i32)
+_zero_reshard_traffic = _sig("zero_reshard_traffic", i32, vp, vp, i32, i32, C.POINTER(f64),
+                             C.POINTER(i64))
 _zero_global_index = _sig("zero_global_index", i32, vp, i32, i64, C.POINTER(i64))
 _zero_owner = _sig("zero_owner", i32, vp, i64, C.POINTER(i32), C.POINTER(i64))
 _zero_pack_copy = _sig("zero_pack_copy", i32, vp, i32, i32, vp, vp, vp, i32, vp, i32, vp)
@@ -122,7 +127,8 @@ _zero_strerror = _sig("zero_strerror", C.c_char_p, i32)
 _zero_last_hip_error = _sig("zero_last_hip_error", C.c_char_p)
 _zero_abi_version = _sig("zero_abi_version", i32)
 
-EXPORTED = ["zero_layout_bytes", "zero_pack", "zero_global_index", "zero_owner", "zero_pack_copy",
+EXPORTED = ["zero_layout_bytes", "zero_pack", "zero_pack_rows", "zero_reshard",
+            "zero_reshard_host", "zero_reshard_traffic", "zero_global_index", "zero_owner", "zero_pack_copy",
             "zero_unpack_copy", "zero_adamw_scalars_for", "zero_adamw_scalars_next", "zero_step",
             "zero_step_host", "zero_offload_step", "zero_step_device_clip",
             "zero_clip_coef_async", "zero_overlap",
@@ -221,6 +227,10 @@ class Layout:
         return np.array([[u.numel, u.padded, u.shard, u.offset, u.local_offset]
                          for u in self.units], dtype=np.int64).reshape(-1, 5)
 
+    def unit_granules(self) -> np.ndarray:
+        """(U,) int64: each unit's granule (1 for the flat layout)."""
+        return np.array([u.granule for u in self.units], dtype=np.int64)
+
 
 def zero_layout_bytes(n_units: int) -> int:
     return int(_zero_layout_bytes(n_units))
@@ -235,6 +245,30 @@ def zero_pack(n_ranks: int, unit_numel: Sequence[int]) -> Layout:
     _check(_zero_pack(n_ranks, len(numel), numel.ctypes.data if len(numel) else None,
                       C.addressof(buf), need.value, None), "zero_pack")
     return Layout(buf)
+
+
+def zero_pack_rows(n_ranks: int, unit_numel: Sequence[int], unit_granule: Sequence[int]) -> Layout:
+    """Row-aligned layout: unit u pads to a multiple of n_ranks * granule[u]."""
+    numel = np.ascontiguousarray(unit_numel, dtype=np.int64)
+    gran = np.ascontiguousarray(unit_granule, dtype=np.int64)
+    if len(gran) != len(numel):
+        raise ValueError("one granule per unit")
+    args = (n_ranks, len(numel), numel.ctypes.data if len(numel) else None,
+            gran.ctypes.data if len(gran) else None)
+    need = sz()
+    _check(_zero_pack_rows(*args, None, 0, C.byref(need)), "zero_pack_rows")
+    buf = (C.c_char * need.value)()
+    _check(_zero_pack_rows(*args, C.addressof(buf), need.value, None), "zero_pack_rows")
+    return Layout(buf)
+
+
+def zero_pack_params(n_ranks: int, shapes, *, rows: bool) -> Layout:
+    """One unit per parameter shape: the row-aligned (FSDP2, dim-0) layout
+    when ``rows``, else per-parameter flat units."""
+    numel = [int(np.prod(s)) for s in shapes]
+    if not rows:
+        return zero_pack(n_ranks, numel)
+    return zero_pack_rows(n_ranks, numel, [int(np.prod(s[1:])) if len(s) > 1 else 1 for s in shapes])
 
 
 def zero_global_index(layout: Layout, rank: int, k: int) -> int:
@@ -285,6 +319,49 @@ def zero_unpack_copy(layout: Layout, rank: int, src, params, units, stream=None)
     _check(_zero_unpack_copy(layout.ptr, rank, _dev_ptr(src, "src"), _flat_dtype(src),
                              len(params), C.addressof(ptrs), numel.ctypes.data, unit.ctypes.data,
                              ddt, _stream(stream)), "zero_unpack_copy")
+
+
+def _reshard_dtype(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return ZERO_F32
+    if t.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return ZERO_BF16
+    raise TypeError("reshard buffers must be float32 or 16-bit (bf16 bits)")
+
+
+def zero_reshard(src_layout: Layout, src, dst_layout: Layout, dst_rank: int, dst, stream=None):
+    """Fill device tensor ``dst`` with rank dst_rank's local shard under
+    dst_layout, from the device tensors ``src`` (one local shard per rank of
+    src_layout).  Asynchronous on ``stream``."""
+    if len(src) != src_layout.n_ranks:
+        raise ValueError("one source shard per rank of the source layout")
+    dt = _reshard_dtype(dst)
+    if any(_reshard_dtype(t) != dt for t in src):
+        raise TypeError("sources and destination must share one element type")
+    arr = (vp * max(len(src), 1))(*[_dev_ptr(t, "src") for t in src])
+    _check(_zero_reshard(src_layout.ptr, C.addressof(arr), dst_layout.ptr, dst_rank,
+                         _dev_ptr(dst, "dst"), dt, _stream(stream)), "zero_reshard")
+
+
+def zero_reshard_host(src_layout: Layout, src, dst_layout: Layout, dst_rank: int, dst):
+    """zero_reshard on host buffers (numpy arrays or CPU tensors); synchronous."""
+    if len(src) != src_layout.n_ranks:
+        raise ValueError("one source shard per rank of the source layout")
+    sp = [_host_ptr(t, "src", "grad") for t in src]
+    dp, dk = _host_ptr(dst, "dst", "grad")
+    if any(k != dk for _, k in sp):
+        raise TypeError("sources and destination must share one element type")
+    arr = (vp * max(len(sp), 1))(*[p for p, _ in sp])
+    _check(_zero_reshard_host(src_layout.ptr, C.addressof(arr), dst_layout.ptr, dst_rank, dp,
+                              ZERO_F32 if dk == "f32" else ZERO_BF16), "zero_reshard_host")
+
+
+def zero_reshard_traffic(src_layout: Layout, dst_layout: Layout, dst_rank: int, dtype: int):
+    b, e = f64(), i64()
+    _check(_zero_reshard_traffic(src_layout.ptr, dst_layout.ptr, dst_rank, dtype, C.byref(b),
+                                 C.byref(e)), "zero_reshard_traffic")
+    return b.value, e.value
 
 
 # -- scalars ------------------------------------------------------------------------------

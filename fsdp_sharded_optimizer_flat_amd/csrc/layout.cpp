@@ -1,10 +1,14 @@
 // layout.cpp -- the flat-buffer packer's host side: unit padding, shard
-// ownership, the local <-> global index maps, and the element runs ("pieces")
-// that the kernels stream over.
+// ownership, the local <-> global index maps, the element runs ("pieces")
+// that the kernels stream over, and the copy plan of a reshard.
 //
 // "ZeRO and FSDP sharding", How it works: each unit's parameters are flattened
 // into one buffer padded to a multiple of N, and rank r owns slice r.  Same
 // page, Pitfalls: without the padding the last rank's slice is corrupted.
+// "Learn: ZeRO & FSDP", section 5 (FSDP1 vs FSDP2): FSDP2 shards each
+// parameter on its own along dim 0; a unit with granule g (its row length)
+// pads to a multiple of N g, so each rank's slice is whole rows.
+#include <algorithm>
 #include <climits>
 #include <cstring>
 
@@ -20,8 +24,12 @@ bool layout_ok(const zero_layout *L)
     int64_t off = 0, loff = 0, numel = 0;
     for (int32_t u = 0; u < L->n_units; ++u) {
         const zero_unit &x = L->unit[u];
-        if (x.numel < 0 || x.shard < 0 || x.padded != x.shard * L->n_ranks || x.padded < x.numel ||
-            x.padded - x.numel >= L->n_ranks || x.offset != off || x.local_offset != loff)
+        // padded is the least multiple of N g at or above numel:
+        // padded - numel < N g, i.e. (padded - numel) / N < g in integers
+        if (x.numel < 0 || x.shard < 0 || x.granule < 1 || x.numel % x.granule != 0 ||
+            x.shard % x.granule != 0 || x.padded != x.shard * L->n_ranks || x.padded < x.numel ||
+            (x.padded - x.numel) / L->n_ranks >= x.granule || x.offset != off ||
+            x.local_offset != loff)
             return false;
         off += x.padded;
         loff += x.shard;
@@ -144,6 +152,61 @@ int64_t norm_partials_bound(const zero_layout *L, int32_t rank)
     return selected_elements(L, rank) / kNormSpan + segs;
 }
 
+bool layouts_match(const zero_layout *from, const zero_layout *to)
+{
+    return layout_ok(from) && layout_ok(to) && from->numel == to->numel;
+}
+
+std::vector<ReshardRun> build_reshard_runs(const zero_layout *from, const zero_layout *to,
+                                           int32_t dst_rank)
+{
+    std::vector<ReshardRun> runs;
+    auto add = [&runs](const ReshardRun &r) {
+        if (r.len <= 0)
+            return;
+        if (!runs.empty()) {
+            ReshardRun &p = runs.back();
+            const bool src_next = r.src_rank < 0 ? p.src_rank < 0
+                                                 : p.src_rank == r.src_rank && p.src_k + p.len == r.src_k;
+            if (src_next && p.dst_k + p.len == r.dst_k) {
+                p.len += r.len;
+                return;
+            }
+        }
+        runs.push_back(r);
+    };
+    // An element is identified by its stream position: its index in the
+    // concatenation of every unit's unpadded elements, in unit order.  The
+    // destination's stream positions only increase, so one forward walk over
+    // the source units finds every owner.
+    int32_t a = 0;
+    int64_t a_start = 0, b_start = 0;
+    for (int32_t u = 0; u < to->n_units; ++u) {
+        const zero_unit &y = to->unit[u];
+        if (y.shard > 0) {
+            // positions within unit u that dst_rank's slice covers
+            const int64_t p0 = (int64_t)dst_rank * y.shard, p1 = p0 + y.shard;
+            const int64_t live = std::min(p1, y.numel);
+            for (int64_t s = b_start + p0, s_end = b_start + live; s < s_end;) {
+                while (a + 1 < from->n_units && s >= a_start + from->unit[a].numel)
+                    a_start += from->unit[a++].numel;  // equal totals: s lies in some unit
+                const zero_unit &x = from->unit[a];
+                const int64_t pos = s - a_start;
+                const int64_t q = pos / x.shard;  // x.shard > 0: the unit holds s
+                const int64_t end =
+                    std::min(s_end, a_start + std::min((q + 1) * x.shard, x.numel));
+                add({(int32_t)q, x.local_offset + (pos - q * x.shard),
+                     y.local_offset + (s - b_start - p0), end - s});
+                s = end;
+            }
+            const int64_t z0 = std::max(p0, live);
+            add({-1, 0, y.local_offset + (z0 - p0), p1 - z0});
+        }
+        b_start += y.numel;
+    }
+    return runs;
+}
+
 int64_t norm_tree_scratch(int64_t n)
 {
     // sum over the levels of ceil(n / kNormFanIn^k), k >= 1, until one value
@@ -166,8 +229,11 @@ extern "C" size_t zero_layout_bytes(int32_t n_units)
     return sizeof(zero_layout) + sizeof(zero_unit) * (size_t)n_units;
 }
 
-extern "C" zero_status zero_pack(int32_t n_ranks, int32_t n_units, const int64_t *unit_numel,
-                                 zero_layout *layout, size_t layout_bytes, size_t *bytes_needed)
+// The packer proper: unit u pads to a multiple of N g_u (g_u = 1 when
+// `granule` is null).
+static zero_status pack_impl(int32_t n_ranks, int32_t n_units, const int64_t *unit_numel,
+                             const int64_t *granule, zero_layout *layout, size_t layout_bytes,
+                             size_t *bytes_needed)
 {
     if (n_ranks < 1 || n_units < 0 || n_units > ZERO_MAX_UNITS ||
         (n_units > 0 && !unit_numel))
@@ -175,34 +241,36 @@ extern "C" zero_status zero_pack(int32_t n_ranks, int32_t n_units, const int64_t
     const size_t need = zero_layout_bytes(n_units);
     if (bytes_needed)
         *bytes_needed = need;
+    int64_t off = 0, numel = 0;
+    for (int32_t u = 0; u < n_units; ++u) {  // validate and check the totals first
+        const int64_t p = unit_numel[u], g = granule ? granule[u] : 1;
+        if (p < 0 || g < 1 || p % g != 0)
+            return ZERO_EINVAL;
+        int64_t ng, padded;
+        if (__builtin_mul_overflow((int64_t)n_ranks, g, &ng) || p > INT64_MAX - (ng - 1))
+            return ZERO_ERANGE;
+        padded = (p + ng - 1) / ng * ng;
+        if (off > INT64_MAX - padded || numel > INT64_MAX - p)
+            return ZERO_ERANGE;
+        off += padded;
+        numel += p;
+    }
     if (!layout)
         return ZERO_OK;  // size query
     if (layout_bytes < need)
         return ZERO_ENOSPC;
-    int64_t off = 0, loff = 0, numel = 0;
-    for (int32_t u = 0; u < n_units; ++u) {
-        const int64_t p = unit_numel[u];
-        if (p < 0)
-            return ZERO_EINVAL;
-        if (p > INT64_MAX - n_ranks)
-            return ZERO_ERANGE;
-        const int64_t shard = (p + n_ranks - 1) / n_ranks;  // ceil(p / N)
-        const int64_t padded = shard * n_ranks;
-        if (off > INT64_MAX - padded || numel > INT64_MAX - p)
-            return ZERO_ERANGE;
-        off += padded;
-        loff += shard;
-        numel += p;
-    }
     layout->magic = ZERO_LAYOUT_MAGIC;
     layout->n_ranks = n_ranks;
     layout->n_units = n_units;
     layout->reserved = 0;
-    off = loff = 0;
+    int64_t loff = 0;
+    off = 0;
     for (int32_t u = 0; u < n_units; ++u) {
         zero_unit &x = layout->unit[u];
         x.numel = unit_numel[u];
-        x.shard = (x.numel + n_ranks - 1) / n_ranks;
+        x.granule = granule ? granule[u] : 1;
+        const int64_t rows = x.numel / x.granule;
+        x.shard = (rows + n_ranks - 1) / n_ranks * x.granule;  // ceil(rows / N) rows
         x.padded = x.shard * n_ranks;
         x.offset = off;
         x.local_offset = loff;
@@ -213,6 +281,22 @@ extern "C" zero_status zero_pack(int32_t n_ranks, int32_t n_units, const int64_t
     layout->padded = off;
     layout->shard = loff;
     return ZERO_OK;
+}
+
+extern "C" zero_status zero_pack(int32_t n_ranks, int32_t n_units, const int64_t *unit_numel,
+                                 zero_layout *layout, size_t layout_bytes, size_t *bytes_needed)
+{
+    return pack_impl(n_ranks, n_units, unit_numel, nullptr, layout, layout_bytes, bytes_needed);
+}
+
+extern "C" zero_status zero_pack_rows(int32_t n_ranks, int32_t n_units, const int64_t *unit_numel,
+                                      const int64_t *unit_granule, zero_layout *layout,
+                                      size_t layout_bytes, size_t *bytes_needed)
+{
+    if (n_units > 0 && !unit_granule)
+        return ZERO_EINVAL;
+    return pack_impl(n_ranks, n_units, unit_numel, unit_granule, layout, layout_bytes,
+                     bytes_needed);
 }
 
 extern "C" zero_status zero_global_index(const zero_layout *L, int32_t rank, int64_t k, int64_t *j)

@@ -1,0 +1,208 @@
+// reshard_kernels.hip -- the device side of a checkpoint reshard: copy the
+// runs of a reshard plan from the old shards into the new one and zero-fill
+// its padding ("ZeRO and FSDP sharding", Implementation notes: a sharded
+// checkpoint is resharded to a new N when it is loaded).
+//
+// Pure data movement, bound by HBM bandwidth.  A plan has one run per (unit,
+// source rank) pair: hundreds of runs of a few KB to a few hundred MB.  Up to
+// kCopyPieces runs travel by value in one launch's kernel arguments, and each
+// workgroup finds its run from the prefix sums of block counts, so a whole
+// plan takes a handful of launches.
+//
+// Within a run every store is a 16-byte vector store aligned in the
+// destination.  Shard boundaries fall anywhere, so the source is usually at
+// another 16-byte phase; then each lane reads the two aligned 16-byte blocks
+// its bytes straddle and funnel-shifts them together (both blocks hold bytes
+// of the run, so no read leaves the source buffer's 16-byte-aligned extent).
+// The few elements before the destination's first aligned block and after
+// its last are copied one by one by the run's first workgroup.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "zero_internal.h"
+
+namespace zero {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kCopyPieces = 96;    // runs per launch (kernel arguments: 2.7 KB)
+constexpr int kCopyPerThread = 4;  // 16-byte blocks per thread
+constexpr int64_t kCopyPerBlock = (int64_t)kBlock * kCopyPerThread;  // 16 KB per workgroup
+constexpr int64_t kMaxPieceBytes = int64_t(1) << 34;
+constexpr int64_t kMaxBlocksPerLaunch = int64_t(1) << 24;  // 2^32 work-items
+
+struct CopyPiece {
+    const unsigned char *src;  // null: zero-fill
+    unsigned char *dst;
+    int64_t n;                 // elements
+};
+
+struct CopyBatch {
+    CopyPiece p[kCopyPieces];
+    uint32_t block_end[kCopyPieces];  // inclusive prefix sums of block counts
+    int32_t n_pieces;
+    int32_t elem;                     // bytes per element: 2 or 4
+};
+
+// Split of a run: `head` elements before dst's first 16-byte boundary, then
+// `blocks` whole 16-byte blocks, then `tail` elements.
+struct Split {
+    int64_t head, blocks, tail;
+};
+
+__host__ __device__ inline Split split_of(const unsigned char *dst, int64_t n, int elem)
+{
+    Split s;
+    s.head = (int64_t)((16u - (unsigned)((uintptr_t)dst % 16u)) % 16u) / elem;
+    if (s.head > n)
+        s.head = n;
+    s.blocks = (n - s.head) * elem / 16;
+    s.tail = n - s.head - s.blocks * (16 / elem);
+    return s;
+}
+
+__device__ __forceinline__ void copy_elem(const unsigned char *s, unsigned char *d, int64_t i,
+                                          int elem)
+{
+    if (elem == 4)
+        reinterpret_cast<uint32_t *>(d)[i] = s ? reinterpret_cast<const uint32_t *>(s)[i] : 0u;
+    else
+        reinterpret_cast<uint16_t *>(d)[i] = s ? reinterpret_cast<const uint16_t *>(s)[i] : 0u;
+}
+
+// Bytes [delta, delta + 16) of the 32-byte concatenation lo:hi (delta even,
+// 0 < delta < 16).
+__device__ __forceinline__ u32x4 funnel(u32x4 lo, u32x4 hi, unsigned delta)
+{
+    unsigned a0, a1, a2, a3, a4;
+    switch (delta >> 2) {  // uniform across the workgroup
+    case 0: a0 = lo.x; a1 = lo.y; a2 = lo.z; a3 = lo.w; a4 = hi.x; break;
+    case 1: a0 = lo.y; a1 = lo.z; a2 = lo.w; a3 = hi.x; a4 = hi.y; break;
+    case 2: a0 = lo.z; a1 = lo.w; a2 = hi.x; a3 = hi.y; a4 = hi.z; break;
+    default: a0 = lo.w; a1 = hi.x; a2 = hi.y; a3 = hi.z; a4 = hi.w; break;
+    }
+    const unsigned b = delta & 3u;  // 0 or 2
+    u32x4 r;
+    r.x = __builtin_amdgcn_alignbyte(a1, a0, b);
+    r.y = __builtin_amdgcn_alignbyte(a2, a1, b);
+    r.z = __builtin_amdgcn_alignbyte(a3, a2, b);
+    r.w = __builtin_amdgcn_alignbyte(a4, a3, b);
+    return r;
+}
+
+__global__ __launch_bounds__(kBlock) void copy_batch_kernel(const CopyBatch b)
+{
+    const uint32_t blk = blockIdx.x;
+    int i = 0;
+    while (i + 1 < b.n_pieces && blk >= b.block_end[i])
+        ++i;
+    const uint32_t first = i ? b.block_end[i - 1] : 0u;
+    const unsigned char *s = b.p[i].src;
+    unsigned char *d = b.p[i].dst;
+    const int e = b.elem;
+    const Split sp = split_of(d, b.p[i].n, e);
+    const int64_t lb = blk - first;
+    const int t = threadIdx.x;
+    if (lb == 0) {  // head and tail elements
+        if (t < sp.head)
+            copy_elem(s, d, t, e);
+        else if (t >= 64 && t < 64 + sp.tail)
+            copy_elem(s, d, sp.head + sp.blocks * (16 / e) + (t - 64), e);
+    }
+    u32x4 *db = reinterpret_cast<u32x4 *>(d + sp.head * e);
+    const int64_t base = lb * kCopyPerBlock;
+    if (!s) {
+#pragma unroll
+        for (int k = 0; k < kCopyPerThread; ++k) {
+            const int64_t j = base + (int64_t)k * kBlock + t;
+            if (j < sp.blocks)
+                __builtin_nontemporal_store(u32x4{0u, 0u, 0u, 0u}, db + j);
+        }
+        return;
+    }
+    const unsigned char *sb = s + sp.head * e;
+    const unsigned delta = (unsigned)((uintptr_t)sb % 16u);
+    const u32x4 *sa = reinterpret_cast<const u32x4 *>(sb - delta);  // aligned
+    if (delta == 0) {
+#pragma unroll
+        for (int k = 0; k < kCopyPerThread; ++k) {
+            const int64_t j = base + (int64_t)k * kBlock + t;
+            if (j < sp.blocks)
+                __builtin_nontemporal_store(__builtin_nontemporal_load(sa + j), db + j);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < kCopyPerThread; ++k) {
+            const int64_t j = base + (int64_t)k * kBlock + t;
+            if (j < sp.blocks) {
+                // block j + 1 holds bytes of block j's span: delta > 0
+                const u32x4 lo = sa[j], hi = sa[j + 1];
+                __builtin_nontemporal_store(funnel(lo, hi, delta), db + j);
+            }
+        }
+    }
+}
+
+struct Batcher {
+    CopyBatch b{};
+    int64_t blocks = 0;
+    hipStream_t stream;
+    int err = hipSuccess;
+
+    void flush()
+    {
+        if (b.n_pieces == 0 || err != hipSuccess)
+            return;
+        hipLaunchKernelGGL(copy_batch_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, stream, b);
+        err = hipGetLastError();
+        const int32_t elem = b.elem;
+        b = CopyBatch{};
+        b.elem = elem;
+        blocks = 0;
+    }
+
+    void add(const unsigned char *src, unsigned char *dst, int64_t n)
+    {
+        const int e = b.elem;
+        while (n > 0 && err == hipSuccess) {
+            const int64_t take = std::min(n, kMaxPieceBytes / e);
+            const Split sp = split_of(dst, take, e);
+            const int64_t nb = std::max<int64_t>(1, (sp.blocks + kCopyPerBlock - 1) / kCopyPerBlock);
+            if (b.n_pieces == kCopyPieces || blocks + nb > kMaxBlocksPerLaunch)
+                flush();
+            CopyPiece &pc = b.p[b.n_pieces];
+            pc.src = src;
+            pc.dst = dst;
+            pc.n = take;
+            blocks += nb;
+            b.block_end[b.n_pieces] = (uint32_t)blocks;
+            ++b.n_pieces;
+            if (src)
+                src += take * e;
+            dst += take * e;
+            n -= take;
+        }
+    }
+};
+
+}  // namespace
+
+int launch_reshard(const std::vector<ReshardRun> &runs, const void *const *src, void *dst,
+                   int elem, void *stream)
+{
+    Batcher bt;
+    bt.b.elem = elem;
+    bt.stream = reinterpret_cast<hipStream_t>(stream);
+    for (const ReshardRun &r : runs) {
+        const unsigned char *s =
+            r.src_rank < 0 ? nullptr
+                           : static_cast<const unsigned char *>(src[r.src_rank]) + r.src_k * elem;
+        bt.add(s, static_cast<unsigned char *>(dst) + r.dst_k * elem, r.len);
+    }
+    bt.flush();
+    return bt.err;
+}
+
+}  // namespace zero

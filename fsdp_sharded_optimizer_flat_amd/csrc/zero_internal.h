@@ -70,6 +70,22 @@ int64_t norm_partials_bound(const zero_layout *L, int32_t rank);
 // Layout sanity (magic, counts, internal consistency of the totals).
 bool layout_ok(const zero_layout *L);
 
+// One run of a reshard's copy plan: `len` elements from local index src_k of
+// source rank src_rank's shard to local index dst_k of the destination shard;
+// src_rank < 0 marks padding to zero-fill.
+struct ReshardRun {
+    int32_t src_rank;
+    int64_t src_k, dst_k, len;
+};
+
+// Both layouts valid and holding the same number of parameter elements.
+bool layouts_match(const zero_layout *from, const zero_layout *to);
+
+// The copy plan that fills rank dst_rank's local shard of `to` from the local
+// shards of `from`, in destination order, contiguous runs merged.
+std::vector<ReshardRun> build_reshard_runs(const zero_layout *from, const zero_layout *to,
+                                           int32_t dst_rank);
+
 // Compute units of the current device (cached per device).  <= 0 on error.
 int device_cu_count();
 
@@ -133,5 +149,10 @@ int64_t norm_tree_scratch(int64_t n_partials);
 int launch_convert(const void *src, int src_dtype, void *dst, int dst_dtype, int64_t n,
                    void *stream);
 int launch_fill_zero(void *dst, int dtype, int64_t n, void *stream);
+
+// Device copies of a reshard plan (src[r] + src_k -> dst + dst_k, zero runs
+// filled), `elem` bytes per element; batched into few launches.
+int launch_reshard(const std::vector<ReshardRun> &runs, const void *const *src, void *dst,
+                   int elem, void *stream);
 
 }  // namespace zero

@@ -76,6 +76,48 @@ def unit_numels(units) -> list[int]:
     return [sum(numel_of(s) for _, s in u) for u in units]
 
 
+def param_shapes(units) -> list[tuple]:
+    """Every parameter's shape, in unit order (one unit per parameter)."""
+    return [tuple(s) for u in units for _, s in u]
+
+
+def row_lengths(shapes) -> list[int]:
+    """Row length of each parameter for the dim-0 (row-aligned) layout: the
+    product of the trailing dimensions, 1 for a vector."""
+    return [numel_of(s[1:]) if len(s) > 1 else 1 for s in shapes]
+
+
+@dataclass(frozen=True)
+class Reshard:
+    """A checkpoint reshard: one destination rank's shard of one fp32 state
+    array, from a flat layout of FSDP units (from_ranks) to a row-aligned,
+    one-unit-per-parameter layout (to_ranks)."""
+    name: str
+    units: tuple              # unit -> ((name, shape), ...) of the source layout
+    from_ranks: int
+    to_ranks: int
+    dst_rank: int
+    dtype: str                # "f32" (master, m, v) or "bf16" (parameters)
+    seed: int = 1350
+    description: str = ""
+
+
+def _frozen(units):
+    return tuple(tuple((n, tuple(s)) for n, s in u) for u in units)
+
+
+RESHARDS = {
+    "gpt2l_reshard": Reshard(
+        "gpt2l_reshard", _frozen(gpt2_large_units()), 8, 4, 1, "f32",
+        description="GPT-2-Large-sized fp32 state: 36 flat block units at N=8 -> 436 "
+                    "per-parameter dim-0 units at N=4, rank 1's shard (193.6M elements)"),
+    "llama8b_reshard": Reshard(
+        "llama8b_reshard", _frozen(llama8b_units()), 64, 32, 5, "f32",
+        description="8B Llama-shaped fp32 state: 34 flat block units at N=64 -> 291 "
+                    "per-parameter dim-0 units at N=32, rank 5's shard (about 251M elements)"),
+}
+
+
 @dataclass(frozen=True)
 class Workload:
     name: str

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define ZERO_ABI_VERSION 1
+#define ZERO_ABI_VERSION 2
 
 typedef int32_t zero_status;
 #define ZERO_OK 0
@@ -80,8 +80,9 @@ typedef int32_t zero_status;
  * the flat numel must divide by N or the last rank's slice is corrupted.
  *
  * For unit u with numel P_u (the sum of its parameters' numels, in the
- * caller's order):
- *   padded_u  = ceil(P_u / N) * N          shard_u = padded_u / N
+ * caller's order) and granule g_u (1 for the flat layout; the row length for
+ * the row-aligned layout of zero_pack_rows):
+ *   padded_u  = ceil(P_u / (N g_u)) * N g_u     shard_u = padded_u / N
  *   offset_u  = sum of padded_{u'} over u' < u   (start in the flat buffer)
  *   local_u   = sum of shard_{u'}  over u' < u   (start inside a rank's shard)
  * Rank r's slice of unit u is global [offset_u + r*shard_u, +shard_u); its
@@ -92,9 +93,10 @@ typedef int32_t zero_status;
 typedef struct zero_unit {
     int64_t numel;         /* P_u */
     int64_t padded;        /* padded_u */
-    int64_t shard;         /* shard_u */
+    int64_t shard;         /* shard_u (a multiple of granule) */
     int64_t offset;        /* offset_u */
     int64_t local_offset;  /* local_u */
+    int64_t granule;       /* g_u: elements per row the shards are aligned to */
 } zero_unit;
 
 typedef struct zero_layout {
@@ -123,6 +125,19 @@ size_t zero_layout_bytes(int32_t n_units);
  *         bytes_needed is still filled). */
 zero_status zero_pack(int32_t n_ranks, int32_t n_units, const int64_t *unit_numel,
                       zero_layout *layout, size_t layout_bytes, size_t *bytes_needed);
+
+/* Row-aligned layout -- [p4 section 5, FSDP1 vs FSDP2]: FSDP2 shards each
+ * parameter on its own along dim 0 (torch.chunk over the rows) instead of
+ * FSDP1's flatten-concat-chunk buffer; [p3, the note after section 5] calls
+ * this row-aligned sharding.  Give
+ * each parameter its own unit with granule = its row length (numel / rows):
+ * rank r then owns rows [r c, (r+1) c) of the parameter, c = ceil(rows / N),
+ * zero-padded to c rows -- FSDP2's shard of that parameter.  unit_granule[u]
+ * >= 1 must divide unit_numel[u] (EINVAL otherwise).  The step, the norm and
+ * the packer work unchanged on row-aligned layouts.  Errors as zero_pack. */
+zero_status zero_pack_rows(int32_t n_ranks, int32_t n_units, const int64_t *unit_numel,
+                           const int64_t *unit_granule, zero_layout *layout,
+                           size_t layout_bytes, size_t *bytes_needed);
 
 /* Index maps of the layout (host only).  zero_global_index: global j of rank
  * r's local k (EINVAL unless 0 <= r < N and 0 <= k < S).  zero_owner: owning
@@ -155,6 +170,37 @@ zero_status zero_unpack_copy(const zero_layout *layout, int32_t rank, const void
                              int32_t src_dtype, int32_t n_params, void *const *params,
                              const int64_t *dst_numel, const int32_t *dst_unit,
                              int32_t dst_dtype, void *stream);
+
+/* Reshard -- [p1 Implementation notes]: a sharded checkpoint (each rank
+ * writes its own shard) is resharded to a different N at load time; [p4
+ * section 5, FSDP1 vs FSDP2]: checkpoints carry over between the flat and the
+ * per-parameter layouts.
+ *
+ * An element is identified by its stream position: its index in the
+ * concatenation of all units' unpadded elements, in unit order.  `from` and
+ * `to` must hold the same number of elements (layout->numel); their units, N
+ * and granules may differ (e.g. one unit per block, flat, N = 64 -> one unit
+ * per parameter, row-aligned, N = 32).  src holds from->n_ranks pointers, rank
+ * q's LOCAL shard in layout `from` (from->shard elements each).  dst receives
+ * rank dst_rank's LOCAL shard in layout `to` (to->shard elements): each
+ * element is copied from the rank and local index that hold the same stream
+ * position in `from`; padding is zero.  dtype: ZERO_F32 (state) or ZERO_BF16
+ * (parameters); values are copied bit for bit, not converted.  zero_reshard:
+ * device pointers, asynchronous on `stream`; zero_reshard_host: host pointers,
+ * synchronous.  Errors: EINVAL (element counts differ, bad rank, NULL, dst
+ * overlapping a source), EALIGN (a pointer not aligned to the element size),
+ * EHIP. */
+zero_status zero_reshard(const zero_layout *from, const void *const *src,
+                         const zero_layout *to, int32_t dst_rank, void *dst, int32_t dtype,
+                         void *stream);
+zero_status zero_reshard_host(const zero_layout *from, const void *const *src,
+                              const zero_layout *to, int32_t dst_rank, void *dst, int32_t dtype);
+
+/* Algorithmic HBM bytes of one zero_reshard: elem * (elements copied from the
+ * sources + to->shard elements written), elem = 4 (ZERO_F32) or 2 (ZERO_BF16);
+ * *elements = to->shard.  EINVAL as zero_reshard. */
+zero_status zero_reshard_traffic(const zero_layout *from, const zero_layout *to, int32_t dst_rank,
+                                 int32_t dtype, double *bytes, int64_t *elements);
 
 /* ------------------------------------------------------------------------
  * AdamW step scalars -- [p1 Code]: AdamW with b1, b2, eps, decoupled weight

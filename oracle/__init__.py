@@ -117,6 +117,8 @@ def _declare(lib):
     lib.orc_layout_rows.restype = C.c_int
     lib.orc_reshard.argtypes = [i32, vp, i32, vp, vp, i32, vp, i32, vp, i32, vp, i32]
     lib.orc_reshard.restype = C.c_int
+    lib.orc_reshard_span.argtypes = [i32, vp, i32, vp, vp, i32, vp, i32, vp, i32, i64, i64, vp, i32]
+    lib.orc_reshard_span.restype = C.c_int
 
 
 def _ptr(a: np.ndarray) -> int:
@@ -177,6 +179,29 @@ class Layout:
         if rc != 0:
             raise ValueError(j)
         return r.value, k.value
+
+
+def reshard_span(numel, n_a, src, n_b, dst_rank, k_begin, k_end, *, row_a=None, row_b=None,
+                 numel_b=None) -> np.ndarray:
+    """Elements k_begin <= k < k_end of what :func:`reshard` returns."""
+    lib = load()
+    na = np.ascontiguousarray(numel, dtype=np.int64)
+    nb = na if numel_b is None else np.ascontiguousarray(numel_b, dtype=np.int64)
+    src = [np.ascontiguousarray(a) for a in src]
+    if len(src) != n_a or len({a.dtype for a in src}) != 1:
+        raise ValueError("one source shard per rank of layout A, one dtype")
+    dt = src[0].dtype
+    dst = np.zeros(max(k_end - k_begin, 0), dt)
+    ra = None if row_a is None else np.ascontiguousarray(row_a, dtype=np.int64)
+    rb = None if row_b is None else np.ascontiguousarray(row_b, dtype=np.int64)
+    keep = _ptr_array(src)
+    opt = lambda a: _ptr(a) if a is not None and len(a) else None
+    rc = lib.orc_reshard_span(len(na), opt(na), n_a, opt(ra), keep, len(nb), opt(nb), n_b, opt(rb),
+                              dst_rank, k_begin, k_end, _ptr(dst) if len(dst) else None,
+                              dt.itemsize)
+    if rc != 0:
+        raise ValueError(f"orc_reshard_span rc={rc}")
+    return dst
 
 
 def reshard(numel, n_a, src, n_b, dst_rank, *, row_a=None, row_b=None, numel_b=None) -> np.ndarray:

@@ -370,10 +370,28 @@ static int lay_make_any(int32_t n, int32_t n_units, const int64_t *numel,
  * past the unit's numel is padding and becomes zero, any other gives a stream
  * position, which gives A's unit and position, A's global index and its owner
  * (rank, local index), read from src.  elem: bytes per element. */
+int orc_reshard_span(int32_t units_a, const int64_t *numel_a, int32_t n_a,
+                     const int64_t *row_a, const void *const *src,
+                     int32_t units_b, const int64_t *numel_b, int32_t n_b,
+                     const int64_t *row_b, int32_t dst_rank, int64_t k_begin,
+                     int64_t k_end, void *dst, int32_t elem);
+
 int orc_reshard(int32_t units_a, const int64_t *numel_a, int32_t n_a,
                 const int64_t *row_a, const void *const *src, int32_t units_b,
                 const int64_t *numel_b, int32_t n_b, const int64_t *row_b,
                 int32_t dst_rank, void *dst, int32_t elem)
+{
+    return orc_reshard_span(units_a, numel_a, n_a, row_a, src, units_b, numel_b,
+                            n_b, row_b, dst_rank, 0, -1, dst, elem);
+}
+
+/* The same for local indices k_begin <= k < k_end of the destination shard
+ * only (k_end < 0: to the end); dst[k - k_begin] receives element k. */
+int orc_reshard_span(int32_t units_a, const int64_t *numel_a, int32_t n_a,
+                     const int64_t *row_a, const void *const *src,
+                     int32_t units_b, const int64_t *numel_b, int32_t n_b,
+                     const int64_t *row_b, int32_t dst_rank, int64_t k_begin,
+                     int64_t k_end, void *dst, int32_t elem)
 {
     if (dst_rank < 0 || dst_rank >= n_b || (elem != 2 && elem != 4))
         return ORC_EINVAL;
@@ -388,7 +406,11 @@ int orc_reshard(int32_t units_a, const int64_t *numel_a, int32_t n_a,
     int st = lay_make_any(n_a, units_a, numel_a, row_a, &A);
     if (st == ORC_OK)
         st = lay_make_any(n_b, units_b, numel_b, row_b, &B);
-    for (int64_t k = 0; st == ORC_OK && k < B.total_shard; ++k) {
+    if (st == ORC_OK && k_end < 0)
+        k_end = B.total_shard;
+    if (st == ORC_OK && (k_begin < 0 || k_begin > k_end || k_end > B.total_shard))
+        st = ORC_EINVAL;
+    for (int64_t k = k_begin; st == ORC_OK && k < k_end; ++k) {
         int64_t j = orc_global_of_local(units_b, B.shard, B.offset,
                                         B.local_offset, dst_rank, k);
         int32_t u = 0;
@@ -398,7 +420,7 @@ int orc_reshard(int32_t units_a, const int64_t *numel_a, int32_t n_a,
             ++u;
         }
         int64_t pos = j - B.offset[u];
-        char *d = (char *)dst + k * elem;
+        char *d = (char *)dst + (k - k_begin) * elem;
         if (pos >= numel_b[u]) {
             memset(d, 0, (size_t)elem);
             continue;

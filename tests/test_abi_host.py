@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported():
     for n in names:
         assert hasattr(lib, n), f"{n} declared in zero.h but not exported"
     assert set(names) == set(z.EXPORTED)
-    assert z.zero_abi_version() == z.ZERO_ABI_VERSION == 1
+    assert z.zero_abi_version() == z.ZERO_ABI_VERSION == 2
 
 
 def test_header_constants_match_binding():
@@ -40,8 +40,8 @@ def test_header_constants_match_binding():
                  "ZERO_F32", "ZERO_BF16", "ZERO_GLOBAL", "ZERO_LOCAL", "ZERO_MAX_RANKS"]:
         m = re.search(rf"#define {name} \(?(-?\d+)\)?", text)
         assert m and int(m.group(1)) == getattr(z, name), name
-    assert C.sizeof(z.ZeroLayoutHeader) == 40 and C.sizeof(z.ZeroUnit) == 40
-    assert z.zero_layout_bytes(36) == 40 + 36 * 40
+    assert C.sizeof(z.ZeroLayoutHeader) == 40 and C.sizeof(z.ZeroUnit) == 48
+    assert z.zero_layout_bytes(36) == 40 + 36 * 48
 
 
 # -- layout ---------------------------------------------------------------------
@@ -90,7 +90,7 @@ def test_pack_errors():
     buf = (C.c_char * 8)()
     need = C.c_size_t()
     assert lib.zero_pack(4, 1, numel.ctypes.data, C.addressof(buf), 8, C.byref(need)) == z.ZERO_ENOSPC
-    assert need.value == 80
+    assert need.value == 88
     L = z.zero_pack(4, [10])
     with pytest.raises(z.ZeroError):
         z.zero_global_index(L, 4, 0)

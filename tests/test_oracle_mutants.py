@@ -27,7 +27,16 @@ MUTANTS = [
     ("wrong divisor", "float g = sum / divisor;    /* average */", "float g = sum / (divisor + 1.0f);"),
     ("ranks' slices reversed", "int64_t j = L.offset[u] + (int64_t)r * L.shard[u] + i;\n            int64_t gi = grad_local ? k : j;\n            /* reduce-scatter",
      "int64_t j = L.offset[u] + (int64_t)(n - 1 - r) * L.shard[u] + i;\n            int64_t gi = grad_local ? k : j;\n            /* reduce-scatter"),
-    ("local offset not accumulated", "next_local += shard[u];", "next_local += 0;"),
+    ("local offset not accumulated",
+     "shard[u] = p / n;\n        offset[u] = next_offset;\n        local_offset[u] = next_local;\n"
+     "        next_offset += padded[u];\n        next_local += shard[u];",
+     "shard[u] = p / n;\n        offset[u] = next_offset;\n        local_offset[u] = next_local;\n"
+     "        next_offset += padded[u];\n        next_local += 0;"),
+    ("row layout's local offset not accumulated",
+     "shard[u] = padded[u] / n;\n        offset[u] = next_offset;\n        local_offset[u] = next_local;\n"
+     "        next_offset += padded[u];\n        next_local += shard[u];",
+     "shard[u] = padded[u] / n;\n        offset[u] = next_offset;\n        local_offset[u] = next_local;\n"
+     "        next_offset += padded[u];\n        next_local += 0;"),
     ("padding rounds up one extra", "while (p % n != 0)     /* pad one element at a time: obviously minimal */\n            p += 1;",
      "do                      /* pad one element at a time: obviously minimal */\n            p += 1;\n        while (p % n != 0);"),
     ("bf16 ties away from zero", "pick = (below & 1u) ? above : below;", "pick = above;"),

@@ -111,3 +111,15 @@ def test_reshard_round_trip_and_edges():
         oracle.reshard([4], 2, [np.zeros(2, np.float32)] * 2, 2, 0, numel_b=[5])
     with pytest.raises(ValueError):
         oracle.Layout(2, [5], row_len=[2])                              # 2 does not divide 5
+
+
+def test_reshard_span_is_a_slice_of_reshard():
+    rng = np.random.default_rng(8)
+    params, numel, row_len = pins.random_params(rng, 5)
+    src = [s.astype(np.float32) for s in pins.flat_local_shards(params, 3)]
+    whole = oracle.reshard(numel, 3, src, 2, 1, row_b=row_len)
+    for a, b in ((0, len(whole)), (1, 5), (len(whole) // 2, len(whole)), (3, 3)):
+        part = oracle.reshard_span(numel, 3, src, 2, 1, a, b, row_b=row_len)
+        assert np.array_equal(part, whole[a:b]), (a, b)
+    with pytest.raises(ValueError):
+        oracle.reshard_span(numel, 3, src, 2, 1, 0, len(whole) + 1, row_b=row_len)
