@@ -30,6 +30,7 @@ PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 KERNEL_SOURCES = ["fsdp_sharded_optimizer_flat_amd/csrc/step_kernels.hip",
                   "fsdp_sharded_optimizer_flat_amd/csrc/norm_kernels.hip",
+                  "fsdp_sharded_optimizer_flat_amd/csrc/reshard_kernels.hip",
                   "fsdp_sharded_optimizer_flat_amd/csrc/device_common.h"]
 
 
@@ -39,6 +40,19 @@ def kernel_source_hash() -> str:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the workload's dominant kernel from the
+    committed PMC summary, or None when the kernels changed since."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    with open(PMC_SUMMARY) as f:
+        pmc = json.load(f)
+    ent = pmc.get("workloads", {}).get(workload)
+    if ent and pmc.get("kernel_source_hash") == kernel_source_hash():
+        return ent["traffic_bytes_per_launch"]
+    return None
 
 
 def parse():
@@ -333,8 +347,10 @@ def reshard_bench(args):
                    "algorithmic_bytes_per_step": nbytes},
         "roofline": {"bound": "hbm", "kernel": "copy_batch_kernel (all launches of one reshard)",
                      "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBPS, "traffic": None,
-                     "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": call_s * 1e3},
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": measured_traffic(R.name),
+                     "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": call_s * 1e3,
+                     "launches_per_call": "one reshard = several copy_batch_kernel launches "
+                                          "back to back; achieved and traffic are per call"},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -459,13 +475,7 @@ def main():
     ms_per_step = wall / args.steps * 1e3
     value = elements * args.steps / wall
 
-    traffic = None
-    if os.path.exists(PMC_SUMMARY):
-        with open(PMC_SUMMARY) as f:
-            pmc = json.load(f)
-        ent = pmc.get("workloads", {}).get(args.workload)
-        if ent and pmc.get("kernel_source_hash") == kernel_source_hash():
-            traffic = ent["traffic_bytes_per_launch"]
+    traffic = measured_traffic(args.workload)
 
     result = {
         "metric": "optimizer-step shard elements/sec and achieved HBM GB/s (% of MI355X peak)",

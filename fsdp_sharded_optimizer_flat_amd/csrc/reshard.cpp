@@ -20,8 +20,8 @@ namespace {
 zero_status check_reshard(const zero_layout *from, const void *const *src, const zero_layout *to,
                           int32_t dst_rank, const void *dst, int32_t dtype, int *elem)
 {
-    if (!layouts_match(from, to) || dst_rank < 0 || dst_rank >= to->n_ranks || !src || !dst ||
-        (dtype != ZERO_F32 && dtype != ZERO_BF16))
+    if (!layouts_match(from, to) || dst_rank < 0 || dst_rank >= to->n_ranks || !src ||
+        (!dst && to->shard > 0) || (dtype != ZERO_F32 && dtype != ZERO_BF16))
         return ZERO_EINVAL;
     const int e = dtype == ZERO_F32 ? 4 : 2;
     if ((uintptr_t)dst % (uintptr_t)e != 0)

@@ -187,7 +187,8 @@ zero_status zero_unpack_copy(const zero_layout *layout, int32_t rank, const void
  * position in `from`; padding is zero.  dtype: ZERO_F32 (state) or ZERO_BF16
  * (parameters); values are copied bit for bit, not converted.  zero_reshard:
  * device pointers, asynchronous on `stream`; zero_reshard_host: host pointers,
- * synchronous.  Errors: EINVAL (element counts differ, bad rank, NULL, dst
+ * synchronous.  dst may be NULL when to->shard is 0, and src[q] when
+ * from->shard is 0.  Errors: EINVAL (element counts differ, bad rank, NULL, dst
  * overlapping a source), EALIGN (a pointer not aligned to the element size),
  * EHIP. */
 zero_status zero_reshard(const zero_layout *from, const void *const *src,

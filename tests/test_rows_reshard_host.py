@@ -179,3 +179,13 @@ def test_reshard_plan_is_batched():
         pos = np.arange(lo, lo + tb[u, 2])
         want = np.where(pos < numel[u], stream_start[u] + pos, 0).astype(np.uint32)
         assert np.array_equal(seg, want), u
+
+
+def test_reshard_empty_shards_take_null_pointers():
+    """All-empty layouts: nothing to read or write, NULL buffers accepted."""
+    lib = z.raw_library()
+    A, B = z.zero_pack(4, [0, 0]), z.zero_pack_rows(3, [0], [5])
+    arr = (C.c_void_p * 4)()
+    assert lib.zero_reshard_host(A.ptr, C.addressof(arr), B.ptr, 2, None, z.ZERO_F32) == z.ZERO_OK
+    assert lib.zero_reshard_host(A.ptr, C.addressof(arr), z.zero_pack(1, [0]).ptr, 0, None,
+                                 z.ZERO_BF16) == z.ZERO_OK
