@@ -182,21 +182,25 @@ size_t occupancy_cap_lds(int waves_per_cu)
 
 int step_waves_per_cu(int n_grads)
 {
-    // 7 resident one-wave workgroups per CU (under 2 per SIMD): with every
-    // wave streaming 2N + 3 reads and 4 writes, a smaller window of tiles in
-    // flight keeps fewer DRAM rows competing per bank.  Measured on MI355X
-    // for N = 8 and N = 64: 6 starves the memory pipeline, 7 is best, 8 / 9 /
-    // 12 / uncapped lose 1 / 2 / 4 / 6 points of the 8 TB/s peak.
+    // Resident one-wave workgroups per CU.  Every wave streams N + 3 reads
+    // and 4 writes; a narrower window of tiles in flight keeps fewer DRAM rows
+    // competing per bank.  Measured on MI355X (same box, interleaved repeats):
+    // N = 8: 7 is best (6 starves the memory pipeline; 8 / 10 / uncapped lose
+    // 1 / 2 / 7 points of the 8 TB/s peak); N = 64: 4 is best (5 within 0.1,
+    // 7 1.5 points lower).  Rank counts in between take the nearer setting.
     static const int v = env_int("ZERO_STEP_WAVES_PER_CU", -1, 0, 64);
-    (void)n_grads;
-    return v >= 0 ? v : 7;
+    if (v >= 0)
+        return v;
+    return n_grads >= 32 ? 4 : 7;
 }
 
 int norm_waves_per_cu(int n_grads)
 {
+    // The norm pass streams N reads and one write; at N = 64 a cap of 7
+    // resident waves per CU measured 1.4 points above no cap.
     static const int v = env_int("ZERO_NORM_WAVES_PER_CU", -1, 0, 64);
     (void)n_grads;
-    return v >= 0 ? v : 0;
+    return v >= 0 ? v : 7;
 }
 
 zero_status hip_fail(int err, const char *where)
