@@ -32,6 +32,11 @@ HOST_SOURCES = ["host_step.cpp"]
 HOST_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-mavx2", "-mno-fma", "-ffp-contract=off",
               "-fno-fast-math", "-pthread", "-Wall"]
 
+# Test support built with the same flags: bare sqrt / division kernels the GPU
+# tests check exhaustively against the host's IEEE operations.
+PROBE_SRC = os.path.join(ROOT, "tests", "support", "fp_probe.hip")
+PROBE_LIB = os.path.join(ROOT, "tests", "support", "libfp_probe.so")
+
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
@@ -76,7 +81,19 @@ def build(jobs: int | None = None) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stderr}")
     os.replace(tmp, LIB)
+    build_probe()
     return LIB
+
+
+def build_probe() -> str:
+    """The test-support probe library (tests/support/libfp_probe.so)."""
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [hipcc(), *FLAGS, "-shared", PROBE_SRC, "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {PROBE_SRC}:\n{res.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
 
 
 def device_ir(src: str = "step_kernels.hip") -> str:

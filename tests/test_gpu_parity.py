@@ -104,7 +104,21 @@ def test_gpt2l_block_full_10_steps():
 # layouts (brute force), against the oracle's rank step.
 # ---------------------------------------------------------------------------
 
-def _run_case(rng, n, numel, rank, gdt, gidx, sidx, oidx, shift, steps=2, with_out=True, n_grads=None):
+def _order_sensitive(gnp, gdt):
+    """True if summing the ranks' values in reverse order gives other binary32
+    bits than in rank order for some element (numpy, test-side check only)."""
+    vals = [g.astype(np.uint32) << 16 if gdt == z.ZERO_BF16 else g for g in gnp]
+    vals = [np.asarray(x).view(np.float32) for x in vals]
+    fwd, rev = vals[0].copy(), vals[-1].copy()
+    for x in vals[1:]:
+        fwd = fwd + x
+    for x in vals[-2::-1]:
+        rev = rev + x
+    return bool(np.any(fwd.view(np.uint32) != rev.view(np.uint32)))
+
+
+def _run_case(rng, n, numel, rank, gdt, gidx, sidx, oidx, shift, steps=2, with_out=True, n_grads=None,
+              dist="normal"):
     h = dict(lr=1e-3, b1=0.9, b2=0.95, eps=1e-8, wd=0.1)
     L = z.zero_pack(n, numel)
     O = oracle.Layout(n, numel)
@@ -122,9 +136,13 @@ def _run_case(rng, n, numel, rank, gdt, gidx, sidx, oidx, shift, steps=2, with_o
     oout = np.zeros(oe, np.uint16)
     for t in range(1, steps + 1):
         for g in grads:
-            vals = (rng.standard_normal(ge) * 1e-3).astype(np.float32)
-            g.copy_(torch.from_numpy(vals).to(tdt))
+            vals = rng.standard_normal(ge) * 1e-3
+            if dist == "wide":   # magnitudes over 48 binades: rank sums round often
+                vals = vals * np.exp2(rng.integers(-24, 25, ge))
+            g.copy_(torch.from_numpy(vals.astype(np.float32)).to(tdt))
         gnp = [np.ascontiguousarray(to_np(g)) for g in grads]
+        if dist == "wide" or gdt == z.ZERO_F32:
+            assert ng == 1 or _order_sensitive(gnp, gdt), "test data cannot see the rank order"
         z.zero_step(L, rank, grads, gidx, float(n), master, m, v, sidx, out, oidx, scalars(t, h))
         if rank < 0:
             oracle.zero_step_all(n, numel, gnp, divisor=float(n), clip=1.0, master=om, m=omm, v=ov,
@@ -179,6 +197,21 @@ def test_rank_counts(n):
     _run_case(rng, n, numel, -1, z.ZERO_BF16, G, G, G, shift=0)
     _run_case(rng, n, numel, n - 1, z.ZERO_BF16, Lc, Lc, Lc, shift=0)
     _run_case(rng, n, numel, 0, z.ZERO_BF16, G, Lc, G, shift=2)
+
+
+@pytest.mark.parametrize("n,gdt,dist", [(8, z.ZERO_BF16, "wide"), (8, z.ZERO_F32, "normal"),
+                                          (64, z.ZERO_BF16, "wide"), (5, z.ZERO_BF16, "wide"),
+                                          (256, z.ZERO_F32, "normal")])
+def test_rank_order_visible(n, gdt, dist):
+    """Data on which another summation order changes bits (checked before
+    the step): bf16 gradients whose magnitudes span 48 binades, or fp32
+    gradients.  Eight bf16 values of one magnitude usually add exactly in
+    binary32 whatever the order, so these cases are what proves the kernel
+    sums in rank order."""
+    rng = np.random.default_rng(100 + n)
+    numel = [n * 4096 + 13] if n <= 64 else [n * 64 + 5]
+    _run_case(rng, n, numel, -1, gdt, G, G, G, shift=0, dist=dist)
+    _run_case(rng, n, numel, n // 2, gdt, Lc, Lc, Lc, shift=1, dist=dist)
 
 
 def test_ragged_multitile_and_no_out():
