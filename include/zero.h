@@ -321,8 +321,12 @@ zero_status zero_step_host(const zero_layout *layout, int32_t rank,
  * (h_grad_stage: 2 * chunk floats; h_out_stage: 2 * chunk bf16): the copy
  * down of chunk c + 1 (stream_down), the host step of chunk c and the copy up
  * of chunk c - 1 (stream_up) overlap.  Every element is bit-identical to
- * zero_step with one fp32 gradient and divisor 1.  Synchronous: returns when
- * the last chunk is on the device.  Errors: EINVAL, EALIGN, EHIP. */
+ * zero_step with one fp32 gradient and divisor 1.  Ordering: the copies read
+ * d_grad in stream_down's order and write d_out in stream_up's order, so the
+ * kernel producing d_grad must run on stream_down (or be complete) and
+ * readers of d_out must follow stream_up (the call returns after both
+ * streams are drained).  Synchronous: returns when the last chunk is on the
+ * device.  Errors: EINVAL, EALIGN, EHIP. */
 zero_status zero_offload_step(const zero_layout *layout, int32_t rank,
                               const float *d_grad, float *h_grad_stage,
                               float *master, float *exp_avg, float *exp_avg_sq,

@@ -18,3 +18,18 @@ def test_c_program_against_header(tmp_path):
                     "-L", LIBDIR, "-lzero", f"-Wl,-rpath,{LIBDIR}", "-lm"], check=True)
     res = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert res.returncode == 0 and res.stdout.strip() == "ok", res.stdout + res.stderr
+
+
+@pytest.mark.gpu
+def test_c_program_on_the_gpu():
+    """tests/c/gpu_step_check.c (built by __graft_entry__.build()): the step
+    and the norm driven from plain C with HIP's C runtime API, checked against
+    the oracle's C library, with no Python in the process."""
+    import torch
+    if torch.cuda.device_count() == 0:
+        pytest.skip("needs a GPU")
+    exe = os.path.join(ROOT, "tests", "c", "gpu_step_check.bin")
+    if not os.path.exists(exe):
+        pytest.fail(f"{exe} is missing: run __graft_entry__.build()")
+    res = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert res.returncode == 0 and res.stdout.strip() == "ok", res.stdout + res.stderr
