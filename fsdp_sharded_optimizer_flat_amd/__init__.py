@@ -105,6 +105,9 @@ _zero_step = _sig("zero_step", i32, vp, i32, vp, i32, i32, i32, f32, vp, vp, vp,
 _zero_step_device_clip = _sig("zero_step_device_clip", i32, vp, i32, vp, i32, i32, i32, f32, vp, vp,
                               vp, i32, vp, i32, C.POINTER(ZeroAdamwScalars), vp, vp)
 _zero_clip_coef_async = _sig("zero_clip_coef_async", i32, vp, f64, vp, vp)
+_zero_clip_coef_ranks = _sig("zero_clip_coef_ranks", i32, vp, i32, f64, C.POINTER(f32),
+                             C.POINTER(f64))
+_zero_clip_coef_ranks_async = _sig("zero_clip_coef_ranks_async", i32, vp, i32, f64, vp, vp, vp)
 _zero_overlap = _sig("zero_overlap", i32, f64, i32, f64, f64, f64, C.POINTER(ZeroOverlapOut))
 _zero_step_host = _sig("zero_step_host", i32, vp, i32, vp, i32, i32, i32, f32, vp, vp, vp, i32, vp,
                        i32, C.POINTER(ZeroAdamwScalars), i32)
@@ -131,7 +134,8 @@ EXPORTED = ["zero_layout_bytes", "zero_pack", "zero_pack_rows", "zero_reshard",
             "zero_reshard_host", "zero_reshard_traffic", "zero_global_index", "zero_owner", "zero_pack_copy",
             "zero_unpack_copy", "zero_adamw_scalars_for", "zero_adamw_scalars_next", "zero_step",
             "zero_step_host", "zero_offload_step", "zero_step_device_clip",
-            "zero_clip_coef_async", "zero_overlap",
+            "zero_clip_coef_async", "zero_clip_coef_ranks", "zero_clip_coef_ranks_async",
+            "zero_overlap",
             "zero_gradnorm_workspace_bytes", "zero_gradnorm", "zero_gradnorm_async",
             "zero_clip_coef", "zero_ledger",
             "zero_gather_buffer_bytes", "zero_step_traffic", "zero_gradnorm_traffic",
@@ -491,6 +495,30 @@ def zero_step_device_clip(layout: Layout, rank: int, grads, grad_index: int, div
                                   _bf16_ptr(out, "out") if out is not None else None, out_index,
                                   C.byref(scalars), _f32_ptr(clip_coef_dev, "clip_coef_dev"),
                                   _stream(stream)), "zero_step_device_clip")
+
+
+def zero_clip_coef_ranks(rank_sums, max_norm: float):
+    """(coef, total): the rank-ordered binary64 total of the ranks' sums of
+    squares and its clip coefficient (host)."""
+    arr = np.ascontiguousarray(rank_sums, dtype=np.float64)
+    c, t = f32(), f64()
+    _check(_zero_clip_coef_ranks(arr.ctypes.data if arr.size else None, arr.size, max_norm,
+                                 C.byref(c), C.byref(t)), "zero_clip_coef_ranks")
+    return c.value, t.value
+
+
+def zero_clip_coef_ranks_async(rank_sums_dev, max_norm: float, coef_dev, total_dev=None,
+                               stream=None):
+    """The same on the device: float64 tensor of the N sums in, float32
+    coefficient (and optionally the float64 total) out."""
+    torch = _torch()
+    if rank_sums_dev.dtype != torch.float64 or (total_dev is not None and total_dev.dtype != torch.float64):
+        raise TypeError("rank sums and total must be float64")
+    _check(_zero_clip_coef_ranks_async(_dev_ptr(rank_sums_dev, "rank_sums_dev"),
+                                       rank_sums_dev.numel(), max_norm,
+                                       _f32_ptr(coef_dev, "coef_dev"),
+                                       _dev_ptr(total_dev, "total_dev") if total_dev is not None else None,
+                                       _stream(stream)), "zero_clip_coef_ranks_async")
 
 
 def zero_clip_coef_async(sumsq_dev, max_norm: float, coef_dev, stream=None):

@@ -338,8 +338,21 @@ extern "C" zero_status zero_clip_coef_async(const double *sumsq_dev, double max_
         return ZERO_EINVAL;
     if (!aligned(sumsq_dev, 8) || !aligned(coef_dev, 4))
         return ZERO_EALIGN;
-    const int err = launch_clip_coef(sumsq_dev, max_norm, coef_dev, stream);
+    const int err = launch_clip_coef(sumsq_dev, 1, max_norm, coef_dev, nullptr, stream);
     return err == hipSuccess ? ZERO_OK : hip_fail(err, "zero_clip_coef_async");
+}
+
+extern "C" zero_status zero_clip_coef_ranks_async(const double *rank_sums_dev, int32_t n_ranks,
+                                                  double max_norm, float *coef_dev,
+                                                  double *total_dev, void *stream)
+{
+    if (!rank_sums_dev || !coef_dev || n_ranks < 1 || n_ranks > ZERO_MAX_UNITS ||
+        !(max_norm > 0.0))
+        return ZERO_EINVAL;
+    if (!aligned(rank_sums_dev, 8) || !aligned(coef_dev, 4) || (total_dev && !aligned(total_dev, 8)))
+        return ZERO_EALIGN;
+    const int err = launch_clip_coef(rank_sums_dev, n_ranks, max_norm, coef_dev, total_dev, stream);
+    return err == hipSuccess ? ZERO_OK : hip_fail(err, "zero_clip_coef_ranks_async");
 }
 
 extern "C" zero_status zero_gradnorm_workspace_bytes(const zero_layout *L, int32_t rank,

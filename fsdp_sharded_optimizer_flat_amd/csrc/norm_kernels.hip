@@ -101,16 +101,24 @@ __global__ __launch_bounds__(kBlock) void norm_level_kernel(const double *__rest
 // sqrt(sumsq), c = max_norm / (norm + 1e-6) in binary64 (correctly rounded
 // sqrt and division), capped at 1, rounded once to binary32 -- the same bits
 // as zero_clip_coef computes on the host.  One thread.
-__global__ void clip_coef_kernel(const double *__restrict__ sumsq, double max_norm,
-                                 float *__restrict__ coef)
+// One thread: the n sums added in order (binary64), then the coefficient of
+// zero_clip_coef with correctly rounded sqrt and division.  n is 1 for one
+// shard's sum, N for the ranks' sums of a sharded norm.
+__global__ void clip_coef_kernel(const double *__restrict__ sums, int n, double max_norm,
+                                 float *__restrict__ coef, double *__restrict__ total)
 {
     if (threadIdx.x != 0 || blockIdx.x != 0)
         return;
-    const double norm = sqrt(*sumsq);
+    double t = sums[0];
+    for (int r = 1; r < n; ++r)
+        t = t + sums[r];
+    const double norm = sqrt(t);
     double c = max_norm / (norm + 1e-6);
     if (c > 1.0)
         c = 1.0;
     *coef = (float)c;
+    if (total)
+        *total = t;
 }
 
 template <int NR, typename GT, typename QD, bool POW2, bool VEC>
@@ -177,10 +185,12 @@ int launch_norm_segment(int64_t len, bool vec, const void *const *grads, int n_g
               : launch_nr<0, float, F32Quad, false, false>(grads, n_grads, g_out, len, c, partials, blocks, st);
 }
 
-int launch_clip_coef(const double *sumsq, double max_norm, float *coef, void *stream)
+int launch_clip_coef(const double *sums, int n, double max_norm, float *coef, double *total,
+                     void *stream)
 {
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    hipLaunchKernelGGL(clip_coef_kernel, dim3(1), dim3(kWave), 0, st, sumsq, max_norm, coef);
+    hipLaunchKernelGGL(clip_coef_kernel, dim3(1), dim3(kWave), 0, st, sums, n, max_norm, coef,
+                       total);
     return hipGetLastError();
 }
 

@@ -88,3 +88,24 @@ extern "C" zero_status zero_clip_coef(double sumsq, double max_norm, float *coef
     *coef = (float)c;
     return ZERO_OK;
 }
+
+// "ZeRO and FSDP sharding", Implementation notes: the global norm combines
+// every shard's sum of squares.  Rank order, binary64, one rounding per add.
+extern "C" zero_status zero_clip_coef_ranks(const double *rank_sums, int32_t n_ranks,
+                                            double max_norm, float *coef, double *total)
+{
+    if (!rank_sums || !coef || n_ranks < 1 || n_ranks > ZERO_MAX_UNITS)
+        return ZERO_EINVAL;
+    double t = rank_sums[0];
+    if (!(t >= 0.0))
+        return ZERO_EINVAL;
+    for (int32_t r = 1; r < n_ranks; ++r) {
+        if (!(rank_sums[r] >= 0.0))
+            return ZERO_EINVAL;
+        t = t + rank_sums[r];
+    }
+    const zero_status st = zero_clip_coef(t, max_norm, coef);
+    if (st == ZERO_OK && total)
+        *total = t;
+    return st;
+}

@@ -142,7 +142,9 @@ bool segment_vec_aligned(const Segment &s, const Request &rq);
 // Reduce n_partials partials to one value at *result (fixed order, several
 // levels of kNormFanIn-way workgroups); scratch holds the intermediate
 // levels (norm_tree_scratch(n_partials) doubles).
-int launch_clip_coef(const double *sumsq, double max_norm, float *coef, void *stream);
+// coef (and *total unless null) from the rank-ordered binary64 sum of n sums.
+int launch_clip_coef(const double *sums, int n, double max_norm, float *coef, double *total,
+                     void *stream);
 int launch_norm_tree(const double *partials, int64_t n_partials, double *scratch, double *result,
                      void *stream);
 int64_t norm_tree_scratch(int64_t n_partials);

@@ -387,6 +387,28 @@ zero_status zero_clip_coef(double sumsq, double max_norm, float *coef);
 zero_status zero_clip_coef_async(const double *sumsq_dev, double max_norm, float *coef_dev,
                                  void *stream);
 
+/* The clip coefficient across ranks -- [p1 Implementation notes]: the global
+ * norm is the square root of the sum of every shard's sum of squares.  Each
+ * of N ranks computes its own shard's sum (zero_gradnorm / _async with its
+ * rank); after they exchange the N binary64 sums (an all-gather of N doubles),
+ * every rank adds them in rank order, sums[0] + sums[1] + ... + sums[N-1],
+ * and forms the coefficient as zero_clip_coef does, so every rank scales by
+ * the same binary32 value.  The total is written to *total when total is not
+ * NULL.  Host: EINVAL for NULL pointers, n_ranks < 1 or > ZERO_MAX_UNITS, a
+ * negative or NaN sum, max_norm <= 0. */
+zero_status zero_clip_coef_ranks(const double *rank_sums, int32_t n_ranks, double max_norm,
+                                 float *coef, double *total);
+
+/* The same on the device (async): reads n_ranks binary64 sums at
+ * rank_sums_dev (8-byte aligned), writes the coefficient to coef_dev and,
+ * if total_dev is not NULL, the total -- bitwise equal to
+ * zero_clip_coef_ranks on the same sums.  A NaN sum gives a NaN
+ * coefficient (the host function refuses it instead).  EINVAL: NULL
+ * pointers, n_ranks out of range, max_norm <= 0; EALIGN; EHIP. */
+zero_status zero_clip_coef_ranks_async(const double *rank_sums_dev, int32_t n_ranks,
+                                       double max_norm, float *coef_dev, double *total_dev,
+                                       void *stream);
+
 /* ------------------------------------------------------------------------
  * Ledger -- [p4 section 3]: model state is (2 + 2 + K) psi bytes with K = 12
  * (bf16 params 2, bf16 grads 2, fp32 master + m + v 12); [p4 section 4]:

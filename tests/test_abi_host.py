@@ -320,3 +320,23 @@ def test_overlap_condition_worked_numbers():
     assert r["hidden"] == 0
     with pytest.raises(z.ZeroError):
         z.zero_overlap(1e9, 8, 0.0, 1.0, 1.0)
+
+
+def test_clip_coef_across_ranks():
+    """The ranks' binary64 sums added in rank order, then the coefficient:
+    equal to the oracle's coefficient of the same rank-ordered total."""
+    rng = np.random.default_rng(17)
+    for n in (1, 2, 8, 64, 1000):
+        sums = np.abs(rng.standard_normal(n)) * 10.0 ** rng.integers(-12, 3, n)
+        total = 0.0
+        for s in sums:               # Python floats: binary64, one rounding per add
+            total = total + float(s)
+        coef, t = z.zero_clip_coef_ranks(sums, 0.5)
+        assert t == total
+        assert coef == oracle.clip_coef(total, 0.5)
+    assert z.zero_clip_coef_ranks([1e-30, 1e-30], 1.0)[0] == 1.0
+    for bad in ([], [1.0, -1.0], [float("nan")]):
+        with pytest.raises(z.ZeroError):
+            z.zero_clip_coef_ranks(bad, 1.0)
+    with pytest.raises(z.ZeroError):
+        z.zero_clip_coef_ranks([1.0], 0.0)
