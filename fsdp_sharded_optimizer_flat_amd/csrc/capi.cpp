@@ -166,18 +166,20 @@ int env_int(const char *name, int dflt, int lo, int hi)
 }
 }  // namespace
 
-size_t occupancy_cap_lds(int waves_per_cu)
+size_t occupancy_cap_lds(int waves_per_cu, size_t static_lds)
 {
     if (waves_per_cu <= 0)
         return 0;
     const DeviceLds d = device_lds();
     if (d.per_cu <= 0 || d.per_block <= 0)
         return 0;
+    // LDS per workgroup in total, in whole allocation granules (rounding
+    // the cap up), of which the kernel's own static LDS is part.
     size_t lds = (size_t)d.per_cu / (size_t)waves_per_cu;
-    lds = lds / 512 * 512;  // whole allocation granules, rounding the cap up
+    lds = lds / 512 * 512;
     if (lds > (size_t)d.per_block)
         lds = (size_t)d.per_block;
-    return lds;
+    return lds > static_lds ? lds - static_lds : 0;
 }
 
 int step_waves_per_cu(int n_grads)
@@ -185,22 +187,26 @@ int step_waves_per_cu(int n_grads)
     // Resident one-wave workgroups per CU.  Every wave streams N + 3 reads
     // and 4 writes; a narrower window of tiles in flight keeps fewer DRAM rows
     // competing per bank.  Measured on MI355X (same box, interleaved repeats):
-    // N = 8: 7 is best (6 starves the memory pipeline; 8 / 10 / uncapped lose
-    // 1 / 2 / 7 points of the 8 TB/s peak); N = 64: 4 is best (5 within 0.1,
-    // 7 1.5 points lower).  Rank counts in between take the nearer setting.
+    // N = 8: 7 is best (6 starves the memory pipeline on some boxes; 8 / 10 /
+    // uncapped lose 1 / 2 / 7 points of the 8 TB/s peak); N = 64: 5 (4 was
+    // equal on one box and 3.4 points lower on another, 6 1.2 lower, 7 1.5
+    // lower).  Rank counts in between take the nearer setting.
     static const int v = env_int("ZERO_STEP_WAVES_PER_CU", -1, 0, 64);
     if (v >= 0)
         return v;
-    return n_grads >= 32 ? 4 : 7;
+    return n_grads >= 32 ? 5 : 7;
 }
 
 int norm_waves_per_cu(int n_grads)
 {
-    // The norm pass streams N reads and one write; at N = 64 a cap of 7
-    // resident waves per CU measured 1.4 points above no cap.
+    // The norm pass streams N reads and one write, 16 bytes per rank per
+    // lane; at N = 64, 5 resident waves per CU measured best (4: 0.5 points
+    // lower, 3: starved).  Fewer ranks keep less in flight per wave and take
+    // the quad step's 7.
     static const int v = env_int("ZERO_NORM_WAVES_PER_CU", -1, 0, 64);
-    (void)n_grads;
-    return v >= 0 ? v : 7;
+    if (v >= 0)
+        return v;
+    return n_grads >= 32 ? 5 : 7;
 }
 
 zero_status hip_fail(int err, const char *where)

@@ -134,12 +134,14 @@ std::vector<Piece> build_pieces(const std::vector<Segment> &segs, const Request 
 
 bool segment_vec_aligned(const Segment &s, const Request &rq)
 {
+    // 16 bytes at the segment start for every gradient (8 bf16 / 4 fp32
+    // elements) and for g_out.
     const int gsize = rq.grad_dtype == ZERO_BF16 ? 2 : 4;
     for (int q = 0; q < rq.n_grads; ++q)
-        if (quad_need(rq.grads[q], gsize, s.g_off) != 0)
+        if (need_mod(rq.grads[q], gsize, s.g_off, 16 / gsize) != 0)
             return false;
     for (int i = 0; i < rq.n_state_ptrs; ++i)
-        if (rq.state_ptrs[i] && quad_need(rq.state_ptrs[i], 4, s.s_off) != 0)
+        if (rq.state_ptrs[i] && need_mod(rq.state_ptrs[i], 4, s.s_off, 4) != 0)
             return false;
     return true;
 }

@@ -6,14 +6,15 @@
 // reduction costing O(1) scalars per rank.
 //
 // Stage 1 fuses the reduction half of the reduce-scatter with the sum of
-// squares: each lane forms g = (rank-ordered sum) / divisor for its quad,
-// optionally writes g (fp32) so the step can read one reduced gradient instead
-// of N, and accumulates g^2 in binary64.  Each wave reduces its lanes in a
-// fixed order to one partial per 256-element tile.  Stage 2 sums the partials
-// in a fixed-order tree of 1024-way workgroups.
-// The partition (segments, grid size, chunk assignment) depends only on the
-// layout, the rank and the index spaces -- never on the device, the pointers'
-// alignment or whether g is written -- so the result is bitwise reproducible.
+// squares: each lane forms g = (rank-ordered sum) / divisor for its eight
+// consecutive elements, optionally writes g (fp32) so the step can read one
+// reduced gradient instead of N, and accumulates g^2 in binary64.  Each wave
+// reduces its lanes in a fixed order to one partial per 512-element tile.
+// Stage 2 sums the partials in a fixed-order tree of 1024-way workgroups.
+// The partition (segments, grid size, element groups) depends only on the
+// layout, the rank and the index spaces -- never on the device, the
+// pointers' alignment or whether g is written -- so the result is bitwise
+// reproducible.
 #include "device_common.h"
 
 namespace zero {
@@ -21,62 +22,73 @@ namespace {
 
 using namespace dev;
 
-// Stage 1 over one segment of `len` elements.  The elements form logical
-// quads (4 consecutive elements; the last quad may be partial) and tiles of
-// 64 quads; workgroup b (one wave64) owns tile b and lane l its quad
-// b * 64 + l.  The lane adds its quad's squares in element order, the wave
-// sums its lanes by a fixed butterfly, and lane 0 writes the tile's partial.
-// Absent elements of a partial quad contribute +0.0, which leaves a binary64
-// sum unchanged.  VEC selects quad-wide loads / stores (every buffer aligned
-// at the segment start); without it the same quads are read element by
-// element.  Either way every value and every addition happen in the same
-// order, so the result depends on neither pointer alignment nor on whether
-// g_out is written.  One tile per workgroup (a non-persistent grid) keeps the
-// tiles in flight in one compact window, as in the step kernel.
-template <int NR, int CAP, typename GT, typename QD, bool POW2, bool VEC>
+// Stage 1 over one segment of `len` elements, cut into tiles of kNormSpan =
+// 512 elements; workgroup b (one wave64) owns tile b and lane l the oct of
+// elements 8l .. 8l+7 of it.  The lane adds its oct's squares in element
+// order, the wave sums its lanes by a fixed butterfly, and lane 0 writes the
+// tile's partial.  Elements past `len` contribute +0.0, which leaves a
+// binary64 sum unchanged.
+//
+// VEC: every gradient is 16-byte aligned at the segment start (and g_out
+// too), so whole tiles load each rank's oct with one 16-byte access -- a 1 KiB
+// span per wave instruction for bf16, the access width that streams N = 64
+// ranks best on MI355X -- and g goes through LDS so that lane l then stores
+// quads l and 64 + l of the tile: two contiguous 1 KiB stores per wave.  The
+// last, partial tile of a segment, and every tile without VEC, reads the
+// same octs element by element.  Either way every value and every addition
+// happen in the same order, so the result depends on neither pointer
+// alignment nor on whether g_out is written.  One tile per workgroup (a
+// non-persistent grid) keeps the tiles in flight in one compact window, as in
+// the step kernel.
+template <int NR, int CAP, typename GT, typename OD, bool POW2, bool VEC>
 __global__ __launch_bounds__(kWave) void norm_kernel(GradSet<CAP> gs, int n,
                                                     float *__restrict__ G, int64_t len,
                                                     StepConsts c,
                                                     double *__restrict__ partials)
 {
-    const int64_t nquads = (len + kQuad - 1) / kQuad;
-    const int64_t i = (int64_t)blockIdx.x * kWave + threadIdx.x;
-    double acc = 0.0;
-    if (i < nquads) {
-        const int64_t e0 = i * kQuad;
-        const int cnt = len - e0 >= kQuad ? kQuad : (int)(len - e0);
-        float g[4];
-        if (VEC && cnt == kQuad) {
-            float s[4];
-            rank_sum<NR, CAP, QD>(gs, n, i, s);
+    static_assert(OD::kN == kOct, "one oct per lane");
+    __shared__ f32x4 xg[2 * kWave];  // the tile's g in element order
+    const int64_t tile = blockIdx.x;
+    const int lane = threadIdx.x;
+    const int64_t e0 = tile * kNormSpan + (int64_t)lane * kOct;  // first element of the oct
+    float g[kOct];
+    if (VEC && (tile + 1) * kNormSpan <= len) {  // uniform over the workgroup
+        float s[kOct];
+        rank_sum<NR, CAP, OD>(gs, n, tile * kWave + lane, s);
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-                g[k] = average<POW2>(s[k], c);
-            if (G)
-                st_stream(f32x4{g[0], g[1], g[2], g[3]}, reinterpret_cast<f32x4 *>(G) + i);
-        } else {
+        for (int k = 0; k < kOct; ++k)
+            g[k] = average<POW2>(s[k], c);
+        if (G) {
+            xg[2 * lane] = f32x4{g[0], g[1], g[2], g[3]};
+            xg[2 * lane + 1] = f32x4{g[4], g[5], g[6], g[7]};
+            __syncthreads();
+            f32x4 *t4 = reinterpret_cast<f32x4 *>(G) + tile * (2 * kWave);
+            st_span(xg[lane], t4, lane);
+            st_span(xg[kWave + lane], t4 + kWave, lane);
+        }
+    } else {
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                g[k] = 0.0f;
-                if (k < cnt) {
-                    float s = grad_at<GT>(gs.p[0], e0 + k);
-                    for (int q = 1; q < n; ++q)
-                        s = s + grad_at<GT>(gs.p[q], e0 + k);
-                    g[k] = average<POW2>(s, c);
-                    if (G)
-                        G[e0 + k] = g[k];
-                }
+        for (int k = 0; k < kOct; ++k) {
+            g[k] = 0.0f;
+            if (e0 + k < len) {
+                float s = grad_at<GT>(gs.p[0], e0 + k);
+                for (int q = 1; q < n; ++q)
+                    s = s + grad_at<GT>(gs.p[q], e0 + k);
+                g[k] = average<POW2>(s, c);
+                if (G)
+                    G[e0 + k] = g[k];
             }
         }
+    }
+    double acc = 0.0;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const double x = (double)g[k];
-            acc = acc + x * x;
-        }
+    for (int k = 0; k < kOct; ++k) {
+        const double x = (double)g[k];
+        acc = acc + x * x;
     }
     const double t = wave_sum(acc);
-    if (threadIdx.x == 0)
-        partials[blockIdx.x] = t;
+    if (lane == 0)
+        partials[tile] = t;
 }
 
 // One level of the fixed-order reduction of the partials: workgroup b sums
@@ -97,13 +109,12 @@ __global__ __launch_bounds__(kBlock) void norm_level_kernel(const double *__rest
         out[blockIdx.x] = t;
 }
 
-// The clip coefficient on the device, with the host formula: norm =
-// sqrt(sumsq), c = max_norm / (norm + 1e-6) in binary64 (correctly rounded
-// sqrt and division), capped at 1, rounded once to binary32 -- the same bits
-// as zero_clip_coef computes on the host.  One thread.
-// One thread: the n sums added in order (binary64), then the coefficient of
-// zero_clip_coef with correctly rounded sqrt and division.  n is 1 for one
-// shard's sum, N for the ranks' sums of a sharded norm.
+// The clip coefficient on the device, with the host formula: the n sums of
+// squares added in order (binary64; n is 1 for one shard's sum, N for the
+// ranks' sums of a sharded norm), norm = sqrt(sum), c = max_norm / (norm +
+// 1e-6) with correctly rounded sqrt and division, capped at 1, rounded once
+// to binary32 -- the same bits as zero_clip_coef computes on the host.  One
+// thread.
 __global__ void clip_coef_kernel(const double *__restrict__ sums, int n, double max_norm,
                                  float *__restrict__ coef, double *__restrict__ total)
 {
@@ -121,7 +132,7 @@ __global__ void clip_coef_kernel(const double *__restrict__ sums, int n, double 
         *total = t;
 }
 
-template <int NR, typename GT, typename QD, bool POW2, bool VEC>
+template <int NR, typename GT, typename OD, bool POW2, bool VEC>
 hipError_t launch_nr(const void *const *grads, int n, float *G, int64_t len, const StepConsts &c,
                      double *partials, int64_t blocks, hipStream_t st)
 {
@@ -129,8 +140,8 @@ hipError_t launch_nr(const void *const *grads, int n, float *G, int64_t len, con
     GradSet<CAP> gs{};
     for (int q = 0; q < n; ++q)
         gs.p[q] = grads[q];
-    const size_t lds = occupancy_cap_lds(norm_waves_per_cu(n));
-    hipLaunchKernelGGL((norm_kernel<NR, CAP, GT, QD, POW2, VEC>), dim3((unsigned)blocks),
+    const size_t lds = occupancy_cap_lds(norm_waves_per_cu(n), 2 * kWave * sizeof(f32x4));
+    hipLaunchKernelGGL((norm_kernel<NR, CAP, GT, OD, POW2, VEC>), dim3((unsigned)blocks),
                        dim3(kWave), lds, st, gs, n, G, len, c, partials);
     return hipGetLastError();
 }
@@ -140,7 +151,7 @@ hipError_t launch_bf16_vec(const void *const *grads, int n, float *G, int64_t le
                            const StepConsts &c, double *partials, int64_t blocks, hipStream_t st)
 {
     using T = uint16_t;
-    using QD = Bf16Quad;
+    using QD = Bf16Oct;
     switch (n) {
     case 1: return launch_nr<1, T, QD, POW2, true>(grads, n, G, len, c, partials, blocks, st);
     case 2: return launch_nr<2, T, QD, POW2, true>(grads, n, G, len, c, partials, blocks, st);
@@ -176,13 +187,13 @@ int launch_norm_segment(int64_t len, bool vec, const void *const *grads, int n_g
         return p2 ? launch_bf16_vec<true>(grads, n_grads, g_out, len, c, partials, blocks, st)
                   : launch_bf16_vec<false>(grads, n_grads, g_out, len, c, partials, blocks, st);
     if (bf)
-        return p2 ? launch_nr<0, uint16_t, Bf16Quad, true, false>(grads, n_grads, g_out, len, c, partials, blocks, st)
-                  : launch_nr<0, uint16_t, Bf16Quad, false, false>(grads, n_grads, g_out, len, c, partials, blocks, st);
+        return p2 ? launch_nr<0, uint16_t, Bf16Oct, true, false>(grads, n_grads, g_out, len, c, partials, blocks, st)
+                  : launch_nr<0, uint16_t, Bf16Oct, false, false>(grads, n_grads, g_out, len, c, partials, blocks, st);
     if (vec)
-        return p2 ? launch_nr<0, float, F32Quad, true, true>(grads, n_grads, g_out, len, c, partials, blocks, st)
-                  : launch_nr<0, float, F32Quad, false, true>(grads, n_grads, g_out, len, c, partials, blocks, st);
-    return p2 ? launch_nr<0, float, F32Quad, true, false>(grads, n_grads, g_out, len, c, partials, blocks, st)
-              : launch_nr<0, float, F32Quad, false, false>(grads, n_grads, g_out, len, c, partials, blocks, st);
+        return p2 ? launch_nr<0, float, F32Oct, true, true>(grads, n_grads, g_out, len, c, partials, blocks, st)
+                  : launch_nr<0, float, F32Oct, false, true>(grads, n_grads, g_out, len, c, partials, blocks, st);
+    return p2 ? launch_nr<0, float, F32Oct, true, false>(grads, n_grads, g_out, len, c, partials, blocks, st)
+              : launch_nr<0, float, F32Oct, false, false>(grads, n_grads, g_out, len, c, partials, blocks, st);
 }
 
 int launch_clip_coef(const double *sums, int n, double max_norm, float *coef, double *total,

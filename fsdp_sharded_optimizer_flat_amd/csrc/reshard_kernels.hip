@@ -15,7 +15,7 @@
 // wave in four passes).
 //
 // Within a run every store is a 16-byte vector store aligned in the
-// destination.  Shard boundaries fall anywhere, so the source is usually at
+// destination, issued as one wave's whole-span store (st_span).  Shard boundaries fall anywhere, so the source is usually at
 // another 16-byte phase; then each lane reads the two aligned 16-byte blocks
 // its bytes straddle and funnel-shifts them together (both blocks hold bytes
 // of the run, so no read leaves the source buffer's 16-byte-aligned extent).
@@ -25,12 +25,13 @@
 
 #include <algorithm>
 
-#include "zero_internal.h"
+#include "device_common.h"
 
 namespace zero {
 namespace {
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+using dev::st_span;
+using dev::u32x4;
 
 constexpr int kCopyPieces = 96;     // runs per launch (kernel arguments: 2.7 KB)
 constexpr int kCopyThreads = kWave; // one wave64 per workgroup
@@ -123,24 +124,25 @@ __global__ __launch_bounds__(kCopyThreads) void copy_batch_kernel(const CopyBatc
             copy_elem(s, d, sp.head + sp.blocks * (16 / e) + (t - 32), e);
     }
     u32x4 *db = reinterpret_cast<u32x4 *>(d + sp.head * e);
+    u32x4 *span = db + lb * kCopyPerBlock;  // this workgroup's 1 KB of the destination
     const int64_t j = lb * kCopyPerBlock + t;
     if (j >= sp.blocks)
         return;
     if (!s) {
-        __builtin_nontemporal_store(u32x4{0u, 0u, 0u, 0u}, db + j);
+        st_span(u32x4{0u, 0u, 0u, 0u}, span, t);
         return;
     }
     const unsigned char *sb = s + sp.head * e;
     const unsigned delta = (unsigned)((uintptr_t)sb % 16u);
     const u32x4 *sa = reinterpret_cast<const u32x4 *>(sb - delta);  // aligned
     if (delta == 0) {
-        __builtin_nontemporal_store(__builtin_nontemporal_load(sa + j), db + j);
+        st_span(__builtin_nontemporal_load(sa + j), span, t);
     } else {
         // block j + 1 holds bytes of block j's span (delta > 0); the
         // neighbouring lane has just fetched it, so the second load is
         // served from cache
         const u32x4 lo = __builtin_nontemporal_load(sa + j), hi = sa[j + 1];
-        __builtin_nontemporal_store(funnel(lo, hi, delta), db + j);
+        st_span(funnel(lo, hi, delta), span, t);
     }
 }
 

@@ -14,10 +14,12 @@
 // fp32 state array -- so each cache line is filled by a single instruction
 // and written back whole.  The grid is not persistent: one tile per
 // workgroup, so the tiles in flight form one compact window that sweeps the
-// buffers in address order.  Loads and stores carry the nontemporal hint.
-// The number of resident waves is capped (7 per CU by default, through a
-// dynamic LDS reservation the kernel never touches): fewer tiles in flight
-// keep fewer DRAM rows competing per bank across the 2N + 7 streams.
+// buffers in address order.  Loads carry the nontemporal hint; stores are
+// whole-span stores with the nontemporal and device-scope bits (st_span).
+// The number of resident waves is capped (7 per CU by default, 5 from 32
+// ranks up, through a dynamic LDS reservation the kernel never touches):
+// fewer tiles in flight keep fewer DRAM rows competing per bank across the
+// N + 7 streams.
 #include "device_common.h"
 
 namespace zero {
@@ -54,12 +56,15 @@ __global__ __launch_bounds__(kWave) void step_quad_kernel(GradSet<CAP> gs, int n
         g = g * clip;
         adamw(g, w[k], m[k], v[k], c);
     }
-    st_stream(f32x4{w[0], w[1], w[2], w[3]}, w4);
-    st_stream(f32x4{m[0], m[1], m[2], m[3]}, m4);
-    st_stream(f32x4{v[0], v[1], v[2], v[3]}, v4);
+    // whole-span stores of the wave's tile (lanes past nquads returned above)
+    const int64_t t0 = (int64_t)blockIdx.x * kWave;
+    const int lane = threadIdx.x;
+    st_span(f32x4{w[0], w[1], w[2], w[3]}, reinterpret_cast<f32x4 *>(W) + t0, lane);
+    st_span(f32x4{m[0], m[1], m[2], m[3]}, reinterpret_cast<f32x4 *>(M) + t0, lane);
+    st_span(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4 *>(V) + t0, lane);
     if (O)
-        st_stream(u32x2{pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3])},
-                  reinterpret_cast<u32x2 *>(O) + i);
+        st_span(u32x2{pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3])},
+                reinterpret_cast<u32x2 *>(O) + t0, lane);
 }
 
 // Any alignment, one element per thread: heads and tails of vector bodies,
@@ -110,7 +115,7 @@ hipError_t launch_quads_nr(const void *const *grads, int n, int gsize_quad, floa
                            hipStream_t st)
 {
     constexpr int CAP = NR > 0 ? NR : ZERO_MAX_RANKS;
-    const size_t lds = occupancy_cap_lds(step_waves_per_cu(n));
+    const size_t lds = occupancy_cap_lds(step_waves_per_cu(n), 0);
     for (int64_t q0 = 0; q0 < nquads; q0 += kMaxQuadsPerLaunch) {
         const int64_t nq = nquads - q0 < kMaxQuadsPerLaunch ? nquads - q0 : kMaxQuadsPerLaunch;
         GradSet<CAP> gs{};

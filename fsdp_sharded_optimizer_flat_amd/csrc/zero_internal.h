@@ -17,7 +17,8 @@ constexpr int kQuad = 4;
 constexpr int kWave = 64;
 constexpr int kTile = kQuad * kWave;       // 256 elements per wave
 constexpr int kBlock = 256;                // threads of the grid-stride / final kernels
-constexpr int kNormSpan = kTile;           // norm: one partial per 256-element tile
+constexpr int kOct = 8;                    // norm: 8 consecutive elements per lane
+constexpr int kNormSpan = kOct * kWave;    // norm: one partial per 512-element tile
 constexpr int kNormFanIn = 1024;           // partials one reduction workgroup combines
 constexpr int64_t kMaxQuadsPerLaunch = int64_t(1) << 30;  // 32-bit dispatch grid size
 
@@ -89,11 +90,12 @@ std::vector<ReshardRun> build_reshard_runs(const zero_layout *from, const zero_l
 // Compute units of the current device (cached per device).  <= 0 on error.
 int device_cu_count();
 
-// Dynamic LDS bytes to reserve per one-wave workgroup so that at most
-// `waves_per_cu` such workgroups are resident on a compute unit of the
-// current device (0 = no cap).  The kernels never touch this LDS: it only
-// bounds how many waves stream at once.  Cached per device.
-size_t occupancy_cap_lds(int waves_per_cu);
+// Dynamic LDS bytes to reserve per one-wave workgroup whose kernel declares
+// `static_lds` bytes of its own, so that at most `waves_per_cu` such
+// workgroups are resident on a compute unit of the current device (0 = no
+// cap).  The kernels never touch this reservation: it only bounds how many
+// waves stream at once.  Cached per device.
+size_t occupancy_cap_lds(int waves_per_cu, size_t static_lds);
 
 // Target resident waves per CU of the step and norm kernels.  Defaults were
 // measured on MI355X; ZERO_STEP_WAVES_PER_CU / ZERO_NORM_WAVES_PER_CU
@@ -136,8 +138,8 @@ int launch_norm_segment(int64_t len, bool vec, const void *const *grads, int n_g
 int64_t norm_segment_blocks(int64_t len);
 
 // True if every gradient (at element g_off) and g_out (at s_off, if given)
-// is aligned for quad accesses, so the norm can use vector accesses on a
-// segment.
+// is 16-byte aligned, so the norm can load whole octs (8 bf16 in one access,
+// 8 fp32 in two) and store g as quads on a segment.
 bool segment_vec_aligned(const Segment &s, const Request &rq);
 // Reduce n_partials partials to one value at *result (fixed order, several
 // levels of kNormFanIn-way workgroups); scratch holds the intermediate

@@ -341,12 +341,13 @@ zero_status zero_offload_step(const zero_layout *layout, int32_t rank,
  *
  * Sum of squares, accumulated in binary64, of g = (rank-ordered binary32 sum
  * of the gradients) / divisor over the processed elements (same selection and
- * index rules as zero_step).  Two kernels: each workgroup of the first reduces
- * a fixed grid-stride partition of 8-element chunks to one binary64 partial; a
- * single workgroup of the second sums the partials in a fixed order.  The
- * partition depends only on the layout, the rank and the index spaces (not on
- * the device, pointer alignment or whether g_out is written), so the result is
- * bitwise reproducible.
+ * index rules as zero_step).  Two stages: one wave of the first reduces each
+ * 512-element tile of a contiguous run to one binary64 partial (each lane
+ * sums the squares of 8 consecutive elements in order, the wave adds its
+ * lanes in a fixed butterfly); the second adds the partials in a fixed-order
+ * tree of 1024-way workgroups.  The partition depends only on the layout, the
+ * rank and the index spaces (not on the device, pointer alignment or whether
+ * g_out is written), so the result is bitwise reproducible.
  *   g_out:      if not NULL, g is also written (fp32, g_index space), so the
  *               step can read one reduced gradient instead of N.
  *   workspace:  caller device memory of at least zero_gradnorm_workspace_bytes.

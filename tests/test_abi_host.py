@@ -255,7 +255,7 @@ def test_gradnorm_argument_errors():
     L = z.zero_pack(4, [1000])
     lib = z.raw_library()
     need = z.zero_gradnorm_workspace_bytes(L, -1)
-    np_ = 1000 // 256 + 1                 # partials: one per 256-element tile, per segment
+    np_ = 1000 // 512 + 1                 # partials: one per 512-element tile, per segment
     tree = 1                              # one 1024-way level reduces them to the result
     assert need == 8 * (np_ + 1 + tree)
     arr = (C.c_void_p * 1)(0x1000)
