@@ -481,6 +481,41 @@ def test_norm_async_equals_sync():
     assert res.item() == 0.0 and not torch.signbit(res).item()
 
 
+@pytest.mark.parametrize("n,gdt", [(8, z.ZERO_BF16), (64, z.ZERO_BF16), (5, z.ZERO_BF16), (8, z.ZERO_F32)])
+def test_norm_partition_independent_of_alignment(n, gdt):
+    """The same gradients in 16-byte-aligned buffers (whole tiles on the
+    vector path) and shifted by 1..7 elements (every tile element by element)
+    give the same sum of squares and the same reduced gradient, bit for bit:
+    the partition into tiles and lanes depends only on the layout."""
+    log(f"norm alignment n={n} gdt={gdt}")
+    rng = np.random.default_rng(15 + n)
+    numel = [n * (512 * 9 + 77), n * 300 + n]      # several tiles, ragged tails, two segments
+    L = z.zero_pack(n, numel)
+    rank = 1
+    tdt = torch.bfloat16 if gdt == z.ZERO_BF16 else torch.float32
+    vals = (rng.standard_t(3, (n, L.shard)) * 1e-3).astype(np.float32)
+    ws = torch.zeros(z.zero_gradnorm_workspace_bytes(L, rank) // 8, dtype=torch.float64, device=DEV)
+    res = {}
+    for shift in (0, 1, 3, 7):
+        grads = [dev_buffer(L.shard, tdt, shift=shift) for _ in range(n)]
+        for q in range(n):
+            grads[q].copy_(torch.from_numpy(vals[q]).to(tdt))
+        g_out = dev_buffer(L.shard, torch.float32, shift=shift)
+        s = z.zero_gradnorm(L, rank, grads, Lc, float(n), g_out, Lc, ws)
+        res[shift] = (s, to_np(g_out).copy())
+    s0, g0 = res[0]
+    for shift in (1, 3, 7):
+        s, g = res[shift]
+        assert s == s0, (shift, s, s0)
+        assert_same_f32(g, g0, f"reduced gradient, shift {shift}")
+    # and the oracle's value
+    gnp = [np.ascontiguousarray(to_np(torch.from_numpy(vals[q]).to(tdt))) for q in range(n)]
+    og = oracle.reduced_grad(n, numel, rank, gnp, grad_local=True, divisor=float(n))
+    assert_same_f32(g0, og, "reduced gradient vs oracle")
+    osum = oracle.sumsq(og)
+    assert abs(s0 - osum) <= 1e-12 * osum
+
+
 def test_norm_closed_form():
     """Every rank's gradient equal to c: the average is c exactly and the sum
     of squares is (elements) * c^2 exactly in binary64."""
