@@ -12,7 +12,9 @@ two-stage norm pass and steps from the reduced gradient it writes.
 
 Prints ONE JSON line: throughput in shard elements per second (value), the
 achieved HBM bandwidth of the dominant kernel against MI355X's 8 TB/s
-(roofline), and the serial CPU oracle on a bounded sample (cpu_baseline).
+(roofline; with this box's plain-copy bandwidth, measured in the same process
+after the timed region, as context), and the serial CPU oracle on a bounded
+sample (cpu_baseline).
 Inputs are resident in HBM before the timed region; gradients are generated
 once and reused by every timed step (their values do not change the work).
 """
@@ -91,6 +93,33 @@ def copy_calibration():
         b.copy_(a)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "dispatches": 3}))
+
+
+def box_copy_ceiling(z, torch, stream, reps: int = 10):
+    """Context for `frac`: this box's own streaming ceiling, a plain 1 GiB
+    device-to-device copy (2 GiB of traffic) through the library's reshard
+    copy kernel -- one rank to one rank under the same flat layout, i.e. a
+    single run, 1 KiB of destination per wave, whole-span stores -- timed
+    with HIP events on the launch stream in this process.  HBM bandwidth
+    differs by a few percent from box to box; the ratio to this copy does
+    not."""
+    import numpy as np
+    n = 1 << 28
+    L1 = z.zero_pack(1, [n])
+    a = torch.zeros(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(2):
+        z.zero_reshard(L1, [a], L1, 0, b, stream)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        z.zero_reshard(L1, [a], L1, 0, b, stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
+    del a, b
+    return 8.0 * n / (ms / 1e3) / 1e9
 
 
 def cpu_baseline(wl, seconds: float):
@@ -334,6 +363,7 @@ def reshard_bench(args):
     call_s = float(np.mean([a.elapsed_time(b) for a, b in events])) / 1e3
     nbytes, elements = z.zero_reshard_traffic(A, B, R.dst_rank, z.ZERO_F32)
     achieved = nbytes / call_s / 1e9
+    box_copy = box_copy_ceiling(z, torch, stream)
     result = {
         "metric": "checkpoint reshard destination elements/sec and achieved HBM GB/s",
         "value": elements * args.steps / wall, "unit": "elements/s", "n_gpus": 1,
@@ -350,7 +380,8 @@ def reshard_bench(args):
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": measured_traffic(R.name),
                      "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": call_s * 1e3,
                      "launches_per_call": "one reshard = several copy_batch_kernel launches "
-                                          "back to back; achieved and traffic are per call"},
+                                          "back to back; achieved and traffic are per call",
+                     "box_copy_GBps": box_copy, "frac_of_box_copy": achieved / box_copy},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -476,6 +507,7 @@ def main():
     value = elements * args.steps / wall
 
     traffic = measured_traffic(args.workload)
+    box_copy = box_copy_ceiling(z, torch, stream)
 
     result = {
         "metric": "optimizer-step shard elements/sec and achieved HBM GB/s (% of MI355X peak)",
@@ -516,6 +548,8 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": dom_bytes,
             "avg_launch_ms": avg_launch_s * 1e3,
+            "box_copy_GBps": box_copy,
+            "frac_of_box_copy": achieved / box_copy,
         },
         "cpu_baseline": None,
     }
