@@ -431,16 +431,25 @@ def main():
     clip = wl.clip_max_norm is not None
 
     # -- inputs, resident before the timed region --------------------------------------
-    master = torch.empty(se, dtype=torch.float32, device=dev)
+    # Every streamed buffer in one allocation, placed by zero_arena_plan
+    # (gradients, master, m, v, out, and the reduced gradient when clipping).
+    specs = [(ge, torch.bfloat16)] * n + [(se, torch.float32)] * 3 + [(oe, torch.int16)]
+    if clip:
+        specs.append((se, torch.float32))
+    sizes = [cnt * torch.empty(0, dtype=dt).element_size() for cnt, dt in specs]
+    offs, total = z.zero_arena_plan(sizes)
+    arena = torch.empty(total, dtype=torch.uint8, device=dev)
+    views = [arena[o:o + b].view(dt) for o, b, (_, dt) in zip(offs, sizes, specs)]
+    grads, (master, m, v, out) = views[:n], views[n:n + 4]
     synth.fill_normal_(master, wl.master_std, synth.seed_of(wl.seed, synth.TAG_MASTER))
-    m, v = torch.zeros_like(master), torch.zeros_like(master)
-    out = torch.zeros(oe, dtype=torch.int16, device=dev)
-    grads = torch.empty(n, ge, dtype=torch.bfloat16, device=dev)
+    m.zero_()
+    v.zero_()
+    out.zero_()
     for r in range(n):
         synth.fill_grad_(grads[r], wl.grad_dist, wl.grad_scale, synth.seed_of(wl.seed, synth.TAG_GRAD, 1, r))
-    gp = z.grad_pointer_array(list(grads))
+    gp = z.grad_pointer_array(grads)
     if clip:
-        g_red = torch.empty(se, dtype=torch.float32, device=dev)
+        g_red = views[n + 4]
         ws = torch.zeros(z.zero_gradnorm_workspace_bytes(L, wl.rank) // 8, dtype=torch.float64, device=dev)
         ss_dev = torch.zeros(1, dtype=torch.float64, device=dev)
         coef_dev = torch.zeros(1, dtype=torch.float32, device=dev)
@@ -460,7 +469,7 @@ def main():
             # host round trip inside the step
             if ev:
                 ev[0].record(stream)
-            z.zero_gradnorm_async(L, wl.rank, list(grads), gidx, float(n), g_red, sidx, ws, ss_dev, stream)
+            z.zero_gradnorm_async(L, wl.rank, grads, gidx, float(n), g_red, sidx, ws, ss_dev, stream)
             if ev:
                 ev[1].record(stream)
             z.zero_clip_coef_async(ss_dev, wl.clip_max_norm, coef_dev, stream)
@@ -554,7 +563,7 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        del grads, master, m, v, out
+        del grads, master, m, v, out, views, arena
         torch.cuda.empty_cache()
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(result))

@@ -122,6 +122,7 @@ _zero_gradnorm_async = _sig("zero_gradnorm_async", i32, vp, i32, vp, i32, i32, i
 _zero_clip_coef = _sig("zero_clip_coef", i32, f64, f64, C.POINTER(f32))
 _zero_ledger = _sig("zero_ledger", i32, f64, i32, i32, i32, C.POINTER(ZeroLedgerOut))
 _zero_gather_buffer_bytes = _sig("zero_gather_buffer_bytes", i32, vp, i32, C.POINTER(f64))
+_zero_arena_plan = _sig("zero_arena_plan", i32, i32, vp, vp, C.POINTER(i64))
 _zero_step_traffic = _sig("zero_step_traffic", i32, vp, i32, i32, i32, i32, C.POINTER(f64),
                           C.POINTER(i64))
 _zero_gradnorm_traffic = _sig("zero_gradnorm_traffic", i32, vp, i32, i32, i32, i32,
@@ -138,7 +139,8 @@ EXPORTED = ["zero_layout_bytes", "zero_pack", "zero_pack_rows", "zero_reshard",
             "zero_overlap",
             "zero_gradnorm_workspace_bytes", "zero_gradnorm", "zero_gradnorm_async",
             "zero_clip_coef", "zero_ledger",
-            "zero_gather_buffer_bytes", "zero_step_traffic", "zero_gradnorm_traffic",
+            "zero_gather_buffer_bytes", "zero_arena_plan", "zero_step_traffic",
+            "zero_gradnorm_traffic",
             "zero_strerror", "zero_last_hip_error", "zero_abi_version"]
 
 
@@ -593,6 +595,17 @@ def zero_gather_buffer_bytes(layout: Layout, units_in_flight: int = 2) -> float:
     _check(_zero_gather_buffer_bytes(layout.ptr, units_in_flight, C.byref(b)),
            "zero_gather_buffer_bytes")
     return b.value
+
+
+def zero_arena_plan(sizes):
+    """Byte offsets of buffers of the given byte sizes inside one allocation,
+    and the allocation's size (see zero.h)."""
+    n = len(sizes)
+    b = (i64 * max(n, 1))(*[int(x) for x in sizes])
+    o = (i64 * max(n, 1))()
+    t = i64()
+    _check(_zero_arena_plan(n, C.addressof(b), C.addressof(o), C.byref(t)), "zero_arena_plan")
+    return [o[i] for i in range(n)], t.value
 
 
 def zero_step_traffic(layout: Layout, rank: int, n_grads: int, grad_dtype: int,

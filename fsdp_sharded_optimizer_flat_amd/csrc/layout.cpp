@@ -341,3 +341,36 @@ extern "C" zero_status zero_owner(const zero_layout *L, int64_t j, int32_t *rank
     *k = x.local_offset + within % x.shard;
     return ZERO_OK;
 }
+
+// Placement of n buffers in one allocation: buffer i starts at the first
+// byte at or after the previous buffer's end whose offset modulo 2 MiB is
+// (i * 256 KiB) mod 2 MiB.  Device memory is mapped in 2 MiB pages, so the
+// phase of a buffer inside its page is the same physically as virtually;
+// staggering the phases keeps buffers that are streamed side by side off the
+// same HBM channels at the same moment.
+extern "C" zero_status zero_arena_plan(int32_t n_buffers, const int64_t *bytes, int64_t *offsets,
+                                       int64_t *total_bytes)
+{
+    constexpr int64_t kPage = int64_t(2) << 20;
+    constexpr int64_t kStagger = int64_t(256) << 10;
+    if (n_buffers < 0 || !total_bytes || (n_buffers > 0 && (!bytes || !offsets)))
+        return ZERO_EINVAL;
+    int64_t end = 0;
+    for (int32_t i = 0; i < n_buffers; ++i)
+        if (bytes[i] < 0)
+            return ZERO_EINVAL;
+    for (int32_t i = 0; i < n_buffers; ++i) {
+        const int64_t phase = ((int64_t)i * kStagger) % kPage;
+        // smallest start >= end with start % kPage == phase
+        const int64_t base = end / kPage * kPage;
+        int64_t start = base + phase;
+        if (start < end)
+            start += kPage;
+        if (start > INT64_MAX - bytes[i])
+            return ZERO_ERANGE;
+        offsets[i] = start;
+        end = start + bytes[i];
+    }
+    *total_bytes = end;
+    return ZERO_OK;
+}

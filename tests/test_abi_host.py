@@ -340,3 +340,32 @@ def test_clip_coef_across_ranks():
             z.zero_clip_coef_ranks(bad, 1.0)
     with pytest.raises(z.ZeroError):
         z.zero_clip_coef_ranks([1.0], 0.0)
+
+
+def test_arena_plan():
+    """zero_arena_plan: buffers in order, non-overlapping, buffer i at phase
+    (i * 256 KiB) mod 2 MiB, no more than one 2 MiB page of slack per buffer;
+    argument errors."""
+    rng = np.random.default_rng(3)
+    page, stag = 2 << 20, 256 << 10
+    cases = [[], [0], [1], [page], [page + 1] * 9, [0, 0, 0]]
+    cases += [list(rng.integers(0, 5 * page, int(rng.integers(1, 70)))) for _ in range(200)]
+    for sizes in cases:
+        offs, total = z.zero_arena_plan(sizes)
+        end = 0
+        for i, (o, s) in enumerate(zip(offs, sizes)):
+            assert o >= end and o % page == (i * stag) % page
+            assert o - end < page           # the first such offset at or after the previous end
+            end = o + int(s)
+        assert total == end
+    lib = z.raw_library()
+    b = (C.c_int64 * 2)(10, -1)
+    o = (C.c_int64 * 2)()
+    t = C.c_int64()
+    assert lib.zero_arena_plan(2, C.addressof(b), C.addressof(o), C.byref(t)) == z.ZERO_EINVAL
+    assert lib.zero_arena_plan(-1, None, None, C.byref(t)) == z.ZERO_EINVAL
+    assert lib.zero_arena_plan(1, None, None, C.byref(t)) == z.ZERO_EINVAL
+    assert lib.zero_arena_plan(0, None, None, None) == z.ZERO_EINVAL
+    assert lib.zero_arena_plan(0, None, None, C.byref(t)) == z.ZERO_OK and t.value == 0
+    big = (C.c_int64 * 2)(2**62, 2**62)
+    assert lib.zero_arena_plan(2, C.addressof(big), C.addressof(o), C.byref(t)) == z.ZERO_ERANGE
