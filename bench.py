@@ -66,6 +66,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-clock budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-box-copy", action="store_true",
+                    help="skip the plain-copy ceiling (for profiler runs: it launches the "
+                         "reshard's copy kernel too)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of known size (PMC calibration)")
     ap.add_argument("--host-step", action="store_true",
@@ -363,7 +366,7 @@ def reshard_bench(args):
     call_s = float(np.mean([a.elapsed_time(b) for a, b in events])) / 1e3
     nbytes, elements = z.zero_reshard_traffic(A, B, R.dst_rank, z.ZERO_F32)
     achieved = nbytes / call_s / 1e9
-    box_copy = box_copy_ceiling(z, torch, stream)
+    box_copy = None if args.no_box_copy else box_copy_ceiling(z, torch, stream)
     result = {
         "metric": "checkpoint reshard destination elements/sec and achieved HBM GB/s",
         "value": elements * args.steps / wall, "unit": "elements/s", "n_gpus": 1,
@@ -381,7 +384,8 @@ def reshard_bench(args):
                      "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": call_s * 1e3,
                      "launches_per_call": "one reshard = several copy_batch_kernel launches "
                                           "back to back; achieved and traffic are per call",
-                     "box_copy_GBps": box_copy, "frac_of_box_copy": achieved / box_copy},
+                     "box_copy_GBps": box_copy,
+                     "frac_of_box_copy": achieved / box_copy if box_copy else None},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -516,7 +520,7 @@ def main():
     value = elements * args.steps / wall
 
     traffic = measured_traffic(args.workload)
-    box_copy = box_copy_ceiling(z, torch, stream)
+    box_copy = None if args.no_box_copy else box_copy_ceiling(z, torch, stream)
 
     result = {
         "metric": "optimizer-step shard elements/sec and achieved HBM GB/s (% of MI355X peak)",
@@ -558,7 +562,7 @@ def main():
             "algorithmic_bytes_per_launch": dom_bytes,
             "avg_launch_ms": avg_launch_s * 1e3,
             "box_copy_GBps": box_copy,
-            "frac_of_box_copy": achieved / box_copy,
+            "frac_of_box_copy": achieved / box_copy if box_copy else None,
         },
         "cpu_baseline": None,
     }
