@@ -1,10 +1,15 @@
 """Full workload sizes, in the launch configuration the benchmark times.
-The whole step runs on the GPU; the oracle recomputes sampled elements one by
-one (random positions plus the first, middle and last element of every unit),
-which is exact because the step is elementwise.  The norm at full size is
-checked through properties that hold at any size (agreement with a binary64
-library sum of the reduced gradient it writes, bitwise reproducibility) and
-its reduced gradient on the sampled elements."""
+The GPT-2-Large-sized model (774M elements, N = 8) and the 8B Llama shard
+(125M elements, N = 64) are compared with the oracle element by element over
+two steps; the clipped step at full size on sampled elements the oracle
+recomputes one by one (random positions plus the first, middle and last
+element of every unit), which is exact because the step is elementwise.  The
+norm at full size is checked through properties that hold at any size
+(agreement with a binary64 library sum of the reduced gradient it writes,
+bitwise reproducibility) and its reduced gradient on the sampled elements."""
+import concurrent.futures as cf
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -19,7 +24,7 @@ import fsdp_sharded_optimizer_flat_amd as z  # noqa: E402
 from fsdp_sharded_optimizer_flat_amd import synth  # noqa: E402
 from fsdp_sharded_optimizer_flat_amd.workloads import WORKLOADS  # noqa: E402
 from gpu_common import (DEV, assert_same_bf16, assert_same_f32, gather_np,  # noqa: E402
-                        oracle_on_samples, sampled_indices, scalars)
+                        hyper_args, oracle_on_samples, sampled_indices, scalars, to_np)
 
 G, Lc = z.ZERO_GLOBAL, z.ZERO_LOCAL
 
@@ -75,12 +80,65 @@ def _run_sampled(name, steps=2, clip=None):
     log(f"{name}: {idx.size} sampled elements bit-exact after {steps} steps")
 
 
-def test_gpt2l_full_size_sampled():
-    _run_sampled("gpt2l")
+def _run_full(name, steps=2):
+    """Every element of the workload after `steps` steps, against the oracle.
+    The oracle runs unit by unit on the unit's slices of the host copies, in
+    a thread pool: a unit's elements map only to its own range in every index
+    space, so this is exactly the oracle's step of the whole layout."""
+    wl = WORKLOADS[name]
+    n, h = wl.n_ranks, wl.hyper
+    L = z.zero_pack(n, wl.unit_numel)
+    all_ranks = wl.rank < 0
+    idx = G if all_ranks else Lc
+    assert (wl.grad_index == "global") == all_ranks and (wl.out_index == "global") == all_ranks
+    E = L.padded if all_ranks else L.shard
+    log(f"{name} full compare: N={n}, {E} elements, {steps} steps")
+    master = torch.empty(E, dtype=torch.float32, device=DEV)
+    synth.fill_normal_(master, wl.master_std, synth.seed_of(wl.seed, synth.TAG_MASTER))
+    m, v = torch.zeros_like(master), torch.zeros_like(master)
+    out = torch.zeros(E, dtype=torch.int16, device=DEV)
+    grads = torch.empty(n, E, dtype=torch.bfloat16, device=DEV)
+    wh, mh, vh = to_np(master).copy(), np.zeros(E, np.float32), np.zeros(E, np.float32)
+    oh = np.zeros(E, np.uint16)
+    units = [(int(nu), int(off if all_ranks else loff), int(pad if all_ranks else sh))
+             for nu, pad, sh, off, loff in L.unit_table()]
+    ha = hyper_args(h)
+
+    def oracle_unit(u, gh, t):
+        numel, a, ln = u
+        gs = [g[a:a + ln] for g in gh]
+        st = dict(master=wh[a:a + ln], m=mh[a:a + ln], v=vh[a:a + ln], t=t, **ha)
+        if all_ranks:
+            oracle.zero_step_all(n, [numel], gs, divisor=float(n), clip=1.0, out=oh[a:a + ln], **st)
+        else:
+            oracle.zero_step_rank(n, [numel], wl.rank, gs, grad_local=True, divisor=float(n),
+                                  clip=1.0, state_global=False, out=oh[a:a + ln],
+                                  out_gather=False, **st)
+
+    workers = min(16, os.cpu_count() or 1)
+    for t in range(1, steps + 1):
+        for r in range(n):
+            synth.fill_grad_(grads[r], wl.grad_dist, wl.grad_scale, synth.seed_of(wl.seed, synth.TAG_GRAD, t, r))
+        z.zero_step(L, wl.rank, list(grads), idx, float(n), master, m, v, idx, out, idx, scalars(t, h))
+        gh = [to_np(grads[r]) for r in range(n)]
+        with cf.ThreadPoolExecutor(workers) as ex:
+            list(ex.map(lambda u: oracle_unit(u, gh, t), units))
+        del gh
+        log(f"{name}: step {t} done on the GPU and in the oracle")
+    torch.cuda.synchronize()
+    assert_same_f32(to_np(master), wh, f"{name} master")
+    assert_same_f32(to_np(m), mh, f"{name} m")
+    assert_same_f32(to_np(v), vh, f"{name} v")
+    assert_same_bf16(to_np(out), oh, f"{name} out")
+    log(f"{name}: all {E} elements bit-exact after {steps} steps")
 
 
-def test_llama8b_z3_shard_full_size_sampled():
-    _run_sampled("llama8b_z3")
+def test_gpt2l_full_size_every_element():
+    _run_full("gpt2l")
+
+
+def test_llama8b_z3_shard_full_size_every_element():
+    _run_full("llama8b_z3")
 
 
 def test_llama8b_z3_clipped_step_full_size_sampled():
