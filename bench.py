@@ -397,6 +397,10 @@ def reshard_bench(args):
 
 def main():
     args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the sharded step for N "
+              "ranks runs here as N simulated ranks' buffers in one GPU's memory", file=sys.stderr)
+        sys.exit(2)
     if args.reshard:
         reshard_bench(args)
         return
@@ -406,10 +410,6 @@ def main():
     if args.host_step:
         host_step_bench(args)
         return
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the sharded step for N "
-              "ranks runs here as N simulated ranks' buffers in one GPU's memory", file=sys.stderr)
-        sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
         return

@@ -1,0 +1,26 @@
+"""bench.py's command line (CPU): more than one GPU is refused in every mode
+before anything touches a device, and the help text lists the modes."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+BENCH = os.path.join(ROOT, "bench.py")
+
+
+@pytest.mark.parametrize("mode", [[], ["--workload", "llama8b_z3_clip"], ["--reshard", "llama8b_reshard"],
+                                  ["--offload"], ["--host-step"]])
+def test_more_than_one_gpu_is_refused(mode):
+    res = subprocess.run([sys.executable, BENCH, "--gpus", "8", *mode], capture_output=True, text=True,
+                         timeout=120)
+    assert res.returncode == 2 and "one GPU only" in res.stderr, res.stderr
+    assert res.stdout == ""
+
+
+def test_help_lists_the_modes():
+    res = subprocess.run([sys.executable, BENCH, "--help"], capture_output=True, text=True, timeout=120)
+    assert res.returncode == 0
+    for flag in ("--workload", "--reshard", "--offload", "--host-step", "--no-box-copy", "--copy-calibration"):
+        assert flag in res.stdout
