@@ -32,6 +32,7 @@ PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 KERNEL_SOURCES = ["fsdp_sharded_optimizer_flat_amd/csrc/step_kernels.hip",
                   "fsdp_sharded_optimizer_flat_amd/csrc/norm_kernels.hip",
+                  "fsdp_sharded_optimizer_flat_amd/csrc/stage_kernels.hip",
                   "fsdp_sharded_optimizer_flat_amd/csrc/reshard_kernels.hip",
                   "fsdp_sharded_optimizer_flat_amd/csrc/device_common.h"]
 
@@ -437,9 +438,15 @@ def main():
     # -- inputs, resident before the timed region --------------------------------------
     # Every streamed buffer in one allocation, placed by zero_arena_plan
     # (gradients, master, m, v, out, and the reduced gradient when clipping).
+    # Unclipped at 32+ ranks: the staged step, through a workspace chunk the
+    # memory-side cache holds (zero_step_staged).
+    ws_elems = 0 if clip else z.zero_step_staged_workspace_bytes(L, wl.rank, n) // 4
+    staged = ws_elems > 0
     specs = [(ge, torch.bfloat16)] * n + [(se, torch.float32)] * 3 + [(oe, torch.int16)]
     if clip:
         specs.append((se, torch.float32))
+    if staged:
+        specs.append((ws_elems, torch.float32))
     sizes = [cnt * torch.empty(0, dtype=dt).element_size() for cnt, dt in specs]
     offs, total = z.zero_arena_plan(sizes)
     arena = torch.empty(total, dtype=torch.uint8, device=dev)
@@ -452,6 +459,8 @@ def main():
     for r in range(n):
         synth.fill_grad_(grads[r], wl.grad_dist, wl.grad_scale, synth.seed_of(wl.seed, synth.TAG_GRAD, 1, r))
     gp = z.grad_pointer_array(grads)
+    if staged:
+        stage_ws = views[n + 4]
     if clip:
         g_red = views[n + 4]
         ws = torch.zeros(z.zero_gradnorm_workspace_bytes(L, wl.rank) // 8, dtype=torch.float64, device=dev)
@@ -482,8 +491,12 @@ def main():
         else:
             if ev:
                 ev[0].record(stream)
-            z.zero_step(L, wl.rank, None, gidx, float(n), master, m, v, sidx, out, oidx, sc, stream,
-                        grad_ptrs=gp)
+            if staged:
+                z.zero_step_staged(L, wl.rank, None, gidx, float(n), master, m, v, sidx, out, oidx, sc,
+                                   stage_ws, stream, grad_ptrs=gp)
+            else:
+                z.zero_step(L, wl.rank, None, gidx, float(n), master, m, v, sidx, out, oidx, sc, stream,
+                            grad_ptrs=gp)
             if ev:
                 ev[1].record(stream)
 
@@ -515,6 +528,9 @@ def main():
         step_bytes, _ = z.zero_step_traffic(L, wl.rank, n, z.ZERO_BF16, True)
         job_bytes = step_bytes
         dom_bytes, dom_name = step_bytes, "step_quad_kernel (fused rank-sum + AdamW + bf16 cast)"
+        if staged:
+            dom_name = ("staged step: stage_reduce_kernel + step_quad_kernel per workspace chunk "
+                        "(all launches of one call; bytes as for the fused step)")
     achieved = dom_bytes / avg_launch_s / 1e9
     ms_per_step = wall / args.steps * 1e3
     value = elements * args.steps / wall
@@ -561,6 +577,7 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": dom_bytes,
             "avg_launch_ms": avg_launch_s * 1e3,
+            "launches_per_call": (2 * -(-elements // (ws_elems or 1))) if staged else 1,
             "box_copy_GBps": box_copy,
             "frac_of_box_copy": achieved / box_copy if box_copy else None,
         },
@@ -568,6 +585,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         del grads, master, m, v, out, views, arena
+        if staged:
+            del stage_ws
         torch.cuda.empty_cache()
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(result))

@@ -102,6 +102,10 @@ _zero_adamw_scalars_next = _sig("zero_adamw_scalars_next", i32, C.POINTER(ZeroAd
                                 C.POINTER(ZeroAdamwScalars))
 _zero_step = _sig("zero_step", i32, vp, i32, vp, i32, i32, i32, f32, vp, vp, vp, i32, vp, i32,
                   C.POINTER(ZeroAdamwScalars), vp)
+_zero_step_staged = _sig("zero_step_staged", i32, vp, i32, vp, i32, i32, i32, f32, vp, vp, vp, i32, vp,
+                         i32, C.POINTER(ZeroAdamwScalars), vp, sz, vp)
+_zero_step_staged_workspace_bytes = _sig("zero_step_staged_workspace_bytes", i32, vp, i32, i32,
+                                         C.POINTER(sz))
 _zero_step_device_clip = _sig("zero_step_device_clip", i32, vp, i32, vp, i32, i32, i32, f32, vp, vp,
                               vp, i32, vp, i32, C.POINTER(ZeroAdamwScalars), vp, vp)
 _zero_clip_coef_async = _sig("zero_clip_coef_async", i32, vp, f64, vp, vp)
@@ -134,6 +138,7 @@ _zero_abi_version = _sig("zero_abi_version", i32)
 EXPORTED = ["zero_layout_bytes", "zero_pack", "zero_pack_rows", "zero_reshard",
             "zero_reshard_host", "zero_reshard_traffic", "zero_global_index", "zero_owner", "zero_pack_copy",
             "zero_unpack_copy", "zero_adamw_scalars_for", "zero_adamw_scalars_next", "zero_step",
+            "zero_step_staged", "zero_step_staged_workspace_bytes",
             "zero_step_host", "zero_offload_step", "zero_step_device_clip",
             "zero_clip_coef_async", "zero_clip_coef_ranks", "zero_clip_coef_ranks_async",
             "zero_overlap",
@@ -416,6 +421,29 @@ def zero_step(layout: Layout, rank: int, grads, grad_index: int, divisor: float,
                       _f32_ptr(exp_avg_sq, "exp_avg_sq"), state_index,
                       _bf16_ptr(out, "out") if out is not None else None, out_index,
                       C.byref(scalars), _stream(stream)), "zero_step")
+
+
+def zero_step_staged(layout: Layout, rank: int, grads, grad_index: int, divisor: float,
+                     master, exp_avg, exp_avg_sq, state_index: int, out, out_index: int,
+                     scalars: ZeroAdamwScalars, workspace, stream=None, *, grad_ptrs=None):
+    """Enqueue the staged step (zero_step's result, two kernels per chunk
+    through ``workspace``, a device tensor; None when fewer than 32
+    gradients)."""
+    arr, gdt = grad_ptrs if grad_ptrs is not None else _grad_ptrs(grads)
+    wp = _dev_ptr(workspace, "workspace") if workspace is not None else None
+    wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_zero_step_staged(layout.ptr, rank, C.addressof(arr), len(arr), gdt, grad_index, divisor,
+                             _f32_ptr(master, "master"), _f32_ptr(exp_avg, "exp_avg"),
+                             _f32_ptr(exp_avg_sq, "exp_avg_sq"), state_index,
+                             _bf16_ptr(out, "out") if out is not None else None, out_index,
+                             C.byref(scalars), wp, wb, _stream(stream)), "zero_step_staged")
+
+
+def zero_step_staged_workspace_bytes(layout: Layout, rank: int, n_grads: int) -> int:
+    b = sz()
+    _check(_zero_step_staged_workspace_bytes(layout.ptr, rank, n_grads, C.byref(b)),
+           "zero_step_staged_workspace_bytes")
+    return b.value
 
 
 def _host_ptr(a, what: str, kind: str):

@@ -25,7 +25,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libzero.so")
 
 SOURCES = ["layout.cpp", "scalars.cpp", "ledger.cpp", "capi.cpp", "offload.cpp", "reshard.cpp",
-           "step_kernels.hip", "norm_kernels.hip", "pack_kernels.hip", "reshard_kernels.hip"]
+           "step_kernels.hip", "norm_kernels.hip", "stage_kernels.hip", "pack_kernels.hip",
+           "reshard_kernels.hip"]
 # Host-only C++ built with g++: the offload step's AVX2 code (no FMA, no
 # fast-math, so every operation rounds once, as on the GPU).
 HOST_SOURCES = ["host_step.cpp"]

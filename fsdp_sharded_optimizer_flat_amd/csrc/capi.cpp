@@ -191,9 +191,14 @@ int step_waves_per_cu(int n_grads)
     // uncapped lose 1 / 2 / 7 points of the 8 TB/s peak); N = 64: 5 (4 was
     // equal on one box and 3.4 points lower on another, 6 1.2 lower, 7 1.5
     // lower).  Rank counts in between take the nearer setting.
+    // One gradient (the staged step's second half, the clipped step on the
+    // norm pass's reduced gradient): 8 streams, best at 8 (6: 3.5 points
+    // lower, 12: equal, uncapped: 1.4 lower).
     static const int v = env_int("ZERO_STEP_WAVES_PER_CU", -1, 0, 64);
     if (v >= 0)
         return v;
+    if (n_grads == 1)
+        return 8;
     return n_grads >= 32 ? 5 : 7;
 }
 
@@ -359,6 +364,112 @@ extern "C" zero_status zero_clip_coef_ranks_async(const double *rank_sums_dev, i
         return ZERO_EALIGN;
     const int err = launch_clip_coef(rank_sums_dev, n_ranks, max_norm, coef_dev, total_dev, stream);
     return err == hipSuccess ? ZERO_OK : hip_fail(err, "zero_clip_coef_ranks_async");
+}
+
+// ---- the staged step ------------------------------------------------------
+
+extern "C" zero_status zero_step_staged_workspace_bytes(const zero_layout *L, int32_t rank,
+                                                        int32_t n_grads, size_t *bytes)
+{
+    if (!layout_ok(L) || !bytes || rank >= L->n_ranks)
+        return ZERO_EINVAL;
+    if (n_grads < 1 || n_grads > ZERO_MAX_RANKS)
+        return ZERO_ERANGE;
+    if (n_grads < kStageMinRanks) {
+        *bytes = 0;
+        return ZERO_OK;
+    }
+    int64_t e = selected_elements(L, rank);
+    e = (e + kNormSpan - 1) / kNormSpan * kNormSpan;
+    if (e < kNormSpan)
+        e = kNormSpan;
+    if (e > kStageMaxChunk)
+        e = kStageMaxChunk;
+    *bytes = (size_t)e * sizeof(float);
+    return ZERO_OK;
+}
+
+extern "C" zero_status zero_step_staged(const zero_layout *L, int32_t rank,
+                                        const void *const *grads, int32_t n_grads,
+                                        int32_t grad_dtype, int32_t grad_index, float divisor,
+                                        float *master, float *exp_avg, float *exp_avg_sq,
+                                        int32_t state_index, uint16_t *out, int32_t out_index,
+                                        const zero_adamw_scalars *sc, void *workspace,
+                                        size_t workspace_bytes, void *stream)
+{
+    zero_status st = validate_step(L, rank, grads, n_grads, grad_dtype, grad_index, divisor,
+                                   master, exp_avg, exp_avg_sq, state_index, out, out_index, sc);
+    if (st != ZERO_OK)
+        return st;
+    if (n_grads < kStageMinRanks)  // few streams: the fused step is the faster one
+        return step_impl(L, rank, grads, n_grads, grad_dtype, grad_index, divisor, master,
+                         exp_avg, exp_avg_sq, state_index, out, out_index, sc, nullptr, stream);
+    if (!workspace)
+        return ZERO_EINVAL;
+    if (!aligned(workspace, 16))
+        return ZERO_EALIGN;
+    if (workspace_bytes < (size_t)kNormSpan * sizeof(float))
+        return ZERO_ENOSPC;
+    const int gsize = dsize(grad_dtype);
+    const Range ws = range_of(workspace, (int64_t)workspace_bytes, 1);
+    const int64_t se = extent(L, state_index), oe = extent(L, out_index);
+    if (overlap(ws, range_of(master, se, 4)) || overlap(ws, range_of(exp_avg, se, 4)) ||
+        overlap(ws, range_of(exp_avg_sq, se, 4)) || (out && overlap(ws, range_of(out, oe, 2))))
+        return ZERO_EINVAL;
+    for (int q = 0; q < n_grads; ++q)
+        if (overlap(ws, range_of(grads[q], extent(L, grad_index), gsize)))
+            return ZERO_EINVAL;
+
+    // chunk: the workspace's whole 512-element tiles, at most kStageMaxChunk
+    int64_t chunk = (int64_t)(workspace_bytes / sizeof(float)) / kNormSpan * kNormSpan;
+    if (chunk > kStageMaxChunk)
+        chunk = kStageMaxChunk;
+    float *g = static_cast<float *>(workspace);
+    const StepConsts ca = make_step_consts(nullptr, divisor);  // the average
+    const StepConsts cb = make_step_consts(sc, 1.0f);          // g is averaged already
+    const void *const g1[1] = {g};
+    Request rq{};  // the second half: one fp32 gradient (the workspace)
+    rq.layout = L;
+    rq.rank = rank;
+    rq.grads = g1;
+    rq.n_grads = 1;
+    rq.grad_dtype = ZERO_F32;
+    rq.grad_index = ZERO_LOCAL;
+    rq.divisor = 1.0f;
+    rq.state_index = state_index;
+    rq.out_index = out_index;
+    rq.state_ptrs[0] = master;
+    rq.state_ptrs[1] = exp_avg;
+    rq.state_ptrs[2] = exp_avg_sq;
+    rq.n_state_ptrs = 3;
+    rq.out_ptr = out;
+    Request ra{};  // alignment of the first half: the gradients and the workspace
+    ra.grads = grads;
+    ra.n_grads = n_grads;
+    ra.grad_dtype = grad_dtype;
+    ra.state_ptrs[0] = g;
+    ra.n_state_ptrs = 1;
+    for (const Segment &sg : build_segments(L, rank, grad_index, state_index, out_index)) {
+        for (int64_t off = 0; off < sg.len; off += chunk) {
+            const int64_t cl = sg.len - off < chunk ? sg.len - off : chunk;
+            const Segment ga{sg.g_off + off, 0, 0, cl};
+            const std::vector<const void *> gp = offset_grads(grads, n_grads, ga.g_off, gsize);
+            int err = launch_stage_reduce(cl, segment_vec_aligned(ga, ra), gp.data(), n_grads,
+                                          grad_dtype, g, ca, stream);
+            if (err != hipSuccess)
+                return hip_fail(err, "zero_step_staged reduce");
+            const Segment sb{0, sg.s_off + off, sg.o_off + off, cl};
+            for (const Piece &pc : build_pieces({sb}, rq)) {
+                const void *const gq[1] = {g + pc.g_off};
+                err = launch_step_piece(pc, gq, 1, ZERO_F32, master + pc.s_off,
+                                        exp_avg + pc.s_off, exp_avg_sq + pc.s_off,
+                                        out ? out + pc.o_off : nullptr, cb, stream);
+                if (err != hipSuccess)
+                    return hip_fail(err, "zero_step_staged step");
+            }
+        }
+    }
+    return ZERO_OK;
 }
 
 extern "C" zero_status zero_gradnorm_workspace_bytes(const zero_layout *L, int32_t rank,

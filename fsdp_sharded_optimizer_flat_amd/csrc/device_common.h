@@ -51,10 +51,14 @@ __device__ __forceinline__ void st_stream(T v, T *p)
 // 1.8 points of the 8 TB/s peak above nt alone (the N = 8 step: 81.7% ->
 // 83.5%).  Only for whole spans: stores that each cover half of every cache
 // line lost 15 points with the same bits.
+//
+// kKeepStorePolicy (sc1 without nt) is for data read back soon from the
+// memory-side cache: the staged step's chunk of reduced gradients.
 constexpr int kRawBufferWord3 = 0x00020000;  // raw (stride 0) buffer, 32-bit format
-constexpr int kSpanStorePolicy = 2 | 16;     // nt | sc1
+constexpr int kSpanStorePolicy = 2 | 16;     // nt | sc1: streamed out, not read again
+constexpr int kKeepStorePolicy = 16;         // sc1: read back by the next kernel
 
-template <typename T>
+template <typename T, int POLICY = kSpanStorePolicy>
 __device__ __forceinline__ void st_span(T v, T *span, int lane)
 {
     static_assert(sizeof(T) == 8 || sizeof(T) == 16, "8- or 16-byte lanes");
@@ -62,10 +66,10 @@ __device__ __forceinline__ void st_span(T v, T *span, int lane)
         __builtin_amdgcn_make_buffer_rsrc(span, 0, 64 * (int)sizeof(T), kRawBufferWord3);
     if constexpr (sizeof(T) == 16)
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, lane * 16, 0,
-                                               kSpanStorePolicy);
+                                               POLICY);
     else
         __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), rs, lane * 8, 0,
-                                              kSpanStorePolicy);
+                                              POLICY);
 }
 
 // binary32 value of the low / high bf16 of a packed pair (exact widening).

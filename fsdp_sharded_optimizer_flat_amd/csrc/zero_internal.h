@@ -21,6 +21,11 @@ constexpr int kOct = 8;                    // norm: 8 consecutive elements per l
 constexpr int kNormSpan = kOct * kWave;    // norm: one partial per 512-element tile
 constexpr int kNormFanIn = 1024;           // partials one reduction workgroup combines
 constexpr int64_t kMaxQuadsPerLaunch = int64_t(1) << 30;  // 32-bit dispatch grid size
+// The staged step: from this many gradients on, reduce chunks of at most
+// kStageMaxChunk elements (128 MB of fp32, half the memory-side cache) into
+// a workspace and step each chunk from it.
+constexpr int32_t kStageMinRanks = 32;
+constexpr int64_t kStageMaxChunk = int64_t(1) << 25;
 
 // One contiguous run of elements whose gradient, state and output indices all
 // advance together.  Offsets are element offsets into the respective buffers.
@@ -136,6 +141,10 @@ int launch_norm_segment(int64_t len, bool vec, const void *const *grads, int n_g
                         int grad_dtype, float *g_out, const StepConsts &c, double *partials,
                         void *stream);
 int64_t norm_segment_blocks(int64_t len);
+// The staged step's first half over len elements: g = (rank-ordered sum) /
+// divisor written to g_out (fp32), 16-byte gradient loads when vec.
+int launch_stage_reduce(int64_t len, bool vec, const void *const *grads, int n_grads,
+                        int grad_dtype, float *g_out, const StepConsts &c, void *stream);
 
 // True if every gradient (at element g_off) and g_out (at s_off, if given)
 // is 16-byte aligned, so the norm can load whole octs (8 bf16 in one access,

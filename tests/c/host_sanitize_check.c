@@ -319,6 +319,28 @@ static void check_device_validation(void)
     CHECK(zero_reshard(L, g, L, 8, w, ZERO_F32, NULL) == ZERO_EINVAL);
     CHECK(zero_offload_step(L, 0, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0, &sc, 1, NULL,
                             NULL) == ZERO_EINVAL);
+    /* the staged step (N = 8 would run fused, so its workspace checks need 32+ gradients) */
+    const int64_t n64[1] = {64 * 1000};
+    zero_layout *L64 = make_layout(64, 1, n64, NULL);
+    const void *g64[64];
+    for (int q = 0; q < 64; ++q)
+        g64[q] = base + 0x10000000 + (size_t)q * 0x10000; /* clear of w, m, v, o and wsp */
+    size_t sb = 0;
+    CHECK(zero_step_staged_workspace_bytes(L64, 0, 64, &sb) == ZERO_OK && sb == 1024 * 4);
+    size_t sb8 = 1;
+    CHECK(zero_step_staged_workspace_bytes(L64, 0, 8, &sb8) == ZERO_OK && sb8 == 0);
+    void *wsp = base + 0x2000000;
+    CHECK(zero_step_staged(L64, 0, g64, 64, ZERO_BF16, Lc, 64.0f, w, m, v, Lc, o, Lc, &sc, NULL,
+                           sb, NULL) == ZERO_EINVAL);
+    CHECK(zero_step_staged(L64, 0, g64, 64, ZERO_BF16, Lc, 64.0f, w, m, v, Lc, o, Lc, &sc,
+                           (char *)wsp + 4, sb, NULL) == ZERO_EALIGN);
+    CHECK(zero_step_staged(L64, 0, g64, 64, ZERO_BF16, Lc, 64.0f, w, m, v, Lc, o, Lc, &sc, wsp, 100,
+                           NULL) == ZERO_ENOSPC);
+    CHECK(zero_step_staged(L64, 0, g64, 64, ZERO_BF16, Lc, 64.0f, w, m, v, Lc, o, Lc, &sc,
+                           (void *)w, sb, NULL) == ZERO_EINVAL);
+    CHECK(zero_step_staged(L64, 0, g64, 0, ZERO_BF16, Lc, 64.0f, w, m, v, Lc, o, Lc, &sc, wsp, sb,
+                           NULL) == ZERO_ERANGE);
+    free(L64);
     free(L);
 }
 

@@ -369,3 +369,34 @@ def test_arena_plan():
     assert lib.zero_arena_plan(0, None, None, C.byref(t)) == z.ZERO_OK and t.value == 0
     big = (C.c_int64 * 2)(2**62, 2**62)
     assert lib.zero_arena_plan(2, C.addressof(big), C.addressof(o), C.byref(t)) == z.ZERO_ERANGE
+
+
+def test_staged_step_workspace_and_errors():
+    """zero_step_staged_workspace_bytes: 0 below 32 gradients, else one
+    chunk's fp32 elements (the selection rounded up to whole 512-element
+    tiles, at most 32M); the staged step's workspace errors, raised before
+    any device work."""
+    _no_gpu()
+    L = z.zero_pack(64, [64 * 1000 + 5, 64 * 3])
+    assert z.zero_step_staged_workspace_bytes(L, 0, 8) == 0
+    assert z.zero_step_staged_workspace_bytes(L, 0, 64) == 4 * ((L.shard + 511) // 512 * 512)
+    assert z.zero_step_staged_workspace_bytes(L, -1, 64) == 4 * ((L.padded + 511) // 512 * 512)
+    big = z.zero_pack(64, [64 * (1 << 26)])
+    assert z.zero_step_staged_workspace_bytes(big, -1, 64) == 4 * (1 << 25)
+    lib = z.raw_library()
+    sc = z.zero_adamw_scalars_for(1, 3e-4, 0.9, 0.95, 1e-8, 0.1)
+    n = 64
+    base = 0x100000000
+    arr = (C.c_void_p * n)(*[base + q * 0x100000 for q in range(n)])
+    w, m, v, o = (base + 0x10000000 + k * 0x1000000 for k in range(4))
+    ws = base + 0x40000000
+
+    def call(wsp, wsb):
+        return lib.zero_step_staged(L.ptr, 0, C.addressof(arr), n, z.ZERO_BF16, z.ZERO_LOCAL, 64.0, w, m, v,
+                                    z.ZERO_LOCAL, o, z.ZERO_LOCAL, C.byref(sc), wsp, wsb, None)
+    assert call(None, 1 << 20) == z.ZERO_EINVAL
+    assert call(ws + 8, 1 << 20) == z.ZERO_EALIGN
+    assert call(ws, 2047) == z.ZERO_ENOSPC
+    assert call(w, 1 << 20) == z.ZERO_EINVAL          # workspace overlapping master
+    assert call(base, 1 << 20) == z.ZERO_EINVAL       # workspace overlapping a gradient
+    assert lib.zero_step_staged_workspace_bytes(L.ptr, 0, 0, C.byref(C.c_size_t())) == z.ZERO_ERANGE

@@ -80,7 +80,7 @@ def _run_sampled(name, steps=2, clip=None):
     log(f"{name}: {idx.size} sampled elements bit-exact after {steps} steps")
 
 
-def _run_full(name, steps=2):
+def _run_full(name, steps=2, staged=False):
     """Every element of the workload after `steps` steps, against the oracle.
     The oracle runs unit by unit on the unit's slices of the host copies, in
     a thread pool: a unit's elements map only to its own range in every index
@@ -116,10 +116,18 @@ def _run_full(name, steps=2):
                                   out_gather=False, **st)
 
     workers = min(16, os.cpu_count() or 1)
+    ws = None
+    if staged:  # the launch configuration bench.py times at this N
+        ws = torch.empty(z.zero_step_staged_workspace_bytes(L, wl.rank, n) // 4, dtype=torch.float32,
+                         device=DEV)
     for t in range(1, steps + 1):
         for r in range(n):
             synth.fill_grad_(grads[r], wl.grad_dist, wl.grad_scale, synth.seed_of(wl.seed, synth.TAG_GRAD, t, r))
-        z.zero_step(L, wl.rank, list(grads), idx, float(n), master, m, v, idx, out, idx, scalars(t, h))
+        if staged:
+            z.zero_step_staged(L, wl.rank, list(grads), idx, float(n), master, m, v, idx, out, idx,
+                               scalars(t, h), ws)
+        else:
+            z.zero_step(L, wl.rank, list(grads), idx, float(n), master, m, v, idx, out, idx, scalars(t, h))
         gh = [to_np(grads[r]) for r in range(n)]
         with cf.ThreadPoolExecutor(workers) as ex:
             list(ex.map(lambda u: oracle_unit(u, gh, t), units))
@@ -130,7 +138,7 @@ def _run_full(name, steps=2):
     assert_same_f32(to_np(m), mh, f"{name} m")
     assert_same_f32(to_np(v), vh, f"{name} v")
     assert_same_bf16(to_np(out), oh, f"{name} out")
-    log(f"{name}: all {E} elements bit-exact after {steps} steps")
+    log(f"{name}: all {E} elements bit-exact after {steps} steps (staged={staged})")
 
 
 def test_gpt2l_full_size_every_element():
@@ -139,6 +147,10 @@ def test_gpt2l_full_size_every_element():
 
 def test_llama8b_z3_shard_full_size_every_element():
     _run_full("llama8b_z3")
+
+
+def test_llama8b_z3_shard_staged_full_size_every_element():
+    _run_full("llama8b_z3", staged=True)
 
 
 def test_llama8b_z3_clipped_step_full_size_sampled():

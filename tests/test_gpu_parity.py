@@ -118,7 +118,9 @@ def _order_sensitive(gnp, gdt):
 
 
 def _run_case(rng, n, numel, rank, gdt, gidx, sidx, oidx, shift, steps=2, with_out=True, n_grads=None,
-              dist="normal", check_order=False):
+              dist="normal", check_order=False, staged=None):
+    """staged: None for zero_step; otherwise zero_step_staged with a
+    workspace of that many fp32 elements (0: the size the library asks for)."""
     h = dict(lr=1e-3, b1=0.9, b2=0.95, eps=1e-8, wd=0.1)
     L = z.zero_pack(n, numel)
     O = oracle.Layout(n, numel)
@@ -134,6 +136,11 @@ def _run_case(rng, n, numel, rank, gdt, gidx, sidx, oidx, shift, steps=2, with_o
     master.copy_(torch.from_numpy(init))
     om, omm, ov = init.copy(), np.zeros(se, np.float32), np.zeros(se, np.float32)
     oout = np.zeros(oe, np.uint16)
+    ws = None
+    if staged is not None:
+        want = z.zero_step_staged_workspace_bytes(L, rank, ng) // 4
+        elems = want if staged == 0 else staged
+        ws = torch.empty(max(elems, 1), dtype=torch.float32, device=DEV) if want else None
     for t in range(1, steps + 1):
         for g in grads:
             vals = rng.standard_normal(ge) * 1e-3
@@ -143,7 +150,11 @@ def _run_case(rng, n, numel, rank, gdt, gidx, sidx, oidx, shift, steps=2, with_o
         gnp = [np.ascontiguousarray(to_np(g)) for g in grads]
         if check_order:   # (with 1 or 2 ranks no order can show: a + b == b + a)
             assert _order_sensitive(gnp, gdt), "test data cannot see the rank order"
-        z.zero_step(L, rank, grads, gidx, float(n), master, m, v, sidx, out, oidx, scalars(t, h))
+        if staged is None:
+            z.zero_step(L, rank, grads, gidx, float(n), master, m, v, sidx, out, oidx, scalars(t, h))
+        else:
+            z.zero_step_staged(L, rank, grads, gidx, float(n), master, m, v, sidx, out, oidx,
+                               scalars(t, h), ws)
         if rank < 0:
             oracle.zero_step_all(n, numel, gnp, divisor=float(n), clip=1.0, master=om, m=omm, v=ov,
                                  out=oout if with_out else None, t=t, **hyper_args(h))
@@ -153,7 +164,7 @@ def _run_case(rng, n, numel, rank, gdt, gidx, sidx, oidx, shift, steps=2, with_o
                                   out=oout if with_out else None, out_gather=(oidx == G), t=t,
                                   **hyper_args(h))
     torch.cuda.synchronize()
-    tag = f"n={n} numel={numel} rank={rank} gdt={gdt} idx={gidx}{sidx}{oidx} shift={shift}"
+    tag = f"n={n} numel={numel} rank={rank} gdt={gdt} idx={gidx}{sidx}{oidx} shift={shift} staged={staged}"
     # compare only the elements the selection owns (others stay as initialised)
     if rank < 0:
         sel_s = np.arange(se)
@@ -212,6 +223,34 @@ def test_rank_order_visible(n, gdt, dist):
     numel = [n * 4096 + 13] if n <= 64 else [n * 64 + 5]
     _run_case(rng, n, numel, -1, gdt, G, G, G, shift=0, dist=dist, check_order=True)
     _run_case(rng, n, numel, n // 2, gdt, Lc, Lc, Lc, shift=1, dist=dist, check_order=True)
+
+
+@pytest.mark.parametrize("n", [32, 64, 100, 256, 8])
+def test_staged_step(n):
+    """zero_step_staged against the oracle, bit for bit: the workspace size
+    sets the chunk, so small workspaces give many chunks with ragged ends
+    inside every contiguous run; every index mode, both gradient types,
+    pointers that are not 16-byte aligned (element path of the reduction,
+    scalar heads of the step).  Below 32 ranks the fused step runs."""
+    log(f"staged n={n}")
+    rng = np.random.default_rng(300 + n)
+    numel = [n * 512 * 3 + 11, 3 * n + 1] if n <= 64 else [n * 64 * 9 + 5]
+    for ws in (0, 512, 512 * 3, 4096):
+        _run_case(rng, n, numel, -1, z.ZERO_BF16, G, G, G, shift=0, staged=ws)
+        _run_case(rng, n, numel, n - 1, z.ZERO_BF16, Lc, Lc, Lc, shift=0, staged=ws)
+        _run_case(rng, n, numel, 0, z.ZERO_F32, G, Lc, G, shift=2, staged=ws)
+        _run_case(rng, n, numel, n // 2, z.ZERO_BF16, Lc, G, Lc, shift=1, staged=ws, with_out=False)
+
+
+def test_staged_step_rank_order_visible():
+    """The staged reduction sums in rank order: data on which another order
+    changes bits (checked before the step), N = 64 and a runtime N."""
+    for n in (64, 77):
+        rng = np.random.default_rng(400 + n)
+        _run_case(rng, n, [n * 4096 + 13], -1, z.ZERO_BF16, G, G, G, shift=0, dist="wide",
+                  check_order=True, staged=2048)
+        _run_case(rng, n, [n * 4096 + 13], n // 3, z.ZERO_F32, Lc, Lc, Lc, shift=0, check_order=True,
+                  staged=0)
 
 
 def test_ragged_multitile_and_no_out():
