@@ -38,10 +38,17 @@ KERNEL_SOURCES = ["fsdp_sharded_optimizer_flat_amd/csrc/step_kernels.hip",
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources' code: comments and blank lines are left
+    out, so the committed counters stay valid across comment edits."""
+    import re
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        code = "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+        h.update(code.encode())
     return h.hexdigest()[:16]
 
 

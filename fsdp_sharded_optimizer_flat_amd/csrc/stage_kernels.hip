@@ -10,10 +10,13 @@
 // it at N = 64).  Split by chunks, the first kernel is a pure N-stream
 // reduction (the norm pass's mix, 0.93 of a copy) and the second a small
 // 4-read / 4-write mix.  A chunk's reduced gradient (up to 32M elements, 128
-// MB of fp32) is written with the device-scope, non-streaming store policy
-// and read back by the next kernel while MI355X's 256 MB memory-side cache
-// still holds it.  Measured at N = 64 (125M-element shard): 78 % of 8 TB/s
-// against 74.5 % fused; the stores with the streaming bit too lost 2 points.
+// MB of fp32, within MI355X's 256 MB memory-side cache) is written with the
+// device-scope, non-streaming store policy and read back by the next kernel.
+// Measured at N = 64 (2^27-element shard): 78.2-78.5 % of 8 TB/s with chunks
+// of 32M or 64M elements, 76.0 % with one 512 MB chunk (larger than the
+// cache), 74.7 % fused: the split mix gains about 1.3 points and the
+// cache-sized chunk, which keeps most of the round trip out of HBM, the rest.
+// The stores with the streaming bit too lost 2 points.
 //
 // The arithmetic is the fused step's, split at a point where the value is
 // stored in binary32 and read back unchanged: g = (rank-ordered binary32

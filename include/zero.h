@@ -317,10 +317,10 @@ zero_status zero_step_device_clip(const zero_layout *layout, int32_t rank,
  * with the same bits, split for large N into two kernels per chunk of
  * elements: the first sums the N gradients in rank order and divides
  * (writing g, fp32, to `workspace`), the second runs the fused step on that
- * one reduced gradient.  On MI355X a chunk of up to 32M elements (128 MB) is
- * read back while the 256 MB memory-side cache still holds it, so the bytes
- * moved stay those of zero_step while each kernel streams a simpler mix: at
- * N = 64 the step runs about 5 % faster than fused.
+ * one reduced gradient.  Each kernel streams a simpler mix than the fused
+ * one, and a chunk of up to 32M elements (128 MB) fits MI355X's 256 MB
+ * memory-side cache, which keeps most of the chunk's round trip out of HBM:
+ * at N = 64 the step runs about 5 % faster than fused.
  *   workspace:  caller device memory, 16-byte aligned, not overlapping any
  *               other buffer of the call; its size sets the chunk (whole
  *               512-element tiles, at most 32M elements; at least 2048 bytes).
