@@ -193,25 +193,28 @@ int step_waves_per_cu(int n_grads)
     // lower).  Rank counts in between take the nearer setting.
     // One gradient (the staged step's second half, the clipped step on the
     // norm pass's reduced gradient): 8 streams, best at 8 (6: 3.5 points
-    // lower, 12: equal, uncapped: 1.4 lower).
+    // lower, 12: equal, uncapped: 1.4 lower).  Rank counts without a
+    // compile-time kernel keep two batches of loads in flight per wave
+    // instead of all ranks' and want more waves: 7 (5: 6-9 points lower).
     static const int v = env_int("ZERO_STEP_WAVES_PER_CU", -1, 0, 64);
     if (v >= 0)
         return v;
     if (n_grads == 1)
         return 8;
-    return n_grads >= 32 ? 5 : 7;
+    return n_grads == 32 || n_grads == 64 ? 5 : 7;
 }
 
 int norm_waves_per_cu(int n_grads)
 {
-    // The norm pass streams N reads and one write, 16 bytes per rank per
-    // lane; at N = 64, 5 resident waves per CU measured best (4: 0.5 points
-    // lower, 3: starved).  Fewer ranks keep less in flight per wave and take
-    // the quad step's 7.
+    // The norm pass (and the staged step's reduction) streams N reads and
+    // one write, 16 bytes per rank per lane; at N = 64, 5 resident waves per
+    // CU measured best (4: 0.5 points lower, 3: starved).  Fewer ranks, and
+    // rank counts without a compile-time kernel (two batches in flight),
+    // keep less in flight per wave and take 7.
     static const int v = env_int("ZERO_NORM_WAVES_PER_CU", -1, 0, 64);
     if (v >= 0)
         return v;
-    return n_grads >= 32 ? 5 : 7;
+    return n_grads == 32 || n_grads == 64 ? 5 : 7;
 }
 
 zero_status hip_fail(int err, const char *where)

@@ -174,20 +174,43 @@ __device__ __forceinline__ void rank_sum(const GradSet<CAP> &gs, int n, int64_t 
             }
         }
     } else {
-        {
+        // Runtime rank count: batches of B ranks (128 bytes of loads per
+        // lane), software-pipelined -- batch k + 1's loads are issued before
+        // batch k is added -- so two batches stay in flight; the adds keep
+        // rank order, rank 0 starting the sum.
+        constexpr int B = 128 / (int)sizeof(QD) < 4 ? 4 : 128 / (int)sizeof(QD);
+        const int nb = n / B;
+        int q = 0;
+        if (nb > 0) {
+            QD cur[B], nxt[B];
+#pragma unroll
+            for (int b = 0; b < B; ++b)
+                cur[b].load(gs.p[b], i);
+            for (int k = 1; k <= nb; ++k) {
+                if (k < nb) {
+#pragma unroll
+                    for (int b = 0; b < B; ++b)
+                        nxt[b].load(gs.p[k * B + b], i);
+                }
+                if (k == 1)
+                    cur[0].template add_to<true>(s);
+                else
+                    cur[0].template add_to<false>(s);
+#pragma unroll
+                for (int b = 1; b < B; ++b)
+                    cur[b].template add_to<false>(s);
+                if (k < nb) {
+#pragma unroll
+                    for (int b = 0; b < B; ++b)
+                        cur[b] = nxt[b];
+                }
+            }
+            q = nb * B;
+        } else {
             QD c0;
             c0.load(gs.p[0], i);
             c0.template add_to<true>(s);
-        }
-        int q = 1;
-        for (; q + 8 <= n; q += 8) {
-            QD c[8];
-#pragma unroll
-            for (int b = 0; b < 8; ++b)
-                c[b].load(gs.p[q + b], i);
-#pragma unroll
-            for (int b = 0; b < 8; ++b)
-                c[b].template add_to<false>(s);
+            q = 1;
         }
         for (; q < n; ++q) {
             QD c;

@@ -23,8 +23,9 @@ constexpr int kNormFanIn = 1024;           // partials one reduction workgroup c
 constexpr int64_t kMaxQuadsPerLaunch = int64_t(1) << 30;  // 32-bit dispatch grid size
 // The staged step: from this many gradients on, reduce chunks of at most
 // kStageMaxChunk elements (128 MB of fp32, half the memory-side cache) into
-// a workspace and step each chunk from it.
-constexpr int32_t kStageMinRanks = 32;
+// a workspace and step each chunk from it.  Measured on MI355X: the fused
+// step is 0.6 points faster at N = 32, the staged one 5 points faster at 64.
+constexpr int32_t kStageMinRanks = 33;
 constexpr int64_t kStageMaxChunk = int64_t(1) << 25;
 
 // One contiguous run of elements whose gradient, state and output indices all

@@ -326,9 +326,9 @@ zero_status zero_step_device_clip(const zero_layout *layout, int32_t rank,
  *               512-element tiles, at most 32M elements; at least 2048 bytes).
  *               zero_step_staged_workspace_bytes gives the size that needs a
  *               single chunk up to that limit.
- * For n_grads < 32 the fused step is the faster one and runs instead; the
- * workspace is then not used and may be NULL (its size query returns 0).
- * Async on `stream`.  Errors as zero_step, plus for n_grads >= 32: EINVAL
+ * For n_grads <= 32 the fused step is as fast or faster and runs instead;
+ * the workspace is then not used and may be NULL (its size query returns 0).
+ * Async on `stream`.  Errors as zero_step, plus for n_grads > 32: EINVAL
  * (NULL workspace, workspace overlapping another buffer), EALIGN (workspace
  * not 16-byte aligned), ENOSPC (workspace_bytes < 2048). */
 zero_status zero_step_staged_workspace_bytes(const zero_layout *layout, int32_t rank,

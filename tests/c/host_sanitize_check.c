@@ -319,7 +319,7 @@ static void check_device_validation(void)
     CHECK(zero_reshard(L, g, L, 8, w, ZERO_F32, NULL) == ZERO_EINVAL);
     CHECK(zero_offload_step(L, 0, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0, &sc, 1, NULL,
                             NULL) == ZERO_EINVAL);
-    /* the staged step (N = 8 would run fused, so its workspace checks need 32+ gradients) */
+    /* the staged step (up to 32 gradients it runs fused, so the workspace checks need more) */
     const int64_t n64[1] = {64 * 1000};
     zero_layout *L64 = make_layout(64, 1, n64, NULL);
     const void *g64[64];

@@ -372,13 +372,15 @@ def test_arena_plan():
 
 
 def test_staged_step_workspace_and_errors():
-    """zero_step_staged_workspace_bytes: 0 below 32 gradients, else one
+    """zero_step_staged_workspace_bytes: 0 up to 32 gradients, else one
     chunk's fp32 elements (the selection rounded up to whole 512-element
     tiles, at most 32M); the staged step's workspace errors, raised before
     any device work."""
     _no_gpu()
     L = z.zero_pack(64, [64 * 1000 + 5, 64 * 3])
     assert z.zero_step_staged_workspace_bytes(L, 0, 8) == 0
+    assert z.zero_step_staged_workspace_bytes(L, 0, 32) == 0
+    assert z.zero_step_staged_workspace_bytes(L, 0, 33) > 0
     assert z.zero_step_staged_workspace_bytes(L, 0, 64) == 4 * ((L.shard + 511) // 512 * 512)
     assert z.zero_step_staged_workspace_bytes(L, -1, 64) == 4 * ((L.padded + 511) // 512 * 512)
     big = z.zero_pack(64, [64 * (1 << 26)])
