@@ -341,16 +341,28 @@ def _reshard_dtype(t) -> int:
     raise TypeError("reshard buffers must be float32 or 16-bit (bf16 bits)")
 
 
-def zero_reshard(src_layout: Layout, src, dst_layout: Layout, dst_rank: int, dst, stream=None):
+def reshard_pointer_array(src):
+    """The sources of zero_reshard marshalled once: ``(array, dtype)`` for
+    ``src_ptrs=`` in loops that reshard the same buffers repeatedly."""
+    dts = {_reshard_dtype(t) for t in src}
+    if len(dts) > 1:
+        raise TypeError("sources must share one element type")
+    arr = (vp * max(len(src), 1))(*[_dev_ptr(t, "src") for t in src])
+    return arr, (dts.pop() if dts else None), len(src)
+
+
+def zero_reshard(src_layout: Layout, src, dst_layout: Layout, dst_rank: int, dst, stream=None, *,
+                 src_ptrs=None):
     """Fill device tensor ``dst`` with rank dst_rank's local shard under
     dst_layout, from the device tensors ``src`` (one local shard per rank of
-    src_layout).  Asynchronous on ``stream``."""
-    if len(src) != src_layout.n_ranks:
+    src_layout).  Asynchronous on ``stream``.  ``src_ptrs`` (from
+    :func:`reshard_pointer_array`) skips re-marshalling ``src``."""
+    arr, sdt, ns = src_ptrs if src_ptrs is not None else reshard_pointer_array(src)
+    if ns != src_layout.n_ranks:
         raise ValueError("one source shard per rank of the source layout")
     dt = _reshard_dtype(dst)
-    if any(_reshard_dtype(t) != dt for t in src):
+    if sdt is not None and sdt != dt:
         raise TypeError("sources and destination must share one element type")
-    arr = (vp * max(len(src), 1))(*[_dev_ptr(t, "src") for t in src])
     _check(_zero_reshard(src_layout.ptr, C.addressof(arr), dst_layout.ptr, dst_rank,
                          _dev_ptr(dst, "dst"), dt, _stream(stream)), "zero_reshard")
 

@@ -289,3 +289,22 @@ def test_full_size_reshard(name):
     torch.cuda.synchronize()
     bad = int((dst != want).sum().item())
     assert bad == 0, f"{bad} elements differ"
+
+
+def test_reshard_with_prepared_source_pointers():
+    """src_ptrs (sources marshalled once) gives the same bytes as passing
+    the tensors, and a mismatched destination type is still refused."""
+    A = z.zero_pack(4, [1000, 37])
+    B = z.zero_pack_rows(3, [1000, 37], [10, 1])
+    g = torch.Generator(device="cpu").manual_seed(7)
+    src = [torch.randn(A.shard, generator=g).to(DEV) for _ in range(4)]
+    sp = z.reshard_pointer_array(src)
+    for r in range(3):
+        d1 = torch.full((B.shard,), -1.0, device=DEV)
+        d2 = torch.full((B.shard,), -2.0, device=DEV)
+        z.zero_reshard(A, src, B, r, d1)
+        z.zero_reshard(A, None, B, r, d2, src_ptrs=sp)
+        torch.cuda.synchronize()
+        assert torch.equal(d1.view(torch.int32), d2.view(torch.int32))
+    with pytest.raises(TypeError):
+        z.zero_reshard(A, None, B, 0, torch.zeros(B.shard, dtype=torch.int16, device=DEV), src_ptrs=sp)
