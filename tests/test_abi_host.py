@@ -122,7 +122,7 @@ def test_scalars_match_oracle_bitwise():
             prev = nxt
 
 
-def test_scalars_survey_hex_pins():
+def test_scalars_hex_pins():
     """bc1, bc2, lr/bc1 and 1 - lr*wd for t = 1..3 as binary32 bit patterns
     (independent of how b^t is formed, since b^t is exact-rounded for t <= 3)."""
     want = {
