@@ -34,7 +34,9 @@ KERNEL_SOURCES = ["fsdp_sharded_optimizer_flat_amd/csrc/step_kernels.hip",
                   "fsdp_sharded_optimizer_flat_amd/csrc/norm_kernels.hip",
                   "fsdp_sharded_optimizer_flat_amd/csrc/stage_kernels.hip",
                   "fsdp_sharded_optimizer_flat_amd/csrc/reshard_kernels.hip",
-                  "fsdp_sharded_optimizer_flat_amd/csrc/device_common.h"]
+                  "fsdp_sharded_optimizer_flat_amd/csrc/device_common.h",
+                  "fsdp_sharded_optimizer_flat_amd/csrc/zero_internal.h",
+                  "fsdp_sharded_optimizer_flat_amd/csrc/capi.cpp"]   # launch shapes and caps
 
 
 def kernel_source_hash() -> str:
