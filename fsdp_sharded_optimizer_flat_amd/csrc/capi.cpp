@@ -191,17 +191,27 @@ int step_waves_per_cu(int n_grads)
     // uncapped lose 1 / 2 / 7 points of the 8 TB/s peak); N = 64: 5 (4 was
     // equal on one box and 3.4 points lower on another, 6 1.2 lower, 7 1.5
     // lower).  Rank counts in between take the nearer setting.
-    // One gradient (the staged step's second half, the clipped step on the
-    // norm pass's reduced gradient): 8 streams, best at 8 (6: 3.5 points
-    // lower, 12: equal, uncapped: 1.4 lower).  Rank counts without a
-    // compile-time kernel keep two batches of loads in flight per wave
-    // instead of all ranks' and want more waves: 7 (5: 6-9 points lower).
+    // One gradient read from HBM (the clipped step on the norm pass's reduced
+    // gradient): 8 streams, best at 10 (8 and 12 within 0.3 points, 6: 3.5
+    // lower, uncapped: 1.4 lower).  Rank counts without a compile-time kernel
+    // keep two batches of loads in flight per wave instead of all ranks' and
+    // want more waves: 7 (5: 6-9 points lower).
     static const int v = env_int("ZERO_STEP_WAVES_PER_CU", -1, 0, 64);
     if (v >= 0)
         return v;
     if (n_grads == 1)
-        return 8;
+        return 10;
     return n_grads == 32 || n_grads == 64 ? 5 : 7;
+}
+
+int staged_step_waves_per_cu()
+{
+    // The staged step's second half reads a gradient chunk that the first
+    // half has just written, mostly from the memory-side cache: shorter load
+    // latency, and more waves keep the HBM streams busy.  At N = 64 on an 8B
+    // model's shard: 12 best (8: 0.8 points lower, 10: 0.2, 14 and 16: 0.2).
+    static const int v = env_int("ZERO_STEP_WAVES_PER_CU", -1, 0, 64);
+    return v >= 0 ? v : 12;
 }
 
 int norm_waves_per_cu(int n_grads)
@@ -466,7 +476,8 @@ extern "C" zero_status zero_step_staged(const zero_layout *L, int32_t rank,
                 const void *const gq[1] = {g + pc.g_off};
                 err = launch_step_piece(pc, gq, 1, ZERO_F32, master + pc.s_off,
                                         exp_avg + pc.s_off, exp_avg_sq + pc.s_off,
-                                        out ? out + pc.o_off : nullptr, cb, stream);
+                                        out ? out + pc.o_off : nullptr, cb, stream,
+                                        staged_step_waves_per_cu());
                 if (err != hipSuccess)
                     return hip_fail(err, "zero_step_staged step");
             }

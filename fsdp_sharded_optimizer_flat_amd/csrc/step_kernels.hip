@@ -112,10 +112,10 @@ int scalar_grid(int64_t len)
 template <int NR, typename QD, bool POW2>
 hipError_t launch_quads_nr(const void *const *grads, int n, int gsize_quad, float *w, float *m,
                            float *v, uint16_t *o, int64_t nquads, const StepConsts &c,
-                           hipStream_t st)
+                           hipStream_t st, int waves = -1)
 {
     constexpr int CAP = NR > 0 ? NR : ZERO_MAX_RANKS;
-    const size_t lds = occupancy_cap_lds(step_waves_per_cu(n), 0);
+    const size_t lds = occupancy_cap_lds(waves >= 0 ? waves : step_waves_per_cu(n), 0);
     for (int64_t q0 = 0; q0 < nquads; q0 += kMaxQuadsPerLaunch) {
         const int64_t nq = nquads - q0 < kMaxQuadsPerLaunch ? nquads - q0 : kMaxQuadsPerLaunch;
         GradSet<CAP> gs{};
@@ -166,7 +166,7 @@ hipError_t launch_scalar(const void *const *grads, int n, float *w, float *m, fl
 
 int launch_step_piece(const Piece &pc, const void *const *grads, int n_grads, int grad_dtype,
                       float *w, float *m, float *v, uint16_t *out, const StepConsts &c,
-                      void *stream)
+                      void *stream, int waves_per_cu)
 {
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     const bool bf = grad_dtype == ZERO_BF16;
@@ -177,8 +177,10 @@ int launch_step_piece(const Piece &pc, const void *const *grads, int n_grads, in
             return p2 ? launch_bf16_quads<true>(grads, n_grads, w, m, v, out, nq, c, st)
                       : launch_bf16_quads<false>(grads, n_grads, w, m, v, out, nq, c, st);
         if (n_grads == 1)  // one reduced gradient, e.g. the clipped step after the norm pass
-            return p2 ? launch_quads_nr<1, F32Quad, true>(grads, n_grads, 16, w, m, v, out, nq, c, st)
-                      : launch_quads_nr<1, F32Quad, false>(grads, n_grads, 16, w, m, v, out, nq, c, st);
+            return p2 ? launch_quads_nr<1, F32Quad, true>(grads, n_grads, 16, w, m, v, out, nq, c,
+                                                          st, waves_per_cu)
+                      : launch_quads_nr<1, F32Quad, false>(grads, n_grads, 16, w, m, v, out, nq, c,
+                                                           st, waves_per_cu);
         return p2 ? launch_quads_nr<0, F32Quad, true>(grads, n_grads, 16, w, m, v, out, nq, c, st)
                   : launch_quads_nr<0, F32Quad, false>(grads, n_grads, 16, w, m, v, out, nq, c, st);
     }

@@ -108,6 +108,8 @@ size_t occupancy_cap_lds(int waves_per_cu, size_t static_lds);
 // override them for launch-shape sweeps (0 disables the cap).
 int step_waves_per_cu(int n_grads);
 int norm_waves_per_cu(int n_grads);
+// The staged step's second half (one fp32 gradient, just written).
+int staged_step_waves_per_cu();
 
 // Record a HIP error code for zero_last_hip_error(); returns ZERO_EHIP.
 zero_status hip_fail(int hip_error, const char *where);
@@ -135,9 +137,11 @@ zero_status validate_step(const zero_layout *L, int32_t rank, const void *const 
 
 // Launchers (defined in the .hip files).  Pointers are already offset to the
 // piece's first element.  Return a hipError_t value.
+// waves_per_cu (one fp32 gradient only): resident waves per CU; < 0 takes
+// step_waves_per_cu(n_grads).
 int launch_step_piece(const Piece &pc, const void *const *grads, int n_grads, int grad_dtype,
                       float *w, float *m, float *v, uint16_t *out, const StepConsts &c,
-                      void *stream);
+                      void *stream, int waves_per_cu = -1);
 int launch_norm_segment(int64_t len, bool vec, const void *const *grads, int n_grads,
                         int grad_dtype, float *g_out, const StepConsts &c, double *partials,
                         void *stream);
