@@ -218,7 +218,8 @@ int norm_waves_per_cu(int n_grads)
 {
     // The norm pass (and the staged step's reduction) streams N reads and
     // one write, 16 bytes per rank per lane; at N = 64, 5 resident waves per
-    // CU measured best (4: 0.5 points lower, 3: starved).  Fewer ranks, and
+    // CU measured best (4: equal to 0.5 points lower, 6: 1.1 lower, 7: 3.8
+    // lower, 3: starved).  Fewer ranks, and
     // rank counts without a compile-time kernel (two batches in flight),
     // keep less in flight per wave and take 7.
     static const int v = env_int("ZERO_NORM_WAVES_PER_CU", -1, 0, 64);
