@@ -135,11 +135,13 @@ def box_copy_ceiling(z, torch, stream, reps: int = 10):
     return 8.0 * n / (ms / 1e3) / 1e9
 
 
-def cpu_baseline(wl, seconds: float):
-    """The oracle as it stands (serial C, one thread) on a bounded sample of
-    the workload: a one-unit layout of 2^22 elements with the workload's rank
-    count, gradient type and distributions, stepped until the budget is
-    spent.  Returns elements per second."""
+def _oracle_sample(wl, seconds: float, threads: int, start_at=None):
+    """Run the oracle as it stands on `threads` independent copies of a
+    bounded sample of the workload at once (one Python thread each; the
+    oracle's C calls release the GIL), until `seconds` have passed.  Returns
+    (oracle steps over all copies, elements per step, seconds)."""
+    import threading
+
     import numpy as np
     import torch
 
@@ -150,33 +152,85 @@ def cpu_baseline(wl, seconds: float):
     P = 1 << 22 if n <= 8 else 1 << 19
     numel = [P * n] if wl.rank >= 0 else [P]
     K = P                                    # elements one oracle step processes
-    grads = []
-    for r in range(n):
-        g = torch.empty(K, dtype=torch.bfloat16)
-        synth.fill_grad_(g, wl.grad_dist, wl.grad_scale, synth.seed_of(wl.seed, synth.TAG_GRAD, 1, r))
-        grads.append(np.ascontiguousarray(g.view(torch.int16).numpy().view(np.uint16)))
-    w = torch.empty(K, dtype=torch.float32)
-    synth.fill_normal_(w, wl.master_std, synth.seed_of(wl.seed, synth.TAG_MASTER))
-    w = w.numpy().copy()
-    m, v = np.zeros(K, np.float32), np.zeros(K, np.float32)
-    out = np.zeros(K, np.uint16)
     h = wl.hyper
-    steps, t0 = 0, time.perf_counter()
-    while True:
+
+    def inputs():
+        grads = []
+        for r in range(n):
+            g = torch.empty(K, dtype=torch.bfloat16)
+            synth.fill_grad_(g, wl.grad_dist, wl.grad_scale,
+                             synth.seed_of(wl.seed, synth.TAG_GRAD, 1, r))
+            grads.append(np.ascontiguousarray(g.view(torch.int16).numpy().view(np.uint16)))
+        w = torch.empty(K, dtype=torch.float32)
+        synth.fill_normal_(w, wl.master_std, synth.seed_of(wl.seed, synth.TAG_MASTER))
+        return (grads, w.numpy().copy(), np.zeros(K, np.float32), np.zeros(K, np.float32),
+                np.zeros(K, np.uint16))
+
+    def one_step(st, t):
+        grads, w, m, v, out = st
         if wl.rank >= 0:
-            oracle.zero_step_rank(n, numel, 0, grads, grad_local=True, divisor=float(n), clip=1.0,
-                                  master=w, m=m, v=v, state_global=False, out=out, out_gather=False,
-                                  t=steps + 1, **h)
+            clip = 1.0
+            if wl.clip_max_norm is not None:     # the norm pass, then the clipped step
+                g = oracle.reduced_grad(n, numel, 0, grads, grad_local=True, divisor=float(n))
+                clip = oracle.clip_coef(oracle.sumsq(g), wl.clip_max_norm)
+            oracle.zero_step_rank(n, numel, 0, grads, grad_local=True, divisor=float(n), clip=clip,
+                                  master=w, m=m, v=v, state_global=False, out=out,
+                                  out_gather=False, t=t, **h)
         else:
             oracle.zero_step_all(n, numel, grads, divisor=float(n), clip=1.0, master=w, m=m, v=v,
-                                 out=out, t=steps + 1, **h)
-        steps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    return {"value": steps * K / el, "unit": "elements/s", "cores": 1, "kind": "oracle",
-            "sample": f"{steps} oracle steps over a {K}-element one-unit sample of the workload "
-                      f"(N={n}, {wl.grad_dist} bf16 gradients), serial C, {el:.1f} s"}
+                                 out=out, t=t, **h)
+
+    states = [inputs() for _ in range(threads)]   # input generation outside the timing
+    oracle.load()
+    counts = [0] * threads
+    go = threading.Barrier(threads + 1)
+    stop = threading.Event()
+
+    def worker(i):
+        go.wait()
+        while not stop.is_set():
+            counts[i] += 1
+            one_step(states[i], counts[i])
+
+    ts = [threading.Thread(target=worker, args=(i,)) for i in range(threads)]
+    for t in ts:
+        t.start()
+    go.wait()
+    t0 = time.perf_counter()
+    time.sleep(seconds)
+    stop.set()
+    for t in ts:
+        t.join()
+    el = time.perf_counter() - t0               # includes the steps running when stopped
+    return sum(counts), K, el
+
+
+def cpu_baseline(wl, seconds: float):
+    """The oracle as it stands (serial C) on a bounded sample of the
+    workload -- a one-unit layout of 2^22 elements (2^19 at more than 8 ranks)
+    with the workload's rank count, gradient type and distributions; for the
+    clipped workload the oracle's reduced gradient, sum of squares and
+    coefficient precede each step -- first on one thread, then on as many
+    threads as the host share allows (up to 16), each on its own copy.
+    Returns elements per second."""
+    steps, K, el = _oracle_sample(wl, seconds, 1)
+    what = ("norm passes, each followed by the clipped step," if wl.clip_max_norm is not None
+            else "steps")
+    res = {"value": steps * K / el, "unit": "elements/s", "cores": 1, "kind": "oracle",
+           "sample": f"{steps} oracle {what} over a {K}-element one-unit sample of the workload "
+                     f"(N={wl.n_ranks}, {wl.grad_dist} bf16 gradients), serial C, {el:.1f} s"}
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    threads = min(16, avail)
+    if threads > 1:
+        steps_t, K, el_t = _oracle_sample(wl, seconds, threads)
+        res["all_cores"] = {
+            "value": steps_t * K / el_t, "unit": "elements/s", "cores": threads,
+            "sample": f"{threads} threads, each running the serial oracle on its own copy of the "
+                      f"same sample: {steps_t} {what} in {el_t:.1f} s"}
+    return res
 
 
 def host_step_bench(args):
@@ -529,10 +583,11 @@ def main():
     launch_ms = [a.elapsed_time(b) for a, b in events]
     avg_launch_s = float(np.mean(launch_ms)) / 1e3
     elements = se if wl.rank < 0 else L.shard
+    fused_bytes, _ = z.zero_step_traffic(L, wl.rank, n, z.ZERO_BF16, True)  # 2N + 26
     if clip:
         step_bytes, _ = z.zero_step_traffic(L, wl.rank, 1, z.ZERO_F32, True)
         norm_bytes, _ = z.zero_gradnorm_traffic(L, wl.rank, n, z.ZERO_BF16, True)
-        job_bytes = step_bytes + norm_bytes
+        job_bytes = step_bytes + norm_bytes   # 2N + 34: the bytes the two passes need
         dom_bytes, dom_name = norm_bytes, "norm_kernel (rank-sum + divide + fp32 g + binary64 sum of squares)"
     else:
         step_bytes, _ = z.zero_step_traffic(L, wl.rank, n, z.ZERO_BF16, True)
@@ -576,6 +631,9 @@ def main():
             "bytes_per_element": job_bytes / elements,
             "hbm_GBps_whole_step": job_bytes / (wall / args.steps) / 1e9,
             "pct_of_peak_whole_step": 100.0 * job_bytes / (wall / args.steps) / 1e9 / PEAK_HBM_GBPS,
+            "fused_convention_bytes_per_step": fused_bytes,
+            "pct_of_peak_whole_step_fused_convention":
+                100.0 * fused_bytes / (wall / args.steps) / 1e9 / PEAK_HBM_GBPS,
         },
         "roofline": {
             "bound": "hbm",
