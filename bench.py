@@ -366,7 +366,11 @@ def reshard_layouts(R, z, workloads):
 def reshard_cpu_baseline(R, seconds: float):
     """The oracle's reshard (serial C) on contiguous spans of the same
     destination shard, from the same source layout, until the budget is
-    spent.  Returns destination elements per second."""
+    spent: on one thread, then on as many threads as the host share allows
+    (up to 16), each with its own destination spans.  Returns destination
+    elements per second."""
+    import threading
+
     import numpy as np
 
     import oracle
@@ -380,19 +384,49 @@ def reshard_cpu_baseline(R, seconds: float):
     shared = np.random.default_rng(R.seed).standard_normal(A.shard).astype(np.float32)
     src = [shared] * R.from_ranks
     span = 1 << 14
-    done, k0, t0 = 0, 0, time.perf_counter()
-    while True:
-        k1 = min(k0 + span, B.shard)
-        oracle.reshard_span(units_a, R.from_ranks, src, R.to_ranks, R.dst_rank, k0, k1,
-                            row_b=row_len, numel_b=numel)
-        done += k1 - k0
-        k0 = (k0 + 7919 * span) % max(B.shard - span, 1)
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    return {"value": done / el, "unit": "elements/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} destination elements in {span}-element spans spread over the "
-                      f"{B.shard}-element shard, serial C, {el:.1f} s"}
+    oracle.load()
+
+    def run(threads):
+        counts = [0] * threads
+        go = threading.Barrier(threads + 1)
+        stop = threading.Event()
+
+        def worker(i):
+            k0 = (i * 104729 * span) % max(B.shard - span, 1)
+            go.wait()
+            while not stop.is_set():
+                k1 = min(k0 + span, B.shard)
+                oracle.reshard_span(units_a, R.from_ranks, src, R.to_ranks, R.dst_rank, k0, k1,
+                                    row_b=row_len, numel_b=numel)
+                counts[i] += k1 - k0
+                k0 = (k0 + 7919 * span) % max(B.shard - span, 1)
+
+        ts = [threading.Thread(target=worker, args=(i,)) for i in range(threads)]
+        for t in ts:
+            t.start()
+        go.wait()
+        t0 = time.perf_counter()
+        time.sleep(seconds)
+        stop.set()
+        for t in ts:
+            t.join()
+        return sum(counts), time.perf_counter() - t0
+
+    done, el = run(1)
+    res = {"value": done / el, "unit": "elements/s", "cores": 1, "kind": "oracle",
+           "sample": f"{done} destination elements in {span}-element spans spread over the "
+                     f"{B.shard}-element shard, serial C, {el:.1f} s"}
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    threads = min(16, avail)
+    if threads > 1:
+        done_t, el_t = run(threads)
+        res["all_cores"] = {"value": done_t / el_t, "unit": "elements/s", "cores": threads,
+                            "sample": f"{threads} threads, each running the serial oracle on its "
+                                      f"own spans: {done_t} elements in {el_t:.1f} s"}
+    return res
 
 
 def reshard_bench(args):
