@@ -180,7 +180,9 @@ def _oracle_sample(wl, seconds: float, threads: int, start_at=None):
             oracle.zero_step_all(n, numel, grads, divisor=float(n), clip=1.0, master=w, m=m, v=v,
                                  out=out, t=t, **h)
 
-    states = [inputs() for _ in range(threads)]   # input generation outside the timing
+    first = inputs()                              # input generation outside the timing
+    states = [first] + [([g.copy() for g in first[0]],) + tuple(a.copy() for a in first[1:])
+                        for _ in range(threads - 1)]
     oracle.load()
     counts = [0] * threads
     go = threading.Barrier(threads + 1)

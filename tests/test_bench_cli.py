@@ -24,3 +24,23 @@ def test_help_lists_the_modes():
     assert res.returncode == 0
     for flag in ("--workload", "--reshard", "--offload", "--host-step", "--no-box-copy", "--copy-calibration"):
         assert flag in res.stdout
+
+
+def test_cpu_baseline_one_thread_and_all_cores():
+    """The oracle leg of bench.py on CPU: one thread, then every available
+    thread on its own copy of the sample; the clipped workload's sample runs
+    the norm pass too."""
+    sys.path.insert(0, ROOT)
+    import bench
+    from fsdp_sharded_optimizer_flat_amd.workloads import WORKLOADS
+
+    for name in ("llama8b_z3_clip", "llama8b_z3"):
+        res = bench.cpu_baseline(WORKLOADS[name], 0.3)
+        assert res["kind"] == "oracle" and res["cores"] == 1 and res["value"] > 0
+        assert ("norm passes" in res["sample"]) == (name == "llama8b_z3_clip")
+        avail = len(os.sched_getaffinity(0))
+        if avail > 1:
+            allc = res["all_cores"]
+            assert allc["cores"] == min(16, avail) and allc["value"] > 0
+        else:
+            assert "all_cores" not in res
