@@ -1,5 +1,6 @@
-"""bench.py's command line (CPU): more than one GPU is refused in every mode
-before anything touches a device, and the help text lists the modes."""
+"""bench.py on the CPU: more than one GPU is refused in every mode before
+anything touches a device, the help text lists the modes, and the oracle
+baseline leg runs on one thread and on all of them."""
 import os
 import subprocess
 import sys
