@@ -455,16 +455,18 @@ def reshard_bench(args):
     for _ in range(args.warmup):
         z.zero_reshard(A, src, B, R.dst_rank, dst, stream, src_ptrs=sp)
     torch.cuda.synchronize()
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
+    # two events bracket the timed region on the launch stream; the average
+    # call is the span / K (an event pair around every call would add its
+    # own markers to each call's time)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for a, b in events:
-        a.record(stream)
+    e0.record(stream)
+    for _ in range(args.steps):
         z.zero_reshard(A, src, B, R.dst_rank, dst, stream, src_ptrs=sp)
-        b.record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    call_s = float(np.mean([a.elapsed_time(b) for a, b in events])) / 1e3
+    call_s = e0.elapsed_time(e1) / 1e3 / args.steps
     nbytes, elements = z.zero_reshard_traffic(A, B, R.dst_rank, z.ZERO_F32)
     achieved = nbytes / call_s / 1e9
     box_copy = None if args.no_box_copy else box_copy_ceiling(z, torch, stream)
@@ -483,6 +485,8 @@ def reshard_bench(args):
                      "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": measured_traffic(R.name),
                      "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": call_s * 1e3,
+                     "timing": "HIP events on the launch stream at the two ends of the timed "
+                               "region; average = span / steps",
                      "launches_per_call": "one reshard = several copy_batch_kernel launches "
                                           "back to back; achieved and traffic are per call",
                      "box_copy_GBps": box_copy,
@@ -606,18 +610,32 @@ def main():
         one_step(t)
     torch.cuda.synchronize()
 
+    # The clipped workload's dominant kernel (the norm pass) is one part of
+    # each step: HIP events around every norm pass.  Otherwise the step is
+    # the whole of each iteration: two events bracket the timed region on the
+    # launch stream (an event pair around every call would add its own
+    # markers to each call's time), and the average call is the span / K.
     events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
+              for _ in range(args.steps if clip else 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    if not clip:
+        events[0][0].record(stream)
     for k in range(args.steps):
         t += 1
-        one_step(t, events[k])
+        one_step(t, events[k] if clip else None)
+    if not clip:
+        events[0][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    launch_ms = [a.elapsed_time(b) for a, b in events]
-    avg_launch_s = float(np.mean(launch_ms)) / 1e3
+    if clip:
+        avg_launch_s = float(np.mean([a.elapsed_time(b) for a, b in events])) / 1e3
+        timing = "HIP events on the launch stream around every timed norm pass"
+    else:
+        avg_launch_s = events[0][0].elapsed_time(events[0][1]) / 1e3 / args.steps
+        timing = ("HIP events on the launch stream at the two ends of the timed region; "
+                  "average = span / steps")
     elements = se if wl.rank < 0 else L.shard
     fused_bytes, _ = z.zero_step_traffic(L, wl.rank, n, z.ZERO_BF16, True)  # 2N + 26
     if clip:
@@ -681,6 +699,7 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": dom_bytes,
             "avg_launch_ms": avg_launch_s * 1e3,
+            "timing": timing,
             "launches_per_call": (2 * -(-elements // (ws_elems or 1))) if staged else 1,
             "box_copy_GBps": box_copy,
             "frac_of_box_copy": achieved / box_copy if box_copy else None,
