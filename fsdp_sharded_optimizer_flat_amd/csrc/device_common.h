@@ -28,17 +28,12 @@ struct GradSet {
     const void *p[CAP];
 };
 
-// Streaming loads / stores: every byte is touched once per step, so they
-// bypass the caches' reuse policy.
+// Streaming loads: every byte is read once per step, so they bypass the
+// caches' reuse policy (stores go through st_span below).
 template <typename T>
 __device__ __forceinline__ T ld_stream(const T *p)
 {
     return __builtin_nontemporal_load(p);
-}
-template <typename T>
-__device__ __forceinline__ void st_stream(T v, T *p)
-{
-    __builtin_nontemporal_store(v, p);
 }
 
 // Store of one wave's contiguous span: lane l writes v at span[l], where
