@@ -2,9 +2,10 @@
 // the rank-ordered gradient sum over a chunk, the average, the AdamW element
 // update and the bf16 packing.  gfx950 only.
 //
-// Bit-exactness rests on three things the build guarantees: no FMA
-// contraction (-ffp-contract=off), IEEE binary32 denormals, and correctly
-// rounded '/' and sqrtf (HIP's defaults for gfx950).
+// Bit-exactness rests on three things the build passes explicitly: no FMA
+// contraction (-ffp-contract=off), IEEE binary32 denormals
+// (-fno-gpu-flush-denormals-to-zero), and correctly rounded '/' and sqrtf
+// (-fhip-fp32-correctly-rounded-divide-sqrt).
 #pragma once
 
 #include <hip/hip_runtime.h>
