@@ -16,7 +16,7 @@
 // workgroup, so the tiles in flight form one compact window that sweeps the
 // buffers in address order.  Workgroups go to the eight XCDs in turn, so
 // neighbouring tiles run on different XCDs; giving each XCD its own range of
-// tiles instead measured 9 to 12 points lower (more DRAM rows open at once).  Loads carry the nontemporal hint; stores are
+// tiles instead measured 8 to 12 points lower (more DRAM rows open at once).  Loads carry the nontemporal hint; stores are
 // whole-span stores with the nontemporal and device-scope bits (st_span).
 // The number of resident waves is capped (7 per CU by default, 5 from 32
 // ranks up, through a dynamic LDS reservation the kernel never touches):
