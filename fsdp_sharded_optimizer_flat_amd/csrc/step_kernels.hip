@@ -6,22 +6,23 @@
 // master / m / v, and the bf16 cast into the all-gather's output slot
 // ("ZeRO and FSDP sharding", How it works and Code).
 //
-// The work is elementwise and streams every byte once, so the kernel is bound
-// by HBM bandwidth: no MFMA, and no LDS traffic.  Mapping: each workgroup is one wave64
-// and owns one tile of 256 consecutive elements; lane l owns the quad
-// 4l .. 4l+3 of the tile.  Every wave-wide access is therefore one contiguous
-// span -- 512 bytes per rank's bf16 gradients and per bf16 output, 1 KiB per
-// fp32 state array -- so each cache line is filled by a single instruction
-// and written back whole.  The grid is not persistent: one tile per
-// workgroup, so the tiles in flight form one compact window that sweeps the
-// buffers in address order.  Workgroups go to the eight XCDs in turn, so
-// neighbouring tiles run on different XCDs; giving each XCD its own range of
-// tiles instead measured 8 to 12 points lower (more DRAM rows open at once).  Loads carry the nontemporal hint; stores are
+// The work is elementwise and streams every byte once, so the kernel is
+// bound by HBM bandwidth: no MFMA, and no LDS traffic.  Mapping: each
+// workgroup is one wave64 and owns one tile of 256 consecutive elements;
+// lane l owns the quad 4l .. 4l+3 of the tile.  Every wave-wide access is
+// therefore one contiguous span -- 512 bytes per rank's bf16 gradients and
+// per bf16 output, 1 KiB per fp32 state array -- so each cache line is
+// filled by a single instruction and written back whole.  The grid is not
+// persistent: one tile per workgroup, so the tiles in flight form one compact
+// window that sweeps the buffers in address order.  Workgroups go to the
+// eight XCDs in turn, so neighbouring tiles run on different XCDs; giving
+// each XCD its own range of tiles instead measured 8 to 12 points lower (more
+// DRAM rows open at once).  Loads carry the nontemporal hint; stores are
 // whole-span stores with the nontemporal and device-scope bits (st_span).
 // The number of resident waves is capped (7 per CU by default, 5 from 32
-// ranks up, through a dynamic LDS reservation the kernel never touches):
-// fewer tiles in flight keep fewer DRAM rows competing per bank across the
-// N + 7 streams.
+// ranks up, 10 or 12 for one fp32 gradient, through a dynamic LDS
+// reservation the kernel never touches): fewer tiles in flight keep fewer
+// DRAM rows competing per bank across the N + 7 streams.
 #include "device_common.h"
 
 namespace zero {
