@@ -16,8 +16,9 @@
 // persistent: one tile per workgroup, so the tiles in flight form one compact
 // window that sweeps the buffers in address order.  Workgroups go to the
 // eight XCDs in turn, so neighbouring tiles run on different XCDs; giving
-// each XCD its own range of tiles instead measured 8 to 12 points lower (more
-// DRAM rows open at once).  Loads carry the nontemporal hint; stores are
+// each XCD its own range of tiles instead (the tiles in flight then sit in
+// eight separate windows) measured 8 to 12 points lower.  Loads carry the
+// nontemporal hint; stores are
 // whole-span stores with the nontemporal and device-scope bits (st_span).
 // The number of resident waves is capped (7 per CU by default, 5 from 32
 // ranks up, 10 or 12 for one fp32 gradient, through a dynamic LDS
