@@ -500,33 +500,20 @@ def reshard_bench(args):
     print(json.dumps(result))
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the sharded step for N "
-              "ranks runs here as N simulated ranks' buffers in one GPU's memory", file=sys.stderr)
-        sys.exit(2)
-    if args.reshard:
-        reshard_bench(args)
-        return
-    if args.offload:
-        offload_bench(args)
-        return
-    if args.host_step:
-        host_step_bench(args)
-        return
-    if args.copy_calibration:
-        copy_calibration()
-        return
+def setup_step(wl):
+    """The benchmark's resident inputs and its step, as bench.py times them:
+    every streamed buffer in one allocation placed by zero_arena_plan, the
+    workload's seeded gradients (the same every step) and master weights,
+    zeroed m / v / out, gradient pointers marshalled once, and `one_step(t,
+    ev)` -- the staged step above 32 ranks, the device-side clip chain for the
+    clipped workload, else the fused step.  Returns a namespace of them."""
+    import types
 
-    import numpy as np
     import torch
 
     import fsdp_sharded_optimizer_flat_amd as z
     from fsdp_sharded_optimizer_flat_amd import synth
-    from fsdp_sharded_optimizer_flat_amd.workloads import WORKLOADS
 
-    wl = WORKLOADS[args.workload]
     n, h = wl.n_ranks, wl.hyper
     dev = torch.device("cuda:0")
     L = z.zero_pack(n, wl.unit_numel)
@@ -603,6 +590,47 @@ def main():
                             grad_ptrs=gp)
             if ev:
                 ev[1].record(stream)
+
+    ns = types.SimpleNamespace(
+        wl=wl, n=n, h=h, L=L, gidx=gidx, sidx=sidx, oidx=oidx, se=se, clip=clip, staged=staged,
+        ws_elems=ws_elems, arena=arena, grads=grads, master=master, m=m, v=v, out=out,
+        stream=stream, one_step=one_step)
+    if clip:
+        ns.g_red, ns.ss_dev, ns.coef_dev = g_red, ss_dev, coef_dev
+    if staged:
+        ns.stage_ws = stage_ws
+    return ns
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the sharded step for N "
+              "ranks runs here as N simulated ranks' buffers in one GPU's memory", file=sys.stderr)
+        sys.exit(2)
+    if args.reshard:
+        reshard_bench(args)
+        return
+    if args.offload:
+        offload_bench(args)
+        return
+    if args.host_step:
+        host_step_bench(args)
+        return
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import numpy as np
+    import torch
+
+    import fsdp_sharded_optimizer_flat_amd as z
+    from fsdp_sharded_optimizer_flat_amd.workloads import WORKLOADS
+
+    wl = WORKLOADS[args.workload]
+    S = setup_step(wl)
+    n, h, L, gidx, sidx, oidx, se = S.n, S.h, S.L, S.gidx, S.sidx, S.oidx, S.se
+    clip, staged, ws_elems, stream, one_step = S.clip, S.staged, S.ws_elems, S.stream, S.one_step
 
     t = 0
     for _ in range(args.warmup):
@@ -707,9 +735,7 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        del grads, master, m, v, out, views, arena
-        if staged:
-            del stage_ws
+        del S, one_step   # the step's device buffers
         torch.cuda.empty_cache()
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(result))
