@@ -424,8 +424,14 @@ extern "C" zero_status zero_step_staged(const zero_layout *L, int32_t rank,
         return ZERO_EALIGN;
     if (workspace_bytes < (size_t)kNormSpan * sizeof(float))
         return ZERO_ENOSPC;
+    // chunk: the workspace's whole 512-element tiles, at most kStageMaxChunk;
+    // the call writes no workspace byte past the first chunk
+    size_t ws_elems = workspace_bytes / sizeof(float);
+    if (ws_elems > (size_t)kStageMaxChunk)
+        ws_elems = (size_t)kStageMaxChunk;
+    const int64_t chunk = (int64_t)ws_elems / kNormSpan * kNormSpan;
     const int gsize = dsize(grad_dtype);
-    const Range ws = range_of(workspace, (int64_t)workspace_bytes, 1);
+    const Range ws = range_of(workspace, chunk * (int64_t)sizeof(float), 1);
     const int64_t se = extent(L, state_index), oe = extent(L, out_index);
     if (overlap(ws, range_of(master, se, 4)) || overlap(ws, range_of(exp_avg, se, 4)) ||
         overlap(ws, range_of(exp_avg_sq, se, 4)) || (out && overlap(ws, range_of(out, oe, 2))))
@@ -434,10 +440,6 @@ extern "C" zero_status zero_step_staged(const zero_layout *L, int32_t rank,
         if (overlap(ws, range_of(grads[q], extent(L, grad_index), gsize)))
             return ZERO_EINVAL;
 
-    // chunk: the workspace's whole 512-element tiles, at most kStageMaxChunk
-    int64_t chunk = (int64_t)(workspace_bytes / sizeof(float)) / kNormSpan * kNormSpan;
-    if (chunk > kStageMaxChunk)
-        chunk = kStageMaxChunk;
     float *g = static_cast<float *>(workspace);
     const StepConsts ca = make_step_consts(nullptr, divisor);  // the average
     const StepConsts cb = make_step_consts(sc, 1.0f);          // g is averaged already

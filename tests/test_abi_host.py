@@ -401,4 +401,8 @@ def test_staged_step_workspace_and_errors():
     assert call(ws, 2047) == z.ZERO_ENOSPC
     assert call(w, 1 << 20) == z.ZERO_EINVAL          # workspace overlapping master
     assert call(base, 1 << 20) == z.ZERO_EINVAL       # workspace overlapping a gradient
+    # a claimed size past what any call writes (one chunk of at most 32M fp32):
+    # overlaps inside the chunk are still refused, SIZE_MAX included
+    assert call(w, (1 << 64) - 1) == z.ZERO_EINVAL
+    assert call(w - 4096, 1 << 40) == z.ZERO_EINVAL
     assert lib.zero_step_staged_workspace_bytes(L.ptr, 0, 0, C.byref(C.c_size_t())) == z.ZERO_ERANGE
