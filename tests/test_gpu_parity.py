@@ -773,3 +773,33 @@ def test_clipped_step_without_host_sync_and_in_a_graph():
         assert_same_f32(to_np(V3), to_np(Vr), f"graph replay {t} v")
         assert_same_bf16(to_np(O3), to_np(Or), f"graph replay {t} out")
     assert_same_f32(to_np(W3), to_np(W), "graph chain vs host-synchronized step")
+
+
+def test_random_sweep():
+    """A seeded sweep across the step's parameter space, each case against the
+    oracle bit for bit: rank counts from 1 to 256 (compile-time and runtime
+    kernels), 1-5 units of random size (padding, empty units, several tiles
+    and ragged tails), every rank or one, every valid index-mode combination,
+    both gradient types, pointers shifted off 16-byte alignment, the bf16
+    output on or off, one or two steps, and the staged step with random
+    workspace sizes."""
+    rng = np.random.default_rng(2024)
+    for case in range(150):
+        n = int(rng.choice([1, 2, 3, 5, 8, 16, 17, 31, 32, 33, 47, 64, 65, 128, 200, 256]))
+        numel = [int(rng.integers(0, 6144)) if rng.random() < 0.8 else int(rng.integers(0, 40))
+                 for _ in range(int(rng.integers(1, 6)))]
+        if sum(numel) == 0:
+            numel[0] = 1
+        rank = int(rng.integers(-1, n))
+        gdt = z.ZERO_BF16 if rng.random() < 0.7 else z.ZERO_F32
+        if rank < 0:
+            gidx = sidx = oidx = G
+        else:
+            gidx, sidx, oidx = (G if rng.random() < 0.5 else Lc for _ in range(3))
+        staged = None
+        if rng.random() < 0.4:
+            staged = int(rng.choice([0, 512, 1024, 512 * int(rng.integers(3, 40))]))
+        kw = dict(steps=int(rng.integers(1, 3)), with_out=bool(rng.random() < 0.85), staged=staged)
+        log(f"sweep case {case}: n={n} numel={numel} rank={rank} gdt={gdt} "
+            f"idx={gidx}{sidx}{oidx} {kw}")
+        _run_case(rng, n, numel, rank, gdt, gidx, sidx, oidx, int(rng.integers(0, 8)), **kw)
