@@ -853,3 +853,64 @@ def test_norm_random_sweep():
         assert_same_f32(to_np(g_out), og, f"g, case {case}")
         osum = oracle.sumsq(og)
         assert abs(s1 - osum) <= 1e-12 * osum, (case, s1, osum)
+
+
+def test_pack_random_sweep():
+    """A seeded sweep of the packer against the oracle's layout: random rank
+    counts, parameter counts and sizes (empty ones included), unit groupings
+    (empty units included), every rank or one, every dtype pair, shifted
+    pointers.  Pack must place every element at its offset with +0.0 padding
+    (bit for bit after the dtype conversion); unpack from the flat buffer
+    must return every parameter, and unpack from a rank's shard exactly the
+    elements that rank owns, leaving the rest untouched."""
+    rng = np.random.default_rng(91)
+    dts = [torch.float32, torch.bfloat16]
+    for case in range(40):
+        n = int(rng.choice([1, 2, 3, 5, 8, 13, 32, 64]))
+        n_params = int(rng.integers(1, 13))
+        numels = [int(rng.integers(0, 3000)) if rng.random() < 0.9 else 0 for _ in range(n_params)]
+        n_units = int(rng.integers(1, 5))
+        units = sorted(int(u) for u in rng.integers(0, n_units, n_params))
+        unit_numel = [sum(k for k, u in zip(numels, units) if u == j) for j in range(n_units)]
+        if sum(unit_numel) == 0:
+            numels[0] = unit_numel[units[0]] = 17
+        src_dt, dst_dt = dts[int(rng.integers(0, 2))], dts[int(rng.integers(0, 2))]
+        rank = int(rng.integers(-1, n))
+        log(f"pack sweep case {case}: n={n} numels={numels} units={units} rank={rank} "
+            f"{src_dt}->{dst_dt}")
+        L = z.zero_pack(n, unit_numel)
+        O = oracle.Layout(n, unit_numel)
+        params = []
+        for k in numels:
+            p = dev_buffer(k, src_dt, shift=int(rng.integers(0, 8)))
+            p.copy_(torch.from_numpy(rng.standard_normal(k).astype(np.float32)).to(src_dt))
+            params.append(p)
+        exp = np.zeros(L.padded, np.float32)
+        pos = [0] * n_units
+        for p, u in zip(params, units):
+            a = O.offset[u] + pos[u]
+            exp[a:a + p.numel()] = p.float().cpu().numpy()
+            pos[u] += p.numel()
+        want = torch.from_numpy(exp).to(dst_dt).float().numpy()
+        flat = dev_buffer(L.padded, dst_dt, shift=int(rng.integers(0, 8)), fill=7)
+        z.zero_pack_copy(L, -1, params, units, flat)
+        assert_same_f32(flat.float().cpu().numpy(), want, f"flat, case {case}")
+        js = np.array([O.global_of_local(max(rank, 0), k) for k in range(L.shard)], np.int64)
+        if rank >= 0:
+            shard = dev_buffer(L.shard, dst_dt, shift=int(rng.integers(0, 8)), fill=7)
+            z.zero_pack_copy(L, rank, params, units, shard)
+            assert_same_f32(shard.float().cpu().numpy(), want[js], f"rank {rank} shard, case {case}")
+        # unpack: from the flat buffer (every element), or from the rank's shard
+        src = flat if rank < 0 else shard
+        back = [dev_buffer(p.numel(), src_dt, shift=int(rng.integers(0, 8)), fill=-3) for p in params]
+        z.zero_unpack_copy(L, rank, src, back, units)
+        torch.cuda.synchronize()
+        owned = np.zeros(L.padded, bool)
+        owned[js if rank >= 0 else slice(None)] = True
+        pos = [0] * n_units
+        for p, b, u in zip(params, back, units):
+            a = O.offset[u] + pos[u]
+            pos[u] += p.numel()
+            full = p.to(dst_dt).to(src_dt).float().cpu().numpy()
+            expect = np.where(owned[a:a + p.numel()], full, np.float32(-3))
+            assert_same_f32(b.float().cpu().numpy(), expect, f"unpack, case {case}")
