@@ -914,3 +914,77 @@ def test_pack_random_sweep():
             full = p.to(dst_dt).to(src_dt).float().cpu().numpy()
             expect = np.where(owned[a:a + p.numel()], full, np.float32(-3))
             assert_same_f32(b.float().cpu().numpy(), expect, f"unpack, case {case}")
+
+
+def test_clip_chain_random_sweep():
+    """A seeded sweep of the sync-free clipped step -- norm pass writing g,
+    coefficient on the device, step reading g and the coefficient -- against
+    the oracle's clipped step from the N gradients: random rank counts,
+    layouts, ranks, gradient types and index spaces, heavy-tailed gradients
+    large enough that clipping is active.  The coefficient must equal the
+    oracle's (formed from the oracle's sum of squares) and master / m / v /
+    bf16 out must match bit for bit."""
+    rng = np.random.default_rng(123)
+    h = dict(lr=1e-3, b1=0.9, b2=0.95, eps=1e-8, wd=0.1)
+    for case in range(30):
+        n = int(rng.choice([1, 2, 4, 8, 16, 33, 64, 100]))
+        numel = [int(rng.integers(1, 6000)) for _ in range(int(rng.integers(1, 4)))]
+        rank = int(rng.integers(-1, n))
+        gidx = G if rank < 0 or rng.random() < 0.5 else Lc
+        sidx = G if rank < 0 else Lc
+        gdt = z.ZERO_BF16 if rng.random() < 0.7 else z.ZERO_F32
+        log(f"clip chain case {case}: n={n} numel={numel} rank={rank} gidx={gidx} gdt={gdt}")
+        L = z.zero_pack(n, numel)
+        O = oracle.Layout(n, numel)
+        ge, se = extent(L, gidx), extent(L, sidx)
+        tdt = torch.bfloat16 if gdt == z.ZERO_BF16 else torch.float32
+        # the average of n Student-t(3) draws has variance 3 s^2 / n: scale so
+        # that the expected norm over the selection is about 10
+        s_ = np.sqrt(100.0 * n / (3.0 * se))
+        vals = (rng.standard_t(3, (n, ge)) * s_).astype(np.float32)
+        if gidx == G:
+            for u in range(len(numel)):
+                vals[:, O.offset[u] + numel[u]:O.offset[u] + O.padded[u]] = 0
+        grads = [dev_buffer(ge, tdt, shift=int(rng.integers(0, 8))) for _ in range(n)]
+        for q in range(n):
+            grads[q].copy_(torch.from_numpy(vals[q]).to(tdt))
+        gnp = [np.ascontiguousarray(to_np(g)) for g in grads]
+        w0 = rng.normal(0, 0.02, se).astype(np.float32)
+        W = dev_buffer(se, torch.float32, shift=int(rng.integers(0, 4)))
+        W.copy_(torch.from_numpy(w0))
+        M, V = torch.zeros(se, device=DEV), torch.zeros(se, device=DEV)
+        out = torch.zeros(se, dtype=torch.int16, device=DEV)
+        g_red = torch.empty(se, dtype=torch.float32, device=DEV)
+        ws = torch.zeros(max(z.zero_gradnorm_workspace_bytes(L, rank) // 8, 1), dtype=torch.float64,
+                         device=DEV)
+        ss = torch.zeros(1, dtype=torch.float64, device=DEV)
+        coef = torch.zeros(1, dtype=torch.float32, device=DEV)
+        z.zero_gradnorm_async(L, rank, grads, gidx, float(n), g_red, sidx, ws, ss)
+        z.zero_clip_coef_async(ss, 1.0, coef)
+        z.zero_step_device_clip(L, rank, [g_red], sidx, 1.0, W, M, V, sidx, out, sidx, scalars(1, h),
+                                coef)
+        torch.cuda.synchronize()
+        if rank < 0:
+            og = np.zeros(se, np.float32)
+            for r in range(n):
+                ks = oracle.reduced_grad(n, numel, r, gnp, grad_local=False, divisor=float(n))
+                og[[O.global_of_local(r, k) for k in range(L.shard)]] = ks
+        else:
+            og = oracle.reduced_grad(n, numel, rank, gnp, grad_local=(gidx == Lc), divisor=float(n))
+        ocoef = oracle.clip_coef(oracle.sumsq(og), 1.0)
+        assert float(coef.item()) == ocoef, (case, float(coef.item()), ocoef)
+        # clipping is active unless the selection is all padding (g = 0, c = 1)
+        assert (ocoef < 1.0) == bool(og.any()), (case, ocoef)
+        om, omm, ov, oo = w0.copy(), np.zeros(se, np.float32), np.zeros(se, np.float32), np.zeros(se, np.uint16)
+        if rank < 0:
+            oracle.zero_step_all(n, numel, gnp, divisor=float(n), clip=ocoef, master=om, m=omm, v=ov,
+                                 out=oo, t=1, **hyper_args(h))
+        else:
+            oracle.zero_step_rank(n, numel, rank, gnp, grad_local=(gidx == Lc), divisor=float(n),
+                                  clip=ocoef, master=om, m=omm, v=ov, state_global=False, out=oo,
+                                  out_gather=False, t=1, **hyper_args(h))
+        tag = f"case {case}"
+        assert_same_f32(to_np(W), om, "master " + tag)
+        assert_same_f32(to_np(M), omm, "m " + tag)
+        assert_same_f32(to_np(V), ov, "v " + tag)
+        assert_same_bf16(to_np(out), oo, "out " + tag)
