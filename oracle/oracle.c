@@ -40,7 +40,11 @@
  *   - v's increment associates as ((1 - b2) * g) * g;
  *   - the update is ((lr / bc1) * m) / (sqrt(v) / bc2 + eps), both true divisions;
  *   - the bf16 cast rounds to nearest, ties to even;
- *   - padding elements are processed like any other (they stay +0).
+ *   - padding elements are processed like any other (they stay +0);
+ *   - the sum of squares adds the binary64 squares serially in element order
+ *     (the pages fix no order for it; a serial sum of n terms is exact to
+ *     n * 2^-53 relative, so at large n tests hold the device's sum to an
+ *     accurate pairwise binary64 sum and this one to that bound).
  */
 #include <math.h>
 #include <stdint.h>
