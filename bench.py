@@ -467,6 +467,15 @@ def reshard_bench(args):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     call_s = e0.elapsed_time(e1) / 1e3 / args.steps
+    per_call = []
+    for _ in range(10):   # per-call spread, after the timed region
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        z.zero_reshard(A, src, B, R.dst_rank, dst, stream, src_ptrs=sp)
+        b.record(stream)
+        per_call.append((a, b))
+    torch.cuda.synchronize()
+    per_ms = sorted(a.elapsed_time(b) for a, b in per_call)
     nbytes, elements = z.zero_reshard_traffic(A, B, R.dst_rank, z.ZERO_F32)
     achieved = nbytes / call_s / 1e9
     box_copy = None if args.no_box_copy else box_copy_ceiling(z, torch, stream)
@@ -487,6 +496,10 @@ def reshard_bench(args):
                      "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": call_s * 1e3,
                      "timing": "HIP events on the launch stream at the two ends of the timed "
                                "region; average = span / steps",
+                     "per_call_ms": {"median": float(np.median(per_ms)), "min": per_ms[0],
+                                     "calls": len(per_ms),
+                                     "timing": "an event pair around each call, 10 calls after "
+                                               "the timed region"},
                      "launches_per_call": "one reshard = several copy_batch_kernel launches "
                                           "back to back; achieved and traffic are per call",
                      "box_copy_GBps": box_copy,
@@ -682,6 +695,20 @@ def main():
     ms_per_step = wall / args.steps * 1e3
     value = elements * args.steps / wall
 
+    # per-call spread, after the timed region: an event pair around each of
+    # 10 more calls (whole iterations: norm pass, coefficient and step for
+    # the clipped workload); reported beside, not in, `value` and `frac`
+    per_call = []
+    for _ in range(10):
+        t += 1
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        one_step(t)
+        b.record(stream)
+        per_call.append((a, b))
+    torch.cuda.synchronize()
+    per_ms = sorted(a.elapsed_time(b) for a, b in per_call)
+
     traffic = measured_traffic(args.workload)
     box_copy = None if args.no_box_copy else box_copy_ceiling(z, torch, stream)
 
@@ -728,6 +755,8 @@ def main():
             "algorithmic_bytes_per_launch": dom_bytes,
             "avg_launch_ms": avg_launch_s * 1e3,
             "timing": timing,
+            "per_call_ms": {"median": float(np.median(per_ms)), "min": per_ms[0], "calls": len(per_ms),
+                            "timing": "an event pair around each call, 10 calls after the timed region"},
             "launches_per_call": (2 * -(-elements // (ws_elems or 1))) if staged else 1,
             "box_copy_GBps": box_copy,
             "frac_of_box_copy": achieved / box_copy if box_copy else None,

@@ -13,7 +13,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KEYS = {"metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
         "scaling", "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline"}
-ROOF = {"bound", "achieved", "peak", "unit", "frac", "traffic", "avg_launch_ms", "timing"}
+ROOF = {"bound", "achieved", "peak", "unit", "frac", "traffic", "avg_launch_ms", "timing", "per_call_ms"}
 
 
 def _run(args):
