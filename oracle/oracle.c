@@ -32,13 +32,16 @@
  *   ledger      p4 section 3 (16 bytes per parameter) and section 4 (per-stage
  *               memory and communication); p3 section 4 (gradients transient).
  *
+ * Fixed by p1 "Code" itself: its update lines are Rust binary32 expressions,
+ * where * and / are left-associative, so v's increment is ((1 - b2) * g) * g
+ * and the update is ((lr / bc1) * m) / (sqrt(v) / bc2 + eps), both true
+ * divisions; the weight decays before the update is subtracted.
+ *
  * Readings where the pages leave a step open (each is listed with its reason
  * in the design notes of the repository):
  *   - rank sum starts from rank 0's value and adds ranks 1..N-1 in order;
  *   - beta^t is the running binary32 product p_t = p_{t-1} * beta, p_0 = 1;
  *   - 1 - beta is formed in binary32 from the binary32 beta;
- *   - v's increment associates as ((1 - b2) * g) * g;
- *   - the update is ((lr / bc1) * m) / (sqrt(v) / bc2 + eps), both true divisions;
  *   - the bf16 cast rounds to nearest, ties to even;
  *   - padding elements are processed like any other (they stay +0);
  *   - the sum of squares adds the binary64 squares serially in element order

@@ -313,6 +313,27 @@ def pin_adamw_vs_torch64(seed=0, P=4096, steps=12):
             assert np.all(np.abs(v - ref_v) <= tol_v), (hp, t, "v")
 
 
+def pin_adamw_order():
+    """The association of the AdamW update that the page's code fixes ("ZeRO and
+    FSDP sharding", Code: `(1.0 - b2) * g[i] * g[i]`, `lr / bc1 * m / (v.sqrt()
+    / bc2 + eps)`), on elements whose bits change under each alternative
+    association.  Expected bits come from tests/golden/adamw_order.json, written
+    by exact rational arithmetic with one binary32 rounding per operation
+    (tests/golden/make_adamw_order.py), not by the oracle."""
+    import f32exact as F
+    gold = golden("adamw_order.json")
+    seen = set()
+    for c in gold["cases"]:
+        hp = [F.value_of(F.from_decimal(c["hyper"][k])) for k in ("lr", "b1", "b2", "eps", "wd")]
+        w, m, v, g = (np.array([int(c[k], 16)], np.uint32).view(np.float32) for k in "wmvg")
+        oracle.adamw_vector(w, m, v, g, c["t"], *hp)
+        got = {"m": int(bits(m)[0]), "v": int(bits(v)[0]), "w": int(bits(w)[0])}
+        exp = {k: int(x, 16) for k, x in c["expect"].items()}
+        assert got == exp, (c, {k: hex(x) for k, x in got.items()})
+        seen.update(c["alternatives_that_differ"])
+    assert seen >= {"v_assoc", "u_assoc", "den_recip", "den_sqrt"}, seen
+
+
 def pin_scalars(t_max=3000):
     """b^t as a running binary32 product (numpy's sequential float32 cumprod),
     and the closed forms of the bias corrections in binary64."""
@@ -419,6 +440,86 @@ def pin_rank_local_equals_global(seed=1):
             assert np.array_equal(o, out_all[idx])
 
 
+def pin_reduced_grad(seed=5):
+    """The averaged gradient of a rank's shard (the reduction half of the
+    reduce-scatter, then the division by N: "ZeRO and FSDP sharding", Code).
+
+    - Exact case: dyadic gradients whose rank sums are exact in binary32; the
+      mean is then fl(sum / N), one rounding of an exactly known rational,
+      read at the brute-force listing's positions (tests/f32exact.py).
+    - Both index spaces: a rank's reduce-scatter chunks (LOCAL, cut from the
+      full gradients by the brute-force listing) give the same g as the full
+      gradients (GLOBAL).
+    - Tied to the pinned step: the step on the N gradients equals, bit for bit,
+      the step on the one reduced gradient with divisor 1."""
+    import f32exact as F
+    from fractions import Fraction
+    rng = np.random.default_rng(seed)
+    hp = dict(lr=f32(1e-3), b1=f32(0.9), b2=f32(0.95), eps=f32(1e-8), wd=f32(0.1))
+    for n in (1, 3, 8):
+        for trial in range(4):
+            U = int(rng.integers(1, 4))
+            numel = [int(x) for x in rng.integers(0, 40, U)]
+            numel[0] = max(numel[0], 1)
+            L = oracle.Layout(n, numel)
+            flat, _, local = brute_layout(n, numel)
+            real = np.array([e is not None for e in flat], bool)
+            for bf in (True, False):
+                # dyadic integers a * 2^-12 with |a| <= 200: bf16-exact, and
+                # any sum of up to 8 of them is exact in binary32
+                ints = [np.where(real, rng.integers(-200, 201, len(flat)), 0) for _ in range(n)]
+                dyad = [(a * 2.0 ** -12).astype(np.float32) for a in ints]
+                gglob = [oracle.bf16(x) if bf else x for x in dyad]
+                for r in range(n):
+                    pos = np.array(local[r], np.int64)
+                    gloc = [np.ascontiguousarray(g[pos]) for g in gglob]
+                    got_g = oracle.reduced_grad(n, numel, r, gglob, grad_local=False, divisor=float(n))
+                    got_l = oracle.reduced_grad(n, numel, r, gloc, grad_local=True, divisor=float(n))
+                    assert np.array_equal(bits(got_g), bits(got_l)), (n, numel, r, "GLOBAL vs LOCAL")
+                    tot = sum(a[pos] for a in ints)
+                    exp = np.array([F.encode(Fraction(int(x), 4096 * n)) for x in tot], np.uint32)
+                    assert np.array_equal(bits(got_g), exp), (n, numel, r, bf, "exact mean")
+                    # the step on N gradients == the step on the reduced one
+                    base = rng.normal(0, 0.02, L.total_shard).astype(np.float32)
+                    st = [base.copy(), np.zeros_like(base), np.zeros_like(base)]
+                    s1 = [base.copy(), np.zeros_like(base), np.zeros_like(base)]
+                    o, o1 = np.zeros(L.total_shard, np.uint16), np.zeros(L.total_shard, np.uint16)
+                    for t in (1, 2):
+                        oracle.zero_step_rank(n, numel, r, gloc, grad_local=True, divisor=float(n), clip=1.0,
+                                              master=st[0], m=st[1], v=st[2], state_global=False, out=o,
+                                              out_gather=False, t=t, **hp)
+                        oracle.zero_step_rank(n, numel, r, [got_l], grad_local=True, divisor=1.0, clip=1.0,
+                                              master=s1[0], m=s1[1], v=s1[2], state_global=False, out=o1,
+                                              out_gather=False, t=t, **hp)
+                    for a, b in zip(st, s1):
+                        assert np.array_equal(bits(a), bits(b)), (n, numel, r, "step on reduced g")
+                    assert np.array_equal(o, o1)
+    # random (not dyadic) gradients, GLOBAL vs LOCAL and vs the step
+    for n, numel in [(3, [10, 11, 12]), (8, [64, 100, 3])]:
+        L = oracle.Layout(n, numel)
+        flat, _, local = brute_layout(n, numel)
+        real = np.array([e is not None for e in flat], bool)
+        gglob = [oracle.bf16(np.where(real, rng.standard_normal(len(flat)) * 1e-3, 0).astype(np.float32))
+                 for _ in range(n)]
+        for r in range(n):
+            pos = np.array(local[r], np.int64)
+            gloc = [np.ascontiguousarray(g[pos]) for g in gglob]
+            got_g = oracle.reduced_grad(n, numel, r, gglob, grad_local=False, divisor=float(n))
+            got_l = oracle.reduced_grad(n, numel, r, gloc, grad_local=True, divisor=float(n))
+            assert np.array_equal(bits(got_g), bits(got_l)), (n, numel, r)
+            base = rng.normal(0, 0.02, L.total_shard).astype(np.float32)
+            st = [base.copy(), np.zeros_like(base), np.zeros_like(base)]
+            s1 = [base.copy(), np.zeros_like(base), np.zeros_like(base)]
+            oracle.zero_step_rank(n, numel, r, gloc, grad_local=True, divisor=float(n), clip=1.0,
+                                  master=st[0], m=st[1], v=st[2], state_global=False, out=None,
+                                  out_gather=False, t=1, **hp)
+            oracle.zero_step_rank(n, numel, r, [got_g], grad_local=True, divisor=1.0, clip=1.0,
+                                  master=s1[0], m=s1[1], v=s1[2], state_global=False, out=None,
+                                  out_gather=False, t=1, **hp)
+            for a, b in zip(st, s1):
+                assert np.array_equal(bits(a), bits(b)), (n, numel, r)
+
+
 # ---------------------------------------------------------------------------
 # The pages' toy.
 # ---------------------------------------------------------------------------
@@ -505,6 +606,6 @@ def pin_ledger():
     assert abs(oracle.comm_elements(1.0, r["n"], r["stage"], True) - r["in_psi"]) < 1e-12
 
 
-ALL_PINS = [pin_layout_bruteforce, pin_bf16_vs_torch, pin_adamw_vs_torch64, pin_scalars,
-            pin_sharded_equals_unsharded, pin_rank_local_equals_global, pin_toy, pin_norm, pin_ledger,
-            pin_rows_vs_torch_chunk, pin_reshard]
+ALL_PINS = [pin_layout_bruteforce, pin_bf16_vs_torch, pin_adamw_vs_torch64, pin_adamw_order,
+            pin_scalars, pin_sharded_equals_unsharded, pin_rank_local_equals_global, pin_reduced_grad,
+            pin_toy, pin_norm, pin_ledger, pin_rows_vs_torch_chunk, pin_reshard]

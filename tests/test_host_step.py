@@ -132,3 +132,27 @@ def test_host_step_empty_and_errors():
     with pytest.raises(z.ZeroError):               # LOCAL with every rank
         z.zero_step_host(L, -1, [np.zeros(4, np.uint16)] * 4, Lc, 4.0, np.zeros(4, np.float32),
                          np.zeros(4, np.float32), np.zeros(4, np.float32), Lc, None, Lc, sc(1))
+
+
+def _order_cases():
+    import f32exact as F
+    for c in pins.golden("adamw_order.json")["cases"]:
+        hp = [F.value_of(F.from_decimal(c["hyper"][k])) for k in ("lr", "b1", "b2", "eps", "wd")]
+        vals = {k: np.uint32(int(c[k], 16)) for k in "wmvg"}
+        exp = {k: int(x, 16) for k, x in c["expect"].items()}
+        yield c, hp, vals, exp
+
+
+@pytest.mark.parametrize("copies", [1, 67])
+def test_adamw_order_golden_host(copies):
+    """The host step on the elements whose bits each alternative association
+    of the page's AdamW code would change (exact-arithmetic golden table);
+    67 copies run the 8-wide vector loop as well as the scalar tail."""
+    for c, hp, vals, exp in _order_cases():
+        L = z.zero_pack(1, [copies])
+        arr = {k: np.full(copies, vals[k], np.uint32).view(np.float32) for k in "wmvg"}
+        s = z.zero_adamw_scalars_for(c["t"], *hp, 1.0)
+        z.zero_step_host(L, 0, [arr["g"]], Lc, 1.0, arr["w"], arr["m"], arr["v"], Lc, None, Lc, s, 2)
+        for k in "mvw":
+            got = arr[k].view(np.uint32)
+            assert np.all(got == exp[k]), (c, k, hex(int(got[0])))

@@ -55,6 +55,19 @@ MUTANTS = [
      "++u;"),
     ("reshard reads the destination rank's shard", "memcpy(d, (const char *)src[q] + ka * elem",
      "memcpy(d, (const char *)src[dst_rank < n_a ? dst_rank : 0] + ka * elem"),
+    # the reduced gradient (the norm pass's reference) and the association of
+    # the AdamW update that the page's code fixes
+    ("reduced gradient: wrong divisor", "g_out[k] = sum / divisor;", "g_out[k] = sum / (divisor + 1.0f);"),
+    ("reduced gradient: index spaces swapped", "int64_t gi = grad_local ? k : j;\n            float sum",
+     "int64_t gi = grad_local ? j : k;\n            float sum"),
+    ("v increment as (1-b2)*(g*g)", "float v_incr = (h->one_minus_b2 * g) * g;",
+     "float v_incr = h->one_minus_b2 * (g * g);"),
+    ("update as (lr/bc1)*(m/den)", "float numer = h->lr_over_bc1 * (*m);\n    float update = numer / den;",
+     "float numer = (*m) / den;\n    float update = h->lr_over_bc1 * numer;"),
+    ("denominator by the reciprocal of bc2", "float den = root / h->bc2 + h->eps;",
+     "float den = root * (1.0f / h->bc2) + h->eps;"),
+    ("denominator as sqrt(v / bc2^2)", "float den = root / h->bc2 + h->eps;",
+     "float den = sqrtf(*v / (h->bc2 * h->bc2)) + h->eps;"),
 ]
 
 

@@ -29,6 +29,31 @@ def test_adamw_vs_torch_binary64():
     pins.pin_adamw_vs_torch64()
 
 
+def test_adamw_operation_order():
+    """The association the page's code fixes, on elements where each
+    alternative association changes the bits (exact-arithmetic golden)."""
+    pins.pin_adamw_order()
+
+
+def test_adamw_order_golden_is_reproducible(tmp_path):
+    """The committed golden table is what its generator writes."""
+    import json
+    import subprocess
+    import sys
+    here = os.path.dirname(os.path.abspath(__file__))
+    gen = os.path.join(here, "golden", "make_adamw_order.py")
+    src = open(gen).read().replace('os.path.join(HERE, "adamw_order.json")',
+                                   repr(str(tmp_path / "adamw_order.json")))
+    (tmp_path / "gen.py").write_text(src.replace("HERE = os.path.dirname(os.path.abspath(__file__))",
+                                                 f"HERE = {os.path.join(here, 'golden')!r}"))
+    subprocess.run([sys.executable, str(tmp_path / "gen.py")], check=True, capture_output=True)
+    assert json.load(open(tmp_path / "adamw_order.json")) == pins.golden("adamw_order.json")
+
+
+def test_reduced_grad():
+    pins.pin_reduced_grad()
+
+
 def test_step_scalars():
     pins.pin_scalars()
 
