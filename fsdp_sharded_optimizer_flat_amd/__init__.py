@@ -212,6 +212,32 @@ def _stream(stream):
     return stream.cuda_stream
 
 
+def _numel(t) -> int:
+    return int(t.numel()) if hasattr(t, "numel") and callable(t.numel) else int(np.asarray(t).size)
+
+
+def _need(t, n: int, what: str):
+    """Refuse a buffer with fewer elements than the call reads or writes: the
+    library sees only pointers, so a short buffer would be overrun."""
+    if t is not None and _numel(t) < n:
+        raise ValueError(f"{what} holds {_numel(t)} elements; the call needs {n}")
+
+
+def _extent(layout, index: int) -> int:
+    """Elements of a buffer in the given index space: P^ (GLOBAL) or S (LOCAL)."""
+    return int(layout.padded) if index == ZERO_GLOBAL else int(layout.shard)
+
+
+def _need_step(layout, grads, grad_index, master, exp_avg, exp_avg_sq, state_index, out,
+               out_index):
+    ge, se = _extent(layout, grad_index), _extent(layout, state_index)
+    for g in grads:
+        _need(g, ge, "grad")
+    for t, what in ((master, "master"), (exp_avg, "exp_avg"), (exp_avg_sq, "exp_avg_sq")):
+        _need(t, se, what)
+    _need(out, _extent(layout, out_index), "out")
+
+
 # -- layout -------------------------------------------------------------------------
 
 class Layout:
@@ -320,6 +346,7 @@ def _flat_dtype(t) -> int:
 
 def zero_pack_copy(layout: Layout, rank: int, params, units, dst, stream=None):
     ptrs, numel, unit, sdt = _param_arrays(params, units)
+    _need(dst, layout.padded if rank < 0 else layout.shard, "dst")
     _check(_zero_pack_copy(layout.ptr, rank, len(params), C.addressof(ptrs), numel.ctypes.data,
                            unit.ctypes.data, sdt, _dev_ptr(dst, "dst"), _flat_dtype(dst),
                            _stream(stream)), "zero_pack_copy")
@@ -327,6 +354,7 @@ def zero_pack_copy(layout: Layout, rank: int, params, units, dst, stream=None):
 
 def zero_unpack_copy(layout: Layout, rank: int, src, params, units, stream=None):
     ptrs, numel, unit, ddt = _param_arrays(params, units)
+    _need(src, layout.padded if rank < 0 else layout.shard, "src")
     _check(_zero_unpack_copy(layout.ptr, rank, _dev_ptr(src, "src"), _flat_dtype(src),
                              len(params), C.addressof(ptrs), numel.ctypes.data, unit.ctypes.data,
                              ddt, _stream(stream)), "zero_unpack_copy")
@@ -348,7 +376,7 @@ def reshard_pointer_array(src):
     if len(dts) > 1:
         raise TypeError("sources must share one element type")
     arr = (vp * max(len(src), 1))(*[_dev_ptr(t, "src") for t in src])
-    return arr, (dts.pop() if dts else None), len(src)
+    return _prepared((arr, (dts.pop() if dts else None), len(src)), src)
 
 
 def zero_reshard(src_layout: Layout, src, dst_layout: Layout, dst_rank: int, dst, stream=None, *,
@@ -360,6 +388,11 @@ def zero_reshard(src_layout: Layout, src, dst_layout: Layout, dst_rank: int, dst
     arr, sdt, ns = src_ptrs if src_ptrs is not None else reshard_pointer_array(src)
     if ns != src_layout.n_ranks:
         raise ValueError("one source shard per rank of the source layout")
+    if src_ptrs is None:
+        for t in src:
+            _need(t, src_layout.shard, "src")
+    _need_prepared(src_ptrs, src_layout.shard, "src")
+    _need(dst, dst_layout.shard, "dst")
     dt = _reshard_dtype(dst)
     if sdt is not None and sdt != dt:
         raise TypeError("sources and destination must share one element type")
@@ -371,6 +404,9 @@ def zero_reshard_host(src_layout: Layout, src, dst_layout: Layout, dst_rank: int
     """zero_reshard on host buffers (numpy arrays or CPU tensors); synchronous."""
     if len(src) != src_layout.n_ranks:
         raise ValueError("one source shard per rank of the source layout")
+    for t in src:
+        _need(t, src_layout.shard, "src")
+    _need(dst, dst_layout.shard, "dst")
     sp = [_host_ptr(t, "src", "grad") for t in src]
     dp, dk = _host_ptr(dst, "dst", "grad")
     if any(k != dk for _, k in sp):
@@ -411,6 +447,18 @@ def zero_clip_coef(sumsq: float, max_norm: float) -> float:
 
 # -- the step and the norm -------------------------------------------------------------
 
+class _Prepared(tuple):
+    """Marshalled buffer pointers; ``min_numel`` is the smallest buffer's
+    element count, so calls taking them still refuse short buffers."""
+    min_numel = 0
+
+
+def _prepared(items, buffers):
+    p = _Prepared(items)
+    p.min_numel = min((_numel(b) for b in buffers), default=0)
+    return p
+
+
 def _grad_ptrs(grads):
     if len(grads) < 1:
         raise ValueError("at least one gradient buffer")
@@ -418,7 +466,12 @@ def _grad_ptrs(grads):
     if len(gdt) != 1:
         raise TypeError("all gradient buffers must share one dtype")
     arr = (vp * len(grads))(*[_dev_ptr(g, "grad") for g in grads])
-    return arr, gdt.pop()
+    return _prepared((arr, gdt.pop()), grads)
+
+
+def _need_prepared(prepared, n: int, what: str):
+    if prepared is not None and getattr(prepared, "min_numel", n) < n:
+        raise ValueError(f"a {what} buffer holds {prepared.min_numel} elements; the call needs {n}")
 
 
 def zero_step(layout: Layout, rank: int, grads, grad_index: int, divisor: float,
@@ -428,6 +481,9 @@ def zero_step(layout: Layout, rank: int, grads, grad_index: int, divisor: float,
     fp32), summed in list order.  ``grad_ptrs`` (a prepared ``(array, dtype)``
     from :func:`grad_pointer_array`) skips re-marshalling in timed loops."""
     arr, gdt = grad_ptrs if grad_ptrs is not None else _grad_ptrs(grads)
+    _need_step(layout, grads if grad_ptrs is None else (), grad_index, master, exp_avg, exp_avg_sq,
+               state_index, out, out_index)
+    _need_prepared(grad_ptrs, _extent(layout, grad_index), "grad")
     _check(_zero_step(layout.ptr, rank, C.addressof(arr), len(arr), gdt, grad_index, divisor,
                       _f32_ptr(master, "master"), _f32_ptr(exp_avg, "exp_avg"),
                       _f32_ptr(exp_avg_sq, "exp_avg_sq"), state_index,
@@ -442,6 +498,9 @@ def zero_step_staged(layout: Layout, rank: int, grads, grad_index: int, divisor:
     through ``workspace``, a device tensor; None when fewer than 32
     gradients)."""
     arr, gdt = grad_ptrs if grad_ptrs is not None else _grad_ptrs(grads)
+    _need_step(layout, grads if grad_ptrs is None else (), grad_index, master, exp_avg, exp_avg_sq,
+               state_index, out, out_index)
+    _need_prepared(grad_ptrs, _extent(layout, grad_index), "grad")
     wp = _dev_ptr(workspace, "workspace") if workspace is not None else None
     wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(_zero_step_staged(layout.ptr, rank, C.addressof(arr), len(arr), gdt, grad_index, divisor,
@@ -489,6 +548,7 @@ def zero_step_host(layout: Layout, rank: int, grads, grad_index: int, divisor: f
     host buffers (numpy arrays or CPU tensors); synchronous."""
     if len(grads) < 1:
         raise ValueError("at least one gradient buffer")
+    _need_step(layout, grads, grad_index, master, exp_avg, exp_avg_sq, state_index, out, out_index)
     gp = [_host_ptr(g, "grad", "grad") for g in grads]
     kinds = {k for _, k in gp}
     if len(kinds) != 1:
@@ -515,6 +575,9 @@ def zero_offload_step(layout: Layout, rank: int, d_grad, h_grad_stage, master, e
             raise ValueError(f"{what} must be a pinned CPU tensor")
         if t.numel() < 2 * chunk:
             raise ValueError(f"{what} needs 2 * chunk elements")
+    for t, what in ((d_grad, "d_grad"), (master, "master"), (exp_avg, "exp_avg"),
+                    (exp_avg_sq, "exp_avg_sq"), (d_out, "d_out")):
+        _need(t, layout.shard, what)
     _check(_zero_offload_step(layout.ptr, rank, _f32_ptr(d_grad, "d_grad"),
                               _host_ptr(h_grad_stage, "h_grad_stage", "f32")[0],
                               _host_ptr(master, "master", "f32")[0],
@@ -531,6 +594,10 @@ def zero_step_device_clip(layout: Layout, rank: int, grads, grad_index: int, div
     """zero_step with the clip multiplier read from the float32 device tensor
     ``clip_coef_dev`` (e.g. filled by zero_clip_coef_async)."""
     arr, gdt = grad_ptrs if grad_ptrs is not None else _grad_ptrs(grads)
+    _need_step(layout, grads if grad_ptrs is None else (), grad_index, master, exp_avg, exp_avg_sq,
+               state_index, out, out_index)
+    _need_prepared(grad_ptrs, _extent(layout, grad_index), "grad")
+    _need(clip_coef_dev, 1, "clip_coef_dev")
     _check(_zero_step_device_clip(layout.ptr, rank, C.addressof(arr), len(arr), gdt, grad_index,
                                   divisor, _f32_ptr(master, "master"), _f32_ptr(exp_avg, "exp_avg"),
                                   _f32_ptr(exp_avg_sq, "exp_avg_sq"), state_index,
@@ -556,6 +623,8 @@ def zero_clip_coef_ranks_async(rank_sums_dev, max_norm: float, coef_dev, total_d
     torch = _torch()
     if rank_sums_dev.dtype != torch.float64 or (total_dev is not None and total_dev.dtype != torch.float64):
         raise TypeError("rank sums and total must be float64")
+    _need(coef_dev, 1, "coef_dev")
+    _need(total_dev, 1, "total_dev")
     _check(_zero_clip_coef_ranks_async(_dev_ptr(rank_sums_dev, "rank_sums_dev"),
                                        rank_sums_dev.numel(), max_norm,
                                        _f32_ptr(coef_dev, "coef_dev"),
@@ -568,6 +637,8 @@ def zero_clip_coef_async(sumsq_dev, max_norm: float, coef_dev, stream=None):
     torch = _torch()
     if sumsq_dev.dtype != torch.float64:
         raise TypeError("sumsq_dev must be float64")
+    _need(sumsq_dev, 1, "sumsq_dev")
+    _need(coef_dev, 1, "coef_dev")
     _check(_zero_clip_coef_async(_dev_ptr(sumsq_dev, "sumsq_dev"), max_norm,
                                  _f32_ptr(coef_dev, "coef_dev"), _stream(stream)),
            "zero_clip_coef_async")
@@ -585,6 +656,13 @@ def grad_pointer_array(grads):
     return _grad_ptrs(grads)
 
 
+def _need_norm(layout, grads, grad_index, g_out, g_index):
+    ge = _extent(layout, grad_index)
+    for g in grads:
+        _need(g, ge, "grad")
+    _need(g_out, _extent(layout, g_index), "g_out")
+
+
 def zero_gradnorm_workspace_bytes(layout: Layout, rank: int) -> int:
     b = sz()
     _check(_zero_gradnorm_workspace_bytes(layout.ptr, rank, C.byref(b)),
@@ -597,6 +675,7 @@ def zero_gradnorm(layout: Layout, rank: int, grads, grad_index: int, divisor: fl
     """Sum of squares (binary64) of the averaged gradient; optionally writes
     the averaged gradient (fp32) into ``g_out``.  Synchronizes the stream."""
     arr, gdt = _grad_ptrs(grads)
+    _need_norm(layout, grads, grad_index, g_out, g_index)
     res = f64()
     _check(_zero_gradnorm(layout.ptr, rank, C.addressof(arr), len(arr), gdt, grad_index, divisor,
                           _f32_ptr(g_out, "g_out") if g_out is not None else None, g_index,
@@ -614,6 +693,8 @@ def zero_gradnorm_async(layout: Layout, rank: int, grads, grad_index: int, divis
     if sumsq_dev.dtype != torch.float64:
         raise TypeError("sumsq_dev must be a float64 device tensor")
     arr, gdt = _grad_ptrs(grads)
+    _need_norm(layout, grads, grad_index, g_out, g_index)
+    _need(sumsq_dev, 1, "sumsq_dev")
     _check(_zero_gradnorm_async(layout.ptr, rank, C.addressof(arr), len(arr), gdt, grad_index,
                                 divisor, _f32_ptr(g_out, "g_out") if g_out is not None else None,
                                 g_index, _dev_ptr(workspace, "workspace"),
