@@ -78,6 +78,14 @@ class ZeroLedgerOut(C.Structure):
         return {k: getattr(self, k) for k, _ in self._fields_}
 
 
+class ZeroFootprintOut(C.Structure):
+    _fields_ = [("grads_bytes", f64), ("state_bytes", f64), ("out_bytes", f64), ("g_bytes", f64),
+                ("total_bytes", f64)]
+
+    def as_dict(self):
+        return {k: getattr(self, k) for k, _ in self._fields_}
+
+
 def _sig(name, res, *args):
     fn = getattr(_lib, name)
     fn.restype = res
@@ -125,6 +133,8 @@ _zero_gradnorm_async = _sig("zero_gradnorm_async", i32, vp, i32, vp, i32, i32, i
                             sz, vp, vp)
 _zero_clip_coef = _sig("zero_clip_coef", i32, f64, f64, C.POINTER(f32))
 _zero_ledger = _sig("zero_ledger", i32, f64, i32, i32, i32, C.POINTER(ZeroLedgerOut))
+_zero_sim_footprint = _sig("zero_sim_footprint", i32, vp, i32, i32, i32, i32, i32, i32, i32,
+                          C.POINTER(ZeroFootprintOut))
 _zero_gather_buffer_bytes = _sig("zero_gather_buffer_bytes", i32, vp, i32, C.POINTER(f64))
 _zero_arena_plan = _sig("zero_arena_plan", i32, i32, vp, vp, C.POINTER(i64))
 _zero_step_traffic = _sig("zero_step_traffic", i32, vp, i32, i32, i32, i32, C.POINTER(f64),
@@ -143,7 +153,7 @@ EXPORTED = ["zero_layout_bytes", "zero_pack", "zero_pack_rows", "zero_reshard",
             "zero_clip_coef_async", "zero_clip_coef_ranks", "zero_clip_coef_ranks_async",
             "zero_overlap",
             "zero_gradnorm_workspace_bytes", "zero_gradnorm", "zero_gradnorm_async",
-            "zero_clip_coef", "zero_ledger",
+            "zero_clip_coef", "zero_ledger", "zero_sim_footprint",
             "zero_gather_buffer_bytes", "zero_arena_plan", "zero_step_traffic",
             "zero_gradnorm_traffic",
             "zero_strerror", "zero_last_hip_error", "zero_abi_version"]
@@ -708,6 +718,16 @@ def zero_gradnorm_async(layout: Layout, rank: int, grads, grad_index: int, divis
 def zero_ledger(psi: float, n_ranks: int, stage: int, grads_transient: bool = False) -> dict:
     o = ZeroLedgerOut()
     _check(_zero_ledger(psi, n_ranks, stage, int(grads_transient), C.byref(o)), "zero_ledger")
+    return o.as_dict()
+
+
+def zero_sim_footprint(layout: Layout, n_grads: int, grad_dtype: int, grad_index: int,
+                       state_index: int, out_index: int, with_out: bool = True,
+                       with_g: bool = False) -> dict:
+    """Bytes the one-GPU simulation's buffers occupy (see zero.h)."""
+    o = ZeroFootprintOut()
+    _check(_zero_sim_footprint(layout.ptr, n_grads, grad_dtype, grad_index, state_index, out_index,
+                               int(with_out), int(with_g), C.byref(o)), "zero_sim_footprint")
     return o.as_dict()
 
 

@@ -81,6 +81,29 @@ extern "C" zero_status zero_gradnorm_traffic(const zero_layout *L, int32_t rank,
     return ZERO_OK;
 }
 
+// "Learn: ZeRO & FSDP", section 3's bytes per element (2 gradient, 12 fp32
+// state, 2 bf16 parameters) over the buffers of the one-GPU simulation.
+extern "C" zero_status zero_sim_footprint(const zero_layout *L, int32_t n_grads, int32_t grad_dtype,
+                                          int32_t grad_index, int32_t state_index,
+                                          int32_t out_index, int32_t with_out, int32_t with_g,
+                                          zero_footprint_out *out)
+{
+    const auto index_ok = [](int32_t x) { return x == ZERO_GLOBAL || x == ZERO_LOCAL; };
+    if (!zero::layout_ok(L) || !out || n_grads < 1 ||
+        (grad_dtype != ZERO_F32 && grad_dtype != ZERO_BF16) || !index_ok(grad_index) ||
+        !index_ok(state_index) || !index_ok(out_index))
+        return ZERO_EINVAL;
+    const auto extent = [L](int32_t x) { return (double)(x == ZERO_GLOBAL ? L->padded : L->shard); };
+    zero_footprint_out o{};
+    o.grads_bytes = n_grads * (grad_dtype == ZERO_BF16 ? kGradBytes : 4.0) * extent(grad_index);
+    o.state_bytes = kOptimBytes * extent(state_index);
+    o.out_bytes = with_out ? kParamBytes * extent(out_index) : 0.0;
+    o.g_bytes = with_g ? 4.0 * extent(state_index) : 0.0;
+    o.total_bytes = o.grads_bytes + o.state_bytes + o.out_bytes + o.g_bytes;
+    *out = o;
+    return ZERO_OK;
+}
+
 // "ZeRO and FSDP sharding", Complexity and constants: a unit's all-gather
 // (2 psi_unit (N-1)/N bytes of bf16 weights per rank) is hidden when it takes
 // no longer than the unit's compute (6 psi_unit flops per token).

@@ -488,6 +488,30 @@ typedef struct zero_ledger_out {
 zero_status zero_ledger(double psi, int32_t n_ranks, int32_t stage, int32_t grads_transient,
                         zero_ledger_out *out);
 
+/* Device memory the one-GPU simulation of the step keeps resident -- [p4
+ * section 3]: per element, 2 bytes of bf16 gradient, 12 bytes of fp32 master
+ * + m + v and 2 bytes of bf16 parameters, applied to the simulation's own
+ * buffers rather than to one model replica: n_grads gradient buffers over the
+ * grad_index space (2 bytes per element for ZERO_BF16, 4 for ZERO_F32),
+ * master, m and v over the state_index space, the bf16 output over the
+ * out_index space (if with_out) and the clipped step's reduced fp32 gradient
+ * over the state_index space (if with_g).  Extents: P^ elements for
+ * ZERO_GLOBAL, S for ZERO_LOCAL.  N simulated ranks' bf16 gradients with
+ * every buffer GLOBAL hold (2N + 14) P^ bytes; one rank's LOCAL shard (2N +
+ * 14) S.  Workspaces (norm partials, staged chunk) are not counted.  Host
+ * only.  EINVAL: bad layout, n_grads < 1, bad dtype or index, NULL out. */
+typedef struct zero_footprint_out {
+    double grads_bytes;
+    double state_bytes;
+    double out_bytes;
+    double g_bytes;
+    double total_bytes;
+} zero_footprint_out;
+
+zero_status zero_sim_footprint(const zero_layout *layout, int32_t n_grads, int32_t grad_dtype,
+                               int32_t grad_index, int32_t state_index, int32_t out_index,
+                               int32_t with_out, int32_t with_g, zero_footprint_out *out);
+
 /* Overlap condition of one FSDP unit -- [p1 Complexity and constants]: the
  * unit's all-gather, 2 psi_unit (N-1)/N bytes of bf16 weights received per
  * rank, takes gather_bytes / busbw; it is hidden behind the unit's compute,

@@ -111,6 +111,8 @@ def _declare(lib):
     lib.orc_toy.restype = C.c_int
     lib.orc_ledger_bytes.argtypes = [f64, i32, i32, i32]
     lib.orc_ledger_bytes.restype = f64
+    lib.orc_sim_footprint.argtypes = [i32, i32, vp, i32, i32, i32, i32, i32]
+    lib.orc_sim_footprint.restype = f64
     lib.orc_comm_elements.argtypes = [f64, i32, i32, i32]
     lib.orc_comm_elements.restype = f64
     lib.orc_layout_rows.argtypes = [i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -343,3 +345,13 @@ def ledger_bytes(psi, n, stage, grads_transient=False) -> float:
 
 def comm_elements(psi, n, stage, exact_ring=False) -> float:
     return float(load().orc_comm_elements(psi, n, stage, int(exact_ring)))
+
+
+def sim_footprint(n, numel, *, every_rank, n_grads, grad_bytes, with_out=True, with_g=False) -> float:
+    numel = np.ascontiguousarray(numel, np.int64)
+    v = float(load().orc_sim_footprint(n, len(numel), _ptr(numel) if len(numel) else None,
+                                       int(every_rank), n_grads, grad_bytes, int(with_out),
+                                       int(with_g)))
+    if v < 0:
+        raise ValueError("oracle layout failed")
+    return v

@@ -727,6 +727,31 @@ double orc_ledger_bytes(double psi, int32_t n, int32_t stage,
     return params + grads + optim;
 }
 
+/* Bytes the one-GPU simulation keeps resident, from p4 section 3's bytes per
+ * element (bf16 gradient 2, fp32 master + m + v 12, bf16 parameters 2) over
+ * the simulation's buffers: n_grads gradients of grad_bytes per element, the
+ * three state arrays, the bf16 output (with_out) and the clipped step's fp32
+ * reduced gradient (with_g).  every_rank == 1: every rank's shards at once,
+ * so each buffer spans the padded flat buffer; 0: one rank's local shard. */
+double orc_sim_footprint(int32_t n, int32_t n_units, const int64_t *numel,
+                         int32_t every_rank, int32_t n_grads, int32_t grad_bytes,
+                         int32_t with_out, int32_t with_g)
+{
+    orc_lay L;
+    if (lay_make(n, n_units, numel, &L) != ORC_OK) {
+        lay_free(&L);
+        return -1.0;
+    }
+    double elems = (double)(every_rank ? L.total_padded : L.total_shard);
+    lay_free(&L);
+    double per = (double)n_grads * grad_bytes + 12.0;
+    if (with_out)
+        per += 2.0;
+    if (with_g)
+        per += 4.0;
+    return per * elems;
+}
+
 /* Elements communicated per step: all-reduce = reduce-scatter + all-gather =
  * 2 psi for stages 0-2; stage 3 gathers twice (forward, backward) and
  * reduce-scatters once = 3 psi.  exact_ring == 1 applies the (N-1)/N factor

@@ -606,6 +606,32 @@ def pin_ledger():
     assert abs(oracle.comm_elements(1.0, r["n"], r["stage"], True) - r["in_psi"]) < 1e-12
 
 
+def pin_sim_footprint(seed=9):
+    """The simulation's resident bytes ("Learn: ZeRO & FSDP", section 3: 2
+    bytes of bf16 gradient, 12 of fp32 master + m + v, 2 of bf16 parameters
+    per element) equal the bytes of the buffers a simulation actually
+    allocates, sized from the brute-force listing: n gradient buffers, three
+    state arrays, the output and, for the clipped step, the reduced gradient."""
+    rng = np.random.default_rng(seed)
+    for _ in range(60):
+        n = int(rng.integers(1, 10))
+        numel = [int(x) for x in rng.integers(0, 50, int(rng.integers(1, 4)))]
+        flat, _, local = brute_layout(n, numel)
+        for every_rank in (True, False):
+            elems = len(flat) if every_rank else len(local[0])
+            for bf in (True, False):
+                for with_out, with_g in ((True, False), (False, False), (True, True)):
+                    bufs = [np.zeros(elems, np.uint16 if bf else np.float32) for _ in range(n)]
+                    bufs += [np.zeros(elems, np.float32) for _ in range(3)]
+                    if with_out:
+                        bufs.append(np.zeros(elems, np.uint16))
+                    if with_g:
+                        bufs.append(np.zeros(elems, np.float32))
+                    got = oracle.sim_footprint(n, numel, every_rank=every_rank, n_grads=n,
+                                               grad_bytes=2 if bf else 4, with_out=with_out, with_g=with_g)
+                    assert got == sum(b.nbytes for b in bufs), (n, numel, every_rank, bf, with_out, with_g)
+
+
 ALL_PINS = [pin_layout_bruteforce, pin_bf16_vs_torch, pin_adamw_vs_torch64, pin_adamw_order,
             pin_scalars, pin_sharded_equals_unsharded, pin_rank_local_equals_global, pin_reduced_grad,
-            pin_toy, pin_norm, pin_ledger, pin_rows_vs_torch_chunk, pin_reshard]
+            pin_toy, pin_norm, pin_ledger, pin_sim_footprint, pin_rows_vs_torch_chunk, pin_reshard]

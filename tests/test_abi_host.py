@@ -159,6 +159,45 @@ def test_clip_coef_matches_oracle():
 
 # -- ledger -------------------------------------------------------------------------------
 
+def test_sim_footprint_matches_oracle_and_workloads():
+    """The simulation's resident bytes: library against the oracle on random
+    layouts (every rank GLOBAL, one rank LOCAL, mixed spaces), and the
+    workloads' figures: the GPT-2 Large model with all N = 8 shards, (2N + 14)
+    P^ = 30 x 774,090,240 = 23,222,707,200 bytes; one N = 64 rank of the 8B
+    Llama shape, (2N + 14) S = 142 x 125,472,832 = 17,817,142,144 bytes, plus 4
+    S for the clipped step's reduced gradient."""
+    from fsdp_sharded_optimizer_flat_amd import workloads as W
+    rng = np.random.default_rng(3)
+    G, Lc = z.ZERO_GLOBAL, z.ZERO_LOCAL
+    for _ in range(40):
+        n = int(rng.integers(1, 9))
+        numel = [int(x) for x in rng.integers(0, 5000, int(rng.integers(1, 5)))]
+        L = z.zero_pack(n, numel)
+        for bf in (True, False):
+            for with_out, with_g in ((True, False), (False, False), (True, True)):
+                gb, dt = (2, z.ZERO_BF16) if bf else (4, z.ZERO_F32)
+                for every, idx in ((True, G), (False, Lc)):
+                    got = z.zero_sim_footprint(L, n, dt, idx, idx, idx, with_out, with_g)
+                    want = oracle.sim_footprint(n, numel, every_rank=every, n_grads=n, grad_bytes=gb,
+                                                with_out=with_out, with_g=with_g)
+                    assert got["total_bytes"] == want
+                # mixed spaces: GLOBAL gradients, LOCAL state and out
+                mix = z.zero_sim_footprint(L, n, dt, G, Lc, Lc, with_out, with_g)
+                assert mix["grads_bytes"] == n * gb * L.padded
+                assert mix["total_bytes"] == n * gb * L.padded + (12 + 2 * with_out + 4 * with_g) * L.shard
+    g = W.WORKLOADS["gpt2l"]
+    L = z.zero_pack(g.n_ranks, list(g.unit_numel))
+    assert z.zero_sim_footprint(L, 8, z.ZERO_BF16, G, G, G)["total_bytes"] == 23_222_707_200
+    ll = W.WORKLOADS["llama8b_z3"]
+    L = z.zero_pack(ll.n_ranks, list(ll.unit_numel))
+    assert z.zero_sim_footprint(L, 64, z.ZERO_BF16, Lc, Lc, Lc)["total_bytes"] == 17_817_142_144
+    assert z.zero_sim_footprint(L, 64, z.ZERO_BF16, Lc, Lc, Lc, True, True)["total_bytes"] == \
+        17_817_142_144 + 4 * 125_472_832
+    for bad in ((0, z.ZERO_BF16, G, G, G), (8, 7, G, G, G), (8, z.ZERO_BF16, 2, G, G)):
+        with pytest.raises(z.ZeroError):
+            z.zero_sim_footprint(L, *bad)
+
+
 def test_ledger_matches_oracle_and_pages():
     for psi in (1.0, 0.774e9, 7.5e9, 70e9):
         for n in (1, 2, 8, 64):

@@ -55,6 +55,7 @@ MUTANTS = [
      "++u;"),
     ("reshard reads the destination rank's shard", "memcpy(d, (const char *)src[q] + ka * elem",
      "memcpy(d, (const char *)src[dst_rank < n_a ? dst_rank : 0] + ka * elem"),
+    ("footprint forgets the output", "    if (with_out)\n        per += 2.0;\n", ""),
     # the reduced gradient (the norm pass's reference) and the association of
     # the AdamW update that the page's code fixes
     ("reduced gradient: wrong divisor", "g_out[k] = sum / divisor;", "g_out[k] = sum / (divisor + 1.0f);"),

@@ -78,6 +78,10 @@ def test_ledger_values_printed_on_pages():
     pins.pin_ledger()
 
 
+def test_sim_footprint():
+    pins.pin_sim_footprint()
+
+
 def test_bf16_special_values():
     x = np.array([0.0, -0.0, np.inf, -np.inf, 1.0, -1.0, 3.4028235e38, 1e-45, -1e-45], np.float32)
     got = oracle.bf16(x)
