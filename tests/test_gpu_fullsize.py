@@ -1,12 +1,11 @@
 """Full workload sizes, in the launch configuration the benchmark times.
 The GPT-2-Large-sized model (774M elements, N = 8) and the 8B Llama shard
 (125M elements, N = 64) are compared with the oracle element by element over
-two steps; the clipped step at full size on sampled elements the oracle
-recomputes one by one (random positions plus the first, middle and last
-element of every unit), which is exact because the step is elementwise.  The
-norm at full size is checked through properties that hold at any size
-(agreement with a binary64 library sum of the reduced gradient it writes,
-bitwise reproducibility) and its reduced gradient on the sampled elements."""
+two steps, and so is the clipped workload (the norm pass's reduced gradient,
+its sum of squares and coefficient, and the clipped step, through the
+benchmark's sync-free chain).  A step of 2^32 + 17 elements (more than one
+dispatch) is checked on sampled elements the oracle recomputes one by one,
+which is exact because the step is elementwise."""
 import concurrent.futures as cf
 import os
 
@@ -24,7 +23,7 @@ import fsdp_sharded_optimizer_flat_amd as z  # noqa: E402
 from fsdp_sharded_optimizer_flat_amd import synth  # noqa: E402
 from fsdp_sharded_optimizer_flat_amd.workloads import WORKLOADS  # noqa: E402
 from gpu_common import (DEV, assert_same_bf16, assert_same_f32, gather_np,  # noqa: E402
-                        hyper_args, oracle_on_samples, sampled_indices, scalars, to_np)
+                        hyper_args, oracle_on_samples, scalars, to_np)
 
 G, Lc = z.ZERO_GLOBAL, z.ZERO_LOCAL
 
@@ -38,46 +37,6 @@ def _free_memory():
     yield
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
-
-
-def _run_sampled(name, steps=2, clip=None):
-    wl = WORKLOADS[name]
-    n, h = wl.n_ranks, wl.hyper
-    L = z.zero_pack(n, wl.unit_numel)
-    gidx = G if wl.grad_index == "global" else Lc
-    sidx = G if wl.rank < 0 else Lc
-    oidx = G if wl.out_index == "global" else Lc
-    ge = L.padded if gidx == G else L.shard
-    se = L.padded if sidx == G else L.shard
-    oe = L.padded if oidx == G else L.shard
-    log(f"{name}: N={n} grads {n}x{ge} bf16, state {se}, out {oe}")
-    master = torch.empty(se, dtype=torch.float32, device=DEV)
-    synth.fill_normal_(master, wl.master_std, synth.seed_of(wl.seed, synth.TAG_MASTER))
-    m, v = torch.zeros_like(master), torch.zeros_like(master)
-    out = torch.zeros(oe, dtype=torch.int16, device=DEV)
-    grads = torch.empty(n, ge, dtype=torch.bfloat16, device=DEV)
-    rng = np.random.default_rng(wl.seed)
-    idx = sampled_indices(se, L.unit_table(), sidx, rng, k=8192)
-    idx_t = torch.from_numpy(idx).to(DEV)
-    # the sampled elements' gradient / output positions (identity maps here:
-    # all-ranks GLOBAL, or one rank with every buffer LOCAL)
-    assert (gidx == sidx == oidx) or (wl.rank >= 0 and gidx == Lc and sidx == Lc and oidx == Lc)
-    master0 = gather_np(master, idx_t)
-    gsamp = []
-    for t in range(1, steps + 1):
-        for r in range(n):
-            synth.fill_grad_(grads[r], wl.grad_dist, wl.grad_scale, synth.seed_of(wl.seed, synth.TAG_GRAD, t, r))
-        gsamp.append([gather_np(grads[r], idx_t) for r in range(n)])
-        z.zero_step(L, wl.rank, list(grads), gidx, float(n), master, m, v, sidx, out, oidx,
-                    scalars(t, h, clip=1.0 if clip is None else clip))
-    torch.cuda.synchronize()
-    w, mm, vv, oo = oracle_on_samples(n, gsamp, master0, steps, h,
-                                      clips=None if clip is None else [clip] * steps)
-    assert_same_f32(gather_np(master, idx_t), w, f"{name} master")
-    assert_same_f32(gather_np(m, idx_t), mm, f"{name} m")
-    assert_same_f32(gather_np(v, idx_t), vv, f"{name} v")
-    assert_same_bf16(gather_np(out, idx_t), oo, f"{name} out")
-    log(f"{name}: {idx.size} sampled elements bit-exact after {steps} steps")
 
 
 def _run_full(name, steps=2, staged=False):
@@ -153,37 +112,82 @@ def test_llama8b_z3_shard_staged_full_size_every_element():
     _run_full("llama8b_z3", staged=True)
 
 
-def test_llama8b_z3_clipped_step_full_size_sampled():
-    # a fixed coefficient in (0, 1): the clipped arithmetic at full size; the
-    # norm -> coefficient -> step chain is checked against the oracle at a
-    # moderate size in test_gpu_parity.
-    _run_sampled("llama8b_z3_clip", clip=float(np.float32(0.4137)))
-
-
-def test_llama8b_z3_norm_full_size():
+def test_llama8b_z3_clip_full_size_every_element():
+    """The clipped workload at full size (N = 64, the 125,472,832-element
+    shard, Student-t(3) x 1e-3 gradients), two steps of the benchmark's
+    sync-free chain -- zero_gradnorm_async (writing the reduced gradient g) ->
+    zero_clip_coef_async -> zero_step_device_clip on g -- against the oracle
+    on every element: g bit for bit against orc_reduced_grad; the device's
+    binary64 sum of squares within n 2^-53 of the oracle's serial sum over its
+    own g (that sum's error bound) and within 1e-12 of a pairwise binary64 sum;
+    the device coefficient equal to the oracle's; master, m, v and the bf16
+    shard bit for bit against the oracle's clipped step on the 64 gradients
+    with the oracle's own coefficient."""
     wl = WORKLOADS["llama8b_z3_clip"]
-    n = wl.n_ranks
+    n, h, rank = wl.n_ranks, wl.hyper, wl.rank
     L = z.zero_pack(n, wl.unit_numel)
-    log(f"norm: N={n}, S={L.shard}")
-    grads = torch.empty(n, L.shard, dtype=torch.bfloat16, device=DEV)
-    for r in range(n):
-        synth.fill_grad_(grads[r], wl.grad_dist, wl.grad_scale, synth.seed_of(wl.seed, synth.TAG_GRAD, 1, r))
-    ws = torch.zeros(z.zero_gradnorm_workspace_bytes(L, 0) // 8, dtype=torch.float64, device=DEV)
-    g_out = torch.empty(L.shard, dtype=torch.float32, device=DEV)
-    s1 = z.zero_gradnorm(L, 0, list(grads), Lc, float(n), g_out, Lc, ws)
-    s2 = z.zero_gradnorm(L, 0, list(grads), Lc, float(n), None, Lc, ws)
-    assert s1 == s2, "norm not reproducible"
-    ref = float(torch.sum(g_out.double() * g_out.double()))
-    assert abs(s1 - ref) <= 1e-12 * ref, (s1, ref)
-    rng = np.random.default_rng(3)
-    idx = sampled_indices(L.shard, L.unit_table(), Lc, rng, k=8192)
-    idx_t = torch.from_numpy(idx).to(DEV)
-    gs = [np.ascontiguousarray(gather_np(grads[r], idx_t)) for r in range(n)]
-    og = oracle.reduced_grad(n, [idx.size * n], 0, gs, grad_local=True, divisor=float(n))
-    assert_same_f32(gather_np(g_out, idx_t), og, "reduced gradient at sampled elements")
-    coef = z.zero_clip_coef(s1, wl.clip_max_norm)
-    log(f"norm: sumsq={s1:.6e} norm={np.sqrt(s1):.4f} clip coef={coef:.6f}")
-    assert 0.0 < coef < 1.0, "Student-t(3) x 1e-3 gradients over 125M elements must trigger clipping"
+    E = L.shard
+    log(f"clip full compare: N={n}, S={E}")
+    master = torch.empty(E, dtype=torch.float32, device=DEV)
+    synth.fill_normal_(master, wl.master_std, synth.seed_of(wl.seed, synth.TAG_MASTER))
+    m, v = torch.zeros_like(master), torch.zeros_like(master)
+    out = torch.zeros(E, dtype=torch.int16, device=DEV)
+    grads = torch.empty(n, E, dtype=torch.bfloat16, device=DEV)
+    g_out = torch.empty(E, dtype=torch.float32, device=DEV)
+    ws = torch.zeros(z.zero_gradnorm_workspace_bytes(L, rank) // 8, dtype=torch.float64, device=DEV)
+    sumsq = torch.zeros(1, dtype=torch.float64, device=DEV)
+    coef = torch.zeros(1, dtype=torch.float32, device=DEV)
+    wh, mh, vh = to_np(master).copy(), np.zeros(E, np.float32), np.zeros(E, np.float32)
+    oh = np.zeros(E, np.uint16)
+    og = np.zeros(E, np.float32)
+    units = [(int(nu), int(loff), int(sh)) for nu, pad, sh, off, loff in L.unit_table()]
+    ha = hyper_args(h)
+    workers = min(16, os.cpu_count() or 1)
+    for t in range(1, 3):
+        for r in range(n):
+            synth.fill_grad_(grads[r], wl.grad_dist, wl.grad_scale, synth.seed_of(wl.seed, synth.TAG_GRAD, t, r))
+        z.zero_gradnorm_async(L, rank, list(grads), Lc, float(n), g_out, Lc, ws, sumsq)
+        z.zero_clip_coef_async(sumsq, wl.clip_max_norm, coef)
+        z.zero_step_device_clip(L, rank, [g_out], Lc, 1.0, master, m, v, Lc, out, Lc, scalars(t, h), coef)
+        torch.cuda.synchronize()
+        dev_sum, dev_coef = float(sumsq.item()), float(coef.item())
+        gh = [to_np(grads[r]) for r in range(n)]
+
+        def reduce_unit(u):
+            numel, a, ln = u
+            og[a:a + ln] = oracle.reduced_grad(n, [numel], rank, [g[a:a + ln] for g in gh],
+                                               grad_local=True, divisor=float(n))
+        with cf.ThreadPoolExecutor(workers) as ex:
+            list(ex.map(reduce_unit, units))
+        assert_same_f32(to_np(g_out), og, f"step {t}: reduced gradient")
+        orc_sum = oracle.sumsq(og)
+        pair = float(np.sum(og.astype(np.float64) ** 2))
+        assert abs(dev_sum - orc_sum) <= E * 2.0 ** -53 * orc_sum, (dev_sum, orc_sum)
+        assert abs(dev_sum - pair) <= 1e-12 * pair, (dev_sum, pair)
+        orc_coef = oracle.clip_coef(orc_sum, wl.clip_max_norm)
+        assert dev_coef == orc_coef, (dev_coef, orc_coef)
+        assert 0.0 < orc_coef < 1.0, "Student-t(3) x 1e-3 gradients over 125M elements must clip"
+        log(f"step {t}: sumsq device {dev_sum:.9e} oracle {orc_sum:.9e}, coef {orc_coef:.7f}")
+
+        def step_unit(u):
+            numel, a, ln = u
+            oracle.zero_step_rank(n, [numel], rank, [g[a:a + ln] for g in gh], grad_local=True,
+                                  divisor=float(n), clip=orc_coef, master=wh[a:a + ln], m=mh[a:a + ln],
+                                  v=vh[a:a + ln], state_global=False, out=oh[a:a + ln],
+                                  out_gather=False, t=t, **ha)
+        with cf.ThreadPoolExecutor(workers) as ex:
+            list(ex.map(step_unit, units))
+        del gh
+        # the norm is reproducible and independent of writing g
+        z.zero_gradnorm_async(L, rank, list(grads), Lc, float(n), None, Lc, ws, sumsq)
+        torch.cuda.synchronize()
+        assert float(sumsq.item()) == dev_sum
+        log(f"clip: step {t} done on the GPU and in the oracle")
+    assert_same_f32(to_np(master), wh, "clip master")
+    assert_same_f32(to_np(m), mh, "clip m")
+    assert_same_f32(to_np(v), vh, "clip v")
+    assert_same_bf16(to_np(out), oh, "clip out")
+    log(f"clip: all {E} elements bit-exact after 2 steps")
 
 
 def test_step_beyond_one_launch():
