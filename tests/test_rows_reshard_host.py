@@ -128,8 +128,9 @@ def test_reshard_argument_errors():
     with pytest.raises(z.ZeroError) as e:              # element counts differ
         z.zero_reshard_host(A, src, z.zero_pack(2, [101]), 0, np.zeros(51, np.float32))
     assert e.value.status == z.ZERO_EINVAL
-    with pytest.raises(z.ZeroError) as e:              # dst overlaps a source
-        z.zero_reshard_host(A, src, B, 0, src[1][:B.shard])
+    big = np.zeros(A.shard + B.shard, np.float32)       # dst overlaps a source
+    with pytest.raises(z.ZeroError) as e:
+        z.zero_reshard_host(A, [src[0], big[:A.shard], src[2], src[3]], B, 0, big[10:10 + B.shard])
     assert e.value.status == z.ZERO_EINVAL
     lib = z.raw_library()
     arr = (C.c_void_p * 4)(*[s.ctypes.data for s in src])
