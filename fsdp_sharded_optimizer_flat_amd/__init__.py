@@ -112,6 +112,8 @@ _zero_step = _sig("zero_step", i32, vp, i32, vp, i32, i32, i32, f32, vp, vp, vp,
                   C.POINTER(ZeroAdamwScalars), vp)
 _zero_step_staged = _sig("zero_step_staged", i32, vp, i32, vp, i32, i32, i32, f32, vp, vp, vp, i32, vp,
                          i32, C.POINTER(ZeroAdamwScalars), vp, sz, vp)
+_zero_step_units = _sig("zero_step_units", i32, vp, i32, i32, i32, vp, i32, i32, i32, f32, vp, vp, vp,
+                        i32, vp, i32, C.POINTER(ZeroAdamwScalars), vp, sz, vp)
 _zero_step_staged_workspace_bytes = _sig("zero_step_staged_workspace_bytes", i32, vp, i32, i32,
                                          C.POINTER(sz))
 _zero_step_device_clip = _sig("zero_step_device_clip", i32, vp, i32, vp, i32, i32, i32, f32, vp, vp,
@@ -148,7 +150,7 @@ _zero_abi_version = _sig("zero_abi_version", i32)
 EXPORTED = ["zero_layout_bytes", "zero_pack", "zero_pack_rows", "zero_reshard",
             "zero_reshard_host", "zero_reshard_traffic", "zero_global_index", "zero_owner", "zero_pack_copy",
             "zero_unpack_copy", "zero_adamw_scalars_for", "zero_adamw_scalars_next", "zero_step",
-            "zero_step_staged", "zero_step_staged_workspace_bytes",
+            "zero_step_staged", "zero_step_staged_workspace_bytes", "zero_step_units",
             "zero_step_host", "zero_offload_step", "zero_step_device_clip",
             "zero_clip_coef_async", "zero_clip_coef_ranks", "zero_clip_coef_ranks_async",
             "zero_overlap",
@@ -518,6 +520,40 @@ def zero_step_staged(layout: Layout, rank: int, grads, grad_index: int, divisor:
                              _f32_ptr(exp_avg_sq, "exp_avg_sq"), state_index,
                              _bf16_ptr(out, "out") if out is not None else None, out_index,
                              C.byref(scalars), wp, wb, _stream(stream)), "zero_step_staged")
+
+
+def unit_range_extent(layout: Layout, unit_begin: int, unit_end: int, index: int) -> int:
+    """Elements of a gradient bucket holding units [unit_begin, unit_end) in an
+    index space (padded sizes for GLOBAL, shard sizes for LOCAL)."""
+    col = 1 if index == ZERO_GLOBAL else 2
+    t = layout.unit_table()
+    return int(t[unit_begin:unit_end, col].sum()) if unit_end > unit_begin else 0
+
+
+def zero_step_units(layout: Layout, rank: int, unit_begin: int, unit_end: int, grads,
+                    grad_index: int, divisor: float, master, exp_avg, exp_avg_sq,
+                    state_index: int, out, out_index: int, scalars: ZeroAdamwScalars,
+                    workspace=None, stream=None, *, grad_ptrs=None):
+    """Enqueue the step of units [unit_begin, unit_end) from gradient buckets
+    that hold only those units (see zero.h); state and out are the whole
+    buffers.  ``workspace`` (device tensor) selects the staged path above 32
+    gradients."""
+    arr, gdt = grad_ptrs if grad_ptrs is not None else _grad_ptrs(grads)
+    if not (0 <= unit_begin <= unit_end <= layout.n_units):
+        raise ValueError("unit range outside the layout")
+    ge = unit_range_extent(layout, unit_begin, unit_end, grad_index)
+    if grad_ptrs is None:
+        for g in grads:
+            _need(g, ge, "grad")
+    _need_prepared(grad_ptrs, ge, "grad")
+    _need_step(layout, (), grad_index, master, exp_avg, exp_avg_sq, state_index, out, out_index)
+    wp = _dev_ptr(workspace, "workspace") if workspace is not None else None
+    wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_zero_step_units(layout.ptr, rank, unit_begin, unit_end, C.addressof(arr), len(arr), gdt,
+                            grad_index, divisor, _f32_ptr(master, "master"),
+                            _f32_ptr(exp_avg, "exp_avg"), _f32_ptr(exp_avg_sq, "exp_avg_sq"),
+                            state_index, _bf16_ptr(out, "out") if out is not None else None,
+                            out_index, C.byref(scalars), wp, wb, _stream(stream)), "zero_step_units")
 
 
 def zero_step_staged_workspace_bytes(layout: Layout, rank: int, n_grads: int) -> int:

@@ -43,9 +43,11 @@ bool overlap(Range a, Range b)
 }
 
 // The checks zero_step and zero_gradnorm share: selection, gradients and
-// divisor.
+// divisor.  empty_grads: the gradient buffers hold no element (an empty unit
+// range), so their pointers may be NULL.
 zero_status check_grads(const zero_layout *L, int32_t rank, const void *const *grads,
-                        int32_t n_grads, int32_t grad_dtype, int32_t grad_index, float divisor)
+                        int32_t n_grads, int32_t grad_dtype, int32_t grad_index, float divisor,
+                        bool empty_grads = false)
 {
     if (!layout_ok(L) || rank >= L->n_ranks || !dtype_ok(grad_dtype) || !index_ok(grad_index))
         return ZERO_EINVAL;
@@ -56,7 +58,7 @@ zero_status check_grads(const zero_layout *L, int32_t rank, const void *const *g
     if (!(divisor > 0.0f) || !std::isfinite(divisor))
         return ZERO_EINVAL;
     for (int q = 0; q < n_grads; ++q) {
-        if (!grads[q])
+        if (!grads[q] && !empty_grads)
             return ZERO_EINVAL;
         if (!aligned(grads[q], (size_t)dsize(grad_dtype)))
             return ZERO_EALIGN;
@@ -247,7 +249,20 @@ zero_status zero::validate_step(const zero_layout *L, int32_t rank, const void *
                                const float *exp_avg_sq, int32_t state_index, const uint16_t *out,
                                int32_t out_index, const zero_adamw_scalars *sc)
 {
-    zero_status st = check_grads(L, rank, grads, n_grads, grad_dtype, grad_index, divisor);
+    return validate_step_ext(L, rank, grads, n_grads, grad_dtype, grad_index, divisor, master,
+                             exp_avg, exp_avg_sq, state_index, out, out_index, sc,
+                             layout_ok(L) && index_ok(grad_index) ? extent(L, grad_index) : 0);
+}
+
+zero_status zero::validate_step_ext(const zero_layout *L, int32_t rank, const void *const *grads,
+                                   int32_t n_grads, int32_t grad_dtype, int32_t grad_index,
+                                   float divisor, const float *master, const float *exp_avg,
+                                   const float *exp_avg_sq, int32_t state_index,
+                                   const uint16_t *out, int32_t out_index,
+                                   const zero_adamw_scalars *sc, int64_t grad_extent)
+{
+    zero_status st = check_grads(L, rank, grads, n_grads, grad_dtype, grad_index, divisor,
+                                 grad_extent == 0);
     if (st != ZERO_OK)
         return st;
     if (!index_ok(state_index) || !index_ok(out_index) || !master || !exp_avg || !exp_avg_sq ||
@@ -263,8 +278,7 @@ zero_status zero::validate_step(const zero_layout *L, int32_t rank, const void *
     // Aliasing: gradients are read-only and may alias each other; nothing
     // written may overlap a gradient or another written buffer.
     const int gsize = dsize(grad_dtype);
-    const int64_t ge = extent(L, grad_index), se = extent(L, state_index),
-                  oe = extent(L, out_index);
+    const int64_t ge = grad_extent, se = extent(L, state_index), oe = extent(L, out_index);
     const Range w = range_of(master, se, 4), m = range_of(exp_avg, se, 4),
                 v = range_of(exp_avg_sq, se, 4),
                 o = out ? range_of(out, oe, 2) : Range{0, 0};
@@ -279,17 +293,16 @@ zero_status zero::validate_step(const zero_layout *L, int32_t rank, const void *
     return ZERO_OK;
 }
 
-static zero_status step_impl(const zero_layout *L, int32_t rank, const void *const *grads,
-                                 int32_t n_grads, int32_t grad_dtype, int32_t grad_index,
-                                 float divisor, float *master, float *exp_avg, float *exp_avg_sq,
-                                 int32_t state_index, uint16_t *out, int32_t out_index,
-                                 const zero_adamw_scalars *sc, const float *clip_dev,
-                                 void *stream)
+// Units [u0, u1) of the selection; from_range: the gradient buffers hold only
+// those units (offsets from the range's start), of grad_extent elements.
+// Arguments already validated.
+static zero_status step_launch(const zero_layout *L, int32_t rank, const void *const *grads,
+                               int32_t n_grads, int32_t grad_dtype, int32_t grad_index,
+                               float divisor, float *master, float *exp_avg, float *exp_avg_sq,
+                               int32_t state_index, uint16_t *out, int32_t out_index,
+                               const zero_adamw_scalars *sc, const float *clip_dev, void *stream,
+                               int32_t u0, int32_t u1, bool from_range)
 {
-    zero_status st = validate_step(L, rank, grads, n_grads, grad_dtype, grad_index, divisor,
-                                   master, exp_avg, exp_avg_sq, state_index, out, out_index, sc);
-    if (st != ZERO_OK)
-        return st;
     const int gsize = dsize(grad_dtype);
     StepConsts c = make_step_consts(sc, divisor);
     c.clip_dev = clip_dev;
@@ -308,8 +321,8 @@ static zero_status step_impl(const zero_layout *L, int32_t rank, const void *con
     rq.state_ptrs[2] = exp_avg_sq;
     rq.n_state_ptrs = 3;
     rq.out_ptr = out;
-    const std::vector<Piece> pieces =
-        build_pieces(build_segments(L, rank, grad_index, state_index, out_index), rq);
+    const std::vector<Piece> pieces = build_pieces(
+        build_segments(L, rank, grad_index, state_index, out_index, u0, u1, from_range), rq);
     for (const Piece &pc : pieces) {
         const std::vector<const void *> gp = offset_grads(grads, n_grads, pc.g_off, gsize);
         const int err = launch_step_piece(pc, gp.data(), n_grads, grad_dtype, master + pc.s_off,
@@ -319,6 +332,20 @@ static zero_status step_impl(const zero_layout *L, int32_t rank, const void *con
             return hip_fail(err, "zero_step launch");
     }
     return ZERO_OK;
+}
+
+static zero_status step_impl(const zero_layout *L, int32_t rank, const void *const *grads,
+                             int32_t n_grads, int32_t grad_dtype, int32_t grad_index,
+                             float divisor, float *master, float *exp_avg, float *exp_avg_sq,
+                             int32_t state_index, uint16_t *out, int32_t out_index,
+                             const zero_adamw_scalars *sc, const float *clip_dev, void *stream)
+{
+    zero_status st = validate_step(L, rank, grads, n_grads, grad_dtype, grad_index, divisor,
+                                   master, exp_avg, exp_avg_sq, state_index, out, out_index, sc);
+    if (st != ZERO_OK)
+        return st;
+    return step_launch(L, rank, grads, n_grads, grad_dtype, grad_index, divisor, master, exp_avg,
+                       exp_avg_sq, state_index, out, out_index, sc, clip_dev, stream, 0, -1, false);
 }
 
 extern "C" zero_status zero_step(const zero_layout *L, int32_t rank, const void *const *grads,
@@ -403,21 +430,17 @@ extern "C" zero_status zero_step_staged_workspace_bytes(const zero_layout *L, in
     return ZERO_OK;
 }
 
-extern "C" zero_status zero_step_staged(const zero_layout *L, int32_t rank,
-                                        const void *const *grads, int32_t n_grads,
-                                        int32_t grad_dtype, int32_t grad_index, float divisor,
-                                        float *master, float *exp_avg, float *exp_avg_sq,
-                                        int32_t state_index, uint16_t *out, int32_t out_index,
-                                        const zero_adamw_scalars *sc, void *workspace,
-                                        size_t workspace_bytes, void *stream)
+// The staged step over units [u0, u1) (from_range: gradient buckets of
+// grad_extent elements holding only those units); step arguments validated,
+// n_grads >= kStageMinRanks.
+static zero_status staged_launch(const zero_layout *L, int32_t rank, const void *const *grads,
+                                 int32_t n_grads, int32_t grad_dtype, int32_t grad_index,
+                                 float divisor, float *master, float *exp_avg, float *exp_avg_sq,
+                                 int32_t state_index, uint16_t *out, int32_t out_index,
+                                 const zero_adamw_scalars *sc, void *workspace,
+                                 size_t workspace_bytes, void *stream, int32_t u0, int32_t u1,
+                                 bool from_range, int64_t grad_extent)
 {
-    zero_status st = validate_step(L, rank, grads, n_grads, grad_dtype, grad_index, divisor,
-                                   master, exp_avg, exp_avg_sq, state_index, out, out_index, sc);
-    if (st != ZERO_OK)
-        return st;
-    if (n_grads < kStageMinRanks)  // few streams: the fused step is the faster one
-        return step_impl(L, rank, grads, n_grads, grad_dtype, grad_index, divisor, master,
-                         exp_avg, exp_avg_sq, state_index, out, out_index, sc, nullptr, stream);
     if (!workspace)
         return ZERO_EINVAL;
     if (!aligned(workspace, 16))
@@ -437,7 +460,7 @@ extern "C" zero_status zero_step_staged(const zero_layout *L, int32_t rank,
         overlap(ws, range_of(exp_avg_sq, se, 4)) || (out && overlap(ws, range_of(out, oe, 2))))
         return ZERO_EINVAL;
     for (int q = 0; q < n_grads; ++q)
-        if (overlap(ws, range_of(grads[q], extent(L, grad_index), gsize)))
+        if (overlap(ws, range_of(grads[q], grad_extent, gsize)))
             return ZERO_EINVAL;
 
     float *g = static_cast<float *>(workspace);
@@ -465,7 +488,8 @@ extern "C" zero_status zero_step_staged(const zero_layout *L, int32_t rank,
     ra.grad_dtype = grad_dtype;
     ra.state_ptrs[0] = g;
     ra.n_state_ptrs = 1;
-    for (const Segment &sg : build_segments(L, rank, grad_index, state_index, out_index)) {
+    for (const Segment &sg :
+         build_segments(L, rank, grad_index, state_index, out_index, u0, u1, from_range)) {
         for (int64_t off = 0; off < sg.len; off += chunk) {
             const int64_t cl = sg.len - off < chunk ? sg.len - off : chunk;
             const Segment ga{sg.g_off + off, 0, 0, cl};
@@ -487,6 +511,56 @@ extern "C" zero_status zero_step_staged(const zero_layout *L, int32_t rank,
         }
     }
     return ZERO_OK;
+}
+
+extern "C" zero_status zero_step_staged(const zero_layout *L, int32_t rank,
+                                        const void *const *grads, int32_t n_grads,
+                                        int32_t grad_dtype, int32_t grad_index, float divisor,
+                                        float *master, float *exp_avg, float *exp_avg_sq,
+                                        int32_t state_index, uint16_t *out, int32_t out_index,
+                                        const zero_adamw_scalars *sc, void *workspace,
+                                        size_t workspace_bytes, void *stream)
+{
+    zero_status st = validate_step(L, rank, grads, n_grads, grad_dtype, grad_index, divisor,
+                                   master, exp_avg, exp_avg_sq, state_index, out, out_index, sc);
+    if (st != ZERO_OK)
+        return st;
+    if (n_grads < kStageMinRanks)  // few streams: the fused step is the faster one
+        return step_launch(L, rank, grads, n_grads, grad_dtype, grad_index, divisor, master,
+                           exp_avg, exp_avg_sq, state_index, out, out_index, sc, nullptr, stream,
+                           0, -1, false);
+    return staged_launch(L, rank, grads, n_grads, grad_dtype, grad_index, divisor, master,
+                         exp_avg, exp_avg_sq, state_index, out, out_index, sc, workspace,
+                         workspace_bytes, stream, 0, -1, false, extent(L, grad_index));
+}
+
+extern "C" zero_status zero_step_units(const zero_layout *L, int32_t rank, int32_t unit_begin,
+                                       int32_t unit_end, const void *const *grads,
+                                       int32_t n_grads, int32_t grad_dtype, int32_t grad_index,
+                                       float divisor, float *master, float *exp_avg,
+                                       float *exp_avg_sq, int32_t state_index, uint16_t *out,
+                                       int32_t out_index, const zero_adamw_scalars *sc,
+                                       void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!layout_ok(L) || !index_ok(grad_index) || unit_begin < 0 || unit_end < unit_begin ||
+        unit_end > L->n_units)
+        return ZERO_EINVAL;
+    // the buckets hold the range's units in the gradient's index space
+    const int64_t ge = rank < 0 && grad_index == ZERO_LOCAL
+                           ? 0
+                           : unit_start(L, unit_end, grad_index) - unit_start(L, unit_begin, grad_index);
+    zero_status st = validate_step_ext(L, rank, grads, n_grads, grad_dtype, grad_index, divisor,
+                                       master, exp_avg, exp_avg_sq, state_index, out, out_index,
+                                       sc, ge);
+    if (st != ZERO_OK)
+        return st;
+    if (workspace && n_grads >= kStageMinRanks)
+        return staged_launch(L, rank, grads, n_grads, grad_dtype, grad_index, divisor, master,
+                             exp_avg, exp_avg_sq, state_index, out, out_index, sc, workspace,
+                             workspace_bytes, stream, unit_begin, unit_end, true, ge);
+    return step_launch(L, rank, grads, n_grads, grad_dtype, grad_index, divisor, master,
+                       exp_avg, exp_avg_sq, state_index, out, out_index, sc, nullptr, stream,
+                       unit_begin, unit_end, true);
 }
 
 extern "C" zero_status zero_gradnorm_workspace_bytes(const zero_layout *L, int32_t rank,

@@ -38,23 +38,39 @@ bool layout_ok(const zero_layout *L)
     return off == L->padded && loff == L->shard && numel == L->numel;
 }
 
+int64_t unit_start(const zero_layout *L, int32_t u, int32_t index)
+{
+    if (u >= L->n_units)
+        return index == ZERO_GLOBAL ? L->padded : L->shard;
+    return index == ZERO_GLOBAL ? L->unit[u].offset : L->unit[u].local_offset;
+}
+
 std::vector<Segment> build_segments(const zero_layout *L, int32_t rank, int32_t grad_index,
-                                    int32_t state_index, int32_t out_index)
+                                    int32_t state_index, int32_t out_index, int32_t u0,
+                                    int32_t u1, bool grads_from_range)
 {
     std::vector<Segment> segs;
-    if (rank < 0) {  // every rank's slices: the whole flat buffer, identity map
-        if (L->padded > 0)
-            segs.push_back({0, 0, 0, L->padded});
+    if (u1 < 0 || u1 > L->n_units)
+        u1 = L->n_units;
+    if (u0 < 0)
+        u0 = 0;
+    if (u0 >= u1)
+        return segs;
+    const int64_t gbase = grads_from_range ? unit_start(L, u0, grad_index) : 0;
+    if (rank < 0) {  // every rank's slices of the units: one identity-mapped run
+        const int64_t a = unit_start(L, u0, ZERO_GLOBAL), b = unit_start(L, u1, ZERO_GLOBAL);
+        if (b > a)
+            segs.push_back({a - gbase, a, a, b - a});
         return segs;
     }
-    for (int32_t u = 0; u < L->n_units; ++u) {
+    for (int32_t u = u0; u < u1; ++u) {
         const zero_unit &x = L->unit[u];
         if (x.shard == 0)
             continue;
         const int64_t j0 = x.offset + (int64_t)rank * x.shard;  // global start
         const int64_t k0 = x.local_offset;                      // local start
         Segment s;
-        s.g_off = grad_index == ZERO_GLOBAL ? j0 : k0;
+        s.g_off = (grad_index == ZERO_GLOBAL ? j0 : k0) - gbase;
         s.s_off = state_index == ZERO_GLOBAL ? j0 : k0;
         s.o_off = out_index == ZERO_GLOBAL ? j0 : k0;
         s.len = x.shard;

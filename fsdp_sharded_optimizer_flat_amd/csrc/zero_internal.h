@@ -60,9 +60,18 @@ struct Request {
 };
 
 // Segments of the elements a (layout, rank, index spaces) selection touches,
-// with contiguous neighbours merged.
+// with contiguous neighbours merged.  Units [u0, u1) only (u1 < 0: to the
+// last unit); with grads_from_range the gradient offsets count from the
+// range's first element in the gradient's index space (offset[u0] for
+// GLOBAL, local_offset[u0] for LOCAL): gradient buckets that hold only the
+// range's units.
 std::vector<Segment> build_segments(const zero_layout *L, int32_t rank, int32_t grad_index,
-                                    int32_t state_index, int32_t out_index);
+                                    int32_t state_index, int32_t out_index, int32_t u0 = 0,
+                                    int32_t u1 = -1, bool grads_from_range = false);
+
+// Start of unit u (u == n_units: the end) in an index space: offset_u for
+// GLOBAL, local_offset_u for LOCAL.
+int64_t unit_start(const zero_layout *L, int32_t u, int32_t index);
 
 // Split segments into vector bodies and scalar heads / tails, given the
 // actual buffer addresses (every gradient, every fp32 state buffer, output).
@@ -134,6 +143,14 @@ zero_status validate_step(const zero_layout *L, int32_t rank, const void *const 
                           const float *master, const float *exp_avg, const float *exp_avg_sq,
                           int32_t state_index, const uint16_t *out, int32_t out_index,
                           const zero_adamw_scalars *sc);
+// The same with the gradient buffers' extent given (elements): a step over a
+// unit range reads gradient buckets that hold only the range.
+zero_status validate_step_ext(const zero_layout *L, int32_t rank, const void *const *grads,
+                              int32_t n_grads, int32_t grad_dtype, int32_t grad_index,
+                              float divisor, const float *master, const float *exp_avg,
+                              const float *exp_avg_sq, int32_t state_index, const uint16_t *out,
+                              int32_t out_index, const zero_adamw_scalars *sc,
+                              int64_t grad_extent);
 
 // Launchers (defined in the .hip files).  Pointers are already offset to the
 // piece's first element.  Return a hipError_t value.

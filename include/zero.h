@@ -342,6 +342,32 @@ zero_status zero_step_staged(const zero_layout *layout, int32_t rank,
                              const zero_adamw_scalars *sc, void *workspace, size_t workspace_bytes,
                              void *stream);
 
+/* The step of a range of units, from gradient buckets -- [p1 How it works]:
+ * each unit's gradients are reduce-scattered as soon as backward has produced
+ * them, and the unit's shards can be stepped then; [p3 section 4]: with
+ * bucketed reduce-scatter each bucket is freed once reduced, so gradients are
+ * transient.  Steps units [unit_begin, unit_end) of the selection (rank < 0:
+ * every rank's slices of those units; rank r: rank r's slices) with the same
+ * arithmetic as zero_step.  grads[q] is a bucket holding only those units in
+ * the grad_index space: element j of the layout (ZERO_GLOBAL) at bucket index
+ * j - offset_{unit_begin}, local index k (ZERO_LOCAL) at k -
+ * local_offset_{unit_begin}; a bucket spans offset_{unit_end} -
+ * offset_{unit_begin} (resp. local_offset) elements, and may be NULL when
+ * that is 0.  master, exp_avg,
+ * exp_avg_sq and out are the whole buffers, indexed as in zero_step.  Steps of
+ * disjoint unit ranges that together cover every unit, in any order and on any
+ * streams, give the bits of one zero_step call, so a caller can step unit k
+ * on a side stream while backward still writes the buckets of the next units.
+ * workspace: as zero_step_staged, used when n_grads > 32 (NULL: the fused
+ * step at any N).  Async on `stream`.  Errors as zero_step / zero_step_staged,
+ * plus EINVAL for a unit range outside 0 <= unit_begin <= unit_end <= U. */
+zero_status zero_step_units(const zero_layout *layout, int32_t rank, int32_t unit_begin,
+                            int32_t unit_end, const void *const *grads, int32_t n_grads,
+                            int32_t grad_dtype, int32_t grad_index, float divisor,
+                            float *master, float *exp_avg, float *exp_avg_sq, int32_t state_index,
+                            uint16_t *out, int32_t out_index, const zero_adamw_scalars *sc,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
 /* ------------------------------------------------------------------------
  * The step on host cores, for ZeRO-Offload -- [p4 section 6]: the optimizer
  * state and the fp32 step live in CPU memory; gradients come down from the

@@ -287,6 +287,20 @@ static void check_device_validation(void)
     uint16_t *o = (uint16_t *)(base + 0x400000);
     const int G = ZERO_GLOBAL, Lc = ZERO_LOCAL;
     CHECK(zero_step(L, -1, NULL, 8, ZERO_BF16, G, 8.0f, w, m, v, G, o, G, &sc, NULL) == ZERO_EINVAL);
+    /* unit ranges: outside the layout refused; an empty range (NULL buckets) is a no-op */
+    CHECK(zero_step_units(L, -1, 1, 0, g, 8, ZERO_BF16, G, 8.0f, w, m, v, G, o, G, &sc, NULL, 0,
+                          NULL) == ZERO_EINVAL);
+    CHECK(zero_step_units(L, -1, 0, 3, g, 8, ZERO_BF16, G, 8.0f, w, m, v, G, o, G, &sc, NULL, 0,
+                          NULL) == ZERO_EINVAL);
+    CHECK(zero_step_units(L, -1, -1, 1, g, 8, ZERO_BF16, G, 8.0f, w, m, v, G, o, G, &sc, NULL, 0,
+                          NULL) == ZERO_EINVAL);
+    {
+        const void *none[8] = {0};
+        CHECK(zero_step_units(L, 3, 1, 1, none, 8, ZERO_BF16, Lc, 8.0f, w, m, v, Lc, o, Lc, &sc,
+                              NULL, 0, NULL) == ZERO_OK);
+        CHECK(zero_step_units(L, 3, 0, 1, none, 8, ZERO_BF16, Lc, 8.0f, w, m, v, Lc, o, Lc, &sc,
+                              NULL, 0, NULL) == ZERO_EINVAL);
+    }
     CHECK(zero_step(L, -1, g, 0, ZERO_BF16, G, 8.0f, w, m, v, G, o, G, &sc, NULL) == ZERO_ERANGE);
     CHECK(zero_step(L, -1, g, 8, 7, G, 8.0f, w, m, v, G, o, G, &sc, NULL) == ZERO_EINVAL);
     CHECK(zero_step(L, -1, g, 8, ZERO_BF16, Lc, 8.0f, w, m, v, G, o, G, &sc, NULL) == ZERO_EINVAL);
