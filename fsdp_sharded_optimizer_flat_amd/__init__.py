@@ -32,6 +32,7 @@ _lib = C.CDLL(LIB_PATH)
 
 # -- constants mirrored from zero.h -------------------------------------------
 ZERO_OK, ZERO_EINVAL, ZERO_ERANGE, ZERO_EALIGN, ZERO_ENOSPC, ZERO_EHIP = 0, -1, -2, -3, -4, -5
+ZERO_EIO, ZERO_ECORRUPT = -6, -7
 ZERO_F32, ZERO_BF16 = 0, 1
 ZERO_GLOBAL, ZERO_LOCAL = 0, 1
 ZERO_MAX_RANKS = 256
@@ -81,6 +82,14 @@ class ZeroLedgerOut(C.Structure):
 class ZeroFootprintOut(C.Structure):
     _fields_ = [("grads_bytes", f64), ("state_bytes", f64), ("out_bytes", f64), ("g_bytes", f64),
                 ("total_bytes", f64)]
+
+    def as_dict(self):
+        return {k: getattr(self, k) for k, _ in self._fields_}
+
+
+class ZeroCkptInfo(C.Structure):
+    _fields_ = [("format", i32), ("abi", i32), ("n_ranks", i32), ("n_units", i32), ("rank", i32),
+                ("step", i32), ("numel", i64), ("shard", i64)]
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}
@@ -143,6 +152,10 @@ _zero_step_traffic = _sig("zero_step_traffic", i32, vp, i32, i32, i32, i32, C.PO
                           C.POINTER(i64))
 _zero_gradnorm_traffic = _sig("zero_gradnorm_traffic", i32, vp, i32, i32, i32, i32,
                               C.POINTER(f64), C.POINTER(i64))
+_zero_ckpt_save = _sig("zero_ckpt_save", i32, C.c_char_p, vp, i32, i32, vp, vp, vp)
+_zero_ckpt_inspect = _sig("zero_ckpt_inspect", i32, C.c_char_p, i32, C.POINTER(ZeroCkptInfo), vp, sz,
+                          C.POINTER(sz))
+_zero_ckpt_load = _sig("zero_ckpt_load", i32, vp, i32, vp, i32, i32, C.POINTER(i32), vp, vp, vp)
 _zero_strerror = _sig("zero_strerror", C.c_char_p, i32)
 _zero_last_hip_error = _sig("zero_last_hip_error", C.c_char_p)
 _zero_abi_version = _sig("zero_abi_version", i32)
@@ -157,7 +170,7 @@ EXPORTED = ["zero_layout_bytes", "zero_pack", "zero_pack_rows", "zero_reshard",
             "zero_gradnorm_workspace_bytes", "zero_gradnorm", "zero_gradnorm_async",
             "zero_clip_coef", "zero_ledger", "zero_sim_footprint",
             "zero_gather_buffer_bytes", "zero_arena_plan", "zero_step_traffic",
-            "zero_gradnorm_traffic",
+            "zero_gradnorm_traffic", "zero_ckpt_save", "zero_ckpt_inspect", "zero_ckpt_load",
             "zero_strerror", "zero_last_hip_error", "zero_abi_version"]
 
 
@@ -799,6 +812,54 @@ def zero_gradnorm_traffic(layout: Layout, rank: int, n_grads: int, grad_dtype: i
     _check(_zero_gradnorm_traffic(layout.ptr, rank, n_grads, grad_dtype, int(with_g_out),
                                   C.byref(b), C.byref(e)), "zero_gradnorm_traffic")
     return b.value, e.value
+
+
+# -- sharded checkpoint ---------------------------------------------------------------------
+
+def _host_f32(a, what: str, n: int):
+    """A C-contiguous float32 host array of at least n elements for a checkpoint
+    call: numpy arrays and CPU tensors as they are, device tensors copied to
+    host memory first.  Returns (keep-alive object, address)."""
+    torch = _torch()
+    if isinstance(a, torch.Tensor) and a.is_cuda:
+        if a.dtype != torch.float32:
+            raise TypeError(f"{what} must be float32")
+        a = a.detach().contiguous().cpu()
+    _need(a, n, what)
+    return a, _host_ptr(a, what, "f32")[0]
+
+
+def zero_ckpt_save(path: str, layout: Layout, rank: int, step: int, master, exp_avg, exp_avg_sq):
+    """Write rank ``rank``'s shard of the optimizer state (host or device
+    float32 arrays of layout.shard elements) to ``path``."""
+    keep = [_host_f32(a, w, layout.shard) for a, w in ((master, "master"), (exp_avg, "exp_avg"),
+                                                        (exp_avg_sq, "exp_avg_sq"))]
+    _check(_zero_ckpt_save(os.fsencode(path), layout.ptr, rank, step, *[p for _, p in keep]),
+           "zero_ckpt_save")
+
+
+def zero_ckpt_inspect(path: str, verify: bool = True):
+    """(info dict, saved Layout) of one shard file."""
+    info, need = ZeroCkptInfo(), sz()
+    _check(_zero_ckpt_inspect(os.fsencode(path), int(verify), C.byref(info), None, 0, C.byref(need)),
+           "zero_ckpt_inspect")
+    buf = (C.c_char * need.value)()
+    _check(_zero_ckpt_inspect(os.fsencode(path), 0, C.byref(info), C.addressof(buf), need.value, None),
+           "zero_ckpt_inspect")
+    return info.as_dict(), Layout(buf)
+
+
+def zero_ckpt_load(paths, layout: Layout, rank: int, verify: bool = True):
+    """Rank ``rank``'s shard of ``layout`` from a checkpoint's shard files
+    (paths[q] = rank q's), resharded at load time.  Returns (step, master,
+    exp_avg, exp_avg_sq) as float32 numpy arrays of layout.shard elements."""
+    enc = [os.fsencode(p) for p in paths]
+    arr = (C.c_char_p * max(len(enc), 1))(*enc)
+    out = [np.zeros(layout.shard, np.float32) for _ in range(3)]
+    step = i32()
+    _check(_zero_ckpt_load(C.addressof(arr), len(enc), layout.ptr, rank, int(verify), C.byref(step),
+                           *[o.ctypes.data for o in out]), "zero_ckpt_load")
+    return (step.value, *out)
 
 
 def zero_strerror(status: int) -> str:

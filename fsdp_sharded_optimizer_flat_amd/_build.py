@@ -28,8 +28,9 @@ SOURCES = ["layout.cpp", "scalars.cpp", "ledger.cpp", "capi.cpp", "offload.cpp",
            "step_kernels.hip", "norm_kernels.hip", "stage_kernels.hip", "pack_kernels.hip",
            "reshard_kernels.hip"]
 # Host-only C++ built with g++: the offload step's AVX2 code (no FMA, no
-# fast-math, so every operation rounds once, as on the GPU).
-HOST_SOURCES = ["host_step.cpp"]
+# fast-math, so every operation rounds once, as on the GPU) and the
+# checkpoint files (the SSE4.2 crc32 instruction, which -mavx2 includes).
+HOST_SOURCES = ["host_step.cpp", "checkpoint.cpp"]
 HOST_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-mavx2", "-mno-fma", "-ffp-contract=off",
               "-fno-fast-math", "-pthread", "-Wall"]
 

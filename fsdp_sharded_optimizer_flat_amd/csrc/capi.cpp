@@ -839,6 +839,8 @@ extern "C" const char *zero_strerror(zero_status s)
     case ZERO_EALIGN: return "pointer not aligned to its element size";
     case ZERO_ENOSPC: return "caller buffer too small";
     case ZERO_EHIP: return "HIP runtime error";
+    case ZERO_EIO: return "checkpoint file could not be opened, read or written";
+    case ZERO_ECORRUPT: return "not a valid checkpoint shard (magic, version, size, checksum or mismatched shards)";
     default: return "unknown status";
     }
 }

@@ -55,6 +55,9 @@ typedef int32_t zero_status;
 #define ZERO_EALIGN (-3)  /* a pointer is not aligned to its element size */
 #define ZERO_ENOSPC (-4)  /* a caller-provided buffer is too small */
 #define ZERO_EHIP (-5)    /* a HIP runtime call or kernel launch failed; see zero_last_hip_error() */
+#define ZERO_EIO (-6)     /* a checkpoint file could not be opened, read or written */
+#define ZERO_ECORRUPT (-7) /* not a valid checkpoint shard: bad magic or version, wrong size,
+                              failed checksum, or shards of different checkpoints */
 
 #define ZERO_MAX_RANKS 256   /* largest N accepted by zero_step / zero_gradnorm */
 #define ZERO_MAX_UNITS (1 << 20)
@@ -488,6 +491,58 @@ zero_status zero_clip_coef_ranks(const double *rank_sums, int32_t n_ranks, doubl
 zero_status zero_clip_coef_ranks_async(const double *rank_sums_dev, int32_t n_ranks,
                                        double max_norm, float *coef_dev, double *total_dev,
                                        void *stream);
+
+/* ------------------------------------------------------------------------
+ * Sharded checkpoint -- [p1 Implementation notes]: each rank writes its own
+ * shard of the checkpoint, and a checkpoint saved at one N is resharded to a
+ * different N when it is loaded; [p4 section 5, FSDP1 vs FSDP2]: the state
+ * carries over between the flat and the per-parameter dim-0 layouts.
+ *
+ * One file per rank holds that rank's fp32 master, exp_avg and exp_avg_sq
+ * shards (layout->shard elements each, bit for bit), the step count and the
+ * layout's unit table (numel and granule per unit, N), after a 64-byte header
+ * (magic "ZEROCKPT", format 1, the ABI version), and ends with a CRC-32C
+ * (Castagnoli) of every byte before it.  Host memory only, synchronous; the
+ * caller moves device state to or from host memory.
+ * ------------------------------------------------------------------------ */
+
+typedef struct zero_ckpt_info {
+    int32_t format;   /* file format version (1) */
+    int32_t abi;      /* ZERO_ABI_VERSION of the writer */
+    int32_t n_ranks;  /* N of the saved layout: the checkpoint has N files */
+    int32_t n_units;
+    int32_t rank;     /* whose shard this file holds */
+    int32_t step;     /* the AdamW step count t of the saved state */
+    int64_t numel;    /* parameter elements (sum of the unit numels) */
+    int64_t shard;    /* elements per array (the saved layout's S) */
+} zero_ckpt_info;
+
+/* Write rank `rank`'s shard to `path` (written to path.tmp, flushed, then
+ * renamed).  master / exp_avg / exp_avg_sq: host arrays of layout->shard
+ * floats (may be NULL when that is 0).  step >= 0.  EINVAL, EIO. */
+zero_status zero_ckpt_save(const char *path, const zero_layout *layout, int32_t rank,
+                           int32_t step, const float *master, const float *exp_avg,
+                           const float *exp_avg_sq);
+
+/* Read one shard file's header and rebuild its saved layout (two-call size
+ * query as zero_pack: layout NULL -> *bytes_needed only).  verify != 0 also
+ * checks the CRC-32C over the whole file.  EINVAL, EIO, ECORRUPT, ENOSPC. */
+zero_status zero_ckpt_inspect(const char *path, int32_t verify, zero_ckpt_info *info,
+                              zero_layout *layout, size_t layout_bytes, size_t *bytes_needed);
+
+/* Load rank dst_rank's shard of layout `to` from a checkpoint's n_files shard
+ * files (paths[q] must hold rank q's shard; n_files is the saved N),
+ * resharding at load time: each element comes from the file and position
+ * that hold the same stream position in the saved layout (as zero_reshard),
+ * padding is zero.  Only the byte runs the destination needs are read.
+ * verify != 0 checks every file's CRC-32C first.  master / exp_avg /
+ * exp_avg_sq: host arrays of to->shard floats; *step (may be NULL) receives
+ * the saved step count.  EINVAL (bad arguments, files out of rank order or
+ * of another N, a destination layout with another element count), EIO,
+ * ECORRUPT. */
+zero_status zero_ckpt_load(const char *const *paths, int32_t n_files, const zero_layout *to,
+                           int32_t dst_rank, int32_t verify, int32_t *step, float *master,
+                           float *exp_avg, float *exp_avg_sq);
 
 /* ------------------------------------------------------------------------
  * Ledger -- [p4 section 3]: model state is (2 + 2 + K) psi bytes with K = 12

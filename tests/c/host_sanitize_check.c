@@ -8,11 +8,13 @@
  * with fake device addresses that never reach a device call.
  * Prints "ok" and exits 0 on success; a sanitizer report aborts the run.
  */
+#define _POSIX_C_SOURCE 200809L
 #include <math.h>
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
+#include <unistd.h>
 
 #include "zero.h"
 
@@ -271,6 +273,80 @@ static void check_host_reshard(void)
     }
 }
 
+/* sharded checkpoint: every rank's shard saved, each rank of another layout
+ * loaded (resharded at load time) and compared with the oracle's reshard of
+ * the saved arrays; then the error paths */
+static void check_checkpoint(void)
+{
+    char dir[] = "/tmp/zero_ckpt_sanXXXXXX";
+    CHECK(mkdtemp(dir) != NULL);
+    char path[8][128];
+    const char *paths[8];
+    for (int it = 0; it < 30; ++it) {
+        const int32_t P = (int32_t)rnd(1, 4);
+        int64_t rows[4], cols[4], pnum[4], total = 0;
+        for (int p = 0; p < P; ++p) {
+            rows[p] = rnd(0, 9);
+            cols[p] = rnd(1, 4);
+            pnum[p] = rows[p] * cols[p];
+            total += pnum[p];
+        }
+        int64_t a_numel[1] = {total};
+        const int32_t na = (int32_t)rnd(1, 8), nb = (int32_t)rnd(1, 8);
+        zero_layout *A = make_layout(na, 1, a_numel, NULL);
+        zero_layout *B = make_layout(nb, P, pnum, cols);
+        float *src = (float *)malloc(sizeof(float) * (size_t)(3 * na * A->shard + 1));
+        const void *sp[3][8];
+        for (int q = 0; q < na; ++q) {
+            for (int a = 0; a < 3; ++a) {
+                float *x = src + (size_t)(3 * q + a) * A->shard;
+                for (int64_t i = 0; i < A->shard; ++i)
+                    x[i] = rndf(1.0f);
+                /* the padding holds zeros, as the step keeps it */
+                const int64_t live = total - (int64_t)q * A->shard;
+                for (int64_t i = live < 0 ? 0 : live; i < A->shard; ++i)
+                    x[i] = 0.0f;
+                sp[a][q] = x;
+            }
+            snprintf(path[q], sizeof path[q], "%s/r%d.zck", dir, q);
+            paths[q] = path[q];
+            CHECK(zero_ckpt_save(paths[q], A, q, it + 1, (const float *)sp[0][q],
+                                 (const float *)sp[1][q], (const float *)sp[2][q]) == ZERO_OK);
+        }
+        zero_ckpt_info info;
+        size_t need = 0;
+        CHECK(zero_ckpt_inspect(paths[0], 1, &info, NULL, 0, &need) == ZERO_OK);
+        CHECK(info.n_ranks == na && info.step == it + 1 && info.shard == A->shard);
+        for (int32_t r = 0; r < nb; ++r) {
+            float *d = (float *)malloc(sizeof(float) * (size_t)(3 * B->shard + 1));
+            float *e = (float *)malloc(sizeof(float) * (size_t)(B->shard + 1));
+            int32_t step = -1;
+            CHECK(zero_ckpt_load(paths, na, B, r, 1, &step, d, d + B->shard, d + 2 * B->shard) == ZERO_OK);
+            CHECK(step == it + 1);
+            for (int a = 0; a < 3; ++a) {
+                CHECK(orc_reshard(1, a_numel, na, NULL, sp[a], P, pnum, nb, cols, r, e, 4) == 0);
+                CHECK(memcmp(d + (size_t)a * B->shard, e, sizeof(float) * (size_t)B->shard) == 0);
+            }
+            free(d);
+            free(e);
+        }
+        if (na > 1) {
+            const char *swapped[8];
+            for (int q = 0; q < na; ++q)
+                swapped[q] = paths[q == 0 ? 1 : q == 1 ? 0 : q];
+            float dummy[1];
+            CHECK(zero_ckpt_load(swapped, na, B, 0, 0, NULL, dummy, dummy, dummy) == ZERO_EINVAL);
+        }
+        for (int q = 0; q < na; ++q)
+            remove(paths[q]);
+        free(src);
+        free(A);
+        free(B);
+    }
+    CHECK(zero_ckpt_inspect("/nonexistent/zero.zck", 0, &(zero_ckpt_info){0}, NULL, 0, NULL) == ZERO_EIO);
+    rmdir(dir);
+}
+
 /* argument errors of the device entry points: rejected before any device work */
 static void check_device_validation(void)
 {
@@ -364,6 +440,7 @@ int main(void)
     check_scalars_ledger_arena();
     check_host_step();
     check_host_reshard();
+    check_checkpoint();
     check_device_validation();
     printf("ok\n");
     return 0;

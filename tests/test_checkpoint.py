@@ -1,0 +1,231 @@
+"""Sharded checkpoints ("ZeRO and FSDP sharding", Implementation notes: each
+rank writes its own shard, and a checkpoint is resharded to a different N when
+it is loaded; "Learn: ZeRO & FSDP", section 5: flat and per-parameter dim-0
+layouts).  CPU only: files are written and read on the host.
+
+- The file's CRC-32C against a bitwise CRC-32C written from its definition
+  here (itself checked on the standard check string).
+- Saved and loaded into the same layout: every rank's state comes back bit
+  for bit.
+- Loaded into another layout (other N, flat <-> rows): equal to the oracle's
+  reshard of the saved shards.
+- Stop at N = 8 flat blocks, save, load at N = 4 row-aligned parameters,
+  continue: the gathered state equals unsharded AdamW straight through (the
+  oracle), bit for bit.
+- Damaged, truncated, mixed, missing or misordered files are refused."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import pins
+
+z = pytest.importorskip("fsdp_sharded_optimizer_flat_amd")
+Lc = z.ZERO_LOCAL
+
+
+def crc32c(data: bytes) -> int:
+    """CRC-32C from its definition: reflected polynomial 0x82F63B78, initial
+    value and final xor 0xFFFFFFFF, one bit at a time."""
+    crc = 0xFFFFFFFF
+    for b in data:
+        crc ^= b
+        for _ in range(8):
+            crc = (crc >> 1) ^ (0x82F63B78 if crc & 1 else 0)
+    return crc ^ 0xFFFFFFFF
+
+
+def test_crc32c_reference():
+    assert crc32c(b"123456789") == 0xE3069283        # the standard check value
+
+
+def _lib_layout(n, units, row_len):
+    return z.zero_pack(n, units) if row_len is None else z.zero_pack_rows(n, units, row_len)
+
+
+def _save_all(tmp_path, L, states, step, tag="ck"):
+    paths = []
+    for q in range(L.n_ranks):
+        p = str(tmp_path / f"{tag}_rank{q:03d}.zck")
+        z.zero_ckpt_save(p, L, q, step, *states[q])
+        paths.append(p)
+    return paths
+
+
+def _random_states(rng, L, row_len=None):
+    """Every rank's (master, m, v) shards with zeros in the padding (what the
+    packer and the step keep there)."""
+    O = oracle.Layout(L.n_ranks, L.unit_table()[:, 0], row_len=row_len)
+    states = []
+    for q in range(L.n_ranks):
+        pad = np.zeros(L.shard, bool)
+        for u in range(O.n_units):
+            a = q * O.shard[u]
+            live = max(0, min(O.shard[u], O.numel[u] - a))
+            pad[O.local_offset[u] + live:O.local_offset[u] + O.shard[u]] = True
+        arrs = []
+        for scale in (0.02, 1e-3, 1e-6):
+            x = (rng.standard_normal(L.shard) * scale).astype(np.float32)
+            x[pad] = 0
+            arrs.append(x)
+        states.append(arrs)
+    return states
+
+
+def test_file_crc_and_header(tmp_path):
+    rng = np.random.default_rng(1)
+    L = z.zero_pack(3, [100, 7, 0, 33])
+    st = _random_states(rng, L)
+    paths = _save_all(tmp_path, L, st, 17)
+    data = open(paths[1], "rb").read()
+    assert data[:8] == b"ZEROCKPT"
+    assert len(data) == 64 + 16 * 4 + 3 * 4 * L.shard + 8
+    body, trailer = data[:-8], data[-8:]
+    assert int.from_bytes(trailer[:4], "little") == crc32c(body)
+    assert trailer[4:] == b"\0\0\0\0"
+    # the payload is the three arrays, bit for bit
+    pay = np.frombuffer(body[64 + 64:], np.float32).reshape(3, L.shard)
+    for a in range(3):
+        assert np.array_equal(pay[a].view(np.uint32), st[1][a].view(np.uint32))
+    info, saved = z.zero_ckpt_inspect(paths[1])
+    assert (info["n_ranks"], info["n_units"], info["rank"], info["step"]) == (3, 4, 1, 17)
+    assert (info["numel"], info["shard"]) == (140, L.shard)
+    assert np.array_equal(saved.unit_table(), L.unit_table())
+    assert not os.path.exists(paths[1] + ".tmp")
+
+
+def test_same_layout_round_trip(tmp_path):
+    rng = np.random.default_rng(2)
+    for n, units, rows in ((1, [5], None), (4, [1000, 7, 64], None), (8, [96 * 10, 50], [96, 5])):
+        L = _lib_layout(n, units, rows)
+        st = _random_states(rng, L, rows)
+        paths = _save_all(tmp_path, L, st, 3, tag=f"n{n}")
+        for q in range(n):
+            step, *got = z.zero_ckpt_load(paths, L, q)
+            assert step == 3
+            for a in range(3):
+                assert np.array_equal(got[a].view(np.uint32), st[q][a].view(np.uint32)), (n, q, a)
+
+
+def test_reshard_at_load_matches_oracle(tmp_path):
+    """Random parameter sets saved under one layout (flat blocks, flat per
+    parameter or dim-0 rows, N_a ranks) and loaded under another (N_b ranks):
+    every destination rank's three arrays equal the oracle's reshard of the
+    saved shards."""
+    rng = np.random.default_rng(3)
+    for case in range(25):
+        params, numel, row_len = pins.random_params(rng, int(rng.integers(1, 6)))
+        n_a, n_b = int(rng.integers(1, 9)), int(rng.integers(1, 9))
+        _, units_a, row_a = pins.layout_case(rng, params, numel, row_len, n_a)
+        _, units_b, row_b = pins.layout_case(rng, params, numel, row_len, n_b)
+        A, B = _lib_layout(n_a, units_a, row_a), _lib_layout(n_b, units_b, row_b)
+        st = _random_states(rng, A, row_a)
+        paths = _save_all(tmp_path, A, st, case + 1, tag=f"c{case}")
+        for r in range(n_b):
+            step, *got = z.zero_ckpt_load(paths, B, r)
+            assert step == case + 1
+            for a in range(3):
+                want = oracle.reshard(units_a, n_a, [s[a] for s in st], n_b, r, row_a=row_a,
+                                      row_b=row_b, numel_b=units_b)
+                assert np.array_equal(got[a].view(np.uint32), want.view(np.uint32)), (case, r, a)
+
+
+def test_resume_through_files_flat8_to_rows4(tmp_path):
+    """Three AdamW steps on N = 8 flat blocks (the host step), every rank
+    saves its shard, the checkpoint is loaded at N = 4 with one dim-0 unit per
+    parameter, three more steps; the state gathered to one rank equals six
+    steps of unsharded AdamW on the same gradients (the oracle), bit for bit."""
+    from fsdp_sharded_optimizer_flat_amd import workloads
+    rng = np.random.default_rng(41)
+    block = [(96,), (288, 96), (288,), (96, 96), (96,), (384, 96), (384,), (96, 384), (96,)]
+    shapes = [(1000, 96)] + block + block + [(96,)]
+    numel = [workloads.numel_of(s) for s in shapes]
+    row_len = workloads.row_lengths(shapes)
+    P = sum(numel)
+    units_a = [sum(numel[:1 + len(block)]), sum(numel[1 + len(block):])]
+    n_a, n_b = 8, 4
+    A, B, full = z.zero_pack(n_a, units_a), z.zero_pack_rows(n_b, numel, row_len), z.zero_pack(1, [P])
+    h = workloads.GPT_HYPER
+    sc = lambda t: z.zero_adamw_scalars_for(t, h["lr"], h["b1"], h["b2"], h["eps"], h["wd"], 1.0)
+    w0 = rng.normal(0, 0.02, P).astype(np.float32)
+    gsteps = [(rng.standard_normal(P) * 1e-3).astype(np.float32) for _ in range(6)]
+
+    def split(vec, n, units, row=None):
+        return [oracle.reshard([P], 1, [vec], n, q, row_b=row, numel_b=units) for q in range(n)]
+
+    state = [[x, np.zeros_like(x), np.zeros_like(x)] for x in split(w0, n_a, units_a)]
+    for t in range(1, 4):
+        gl = split(gsteps[t - 1], n_a, units_a)
+        for q in range(n_a):
+            z.zero_step_host(A, q, [gl[q]], Lc, 1.0, *state[q], Lc, None, Lc, sc(t), 1)
+    paths = _save_all(tmp_path, A, state, 3, tag="resume")
+    del state
+    new = []
+    for r in range(n_b):
+        step, w, m, v = z.zero_ckpt_load(paths, B, r)
+        assert step == 3
+        new.append([w, m, v])
+    outs = [np.zeros(B.shard, np.uint16) for _ in range(n_b)]
+    for t in range(step + 1, 7):
+        gl = split(gsteps[t - 1], n_b, numel, row=row_len)
+        for r in range(n_b):
+            z.zero_step_host(B, r, [gl[r]], Lc, 1.0, *new[r], Lc, outs[r], Lc, sc(t), 1)
+    got = []
+    for a in range(3):
+        dst = np.zeros(P, np.float32)
+        z.zero_reshard_host(B, [s[a] for s in new], full, 0, dst)
+        got.append(dst)
+    out_full = np.zeros(P, np.uint16)
+    z.zero_reshard_host(B, outs, full, 0, out_full)
+    w, m, v = w0.copy(), np.zeros(P, np.float32), np.zeros(P, np.float32)
+    for t in range(1, 7):
+        oracle.adamw_unsharded([gsteps[t - 1]], divisor=1.0, clip=1.0, w=w, m=m, v=v, t=t,
+                               lr=h["lr"], b1=h["b1"], b2=h["b2"], eps=h["eps"], wd=h["wd"])
+    for a, want in enumerate((w, m, v)):
+        assert np.array_equal(got[a].view(np.uint32), want.view(np.uint32)), a
+    assert np.array_equal(out_full, oracle.bf16(w))
+
+
+def test_damaged_and_mismatched_files_are_refused(tmp_path):
+    rng = np.random.default_rng(5)
+    L = z.zero_pack(4, [1000, 37])
+    st = _random_states(rng, L)
+    paths = _save_all(tmp_path, L, st, 2)
+
+    def status(fn, *a):
+        with pytest.raises(z.ZeroError) as e:
+            fn(*a)
+        return e.value.status
+
+    # one flipped payload bit: caught by the checksum, loaded as is without it
+    bad = str(tmp_path / "flip.zck")
+    data = bytearray(open(paths[2], "rb").read())
+    data[64 + 32 + 4 * 10] ^= 0x10
+    open(bad, "wb").write(bytes(data))
+    mixed = paths[:2] + [bad] + paths[3:]
+    assert status(z.zero_ckpt_load, mixed, L, 2) == z.ZERO_ECORRUPT
+    assert status(z.zero_ckpt_inspect, bad) == z.ZERO_ECORRUPT
+    z.zero_ckpt_load(mixed, L, 2, False)
+    # truncated file, wrong magic
+    trunc = str(tmp_path / "trunc.zck")
+    open(trunc, "wb").write(open(paths[1], "rb").read()[:-12])
+    assert status(z.zero_ckpt_load, [paths[0], trunc] + paths[2:], L, 0) == z.ZERO_ECORRUPT
+    magic = str(tmp_path / "magic.zck")
+    open(magic, "wb").write(b"X" + open(paths[1], "rb").read()[1:])
+    assert status(z.zero_ckpt_inspect, magic, False) == z.ZERO_ECORRUPT
+    # missing file, files out of rank order, too few files
+    assert status(z.zero_ckpt_load, paths[:3] + [str(tmp_path / "none.zck")], L, 0) == z.ZERO_EIO
+    assert status(z.zero_ckpt_load, [paths[1], paths[0]] + paths[2:], L, 0) == z.ZERO_EINVAL
+    assert status(z.zero_ckpt_load, paths[:3], L, 0) == z.ZERO_EINVAL
+    # a shard of another checkpoint (another unit table) among them
+    other = z.zero_pack(4, [1001, 36])
+    op = _save_all(tmp_path, other, _random_states(rng, other), 2, tag="other")
+    assert status(z.zero_ckpt_load, paths[:3] + [op[3]], L, 0) == z.ZERO_ECORRUPT
+    # a destination layout holding another number of elements
+    assert status(z.zero_ckpt_load, paths, z.zero_pack(2, [1000]), 0) == z.ZERO_EINVAL
+    # arguments
+    assert status(z.zero_ckpt_save, str(tmp_path / "x.zck"), L, 4, 1, *st[0]) == z.ZERO_EINVAL
+    assert status(z.zero_ckpt_save, str(tmp_path / "no_dir" / "x.zck"), L, 0, 1, *st[0]) == z.ZERO_EIO
+    with pytest.raises(ValueError):
+        z.zero_ckpt_save(str(tmp_path / "y.zck"), L, 0, 1, st[0][0][:-1], st[0][1], st[0][2])
