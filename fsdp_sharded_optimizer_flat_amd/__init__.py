@@ -38,6 +38,7 @@ ZERO_GLOBAL, ZERO_LOCAL = 0, 1
 ZERO_MAX_RANKS = 256
 ZERO_LAYOUT_MAGIC = 0x5A45524F
 ZERO_ABI_VERSION = 2
+ZERO_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 i32, i64, f32, f64, vp, sz = C.c_int32, C.c_int64, C.c_float, C.c_double, C.c_void_p, C.c_size_t
 
@@ -142,6 +143,8 @@ _zero_gradnorm = _sig("zero_gradnorm", i32, vp, i32, vp, i32, i32, i32, f32, vp,
                       C.POINTER(f64), vp)
 _zero_gradnorm_async = _sig("zero_gradnorm_async", i32, vp, i32, vp, i32, i32, i32, f32, vp, i32, vp,
                             sz, vp, vp)
+_zero_gradnorm_async_noalloc = _sig("zero_gradnorm_async_noalloc", i32, vp, i32, vp, i32, i32, i32,
+                                    f32, vp, i32, vp, vp)
 _zero_clip_coef = _sig("zero_clip_coef", i32, f64, f64, C.POINTER(f32))
 _zero_ledger = _sig("zero_ledger", i32, f64, i32, i32, i32, C.POINTER(ZeroLedgerOut))
 _zero_sim_footprint = _sig("zero_sim_footprint", i32, vp, i32, i32, i32, i32, i32, i32, i32,
@@ -168,6 +171,7 @@ EXPORTED = ["zero_layout_bytes", "zero_pack", "zero_pack_rows", "zero_reshard",
             "zero_clip_coef_async", "zero_clip_coef_ranks", "zero_clip_coef_ranks_async",
             "zero_overlap",
             "zero_gradnorm_workspace_bytes", "zero_gradnorm", "zero_gradnorm_async",
+            "zero_gradnorm_async_noalloc",
             "zero_clip_coef", "zero_ledger", "zero_sim_footprint",
             "zero_gather_buffer_bytes", "zero_arena_plan", "zero_step_traffic",
             "zero_gradnorm_traffic", "zero_ckpt_save", "zero_ckpt_inspect", "zero_ckpt_load",
@@ -760,6 +764,24 @@ def zero_gradnorm_async(layout: Layout, rank: int, grads, grad_index: int, divis
                                 workspace.numel() * workspace.element_size(),
                                 _dev_ptr(sumsq_dev, "sumsq_dev"), _stream(stream)),
            "zero_gradnorm_async")
+
+
+def zero_gradnorm_async_noalloc(layout: Layout, rank: int, grads, grad_index: int,
+                                divisor: float, g_out, g_index: int, sumsq_dev, stream=None):
+    """zero_gradnorm_async without a workspace: the partial sums live in the
+    library's own device array (for callers that cannot allocate; calls on one
+    GPU must not overlap)."""
+    torch = _torch()
+    if sumsq_dev.dtype != torch.float64:
+        raise TypeError("sumsq_dev must be a float64 device tensor")
+    arr, gdt = _grad_ptrs(grads)
+    _need_norm(layout, grads, grad_index, g_out, g_index)
+    _need(sumsq_dev, 1, "sumsq_dev")
+    _check(_zero_gradnorm_async_noalloc(layout.ptr, rank, C.addressof(arr), len(arr), gdt,
+                                        grad_index, divisor,
+                                        _f32_ptr(g_out, "g_out") if g_out is not None else None,
+                                        g_index, _dev_ptr(sumsq_dev, "sumsq_dev"), _stream(stream)),
+           "zero_gradnorm_async_noalloc")
 
 
 # -- ledger -------------------------------------------------------------------------------

@@ -706,6 +706,39 @@ extern "C" zero_status zero_gradnorm_async(const zero_layout *L, int32_t rank,
     return err == hipSuccess ? ZERO_OK : hip_fail(err, "zero_gradnorm_async");
 }
 
+extern "C" zero_status zero_gradnorm_async_noalloc(const zero_layout *L, int32_t rank,
+                                                   const void *const *grads, int32_t n_grads,
+                                                   int32_t grad_dtype, int32_t grad_index,
+                                                   float divisor, float *g_out, int32_t g_index,
+                                                   double *sumsq_dev, void *stream)
+{
+    // every argument check before the first HIP call
+    if (!sumsq_dev)
+        return ZERO_EINVAL;
+    zero_status st = check_grads(L, rank, grads, n_grads, grad_dtype, grad_index, divisor);
+    if (st != ZERO_OK)
+        return st;
+    if (!index_ok(g_index) || (rank < 0 && (grad_index != ZERO_GLOBAL || g_index != ZERO_GLOBAL)))
+        return ZERO_EINVAL;
+    if ((g_out && !aligned(g_out, 4)) || !aligned(sumsq_dev, 8))
+        return ZERO_EALIGN;
+    size_t need = 0;
+    zero_gradnorm_workspace_bytes(L, rank, &need);
+    if (need > (size_t)ZERO_NOALLOC_SCRATCH_BYTES)
+        return ZERO_ENOSPC;
+    void *ws = nullptr;
+    const int err = noalloc_scratch(&ws);
+    if (err != hipSuccess)
+        return hip_fail(err, "zero_gradnorm_async_noalloc scratch");
+    int64_t np = 0;
+    st = gradnorm_launch(L, rank, grads, n_grads, grad_dtype, grad_index, divisor, g_out, g_index,
+                         ws, (size_t)ZERO_NOALLOC_SCRATCH_BYTES, sumsq_dev, stream, &np);
+    if (st != ZERO_OK || np > 0)
+        return st;
+    const int e2 = launch_fill_zero(sumsq_dev, ZERO_F32, 2, stream);
+    return e2 == hipSuccess ? ZERO_OK : hip_fail(e2, "zero_gradnorm_async_noalloc");
+}
+
 // ---------------------------------------------------------------------------
 // Packer copies.
 // ---------------------------------------------------------------------------

@@ -15,7 +15,17 @@
 // layout, the rank and the index spaces -- never on the device, the
 // pointers' alignment or whether g is written -- so the result is bitwise
 // reproducible.
+#include <mutex>
+#include <vector>
+
 #include "device_common.h"
+
+// Partials of zero_gradnorm_async_noalloc: device memory that belongs to the
+// library's code object, one copy per GPU, so that call allocates nothing.
+// Host code never passes this name to a kernel (on the host it is only a
+// stand-in for the symbol); it uses the per-device address that
+// noalloc_scratch() looks up.
+static __device__ __align__(256) double scratch[ZERO_NOALLOC_SCRATCH_BYTES / sizeof(double)];
 
 namespace zero {
 namespace {
@@ -194,6 +204,32 @@ int launch_norm_segment(int64_t len, bool vec, const void *const *grads, int n_g
                   : launch_nr<0, float, F32Oct, false, true>(grads, n_grads, g_out, len, c, partials, blocks, st);
     return p2 ? launch_nr<0, float, F32Oct, true, false>(grads, n_grads, g_out, len, c, partials, blocks, st)
               : launch_nr<0, float, F32Oct, false, false>(grads, n_grads, g_out, len, c, partials, blocks, st);
+}
+
+int noalloc_scratch(void **ptr)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0)
+        return hipErrorInvalidDevice;
+    static std::mutex mu;
+    static std::vector<void *> addr;  // per device, looked up once
+    std::lock_guard<std::mutex> lock(mu);
+    if ((size_t)dev >= addr.size())
+        addr.resize((size_t)dev + 1, nullptr);
+    if (!addr[(size_t)dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        if (!p)
+            return hipErrorInvalidSymbol;
+        addr[(size_t)dev] = p;
+    }
+    *ptr = addr[(size_t)dev];
+    return hipSuccess;
 }
 
 int launch_clip_coef(const double *sums, int n, double max_norm, float *coef, double *total,

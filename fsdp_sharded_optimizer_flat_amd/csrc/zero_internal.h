@@ -180,6 +180,10 @@ int launch_clip_coef(const double *sums, int n, double max_norm, float *coef, do
                      void *stream);
 int launch_norm_tree(const double *partials, int64_t n_partials, double *scratch, double *result,
                      void *stream);
+// Device address, on the current device, of the library-owned partials array
+// of zero_gradnorm_async_noalloc (ZERO_NOALLOC_SCRATCH_BYTES); looked up once
+// per device.  Returns a hipError_t value.
+int noalloc_scratch(void **ptr);
 int64_t norm_tree_scratch(int64_t n_partials);
 int launch_convert(const void *src, int src_dtype, void *dst, int dst_dtype, int64_t n,
                    void *stream);

@@ -457,6 +457,28 @@ zero_status zero_gradnorm_async(const zero_layout *layout, int32_t rank,
                                 void *workspace, size_t workspace_bytes,
                                 double *sumsq_dev, void *stream);
 
+/* zero_gradnorm_async for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  No workspace is passed: the partial sums live in a
+ * library-owned device array of ZERO_NOALLOC_SCRATCH_BYTES per GPU (static
+ * device memory of the library's code object, held by every GPU the library
+ * runs on until the process ends).  The selection's partials must fit
+ * (zero_gradnorm_workspace_bytes <= ZERO_NOALLOC_SCRATCH_BYTES, about 1.07G
+ * elements; ENOSPC otherwise, before any device work).  The call allocates
+ * nothing and calls no allocating routine.  Every call on one GPU shares that
+ * GPU's array, which keeps the last call's contents (every partial is written
+ * before it is read, so nothing needs clearing): calls that overlap on one GPU
+ * (different streams without ordering, or threads) race and give wrong sums.
+ * The first call on a device looks the array's address up
+ * (hipGetSymbolAddress); make one call on that device before capturing a
+ * graph.  Result, g_out and errors otherwise as zero_gradnorm_async. */
+#define ZERO_NOALLOC_SCRATCH_BYTES (16u << 20)
+zero_status zero_gradnorm_async_noalloc(const zero_layout *layout, int32_t rank,
+                                        const void *const *grads, int32_t n_grads,
+                                        int32_t grad_dtype, int32_t grad_index, float divisor,
+                                        float *g_out, int32_t g_index, double *sumsq_dev,
+                                        void *stream);
+
 /* Clip coefficient from a sum of squares (host): norm = sqrt(sumsq) and
  * coef = min(1, max_norm / (norm + 1e-6)) in binary64, rounded once to
  * binary32 -- the convention of the clip_grad_norm_ routine [p1

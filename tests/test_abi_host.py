@@ -157,6 +157,36 @@ def test_clip_coef_matches_oracle():
         z.zero_clip_coef(1.0, 0.0)
 
 
+def test_gradnorm_noalloc_validation_without_device():
+    """zero_gradnorm_async_noalloc checks every argument, and the size of the
+    selection's partials against its fixed array, before its first HIP call:
+    on this host (no GPU) the errors come back as status codes."""
+    lib = z.raw_library()
+    f = lib.zero_gradnorm_async_noalloc
+    f.restype = C.c_int32
+    f.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, C.c_int32,
+                  C.c_int32, C.c_float, C.c_void_p, C.c_int32, C.c_void_p,
+                  C.c_void_p]
+    fake = 1 << 40                       # never dereferenced: no launch happens
+    grads = (C.c_void_p * 2)(fake, fake + (1 << 34))
+    big = z.zero_pack(1, [1 << 31])     # 4M partials: 32 MiB > the 16 MiB array
+    need = z.zero_gradnorm_workspace_bytes(big, 0)
+    assert need > z.ZERO_NOALLOC_SCRATCH_BYTES
+    G, Lc = z.ZERO_GLOBAL, z.ZERO_LOCAL
+    args = lambda L, rank=0, n=1, gi=Lc, div=1.0, gidx=Lc, sq=fake + (1 << 36): (
+        L.ptr, rank, C.addressof(grads), n, z.ZERO_BF16, gi, div, None, gidx, sq, None)
+    assert f(*args(big)) == z.ZERO_ENOSPC
+    ok = z.zero_pack(2, [1 << 20])      # 2048 partials: fits
+    assert z.zero_gradnorm_workspace_bytes(ok, 0) <= z.ZERO_NOALLOC_SCRATCH_BYTES
+    assert f(*args(ok, sq=None)) == z.ZERO_EINVAL
+    assert f(*args(ok, sq=fake + 4)) == z.ZERO_EALIGN
+    assert f(*args(ok, rank=2)) == z.ZERO_EINVAL
+    assert f(*args(ok, n=0)) == z.ZERO_ERANGE
+    assert f(*args(ok, div=0.0)) == z.ZERO_EINVAL
+    assert f(*args(ok, rank=-1, gi=Lc)) == z.ZERO_EINVAL
+    assert f(*args(ok, gidx=5)) == z.ZERO_EINVAL
+
+
 # -- ledger -------------------------------------------------------------------------------
 
 def test_sim_footprint_matches_oracle_and_workloads():
