@@ -183,9 +183,12 @@ def test_step_on_row_layout_vs_oracle(n, rank):
 # Stop, reshard, resume
 # ---------------------------------------------------------------------------
 
-def test_resume_after_reshard_flat8_to_rows4():
-    """Three steps on N = 8 flat blocks, reshard master / m / v on the device
-    to N = 4 row-aligned parameters, three more steps; gathering the shards
+@pytest.mark.parametrize("via_files", [False, True])
+def test_resume_after_reshard_flat8_to_rows4(via_files, tmp_path):
+    """Three steps on N = 8 flat blocks, reshard master / m / v to N = 4
+    row-aligned parameters -- on the device, or through a sharded checkpoint
+    (every rank saves its shard to a file, each new rank loads its shard of
+    the new layout from the files) -- three more steps; gathering the shards
     gives exactly six steps of unsharded AdamW on the same gradients."""
     rng = np.random.default_rng(41)
     block = [(96,), (288, 96), (288,), (96, 96), (96,), (384, 96), (384,), (96, 384), (96,)]
@@ -215,12 +218,23 @@ def test_resume_after_reshard_flat8_to_rows4():
         for q in range(n_a):
             z.zero_step(A, q, [gl[q]], Lc, 1.0, state["w"][q], state["m"][q], state["v"][q], Lc,
                         None, Lc, scalars(t, h))
-    # reshard every state array to the row layout, on the device
     new = {}
-    for k in ("w", "m", "v"):
-        new[k] = [torch.full((B.shard,), float("nan"), device=DEV) for _ in range(n_b)]
-        for r in range(n_b):
-            z.zero_reshard(A, state[k], B, r, new[k][r])
+    if via_files:
+        # every rank saves its shard; each new rank loads its shard of B
+        paths = [str(tmp_path / f"rank{q}.zck") for q in range(n_a)]
+        for q in range(n_a):
+            z.zero_ckpt_save(paths[q], A, q, 3, state["w"][q], state["m"][q], state["v"][q])
+        del state
+        loaded = [z.zero_ckpt_load(paths, B, r) for r in range(n_b)]
+        assert all(x[0] == 3 for x in loaded)
+        for i, k in enumerate(("w", "m", "v")):
+            new[k] = [torch.from_numpy(loaded[r][1 + i]).to(DEV) for r in range(n_b)]
+    else:
+        # reshard every state array to the row layout, on the device
+        for k in ("w", "m", "v"):
+            new[k] = [torch.full((B.shard,), float("nan"), device=DEV) for _ in range(n_b)]
+            for r in range(n_b):
+                z.zero_reshard(A, state[k], B, r, new[k][r])
     # phase 2: row layout, N = 4
     outs = [torch.zeros(B.shard, dtype=torch.int16, device=DEV) for _ in range(n_b)]
     for t in range(4, 7):
