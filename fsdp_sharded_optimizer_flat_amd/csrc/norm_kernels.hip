@@ -123,8 +123,10 @@ __global__ __launch_bounds__(kBlock) void norm_level_kernel(const double *__rest
 // squares added in order (binary64; n is 1 for one shard's sum, N for the
 // ranks' sums of a sharded norm), norm = sqrt(sum), c = max_norm / (norm +
 // 1e-6) with correctly rounded sqrt and division, capped at 1, rounded once
-// to binary32 -- the same bits as zero_clip_coef computes on the host.  One
-// thread.
+// to binary32 -- the same bits as zero_clip_coef computes on the host.  A
+// total that is negative, NaN or infinite (a non-finite gradient; the host
+// function refuses it) gives a NaN coefficient, which makes the device-clip
+// step leave the state unchanged.  One thread.
 __global__ void clip_coef_kernel(const double *__restrict__ sums, int n, double max_norm,
                                  float *__restrict__ coef, double *__restrict__ total)
 {
@@ -133,10 +135,13 @@ __global__ void clip_coef_kernel(const double *__restrict__ sums, int n, double 
     double t = sums[0];
     for (int r = 1; r < n; ++r)
         t = t + sums[r];
-    const double norm = sqrt(t);
-    double c = max_norm / (norm + 1e-6);
-    if (c > 1.0)
-        c = 1.0;
+    double c = __builtin_nan("");
+    if (t >= 0.0 && t <= 1.7976931348623157e308) {
+        const double norm = sqrt(t);
+        c = max_norm / (norm + 1e-6);
+        if (c > 1.0)
+            c = 1.0;
+    }
     *coef = (float)c;
     if (total)
         *total = t;

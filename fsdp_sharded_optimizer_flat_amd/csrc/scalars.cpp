@@ -8,6 +8,7 @@
 // Everything is binary32 with one rounding per operation; this file is
 // compiled without FMA contraction (see the build flags) so the compiler
 // keeps each product and sum separately rounded.
+#include <cfloat>
 #include <cmath>
 
 #include "zero_internal.h"
@@ -79,7 +80,9 @@ extern "C" zero_status zero_adamw_scalars_next(const zero_adamw_scalars *prev,
 // follows clip_grad_norm_'s convention max_norm / (norm + 1e-6), capped at 1.
 extern "C" zero_status zero_clip_coef(double sumsq, double max_norm, float *coef)
 {
-    if (!coef || !(sumsq >= 0.0) || !(max_norm > 0.0))
+    // a sum of squares that is negative, NaN or infinite (a non-finite
+    // gradient) has no clip coefficient
+    if (!coef || !(sumsq >= 0.0 && sumsq <= DBL_MAX) || !(max_norm > 0.0))
         return ZERO_EINVAL;
     const double norm = std::sqrt(sumsq);
     double c = max_norm / (norm + 1e-6);

@@ -54,6 +54,10 @@ __global__ __launch_bounds__(kWave) void step_quad_kernel(GradSet<CAP> gs, int n
     float w[4] = {wq.x, wq.y, wq.z, wq.w};
     float m[4] = {mq.x, mq.y, mq.z, mq.w};
     float v[4] = {vq.x, vq.y, vq.z, vq.w};
+    // a NaN multiplier from the device (the norm was not finite): the step is
+    // skipped and the state left as it is (uniform over the launch)
+    if (c.clip_dev && !(clip == clip))
+        return;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         float g = average<POW2>(s[k], c);
@@ -83,6 +87,8 @@ __global__ __launch_bounds__(kBlock) void step_scalar_kernel(GradSet<ZERO_MAX_RA
 {
     const int64_t stride = (int64_t)gridDim.x * kBlock;
     const float clip = c.clip_dev ? *c.clip_dev : c.clip;
+    if (c.clip_dev && !(clip == clip))  // skipped step, as in the quad kernel
+        return;
     for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < len; i += stride) {
         float s = grad_at<GT>(gs.p[0], i);
         for (int q = 1; q < n; ++q)

@@ -305,8 +305,12 @@ zero_status zero_step(const zero_layout *layout, int32_t rank,
  * stream has produced, e.g. by zero_clip_coef_async) instead of
  * sc->clip_coef.  With zero_gradnorm_async and zero_clip_coef_async this
  * makes the whole clipped step free of host synchronization, so it can be
- * enqueued ahead or captured in a graph.  clip_coef_dev must not overlap any
- * buffer the step writes (EINVAL).  Otherwise as zero_step. */
+ * enqueued ahead or captured in a graph.  A NaN multiplier (the coefficient
+ * of a non-finite norm) skips the step: master, exp_avg, exp_avg_sq and out
+ * are left unchanged, as a loss scaler skips the step of an overflowed
+ * gradient; the caller can read the multiplier to see that it happened (and
+ * not advance t).  clip_coef_dev must not overlap any buffer the step writes
+ * (EINVAL).  Otherwise as zero_step. */
 zero_status zero_step_device_clip(const zero_layout *layout, int32_t rank,
                                   const void *const *grads, int32_t n_grads, int32_t grad_dtype,
                                   int32_t grad_index, float divisor,
@@ -482,13 +486,16 @@ zero_status zero_gradnorm_async_noalloc(const zero_layout *layout, int32_t rank,
 /* Clip coefficient from a sum of squares (host): norm = sqrt(sumsq) and
  * coef = min(1, max_norm / (norm + 1e-6)) in binary64, rounded once to
  * binary32 -- the convention of the clip_grad_norm_ routine [p1
- * Implementation notes] names.  EINVAL: sumsq < 0 or NaN, max_norm <= 0. */
+ * Implementation notes] names.  EINVAL: sumsq negative, NaN or infinite (a
+ * non-finite gradient has no coefficient), max_norm <= 0. */
 zero_status zero_clip_coef(double sumsq, double max_norm, float *coef);
 
 /* The same coefficient on the device (async): reads the binary64 sum of
  * squares at sumsq_dev (8-byte aligned) and writes the binary32 coefficient
- * to coef_dev (4-byte aligned) -- bitwise equal to zero_clip_coef.  EINVAL:
- * NULL pointers or max_norm <= 0. */
+ * to coef_dev (4-byte aligned) -- bitwise equal to zero_clip_coef.  Where
+ * the host function refuses the sum (negative, NaN or infinite), a NaN is
+ * written, which makes zero_step_device_clip skip the step.  EINVAL: NULL
+ * pointers or max_norm <= 0. */
 zero_status zero_clip_coef_async(const double *sumsq_dev, double max_norm, float *coef_dev,
                                  void *stream);
 
@@ -500,15 +507,16 @@ zero_status zero_clip_coef_async(const double *sumsq_dev, double max_norm, float
  * and forms the coefficient as zero_clip_coef does, so every rank scales by
  * the same binary32 value.  The total is written to *total when total is not
  * NULL.  Host: EINVAL for NULL pointers, n_ranks < 1 or > ZERO_MAX_UNITS, a
- * negative or NaN sum, max_norm <= 0. */
+ * negative or NaN sum, an infinite total, max_norm <= 0. */
 zero_status zero_clip_coef_ranks(const double *rank_sums, int32_t n_ranks, double max_norm,
                                  float *coef, double *total);
 
 /* The same on the device (async): reads n_ranks binary64 sums at
  * rank_sums_dev (8-byte aligned), writes the coefficient to coef_dev and,
  * if total_dev is not NULL, the total -- bitwise equal to
- * zero_clip_coef_ranks on the same sums.  A NaN sum gives a NaN
- * coefficient (the host function refuses it instead).  EINVAL: NULL
+ * zero_clip_coef_ranks on the same sums.  A total the host function refuses
+ * (a negative, NaN or infinite sum) gives a NaN coefficient instead, which
+ * makes zero_step_device_clip skip the step.  EINVAL: NULL
  * pointers, n_ranks out of range, max_norm <= 0; EALIGN; EHIP. */
 zero_status zero_clip_coef_ranks_async(const double *rank_sums_dev, int32_t n_ranks,
                                        double max_norm, float *coef_dev, double *total_dev,

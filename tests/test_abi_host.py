@@ -157,6 +157,23 @@ def test_clip_coef_matches_oracle():
         z.zero_clip_coef(1.0, 0.0)
 
 
+def test_nonfinite_norm_has_no_coefficient():
+    """A gradient with an infinite or NaN element has an infinite or NaN sum
+    of squares: the host refuses it (the device chain writes a NaN coefficient
+    and skips the step instead, tested on the GPU), also when finite rank sums
+    overflow in their rank-ordered total."""
+    for bad in (float("inf"), float("nan"), -0.5):
+        with pytest.raises(z.ZeroError) as e:
+            z.zero_clip_coef(bad, 1.0)
+        assert e.value.status == z.ZERO_EINVAL
+        with pytest.raises(z.ZeroError):
+            z.zero_clip_coef_ranks([1.0, bad, 2.0], 1.0)
+    with pytest.raises(z.ZeroError):
+        z.zero_clip_coef_ranks([1.7e308, 1.7e308], 1.0)      # the total overflows
+    assert z.zero_clip_coef(1.7e308, 1.0) == oracle.clip_coef(1.7e308, 1.0)   # finite: as before
+    assert z.zero_clip_coef_ranks([1.0, 3.0], 1.0)[0] == oracle.clip_coef(4.0, 1.0)
+
+
 def test_gradnorm_noalloc_validation_without_device():
     """zero_gradnorm_async_noalloc checks every argument, and the size of the
     selection's partials against its fixed array, before its first HIP call:

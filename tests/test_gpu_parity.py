@@ -675,6 +675,71 @@ def test_device_clip_coefficient_equals_host():
             assert res.item() == z.zero_clip_coef(float(vals[i]), mx), (vals[i], mx)
 
 
+def test_nonfinite_norm_skips_the_device_clip_step():
+    """The sync-free chain on a gradient with an infinite or NaN element: the
+    norm pass's sum is not finite, zero_clip_coef_async writes NaN (where the
+    host refuses the sum), and zero_step_device_clip leaves master, m, v and
+    the bf16 output bit for bit as they were -- on the quad path and on the
+    one-element path (shifted pointers).  The same chain on the repaired
+    gradient then steps, equal to the oracle's clipped step."""
+    coef = torch.empty(1, dtype=torch.float32, device=DEV)
+    for sums in ([np.inf], [np.nan], [-1.0], [1.0, np.inf], [1.7e308, 1.7e308]):
+        d = torch.tensor(sums, dtype=torch.float64, device=DEV)
+        if len(sums) == 1:
+            z.zero_clip_coef_async(d, 1.0, coef)
+        else:
+            z.zero_clip_coef_ranks_async(d, 1.0, coef)
+        assert np.isnan(coef.item()), sums
+    n, numel, rank = 8, [4096 * 3 + 5, 77], 3
+    L = z.zero_pack(n, numel)
+    h = GPT_HYPER
+    rng = np.random.default_rng(51)
+    for bad in (np.inf, -np.inf, np.nan):
+        for shift in (0, 1):
+            grads = [dev_buffer(L.shard, torch.bfloat16, shift=shift) for _ in range(n)]
+            for g in grads:
+                g.copy_(torch.from_numpy((rng.standard_normal(L.shard) * 1e-3).astype(np.float32)))
+            master = dev_buffer(L.shard, torch.float32, shift=shift)
+            m = dev_buffer(L.shard, torch.float32, shift=shift)
+            v = dev_buffer(L.shard, torch.float32, shift=shift)
+            for t_ in (master, m, v):
+                t_.copy_(torch.from_numpy(np.abs(rng.normal(0, 0.02, L.shard)).astype(np.float32)))
+            out = dev_buffer(L.shard, torch.int16, shift=shift, fill=0x1234)
+            g_red = dev_buffer(L.shard, torch.float32, shift=shift)
+            ws = torch.zeros(z.zero_gradnorm_workspace_bytes(L, rank) // 8, dtype=torch.float64, device=DEV)
+            ss = torch.zeros(1, dtype=torch.float64, device=DEV)
+            before = [to_np(x).copy() for x in (master, m, v, out)]
+            good = grads[2][100].item()
+            grads[2][100] = float(bad)
+            z.zero_gradnorm_async(L, rank, grads, Lc, float(n), g_red, Lc, ws, ss)
+            z.zero_clip_coef_async(ss, 1.0, coef)
+            z.zero_step_device_clip(L, rank, [g_red], Lc, 1.0, master, m, v, Lc, out, Lc, scalars(2, h), coef)
+            torch.cuda.synchronize()
+            assert not np.isfinite(ss.item()) and np.isnan(coef.item()), (bad, ss.item())
+            for got, want, name in zip((master, m, v, out), before, ("master", "m", "v", "out")):
+                assert np.array_equal(to_np(got).view(np.uint32 if want.dtype == np.float32 else np.uint16),
+                                      want.view(np.uint32 if want.dtype == np.float32 else np.uint16)), \
+                    f"{name} changed by a skipped step (bad={bad}, shift={shift})"
+            # repaired: the chain steps, as the oracle does with its own coefficient
+            grads[2][100] = good
+            z.zero_gradnorm_async(L, rank, grads, Lc, float(n), g_red, Lc, ws, ss)
+            z.zero_clip_coef_async(ss, 1.0, coef)
+            z.zero_step_device_clip(L, rank, [g_red], Lc, 1.0, master, m, v, Lc, out, Lc, scalars(2, h), coef)
+            torch.cuda.synchronize()
+            gnp = [np.ascontiguousarray(to_np(g)) for g in grads]
+            og = oracle.reduced_grad(n, numel, rank, gnp, grad_local=True, divisor=float(n))
+            oc = oracle.clip_coef(oracle.sumsq(og), 1.0)
+            assert coef.item() == oc
+            ow, om, ov = (x.copy() for x in before[:3])
+            oo = before[3].copy()
+            oracle.zero_step_rank(n, numel, rank, gnp, grad_local=True, divisor=float(n), clip=oc,
+                                  master=ow, m=om, v=ov, state_global=False, out=oo, out_gather=False,
+                                  t=2, **hyper_args(h))
+            assert_same_f32(to_np(master), ow, "master after the repaired step")
+            assert_same_f32(to_np(v), ov, "v after the repaired step")
+            assert_same_bf16(to_np(out), oo, "out after the repaired step")
+
+
 def test_clip_coefficient_across_ranks_on_the_device():
     """Every rank's sum of squares left on the device (zero_gradnorm_async
     per rank), combined in rank order on the device: bitwise equal to the host
