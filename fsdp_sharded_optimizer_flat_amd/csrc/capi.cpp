@@ -426,7 +426,8 @@ extern "C" zero_status zero_step_staged_workspace_bytes(const zero_layout *L, in
         e = kNormSpan;
     if (e > kStageMaxChunk)
         e = kStageMaxChunk;
-    *bytes = (size_t)e * sizeof(float);
+    // one chunk, plus 16 bytes to place it at the state's 16-byte phase
+    *bytes = (size_t)(e + kStageSlack) * sizeof(float);
     return ZERO_OK;
 }
 
@@ -447,14 +448,21 @@ static zero_status staged_launch(const zero_layout *L, int32_t rank, const void 
         return ZERO_EALIGN;
     if (workspace_bytes < (size_t)kNormSpan * sizeof(float))
         return ZERO_ENOSPC;
-    // chunk: the workspace's whole 512-element tiles, at most kStageMaxChunk;
-    // the call writes no workspace byte past the first chunk
+    // chunk: the workspace's whole 512-element tiles, at most kStageMaxChunk,
+    // less kStageSlack elements when there is room for them: each chunk's g
+    // then starts at the state's 16-byte phase, so that the second half's
+    // quads line up with the state's.  The call writes no workspace byte past
+    // chunk + slack elements.
     size_t ws_elems = workspace_bytes / sizeof(float);
+    const bool shift_ok = ws_elems >= (size_t)(kNormSpan + kStageSlack);
+    if (shift_ok)
+        ws_elems -= kStageSlack;
     if (ws_elems > (size_t)kStageMaxChunk)
         ws_elems = (size_t)kStageMaxChunk;
     const int64_t chunk = (int64_t)ws_elems / kNormSpan * kNormSpan;
     const int gsize = dsize(grad_dtype);
-    const Range ws = range_of(workspace, chunk * (int64_t)sizeof(float), 1);
+    const Range ws =
+        range_of(workspace, (chunk + (shift_ok ? kStageSlack : 0)) * (int64_t)sizeof(float), 1);
     const int64_t se = extent(L, state_index), oe = extent(L, out_index);
     if (overlap(ws, range_of(master, se, 4)) || overlap(ws, range_of(exp_avg, se, 4)) ||
         overlap(ws, range_of(exp_avg_sq, se, 4)) || (out && overlap(ws, range_of(out, oe, 2))))
@@ -466,7 +474,7 @@ static zero_status staged_launch(const zero_layout *L, int32_t rank, const void 
     float *g = static_cast<float *>(workspace);
     const StepConsts ca = make_step_consts(nullptr, divisor);  // the average
     const StepConsts cb = make_step_consts(sc, 1.0f);          // g is averaged already
-    const void *const g1[1] = {g};
+    const void *g1[1] = {g};
     Request rq{};  // the second half: one fp32 gradient (the workspace)
     rq.layout = L;
     rq.rank = rank;
@@ -492,15 +500,46 @@ static zero_status staged_launch(const zero_layout *L, int32_t rank, const void 
          build_segments(L, rank, grad_index, state_index, out_index, u0, u1, from_range)) {
         for (int64_t off = 0; off < sg.len; off += chunk) {
             const int64_t cl = sg.len - off < chunk ? sg.len - off : chunk;
-            const Segment ga{sg.g_off + off, 0, 0, cl};
-            const std::vector<const void *> gp = offset_grads(grads, n_grads, ga.g_off, gsize);
-            int err = launch_stage_reduce(cl, segment_vec_aligned(ga, ra), gp.data(), n_grads,
-                                          grad_dtype, g, ca, stream);
+            const int64_t g0 = sg.g_off + off, s0 = sg.s_off + off;
+            // Place the chunk's g at the state's phase p (elements past a
+            // 16-byte boundary) and find the head h after which both the
+            // gradients (16-byte octs) and g are 16-byte aligned, so both
+            // halves run their vector kernels.  Such an h exists exactly when
+            // the gradients and the state share a quad phase, which is also
+            // when the fused step vectorizes; otherwise g starts at the
+            // workspace's own alignment.
+            int64_t p = 0, head = -1;
+            if (shift_ok) {
+                p = (int64_t)(((uintptr_t)master / sizeof(float) + (uint64_t)s0) % 4);
+                ra.state_ptrs[0] = g + p;
+                for (int64_t h = 0; h < 8 && head < 0; ++h)
+                    if (segment_vec_aligned(Segment{g0 + h, h, 0, cl - h}, ra))
+                        head = h;
+                if (head < 0)
+                    p = 0;
+            }
+            float *gb = g + p;
+            ra.state_ptrs[0] = gb;
+            const std::vector<const void *> gp = offset_grads(grads, n_grads, g0, gsize);
+            int err = hipSuccess;
+            if (head < 0) {  // no common phase: one launch, vector only if already aligned
+                err = launch_stage_reduce(cl, segment_vec_aligned(Segment{g0, 0, 0, cl}, ra),
+                                          gp.data(), n_grads, grad_dtype, gb, ca, stream);
+            } else {
+                const int64_t hl = head < cl ? head : cl;
+                err = launch_stage_reduce(hl, false, gp.data(), n_grads, grad_dtype, gb, ca, stream);
+                if (err == hipSuccess && cl > hl) {
+                    const std::vector<const void *> gv = offset_grads(grads, n_grads, g0 + hl, gsize);
+                    err = launch_stage_reduce(cl - hl, true, gv.data(), n_grads, grad_dtype, gb + hl,
+                                              ca, stream);
+                }
+            }
             if (err != hipSuccess)
                 return hip_fail(err, "zero_step_staged reduce");
-            const Segment sb{0, sg.s_off + off, sg.o_off + off, cl};
+            g1[0] = gb;  // the second half's gradient, for its alignment
+            const Segment sb{0, s0, sg.o_off + off, cl};
             for (const Piece &pc : build_pieces({sb}, rq)) {
-                const void *const gq[1] = {g + pc.g_off};
+                const void *const gq[1] = {gb + pc.g_off};
                 err = launch_step_piece(pc, gq, 1, ZERO_F32, master + pc.s_off,
                                         exp_avg + pc.s_off, exp_avg_sq + pc.s_off,
                                         out ? out + pc.o_off : nullptr, cb, stream,

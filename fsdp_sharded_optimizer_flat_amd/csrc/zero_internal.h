@@ -27,6 +27,7 @@ constexpr int64_t kMaxQuadsPerLaunch = int64_t(1) << 30;  // 32-bit dispatch gri
 // step is 0.6 points faster at N = 32, the staged one 5 points faster at 64.
 constexpr int32_t kStageMinRanks = 33;
 constexpr int64_t kStageMaxChunk = int64_t(1) << 25;
+constexpr int64_t kStageSlack = 4;  // elements to place a chunk at the state's 16-byte phase
 
 // One contiguous run of elements whose gradient, state and output indices all
 // advance together.  Offsets are element offsets into the respective buffers.

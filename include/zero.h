@@ -332,8 +332,12 @@ zero_status zero_step_device_clip(const zero_layout *layout, int32_t rank,
  *   workspace:  caller device memory, 16-byte aligned, not overlapping any
  *               other buffer of the call; its size sets the chunk (whole
  *               512-element tiles, at most 32M elements; at least 2048 bytes).
+ *               With 16 bytes to spare beyond the chunk, each chunk's reduced
+ *               gradient is placed at the state's 16-byte phase, so both
+ *               kernels take their vector paths whenever the gradients and
+ *               the state share a phase (as the fused step needs too).
  *               zero_step_staged_workspace_bytes gives the size that needs a
- *               single chunk up to that limit.
+ *               single chunk up to that limit, spare bytes included.
  * For n_grads <= 32 the fused step is as fast or faster and runs instead;
  * the workspace is then not used and may be NULL (its size query returns 0).
  * Async on `stream`.  Errors as zero_step, plus for n_grads > 32: EINVAL

@@ -416,7 +416,8 @@ static void check_device_validation(void)
     for (int q = 0; q < 64; ++q)
         g64[q] = base + 0x10000000 + (size_t)q * 0x10000; /* clear of w, m, v, o and wsp */
     size_t sb = 0;
-    CHECK(zero_step_staged_workspace_bytes(L64, 0, 64, &sb) == ZERO_OK && sb == 1024 * 4);
+    /* one chunk of whole 512-element tiles, plus 4 elements to place it at the state's phase */
+    CHECK(zero_step_staged_workspace_bytes(L64, 0, 64, &sb) == ZERO_OK && sb == (1024 + 4) * 4);
     size_t sb8 = 1;
     CHECK(zero_step_staged_workspace_bytes(L64, 0, 8, &sb8) == ZERO_OK && sb8 == 0);
     void *wsp = base + 0x2000000;

@@ -467,10 +467,12 @@ def test_staged_step_workspace_and_errors():
     assert z.zero_step_staged_workspace_bytes(L, 0, 8) == 0
     assert z.zero_step_staged_workspace_bytes(L, 0, 32) == 0
     assert z.zero_step_staged_workspace_bytes(L, 0, 33) > 0
-    assert z.zero_step_staged_workspace_bytes(L, 0, 64) == 4 * ((L.shard + 511) // 512 * 512)
-    assert z.zero_step_staged_workspace_bytes(L, -1, 64) == 4 * ((L.padded + 511) // 512 * 512)
+    # one chunk of whole 512-element tiles, plus 4 elements to place it at the
+    # state's 16-byte phase
+    assert z.zero_step_staged_workspace_bytes(L, 0, 64) == 4 * ((L.shard + 511) // 512 * 512 + 4)
+    assert z.zero_step_staged_workspace_bytes(L, -1, 64) == 4 * ((L.padded + 511) // 512 * 512 + 4)
     big = z.zero_pack(64, [64 * (1 << 26)])
-    assert z.zero_step_staged_workspace_bytes(big, -1, 64) == 4 * (1 << 25)
+    assert z.zero_step_staged_workspace_bytes(big, -1, 64) == 4 * ((1 << 25) + 4)
     lib = z.raw_library()
     sc = z.zero_adamw_scalars_for(1, 3e-4, 0.9, 0.95, 1e-8, 0.1)
     n = 64
