@@ -88,6 +88,29 @@ def parse():
                     help="time the ZeRO-Offload step: norm pass on the GPU, reduced gradient "
                          "down over PCIe, host step, bf16 parameters up (one rank's shard)")
     ap.add_argument("--chunk", type=int, default=1 << 22, help="offload pipeline chunk (elements)")
+    ap.add_argument("--ranks", type=int, default=None,
+                    help="simulated ranks N (default: the workload's); the same model at another N "
+                         "(one rank's shard for the ZeRO-3 workloads)")
+    ap.add_argument("--fused", action="store_true",
+                    help="above 32 ranks, time the fused step instead of the staged one")
+    ap.add_argument("--sweep-waves", default=None, metavar="FAMILY:CAPS",
+                    help="instead of the JSON contract line, time the step at several occupancy caps "
+                         "in interleaved rounds, e.g. step:4,5,6,7 (families: step, step1, norm)")
+    ap.add_argument("--rounds", type=int, default=3, help="rounds of --sweep-waves")
+    ap.add_argument("--stage-chunk", type=int, default=None,
+                    help="elements per chunk of the staged step (default: the largest, 32M)")
+    ap.add_argument("--stagger-kib", type=int, default=None,
+                    help="place buffer i at phase (i * KiB) mod 2 MiB instead of zero_arena_plan's "
+                         "256 KiB step (0: all at phase 0)")
+    ap.add_argument("--streamed", action="store_true",
+                    help="time the per-unit step streamed beside a backward stand-in: each unit's "
+                         "gradient buckets written in backward order, the unit stepped serially "
+                         "after it or overlapped on a side stream (two recycled bucket slots)")
+    ap.add_argument("--producer", default="gemm", choices=["gemm", "copy"],
+                    help="backward stand-in for --streamed: the weight-gradient GEMMs "
+                         "dW = dY^T X (MFMA) or a copy of resident gradients (HBM)")
+    ap.add_argument("--tokens", type=int, default=1024,
+                    help="tokens per simulated rank of the --streamed GEMM producer")
     ap.add_argument("--reshard", default=None, metavar="NAME",
                     help="time a checkpoint reshard (gpt2l_reshard, llama8b_reshard) instead of "
                          "the step: one destination rank's fp32 shard from flat block units to "
@@ -513,7 +536,33 @@ def reshard_bench(args):
     print(json.dumps(result))
 
 
-def setup_step(wl):
+def workload_from_args(args):
+    """The named workload, at --ranks N if given."""
+    import dataclasses
+
+    from fsdp_sharded_optimizer_flat_amd.workloads import WORKLOADS
+    wl = WORKLOADS[args.workload]
+    if args.ranks and args.ranks != wl.n_ranks:
+        wl = dataclasses.replace(wl, n_ranks=args.ranks, name=f"{wl.name}_n{args.ranks}",
+                                 description=wl.description + f" (at N = {args.ranks})")
+    return wl
+
+
+def stagger_plan(sizes, step_bytes):
+    """Buffer offsets in one allocation with buffer i at phase (i * step) mod
+    2 MiB (step 0: every buffer at phase 0); the library's zero_arena_plan is
+    this rule with a 256 KiB step.  For sweeping the step."""
+    page = 2 << 20
+    offs, at = [], 0
+    for i, b in enumerate(sizes):
+        want = (i * step_bytes) % page
+        at += (want - at % page) % page
+        offs.append(at)
+        at += b
+    return offs, at
+
+
+def setup_step(wl, fused=False, stage_chunk=None, stagger_kib=None):
     """The benchmark's resident inputs and its step, as bench.py times them:
     every streamed buffer in one allocation placed by zero_arena_plan, the
     workload's seeded gradients (the same every step) and master weights,
@@ -544,7 +593,9 @@ def setup_step(wl):
     # (gradients, master, m, v, out, and the reduced gradient when clipping).
     # Unclipped at 32+ ranks: the staged step, through a workspace chunk the
     # memory-side cache holds (zero_step_staged).
-    ws_elems = 0 if clip else z.zero_step_staged_workspace_bytes(L, wl.rank, n) // 4
+    ws_elems = 0 if clip or fused else z.zero_step_staged_workspace_bytes(L, wl.rank, n) // 4
+    if ws_elems and stage_chunk:   # a chosen chunk (whole 512-element tiles) plus the spare
+        ws_elems = stage_chunk + 4
     staged = ws_elems > 0
     specs = [(ge, torch.bfloat16)] * n + [(se, torch.float32)] * 3 + [(oe, torch.int16)]
     if clip:
@@ -552,7 +603,10 @@ def setup_step(wl):
     if staged:
         specs.append((ws_elems, torch.float32))
     sizes = [cnt * torch.empty(0, dtype=dt).element_size() for cnt, dt in specs]
-    offs, total = z.zero_arena_plan(sizes)
+    if stagger_kib is None:
+        offs, total = z.zero_arena_plan(sizes)
+    else:
+        offs, total = stagger_plan(sizes, stagger_kib << 10)
     arena = torch.empty(total, dtype=torch.uint8, device=dev)
     views = [arena[o:o + b].view(dt) for o, b, (_, dt) in zip(offs, sizes, specs)]
     grads, (master, m, v, out) = views[:n], views[n:n + 4]
@@ -615,6 +669,248 @@ def setup_step(wl):
     return ns
 
 
+def streamed_bench(args):
+    """The per-unit step streamed beside a backward stand-in (one GPU).
+
+    "ZeRO and FSDP sharding", How it works: each unit's gradients are
+    reduce-scattered as soon as backward has produced them, and the unit's
+    shards stepped; "ZeRO: Three Ledgers", section 4: bucketed reduce-scatter
+    makes gradients transient.  For the all-ranks workload (every simulated
+    rank's shards, GLOBAL buckets) a producer writes each unit's N gradient
+    buckets into one of two bucket slots, last unit first (backward order):
+
+      gemm -- every 2-D parameter's weight gradient dW = dY^T X with `tokens`
+              rows per simulated rank (bf16 MFMA through torch.matmul, written
+              straight into the bucket): the shape of backward's weight-
+              gradient work (the vector parameters, 0.05 % of a GPT-2 block,
+              keep their values: thousands of tiny launches per pass would
+              make the stand-in launch-bound);
+      copy -- the unit's buckets copied from resident gradients (HBM-bound).
+
+    Three passes over the whole model, each timed between synchronizations
+    (median of `steps` repetitions after `warmup`): the producer alone;
+    serial -- produce unit k, then step it (zero_step_units), one stream;
+    overlapped -- produce on the main stream, step unit k on a side stream
+    while unit k-1 is produced (events order the slot reuse).  Also the
+    whole-model step in one zero_step call.  hidden_fraction = (serial -
+    overlapped) / step-only time: how much of the optimizer step the overlap
+    hides behind the producer."""
+    import numpy as np
+    import torch
+
+    import fsdp_sharded_optimizer_flat_amd as z
+    from fsdp_sharded_optimizer_flat_amd import synth, workloads
+    from fsdp_sharded_optimizer_flat_amd.workloads import WORKLOADS
+
+    wl = workload_from_args(args)
+    if wl.rank >= 0 or wl.grad_index != "global":
+        raise SystemExit("--streamed runs the all-ranks workloads (gpt2l, gpt2l_block)")
+    n, h = wl.n_ranks, wl.hyper
+    dev = torch.device("cuda:0")
+    L = z.zero_pack(n, wl.unit_numel)
+    T = L.unit_table()
+    U, P = L.n_units, L.padded
+    G = z.ZERO_GLOBAL
+    shapes = {"gpt2l": workloads.gpt2_large_units(),
+              "gpt2l_block": [workloads.gpt2_block()]}[args.workload]
+    shapes = [[s for _, s in u] for u in shapes]
+    cap = int(T[:, 1].max())
+    master = torch.empty(P, dtype=torch.float32, device=dev)
+    synth.fill_normal_(master, wl.master_std, synth.seed_of(wl.seed, synth.TAG_MASTER))
+    m, v = torch.zeros_like(master), torch.zeros_like(master)
+    out = torch.zeros(P, dtype=torch.int16, device=dev)
+    slots = torch.empty(2, n, cap, dtype=torch.bfloat16, device=dev)
+    main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+    tok = args.tokens
+    if args.producer == "gemm":
+        # one contiguous activation matrix per input width, one dY^T per
+        # output height (row slices of the tallest are contiguous)
+        X = {k: (torch.randn(tok, k, device=dev) * 0.5).to(torch.bfloat16)
+             for k in sorted({s[1] for u in shapes for s in u if len(s) == 2})}
+        max_out = max(s[0] for u in shapes for s in u if len(s) == 2)
+        dYT = (torch.randn(max_out, tok, device=dev) * 1e-3).to(torch.bfloat16)
+        flops = 2.0 * tok * n * sum(s[0] * s[1] for u in shapes for s in u if len(s) == 2)
+    else:
+        src = torch.empty(n, P, dtype=torch.bfloat16, device=dev)
+        for r in range(n):
+            synth.fill_grad_(src[r], wl.grad_dist, wl.grad_scale, synth.seed_of(wl.seed, synth.TAG_GRAD, 1, r))
+        flops = 0.0
+
+    def produce(u, slot):
+        pad = int(T[u, 1])
+        if args.producer == "copy":
+            off = int(T[u, 3])
+            slots[slot, :, :pad].copy_(src[:, off:off + pad])
+            return
+        for r in range(n):
+            at = 0
+            for s in shapes[u]:
+                k = workloads.numel_of(s)
+                if len(s) == 2:   # dW [out, in] = dY^T [out, T] @ X [T, in]
+                    torch.matmul(dYT[:s[0]], X[s[1]], out=slots[slot, r, at:at + k].view(s[0], s[1]))
+                at += k
+
+    sc_t = [0]
+
+    def sc():
+        sc_t[0] += 1
+        return z.zero_adamw_scalars_for(sc_t[0], h["lr"], h["b1"], h["b2"], h["eps"], h["wd"], 1.0)
+
+    def step_unit(u, slot, stream, s):
+        pad = int(T[u, 1])
+        z.zero_step_units(L, -1, u, u + 1, [slots[slot, r, :pad] for r in range(n)], G, float(n),
+                          master, m, v, G, out, G, s, stream=stream)
+
+    order = list(range(U - 1, -1, -1))
+
+    def producer_only():
+        for i, u in enumerate(order):
+            produce(u, i % 2)
+
+    def serial():
+        s = sc()
+        for i, u in enumerate(order):
+            produce(u, i % 2)
+            step_unit(u, i % 2, main, s)
+
+    def overlapped():
+        s = sc()
+        stepped = [None] * U
+        for i, u in enumerate(order):
+            if i >= 2:
+                main.wait_event(stepped[i - 2])
+            produce(u, i % 2)
+            ready = torch.cuda.Event()
+            ready.record(main)
+            side.wait_event(ready)
+            step_unit(u, i % 2, side, s)
+            stepped[i] = torch.cuda.Event()
+            stepped[i].record(side)
+        main.wait_event(stepped[-1])
+
+    def overlapped_uncapped():
+        # the step's occupancy cap reserves LDS per workgroup, which can keep
+        # a GEMM's workgroups from becoming resident beside it: uncapped here
+        z.zero_set_waves_per_cu(z.ZERO_CAP_STEP, 0)
+        try:
+            overlapped()
+        finally:
+            z.zero_set_waves_per_cu(z.ZERO_CAP_STEP, -1)
+
+    def steps_only():
+        s = sc()
+        for i, u in enumerate(order):
+            step_unit(u, i % 2, main, s)
+
+    grads_full = None
+
+    def whole_step():
+        nonlocal grads_full
+        if grads_full is None:   # one resident set of N full gradients (12.4 GB for gpt2l)
+            grads_full = [torch.zeros(P, dtype=torch.bfloat16, device=dev) for _ in range(n)]
+        z.zero_step(L, -1, grads_full, G, float(n), master, m, v, G, out, G, sc())
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(args.steps):
+            t0 = time.perf_counter()
+            fn()
+            torch.cuda.synchronize()
+            ts.append(time.perf_counter() - t0)
+        return float(np.median(ts)) * 1e3, float(np.min(ts)) * 1e3
+
+    res = {}
+    for name, fn in (("producer_only", producer_only), ("steps_only", steps_only),
+                     ("serial", serial), ("overlapped", overlapped), ("serial_again", serial),
+                     ("overlapped_again", overlapped), ("overlapped_uncapped", overlapped_uncapped)):
+        res[name] = timed(fn)
+    del slots
+    if args.producer == "copy":
+        del src
+    torch.cuda.empty_cache()
+    res["whole_model_step"] = timed(whole_step)
+    ser = min(res["serial"][0], res["serial_again"][0])
+    ovl = min(res["overlapped"][0], res["overlapped_again"][0])
+    step_ms = res["steps_only"][0]
+    step_bytes, elements = z.zero_step_traffic(L, -1, n, z.ZERO_BF16, True)
+    result = {
+        "metric": "streamed per-unit optimizer step beside a backward stand-in: fraction of the "
+                  "step's time hidden by overlap",
+        "value": (ser - ovl) / step_ms,
+        "unit": "fraction of step time",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "higher_is_better": True,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "simulated_ranks": n, "units": U, "elements": int(elements),
+                   "producer": args.producer, "tokens_per_rank": tok if args.producer == "gemm" else None,
+                   "producer_tflop_per_pass": flops / 1e12 if flops else None,
+                   "bucket_slots_bytes": 2 * n * cap * 2,
+                   "full_gradients_bytes": n * P * 2},
+        "ms": {k: {"median": a, "min": b} for k, (a, b) in res.items()},
+        "serial_ms": ser,
+        "overlapped_ms": ovl,
+        "steps_only_hbm_GBps": step_bytes / (step_ms / 1e3) / 1e9,
+        "whole_model_step_hbm_GBps": step_bytes / (res["whole_model_step"][0] / 1e3) / 1e9,
+        "producer_tflops": flops / (res["producer_only"][0] / 1e3) / 1e12 if flops else None,
+        "timing": "wall clock between synchronizations, median of `steps` passes after `warmup`",
+    }
+    print(json.dumps(result))
+
+
+def sweep_waves(args, wl, S):
+    """Time the workload's step at several occupancy caps of one kernel
+    family, in interleaved rounds in one process (the buffers stay where they
+    are, so placement does not differ between caps).  Prints one JSON line
+    with each cap's % of 8 TB/s per round and the best cap."""
+    import numpy as np
+    import torch
+
+    import fsdp_sharded_optimizer_flat_amd as z
+
+    fam, caps = args.sweep_waves.split(":")
+    kind = {"step": z.ZERO_CAP_STEP, "step1": z.ZERO_CAP_STEP1, "norm": z.ZERO_CAP_NORM}[fam]
+    caps = [int(c) for c in caps.split(",")]
+    n = S.n
+    if S.clip:
+        step_bytes, _ = z.zero_step_traffic(S.L, wl.rank, 1, z.ZERO_F32, True)
+        norm_bytes, _ = z.zero_gradnorm_traffic(S.L, wl.rank, n, z.ZERO_BF16, True)
+        job_bytes = step_bytes + norm_bytes
+    else:
+        job_bytes, _ = z.zero_step_traffic(S.L, wl.rank, n, z.ZERO_BF16, True)
+    t = 0
+    for _ in range(args.warmup):
+        t += 1
+        S.one_step(t)
+    res = {c: [] for c in caps}
+    for _ in range(args.rounds):
+        for c in caps:
+            z.zero_set_waves_per_cu(kind, c)
+            t += 1
+            S.one_step(t)     # one untimed call at the new cap
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(S.stream)
+            for _ in range(args.steps):
+                t += 1
+                S.one_step(t)
+            b.record(S.stream)
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b) / args.steps
+            res[c].append(100.0 * job_bytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBPS)
+    z.zero_set_waves_per_cu(kind, -1)
+    med = {c: float(np.median(v)) for c, v in res.items()}
+    print(json.dumps({"sweep": fam, "workload": wl.name, "simulated_ranks": n,
+                      "staged": S.staged, "clip": S.clip, "steps_per_point": args.steps,
+                      "rounds": args.rounds, "pct_of_8TBps": res, "median": med,
+                      "best": max(med, key=med.get),
+                      "default": z.zero_get_waves_per_cu(kind, n)}))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -623,6 +919,9 @@ def main():
         sys.exit(2)
     if args.reshard:
         reshard_bench(args)
+        return
+    if args.streamed:
+        streamed_bench(args)
         return
     if args.offload:
         offload_bench(args)
@@ -640,8 +939,11 @@ def main():
     import fsdp_sharded_optimizer_flat_amd as z
     from fsdp_sharded_optimizer_flat_amd.workloads import WORKLOADS
 
-    wl = WORKLOADS[args.workload]
-    S = setup_step(wl)
+    wl = workload_from_args(args)
+    S = setup_step(wl, fused=args.fused, stage_chunk=args.stage_chunk, stagger_kib=args.stagger_kib)
+    if args.sweep_waves:
+        sweep_waves(args, wl, S)
+        return
     n, h, L, gidx, sidx, oidx, se = S.n, S.h, S.L, S.gidx, S.sidx, S.oidx, S.se
     clip, staged, ws_elems, stream, one_step = S.clip, S.staged, S.ws_elems, S.stream, S.one_step
 
@@ -709,7 +1011,7 @@ def main():
     torch.cuda.synchronize()
     per_ms = sorted(a.elapsed_time(b) for a, b in per_call)
 
-    traffic = measured_traffic(args.workload)
+    traffic = None if args.fused else measured_traffic(wl.name)
     box_copy = None if args.no_box_copy else box_copy_ceiling(z, torch, stream)
 
     result = {

@@ -39,6 +39,7 @@ ZERO_MAX_RANKS = 256
 ZERO_LAYOUT_MAGIC = 0x5A45524F
 ZERO_ABI_VERSION = 2
 ZERO_NOALLOC_SCRATCH_BYTES = 16 << 20
+ZERO_CAP_STEP, ZERO_CAP_STEP1, ZERO_CAP_NORM = 0, 1, 2
 
 i32, i64, f32, f64, vp, sz = C.c_int32, C.c_int64, C.c_float, C.c_double, C.c_void_p, C.c_size_t
 
@@ -159,6 +160,8 @@ _zero_ckpt_save = _sig("zero_ckpt_save", i32, C.c_char_p, vp, i32, i32, vp, vp, 
 _zero_ckpt_inspect = _sig("zero_ckpt_inspect", i32, C.c_char_p, i32, C.POINTER(ZeroCkptInfo), vp, sz,
                           C.POINTER(sz))
 _zero_ckpt_load = _sig("zero_ckpt_load", i32, vp, i32, vp, i32, i32, C.POINTER(i32), vp, vp, vp)
+_zero_set_waves_per_cu = _sig("zero_set_waves_per_cu", i32, i32, i32)
+_zero_get_waves_per_cu = _sig("zero_get_waves_per_cu", i32, i32, i32, C.POINTER(i32))
 _zero_strerror = _sig("zero_strerror", C.c_char_p, i32)
 _zero_last_hip_error = _sig("zero_last_hip_error", C.c_char_p)
 _zero_abi_version = _sig("zero_abi_version", i32)
@@ -175,6 +178,7 @@ EXPORTED = ["zero_layout_bytes", "zero_pack", "zero_pack_rows", "zero_reshard",
             "zero_clip_coef", "zero_ledger", "zero_sim_footprint",
             "zero_gather_buffer_bytes", "zero_arena_plan", "zero_step_traffic",
             "zero_gradnorm_traffic", "zero_ckpt_save", "zero_ckpt_inspect", "zero_ckpt_load",
+            "zero_set_waves_per_cu", "zero_get_waves_per_cu",
             "zero_strerror", "zero_last_hip_error", "zero_abi_version"]
 
 
@@ -882,6 +886,17 @@ def zero_ckpt_load(paths, layout: Layout, rank: int, verify: bool = True):
     _check(_zero_ckpt_load(C.addressof(arr), len(enc), layout.ptr, rank, int(verify), C.byref(step),
                            *[o.ctypes.data for o in out]), "zero_ckpt_load")
     return (step.value, *out)
+
+
+def zero_set_waves_per_cu(kind: int, waves: int):
+    """Cap resident waves per CU of a kernel family (-1: back to the default)."""
+    _check(_zero_set_waves_per_cu(kind, waves), "zero_set_waves_per_cu")
+
+
+def zero_get_waves_per_cu(kind: int, n_grads: int = 1) -> int:
+    w = i32()
+    _check(_zero_get_waves_per_cu(kind, n_grads, C.byref(w)), "zero_get_waves_per_cu")
+    return w.value
 
 
 def zero_strerror(status: int) -> str:

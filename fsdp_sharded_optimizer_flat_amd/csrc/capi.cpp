@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
+#include <atomic>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -184,50 +185,85 @@ size_t occupancy_cap_lds(int waves_per_cu, size_t static_lds)
     return lds > static_lds ? lds - static_lds : 0;
 }
 
-int step_waves_per_cu(int n_grads)
+namespace {
+// Occupancy caps set at run time (zero_set_waves_per_cu); -1 = not set.
+std::atomic<int> g_cap_override[3] = {{-1}, {-1}, {-1}};
+
+// The cap of one kernel family: the run-time setting, else the environment
+// variable (read once), else the built-in default.
+int cap_for(int kind, const char *env, int dflt)
 {
-    // Resident one-wave workgroups per CU.  Every wave streams N + 3 reads
-    // and 4 writes; a narrower window of tiles in flight keeps fewer DRAM rows
-    // competing per bank.  Measured on MI355X (same box, interleaved repeats):
-    // N = 8: 7 is best (6 starves the memory pipeline on some boxes; 8 / 10 /
-    // uncapped lose 1 / 2 / 7 points of the 8 TB/s peak); N = 64: 5 (4 was
-    // equal on one box and 3.4 points lower on another, 6 1.2 lower, 7 1.5
-    // lower).  Rank counts in between take the nearer setting.
-    // One gradient read from HBM (the clipped step on the norm pass's reduced
-    // gradient): 8 streams, best at 10 (8 and 12 within 0.3 points, 6: 3.5
-    // lower, uncapped: 1.4 lower).  Rank counts without a compile-time kernel
-    // keep two batches of loads in flight per wave instead of all ranks' and
-    // want more waves: 7 (5: 6-9 points lower).
-    static const int v = env_int("ZERO_STEP_WAVES_PER_CU", -1, 0, 64);
-    if (v >= 0)
-        return v;
-    if (n_grads == 1)
-        return 10;
-    return n_grads == 32 || n_grads == 64 ? 5 : 7;
+    const int o = g_cap_override[kind].load(std::memory_order_relaxed);
+    if (o >= 0)
+        return o;
+    static const int e[3] = {env_int("ZERO_STEP_WAVES_PER_CU", -1, 0, 64),
+                             env_int("ZERO_STEP1_WAVES_PER_CU", -1, 0, 64),
+                             env_int("ZERO_NORM_WAVES_PER_CU", -1, 0, 64)};
+    (void)env;
+    return e[kind] >= 0 ? e[kind] : dflt;
 }
 
-int staged_step_waves_per_cu()
+// Streams a wave of the fused step keeps in flight: every gradient whose
+// quad it loads before the first add (all N for the compile-time rank
+// counts; two batches of 16 for the run-time kernel), plus master, m, v.
+int step_streams_in_flight(int n_grads)
 {
-    // The staged step's second half reads a gradient chunk that the first
-    // half has just written, mostly from the memory-side cache: shorter load
-    // latency, and more waves keep the HBM streams busy.  At N = 64 on an 8B
-    // model's shard: 12 best (8: 0.8 points lower, 10: 0.2, 14 and 16: 0.2).
-    static const int v = env_int("ZERO_STEP_WAVES_PER_CU", -1, 0, 64);
-    return v >= 0 ? v : 12;
+    const bool compile_time = n_grads == 1 || n_grads == 2 || n_grads == 4 || n_grads == 8 ||
+                              n_grads == 16 || n_grads == 32 || n_grads == 64;
+    return (compile_time ? n_grads : (n_grads < 32 ? n_grads : 32)) + 3;
+}
+}  // namespace
+
+int step_waves_per_cu(int n_grads)
+{
+    // Resident one-wave workgroups per CU of the fused step, falling as the
+    // number of streams a wave keeps in flight grows (fewer tiles in flight
+    // keep fewer DRAM rows competing per bank; too few starve the memory
+    // pipeline).  Measured on MI355X with interleaved sweeps in one process
+    // (bench.py --sweep-waves step:...), % of 8 TB/s at each cap:
+    //    4 streams (N = 1): 10
+    //    5 streams (N = 2):  5: 53.0  6: 62.8  7: 78.0  8: 82.9  10: 84.1
+    //    7 streams (N = 4):  5: 58.8  6: 68.4  7: 80.8  8: 82.1  10: 82.4
+    //   11 streams (N = 8):  5: 66.0  6: 75.9  7: 84.0  8: 82.0  10: 80.9
+    //   19 streams (N = 16): 5: 76.3  6: 81.8  7: 78.9  8: 78.3  10: 77.3
+    //   67 streams (N = 64): 4: 72.5  5: 72.6  6: 71.8  7: 71.3
+    // The run-time kernel (any other N) issues one batch of 16 ranks at a
+    // time, two batches in flight, and wants more waves than its stream
+    // count suggests: N = 48: 5: 63.9  6: 69.7  7: 73.7  8: 73.6  10: 72.8;
+    // N = 128: 5: 64.4  6: 69.3  7: 72.0  8: 71.6  10: 71.0.
+    const int streams = step_streams_in_flight(n_grads);
+    const bool runtime_kernel = streams == 35 && n_grads != 32;
+    int dflt = streams <= 7 ? 10 : streams <= 11 ? 7 : streams <= 19 ? 6 : 5;
+    if (runtime_kernel)
+        dflt = 7;
+    return cap_for(0, "ZERO_STEP_WAVES_PER_CU", dflt);
+}
+
+int step1_waves_per_cu(bool staged_chunk)
+{
+    // The step on one fp32 gradient (4 streams in flight): the clipped step
+    // after the norm pass, best at 10 (8 and 12 within 0.3 points, 6: 3.5
+    // lower, uncapped: 1.4 lower); the staged step's second half, whose
+    // gradient chunk was just written and is mostly read back from the
+    // memory-side cache (shorter load latency), best at 12 (8: 0.8 points
+    // lower, 10: 0.2, 14 and 16: 0.2).
+    return cap_for(1, "ZERO_STEP1_WAVES_PER_CU", staged_chunk ? 12 : 10);
 }
 
 int norm_waves_per_cu(int n_grads)
 {
-    // The norm pass (and the staged step's reduction) streams N reads and
-    // one write, 16 bytes per rank per lane; at N = 64, 5 resident waves per
-    // CU measured best (4: equal to 0.5 points lower, 6: 1.1 lower, 7: 3.8
-    // lower, 3: starved).  Fewer ranks, and
-    // rank counts without a compile-time kernel (two batches in flight),
-    // keep less in flight per wave and take 7.
-    static const int v = env_int("ZERO_NORM_WAVES_PER_CU", -1, 0, 64);
-    if (v >= 0)
-        return v;
-    return n_grads == 32 || n_grads == 64 ? 5 : 7;
+    // The norm pass and the staged step's reduction: N reads of 16 bytes per
+    // lane and one write.  Measured (bench.py --sweep-waves norm:...):
+    // compile-time N = 64 (staged reduction) 4: 78.5  5: 78.6  6: 77.8
+    // 7: 76.4, and N = 32 like it (3 starves at 57 %); the run-time kernel,
+    // two batches of 16 ranks in flight, N = 48: 5: 72.1  6: 76.9  7: 76.3
+    // 8: 75.9; N = 128: 5: 74.8  6: 77.3  7: 77.8  8: 76.9; N = 256: 5: 74.7
+    // 6: 76.7  7: 79.5  8: 78.9, so 7; fewer ranks keep less in flight and
+    // take 7 as well.
+    const int streams = step_streams_in_flight(n_grads);
+    const bool runtime_kernel = streams == 35 && n_grads != 32;
+    const int dflt = !runtime_kernel && streams > 19 ? 5 : 7;
+    return cap_for(2, "ZERO_NORM_WAVES_PER_CU", dflt);
 }
 
 zero_status hip_fail(int err, const char *where)
@@ -543,7 +579,7 @@ static zero_status staged_launch(const zero_layout *L, int32_t rank, const void 
                 err = launch_step_piece(pc, gq, 1, ZERO_F32, master + pc.s_off,
                                         exp_avg + pc.s_off, exp_avg_sq + pc.s_off,
                                         out ? out + pc.o_off : nullptr, cb, stream,
-                                        staged_step_waves_per_cu());
+                                        step1_waves_per_cu(true));
                 if (err != hipSuccess)
                     return hip_fail(err, "zero_step_staged step");
             }
@@ -918,5 +954,24 @@ extern "C" const char *zero_strerror(zero_status s)
 }
 
 extern "C" const char *zero_last_hip_error(void) { return t_last_hip_error.c_str(); }
+
+extern "C" zero_status zero_set_waves_per_cu(int32_t kind, int32_t waves)
+{
+    if (kind < ZERO_CAP_STEP || kind > ZERO_CAP_NORM || waves < -1 || waves > 64)
+        return ZERO_EINVAL;
+    g_cap_override[kind].store(waves, std::memory_order_relaxed);
+    return ZERO_OK;
+}
+
+extern "C" zero_status zero_get_waves_per_cu(int32_t kind, int32_t n_grads, int32_t *waves)
+{
+    if (kind < ZERO_CAP_STEP || kind > ZERO_CAP_NORM || !waves || n_grads < 1 ||
+        n_grads > ZERO_MAX_RANKS)
+        return ZERO_EINVAL;
+    *waves = kind == ZERO_CAP_STEP ? step_waves_per_cu(n_grads)
+           : kind == ZERO_CAP_STEP1 ? step1_waves_per_cu(false)
+                                    : norm_waves_per_cu(n_grads);
+    return ZERO_OK;
+}
 
 extern "C" int32_t zero_abi_version(void) { return ZERO_ABI_VERSION; }

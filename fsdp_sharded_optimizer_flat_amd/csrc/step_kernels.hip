@@ -186,11 +186,13 @@ int launch_step_piece(const Piece &pc, const void *const *grads, int n_grads, in
         if (bf)
             return p2 ? launch_bf16_quads<true>(grads, n_grads, w, m, v, out, nq, c, st)
                       : launch_bf16_quads<false>(grads, n_grads, w, m, v, out, nq, c, st);
-        if (n_grads == 1)  // one reduced gradient, e.g. the clipped step after the norm pass
+        if (n_grads == 1) {  // one reduced gradient, e.g. the clipped step after the norm pass
+            const int wv = waves_per_cu >= 0 ? waves_per_cu : step1_waves_per_cu(false);
             return p2 ? launch_quads_nr<1, F32Quad, true>(grads, n_grads, 16, w, m, v, out, nq, c,
-                                                          st, waves_per_cu)
+                                                          st, wv)
                       : launch_quads_nr<1, F32Quad, false>(grads, n_grads, 16, w, m, v, out, nq, c,
-                                                           st, waves_per_cu);
+                                                           st, wv);
+        }
         return p2 ? launch_quads_nr<0, F32Quad, true>(grads, n_grads, 16, w, m, v, out, nq, c, st)
                   : launch_quads_nr<0, F32Quad, false>(grads, n_grads, 16, w, m, v, out, nq, c, st);
     }

@@ -113,13 +113,12 @@ int device_cu_count();
 // waves stream at once.  Cached per device.
 size_t occupancy_cap_lds(int waves_per_cu, size_t static_lds);
 
-// Target resident waves per CU of the step and norm kernels.  Defaults were
-// measured on MI355X; ZERO_STEP_WAVES_PER_CU / ZERO_NORM_WAVES_PER_CU
-// override them for launch-shape sweeps (0 disables the cap).
-int step_waves_per_cu(int n_grads);
-int norm_waves_per_cu(int n_grads);
-// The staged step's second half (one fp32 gradient, just written).
-int staged_step_waves_per_cu();
+// Target resident waves per CU of the streaming kernels (0 = no cap):
+// zero_set_waves_per_cu, else ZERO_STEP_WAVES_PER_CU / ZERO_STEP1_WAVES_PER_CU
+// / ZERO_NORM_WAVES_PER_CU, else the defaults measured on MI355X.
+int step_waves_per_cu(int n_grads);   // the fused step over N gradients
+int step1_waves_per_cu(bool staged_chunk);  // the step on one fp32 gradient
+int norm_waves_per_cu(int n_grads);   // the norm pass and the staged reduction
 
 // Record a HIP error code for zero_last_hip_error(); returns ZERO_EHIP.
 zero_status hip_fail(int hip_error, const char *where);

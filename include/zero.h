@@ -665,6 +665,35 @@ zero_status zero_gradnorm_traffic(const zero_layout *layout, int32_t rank, int32
                                   double *bytes, int64_t *elements);
 
 /* ------------------------------------------------------------------------
+ * Launch shape.  Every streaming kernel runs one wave64 per workgroup and
+ * caps how many are resident per compute unit (through a dynamic LDS
+ * reservation the kernels never touch): fewer tiles in flight keep fewer DRAM
+ * rows competing, too few starve the memory pipeline.  The defaults were
+ * measured on MI355X per kernel family, from the number of streams a wave
+ * keeps in flight; these calls let a caller read them and sweep them
+ * (bench.py --sweep-waves).  The environment variables
+ * ZERO_STEP_WAVES_PER_CU, ZERO_STEP1_WAVES_PER_CU and ZERO_NORM_WAVES_PER_CU
+ * (read once) set the same three families.
+ *   ZERO_CAP_STEP   the fused step over N gradients
+ *   ZERO_CAP_STEP1  the step on one fp32 gradient (the clipped step after
+ *                   the norm pass, the staged step's second half)
+ *   ZERO_CAP_NORM   the norm pass and the staged step's reduction
+ * ------------------------------------------------------------------------ */
+#define ZERO_CAP_STEP 0
+#define ZERO_CAP_STEP1 1
+#define ZERO_CAP_NORM 2
+
+/* Set a family's cap for later launches of this process: waves 1..64, 0 = no
+ * cap, -1 = back to the environment / default.  Not ordered with launches on
+ * other threads.  EINVAL: bad kind or value. */
+zero_status zero_set_waves_per_cu(int32_t kind, int32_t waves);
+
+/* The cap a launch of the family over n_grads gradients would use now (for
+ * ZERO_CAP_STEP1 the clipped step's).  EINVAL: bad kind, n_grads out of
+ * 1..ZERO_MAX_RANKS, NULL. */
+zero_status zero_get_waves_per_cu(int32_t kind, int32_t n_grads, int32_t *waves);
+
+/* ------------------------------------------------------------------------
  * Diagnostics.
  * ------------------------------------------------------------------------ */
 

@@ -494,3 +494,31 @@ def test_staged_step_workspace_and_errors():
     assert call(w, (1 << 64) - 1) == z.ZERO_EINVAL
     assert call(w - 4096, 1 << 40) == z.ZERO_EINVAL
     assert lib.zero_step_staged_workspace_bytes(L.ptr, 0, 0, C.byref(C.c_size_t())) == z.ZERO_ERANGE
+
+
+def test_occupancy_caps_table_and_setter():
+    """The measured defaults per kernel family (from the streams a wave keeps
+    in flight), the run-time setter, and its argument checks."""
+    S, S1, NRM = z.ZERO_CAP_STEP, z.ZERO_CAP_STEP1, z.ZERO_CAP_NORM
+    want = {1: 10, 2: 10, 4: 10, 8: 7, 16: 6, 32: 5, 33: 7, 48: 7, 64: 5, 100: 7, 256: 7}
+    if any(os.environ.get(v) for v in ("ZERO_STEP_WAVES_PER_CU", "ZERO_STEP1_WAVES_PER_CU",
+                                      "ZERO_NORM_WAVES_PER_CU")):
+        pytest.skip("occupancy environment overrides set")
+    assert {n: z.zero_get_waves_per_cu(S, n) for n in want} == want
+    assert z.zero_get_waves_per_cu(S1, 1) == 10
+    assert [z.zero_get_waves_per_cu(NRM, n) for n in (8, 32, 48, 64, 128)] == [7, 5, 7, 5, 7]
+    try:
+        z.zero_set_waves_per_cu(S, 3)
+        assert z.zero_get_waves_per_cu(S, 64) == 3 and z.zero_get_waves_per_cu(S, 8) == 3
+        assert z.zero_get_waves_per_cu(NRM, 64) == 5          # other families untouched
+        z.zero_set_waves_per_cu(S1, 0)
+        assert z.zero_get_waves_per_cu(S1, 1) == 0
+    finally:
+        z.zero_set_waves_per_cu(S, -1)
+        z.zero_set_waves_per_cu(S1, -1)
+    assert z.zero_get_waves_per_cu(S, 64) == 5
+    for kind, waves in ((3, 5), (-1, 5), (S, 65), (S, -2)):
+        with pytest.raises(z.ZeroError):
+            z.zero_set_waves_per_cu(kind, waves)
+    with pytest.raises(z.ZeroError):
+        z.zero_get_waves_per_cu(S, 0)

@@ -45,3 +45,20 @@ def test_cpu_baseline_one_thread_and_all_cores():
             assert allc["cores"] == min(16, avail) and allc["value"] > 0
         else:
             assert "all_cores" not in res
+
+
+def test_stagger_plan_reproduces_the_arena_plan():
+    """bench.py --stagger-kib 256 places the buffers exactly as the library's
+    zero_arena_plan (which --stagger-kib sweeps around)."""
+    import numpy as np
+    z = pytest.importorskip("fsdp_sharded_optimizer_flat_amd")
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import bench
+    rng = np.random.default_rng(4)
+    for _ in range(50):
+        sizes = [int(x) for x in rng.integers(0, 40 << 20, int(rng.integers(1, 70)))]
+        offs, total = bench.stagger_plan(sizes, 256 << 10)
+        lib_offs, lib_total = z.zero_arena_plan(sizes)
+        assert list(offs) == list(lib_offs) and total == lib_total
+        offs, total = bench.stagger_plan(sizes, 0)
+        assert all(o % (2 << 20) == 0 for o in offs) and total == offs[-1] + sizes[-1]
