@@ -97,6 +97,10 @@ def parse():
                     help="instead of the JSON contract line, time the step at several occupancy caps "
                          "in interleaved rounds, e.g. step:4,5,6,7 (families: step, step1, norm)")
     ap.add_argument("--rounds", type=int, default=3, help="rounds of --sweep-waves")
+    ap.add_argument("--norm-only", action="store_true",
+                    help="clipped workload: time the norm pass alone (it writes g unless --no-g)")
+    ap.add_argument("--no-g", action="store_true",
+                    help="with --norm-only: the norm pass without writing the reduced gradient")
     ap.add_argument("--stage-chunk", type=int, default=None,
                     help="elements per chunk of the staged step (default: the largest, 32M)")
     ap.add_argument("--stagger-kib", type=int, default=None,
@@ -562,7 +566,7 @@ def stagger_plan(sizes, step_bytes):
     return offs, at
 
 
-def setup_step(wl, fused=False, stage_chunk=None, stagger_kib=None):
+def setup_step(wl, fused=False, stage_chunk=None, stagger_kib=None, norm_only=None):
     """The benchmark's resident inputs and its step, as bench.py times them:
     every streamed buffer in one allocation placed by zero_arena_plan, the
     workload's seeded gradients (the same every step) and master weights,
@@ -640,9 +644,12 @@ def setup_step(wl, fused=False, stage_chunk=None, stagger_kib=None):
             # host round trip inside the step
             if ev:
                 ev[0].record(stream)
-            z.zero_gradnorm_async(L, wl.rank, grads, gidx, float(n), g_red, sidx, ws, ss_dev, stream)
+            z.zero_gradnorm_async(L, wl.rank, grads, gidx, float(n), None if norm_only == "no_g" else g_red,
+                                  sidx, ws, ss_dev, stream)
             if ev:
                 ev[1].record(stream)
+            if norm_only:   # the norm pass alone (--norm-only), with or without writing g
+                return
             z.zero_clip_coef_async(ss_dev, wl.clip_max_norm, coef_dev, stream)
             z.zero_step_device_clip(L, wl.rank, [g_red], sidx, 1.0, master, m, v, sidx, out, oidx, sc,
                                     coef_dev, stream)
@@ -940,7 +947,10 @@ def main():
     from fsdp_sharded_optimizer_flat_amd.workloads import WORKLOADS
 
     wl = workload_from_args(args)
-    S = setup_step(wl, fused=args.fused, stage_chunk=args.stage_chunk, stagger_kib=args.stagger_kib)
+    if args.norm_only and wl.clip_max_norm is None:
+        raise SystemExit("--norm-only needs the clipped workload (llama8b_z3_clip)")
+    S = setup_step(wl, fused=args.fused, stage_chunk=args.stage_chunk, stagger_kib=args.stagger_kib,
+                   norm_only=("no_g" if args.no_g else "g") if args.norm_only else None)
     if args.sweep_waves:
         sweep_waves(args, wl, S)
         return
@@ -983,7 +993,9 @@ def main():
     fused_bytes, _ = z.zero_step_traffic(L, wl.rank, n, z.ZERO_BF16, True)  # 2N + 26
     if clip:
         step_bytes, _ = z.zero_step_traffic(L, wl.rank, 1, z.ZERO_F32, True)
-        norm_bytes, _ = z.zero_gradnorm_traffic(L, wl.rank, n, z.ZERO_BF16, True)
+        norm_bytes, _ = z.zero_gradnorm_traffic(L, wl.rank, n, z.ZERO_BF16, not args.no_g)
+        if args.norm_only:
+            step_bytes = 0.0
         job_bytes = step_bytes + norm_bytes   # 2N + 34: the bytes the two passes need
         dom_bytes, dom_name = norm_bytes, "norm_kernel (rank-sum + divide + fp32 g + binary64 sum of squares)"
     else:
@@ -1011,7 +1023,8 @@ def main():
     torch.cuda.synchronize()
     per_ms = sorted(a.elapsed_time(b) for a, b in per_call)
 
-    traffic = None if args.fused else measured_traffic(wl.name)
+    traffic = None if args.fused or args.norm_only or args.stage_chunk or args.stagger_kib is not None \
+        else measured_traffic(wl.name)
     box_copy = None if args.no_box_copy else box_copy_ceiling(z, torch, stream)
 
     result = {
@@ -1038,6 +1051,12 @@ def main():
             "state_dtype": "f32",
             "out_dtype": "bf16",
             "clip_max_norm": wl.clip_max_norm,
+            "variant": ", ".join(v for v in (
+                "fused step above 32 ranks" if args.fused else "",
+                ("norm pass only, " + ("g not written" if args.no_g else "g written")) if args.norm_only else "",
+                f"staged chunk {args.stage_chunk} elements" if args.stage_chunk else "",
+                f"buffers staggered by {args.stagger_kib} KiB" if args.stagger_kib is not None else "") if v)
+                or None,
             "algorithmic_bytes_per_step": job_bytes,
             "bytes_per_element": job_bytes / elements,
             "hbm_GBps_whole_step": job_bytes / (wall / args.steps) / 1e9,
