@@ -5,9 +5,18 @@
 //
 // Pure data movement, bound by HBM bandwidth.  A plan has one run per (unit,
 // source rank) pair: hundreds of runs of a few KB to a few hundred MB.  Up to
-// kCopyPieces runs travel by value in one launch's kernel arguments, and each
-// workgroup finds its run from the prefix sums of block counts, so a whole
-// plan takes a handful of launches.
+// kCopyPieces runs travel by value in one launch's kernel arguments, so a
+// whole plan takes a handful of launches.
+//
+// Finding its run is the only work a workgroup does before its load, and it
+// lengthens the life of every 1 KB workgroup: a binary search over the runs'
+// block prefix sums (seven dependent scalar loads) cost 3 to 6 points of the
+// 8 TB/s peak against a plain copy.  So the launch also carries a group table:
+// the grid's blocks in 512 equal groups, and for each the run that holds the
+// group's first block, with a flag when the whole group lies in that run.  A
+// workgroup reads its group's entry (one scalar load, its address known from
+// blockIdx alone), steps forward over run ends only when its group is
+// flagged as holding a run boundary, then loads its run.
 //
 // Each workgroup is one wave64 and each lane moves one 16-byte block: 1 KB
 // per workgroup.  Measured on MI355X, spans that small stream best (a plain
@@ -33,24 +42,32 @@ namespace {
 using dev::st_span;
 using dev::u32x4;
 
-constexpr int kCopyPieces = 96;     // runs per launch (kernel arguments: 2.7 KB)
+constexpr int kCopyPieces = 96;     // runs per launch
 constexpr int kCopyThreads = kWave; // one wave64 per workgroup
 constexpr int64_t kCopyPerBlock = kCopyThreads;  // 16-byte blocks per workgroup (1 KB)
-constexpr int64_t kMaxPieceBytes = int64_t(1) << 34;
-constexpr int64_t kMaxBlocksPerLaunch = int64_t(1) << 26;  // 2^32 work-items
+constexpr int kGroups = 512;        // group-table entries per launch
+constexpr int kMinGroupShift = 9;   // blocks per group: 2^9 .. 2^17
+constexpr int kMaxGroupShift = 17;
+constexpr int64_t kMaxBlocksPerLaunch = int64_t(kGroups) << kMaxGroupShift;  // 2^26
+constexpr int64_t kMaxPieceBytes = int64_t(1) << 31;  // element count fits 32 bits
 
 struct CopyPiece {
     const unsigned char *src;  // null: zero-fill
     unsigned char *dst;
-    int64_t n;                 // elements
+    uint32_t n;                // elements
+    uint32_t first;            // the launch's first block of this piece
 };
 
+// Kernel arguments of one launch: 3,208 bytes.
 struct CopyBatch {
     CopyPiece p[kCopyPieces];
-    uint32_t block_end[kCopyPieces];  // inclusive prefix sums of block counts
+    uint32_t end[kCopyPieces];   // piece i covers blocks [p[i].first, end[i])
+    uint32_t group[kGroups / 4]; // byte g: the piece holding group g's first
+                                 // block; bit 7 set when the group lies in it whole
     int32_t n_pieces;
-    int32_t elem;                     // bytes per element: 2 or 4
+    int32_t elem;                // bytes per element: 2 or 4
 };
+static_assert(sizeof(CopyBatch) <= 4096, "kernel arguments are limited to 4 KB");
 
 // Split of a run: `head` elements before dst's first 16-byte boundary, then
 // `blocks` whole 16-byte blocks, then `tail` elements.
@@ -98,19 +115,19 @@ __device__ __forceinline__ u32x4 funnel(u32x4 lo, u32x4 hi, unsigned delta)
     return r;
 }
 
+// SHIFT: log2 of the blocks per group, fixed per launch so that the group
+// index needs no argument.
+template <int SHIFT>
 __global__ __launch_bounds__(kCopyThreads) void copy_batch_kernel(const CopyBatch b)
 {
     const uint32_t blk = blockIdx.x;
-    int lo = 0, hi = b.n_pieces - 1;  // first piece whose block_end exceeds blk
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (blk >= b.block_end[mid])
-            lo = mid + 1;
-        else
-            hi = mid;
-    }
-    const int i = lo;
-    const uint32_t first = i ? b.block_end[i - 1] : 0u;
+    const uint32_t g = blk >> SHIFT;
+    const uint32_t entry = (b.group[g >> 2] >> ((g & 3u) * 8u)) & 0xffu;
+    int i = (int)(entry & 0x7fu);
+    if (!(entry & 0x80u))
+        while (blk >= b.end[i])  // the last piece ends at the grid size: the walk stops there
+            ++i;
+    const uint32_t first = b.p[i].first;
     const unsigned char *s = b.p[i].src;
     unsigned char *d = b.p[i].dst;
     const int e = b.elem;
@@ -146,6 +163,32 @@ __global__ __launch_bounds__(kCopyThreads) void copy_batch_kernel(const CopyBatc
     }
 }
 
+// The group table of a launch of `total` blocks in pieces ending at end[0..n).
+void fill_groups(CopyBatch &b, uint32_t total, int shift)
+{
+    int first_piece = 0, last_piece = 0;
+    for (uint32_t g = 0; g < (uint32_t)kGroups; ++g) {
+        const uint32_t a = g << shift;
+        if (a >= total)
+            break;
+        const uint32_t z = std::min<uint64_t>((uint64_t)a + (1u << shift) - 1u, total - 1u);
+        while (b.end[first_piece] <= a)
+            ++first_piece;
+        if (last_piece < first_piece)
+            last_piece = first_piece;
+        while (b.end[last_piece] <= z)
+            ++last_piece;
+        const uint32_t entry = (uint32_t)first_piece | (first_piece == last_piece ? 0x80u : 0u);
+        b.group[g >> 2] |= entry << ((g & 3u) * 8u);
+    }
+}
+
+template <int SHIFT>
+void launch_copy(const CopyBatch &b, uint32_t blocks, hipStream_t stream)
+{
+    hipLaunchKernelGGL(copy_batch_kernel<SHIFT>, dim3(blocks), dim3(kCopyThreads), 0, stream, b);
+}
+
 struct Batcher {
     CopyBatch b{};
     int64_t blocks = 0;
@@ -156,8 +199,22 @@ struct Batcher {
     {
         if (b.n_pieces == 0 || err != hipSuccess)
             return;
-        hipLaunchKernelGGL(copy_batch_kernel, dim3((unsigned)blocks), dim3(kCopyThreads), 0, stream,
-                           b);
+        const uint32_t total = (uint32_t)blocks;
+        int shift = kMinGroupShift;
+        while (((total - 1u) >> shift) >= (uint32_t)kGroups)
+            ++shift;
+        fill_groups(b, total, shift);
+        switch (shift) {
+        case 9: launch_copy<9>(b, total, stream); break;
+        case 10: launch_copy<10>(b, total, stream); break;
+        case 11: launch_copy<11>(b, total, stream); break;
+        case 12: launch_copy<12>(b, total, stream); break;
+        case 13: launch_copy<13>(b, total, stream); break;
+        case 14: launch_copy<14>(b, total, stream); break;
+        case 15: launch_copy<15>(b, total, stream); break;
+        case 16: launch_copy<16>(b, total, stream); break;
+        default: launch_copy<kMaxGroupShift>(b, total, stream); break;
+        }
         err = hipGetLastError();
         const int32_t elem = b.elem;
         b = CopyBatch{};
@@ -177,9 +234,10 @@ struct Batcher {
             CopyPiece &pc = b.p[b.n_pieces];
             pc.src = src;
             pc.dst = dst;
-            pc.n = take;
+            pc.n = (uint32_t)take;
+            pc.first = (uint32_t)blocks;
             blocks += nb;
-            b.block_end[b.n_pieces] = (uint32_t)blocks;
+            b.end[b.n_pieces] = (uint32_t)blocks;
             ++b.n_pieces;
             if (src)
                 src += take * e;

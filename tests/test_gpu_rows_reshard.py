@@ -305,6 +305,28 @@ def test_full_size_reshard(name):
     assert bad == 0, f"{bad} elements differ"
 
 
+@pytest.mark.parametrize("dst_shift", [0, 1])
+def test_reshard_large_launch_group_table(dst_shift):
+    """One launch of more than 2^18 blocks (its group table at 2^11 blocks
+    per group) in which long runs and runs of a few elements share groups;
+    the destination at the sources' 16-byte phase, or one element off it."""
+    units = [70_000_003, 5, 3, 70_000_001, 7, 2]
+    A, B = z.zero_pack(2, units), z.zero_pack(1, units)
+    log(f"large launch: 2 x {A.shard} -> {B.shard}, destination shifted by {dst_shift}")
+    src = []
+    for q in range(2):
+        b = torch.empty(A.shard, dtype=torch.int32, device=DEV)
+        fill_stream_positions(A, q, b)
+        src.append(b.view(torch.float32))
+    dst = dev_buffer(B.shard, torch.int32, shift=dst_shift, fill=-1)
+    z.zero_reshard(A, src, B, 0, dst.view(torch.float32))
+    want = torch.empty(B.shard, dtype=torch.int32, device=DEV)
+    fill_stream_positions(B, 0, want)
+    torch.cuda.synchronize()
+    bad = int((dst != want).sum().item())
+    assert bad == 0, f"{bad} elements differ"
+
+
 def test_reshard_with_prepared_source_pointers():
     """src_ptrs (sources marshalled once) gives the same bytes as passing
     the tensors, and a mismatched destination type is still refused."""
