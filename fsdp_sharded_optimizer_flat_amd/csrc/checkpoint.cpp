@@ -39,6 +39,7 @@ namespace {
 constexpr char kMagic[8] = {'Z', 'E', 'R', 'O', 'C', 'K', 'P', 'T'};
 constexpr uint32_t kFormat = 1;
 constexpr int32_t kArrays = 3;  // master, exp_avg, exp_avg_sq
+constexpr int64_t kMaxShard = int64_t(1) << 56;  // keeps every file offset within int64
 
 struct FileHeader {
     char magic[8];
@@ -143,7 +144,8 @@ zero_status read_header(int fd, Saved *s)
     const FileHeader &h = s->h;
     if (std::memcmp(h.magic, kMagic, 8) != 0 || h.format != kFormat || h.n_arrays != kArrays ||
         h.dtype != ZERO_F32 || h.n_ranks < 1 || h.n_units < 0 || h.n_units > ZERO_MAX_UNITS ||
-        h.rank < 0 || h.rank >= h.n_ranks || h.step < 0 || h.shard < 0 || h.numel < 0)
+        h.rank < 0 || h.rank >= h.n_ranks || h.step < 0 || h.shard < 0 || h.numel < 0 ||
+        h.shard > kMaxShard)
         return ZERO_ECORRUPT;
     s->units.resize((size_t)h.n_units);
     if (h.n_units > 0 && !pread_all(fd, s->units.data(), 16 * (size_t)h.n_units, sizeof h))

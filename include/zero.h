@@ -573,7 +573,9 @@ zero_status zero_ckpt_inspect(const char *path, int32_t verify, zero_ckpt_info *
  * exp_avg_sq: host arrays of to->shard floats; *step (may be NULL) receives
  * the saved step count.  EINVAL (bad arguments, files out of rank order or
  * of another N, a destination layout with another element count), EIO,
- * ECORRUPT. */
+ * ECORRUPT.  Every file is opened and checked before the first byte of the
+ * destination is written; a read that fails after that (EIO) leaves the
+ * destination partly filled. */
 zero_status zero_ckpt_load(const char *const *paths, int32_t n_files, const zero_layout *to,
                            int32_t dst_rank, int32_t verify, int32_t *step, float *master,
                            float *exp_avg, float *exp_avg_sq);

@@ -214,6 +214,12 @@ def test_damaged_and_mismatched_files_are_refused(tmp_path):
     magic = str(tmp_path / "magic.zck")
     open(magic, "wb").write(b"X" + open(paths[1], "rb").read()[1:])
     assert status(z.zero_ckpt_inspect, magic, False) == z.ZERO_ECORRUPT
+    # a header whose shard size would overflow the file offsets (bytes 40..47)
+    huge = str(tmp_path / "huge.zck")
+    data = bytearray(open(paths[1], "rb").read())
+    data[40:48] = (1 << 60).to_bytes(8, "little")
+    open(huge, "wb").write(bytes(data))
+    assert status(z.zero_ckpt_inspect, huge, False) == z.ZERO_ECORRUPT
     # missing file, files out of rank order, too few files
     assert status(z.zero_ckpt_load, paths[:3] + [str(tmp_path / "none.zck")], L, 0) == z.ZERO_EIO
     assert status(z.zero_ckpt_load, [paths[1], paths[0]] + paths[2:], L, 0) == z.ZERO_EINVAL
