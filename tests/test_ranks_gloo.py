@@ -9,7 +9,12 @@ every rank scales by the same coefficient, and the bf16 shards are gathered.
 The gathered parameters and state must equal the single-process all-ranks
 step bit for bit ("ZeRO and FSDP sharding", Code: reduce-scatter, the local
 AdamW, all-gather; Implementation notes: the global norm from the shards'
-sums of squares)."""
+sums of squares).
+
+A second test runs the checkpoint across world sizes: every rank of one world
+writes its own shard file, the ranks of another world size each load their
+shard from all the files (resharded from flat blocks to dim-0 rows) and train
+on; the result equals unsharded AdamW on the same gradients, bit for bit."""
 import os
 import socket
 
@@ -126,3 +131,106 @@ def test_ranks_over_gloo_equal_the_all_ranks_step(world, tmp_path):
         for name, ref in (("w", w), ("m", m), ("v", v)):
             assert np.array_equal(res[f"{name}{q}"].view(np.uint32), ref[js].view(np.uint32)), (name, q)
         assert np.array_equal(res[f"out{q}"].astype(np.uint16), out[js]), ("out", q)
+
+
+# ---------------------------------------------------------------------------
+# Every rank writes its own checkpoint shard; another world size loads it
+# ---------------------------------------------------------------------------
+
+SHAPES = [(100, 10), (37,), (2053,), (64, 48)]
+
+
+def _ck_grad(q, t, p):
+    return (np.random.default_rng(5000 * t + q).standard_normal(p) * 1e-3).astype(np.float32)
+
+
+def _ck_model():
+    from fsdp_sharded_optimizer_flat_amd import workloads
+    numel = [workloads.numel_of(s) for s in SHAPES]
+    return numel, workloads.row_lengths(SHAPES), sum(numel)
+
+
+def _global_buffer(L, vec):
+    """vec (the parameters' elements in order) placed in L's padded GLOBAL
+    index space, padding zero."""
+    buf = np.zeros(L.padded, np.float32)
+    start = 0
+    for numel, padded, shard, offset, loff in L.unit_table():
+        buf[offset:offset + numel] = vec[start:start + numel]
+        start += numel
+    return buf
+
+
+def _ck_worker(rank, world, port, ck_dir, phase, steps, out_dir):
+    os.environ.update(MASTER_ADDR="127.0.0.1", MASTER_PORT=str(port))
+    dist.init_process_group("gloo", rank=rank, world_size=world)
+    try:
+        numel, row_len, P = _ck_model()
+        h = H
+        if phase == 0:    # flat blocks, state from the initial parameters
+            L = z.zero_pack(world, [numel[0] + numel[1], numel[2] + numel[3]])
+            w = _global_buffer(L, np.random.default_rng(9).normal(0, 0.02, P).astype(np.float32))
+            w = w[_shard_index(L, rank)].copy()
+            m, v = np.zeros_like(w), np.zeros_like(w)
+            t0 = 0
+        else:             # dim-0 rows per parameter, state loaded from the files
+            L = z.zero_pack_rows(world, numel, row_len)
+            paths = sorted(os.path.join(ck_dir, f) for f in os.listdir(ck_dir) if f.endswith(".zck"))
+            t0, w, m, v = z.zero_ckpt_load(paths, L, rank)
+        sc = None
+        for t in range(t0 + 1, t0 + steps + 1):
+            own = torch.from_numpy(_global_buffer(L, _ck_grad(rank, t, P)))
+            allg = [torch.empty_like(own) for _ in range(world)]
+            dist.all_gather(allg, own)
+            sc = (z.zero_adamw_scalars_for(t, h["lr"], h["b1"], h["b2"], h["eps"], h["wd"], 1.0)
+                  if sc is None else z.zero_adamw_scalars_next(sc))
+            z.zero_step_host(L, rank, [a.numpy() for a in allg], z.ZERO_GLOBAL, float(world), w, m, v,
+                             z.ZERO_LOCAL, None, z.ZERO_LOCAL, sc)
+        if phase == 0:
+            z.zero_ckpt_save(os.path.join(ck_dir, f"rank{rank:03d}.zck"), L, rank, t0 + steps, w, m, v)
+        else:
+            parts = {}
+            for name, a in (("w", w), ("m", m), ("v", v)):
+                ta = torch.from_numpy(a.copy())
+                lst = [torch.empty_like(ta) for _ in range(world)]
+                dist.all_gather(lst, ta)
+                parts[name] = [x.numpy() for x in lst]
+            if rank == 0:
+                np.savez(os.path.join(out_dir, "resumed.npz"),
+                         **{f"{k}{q}": parts[k][q] for k in parts for q in range(world)})
+        dist.barrier()
+    finally:
+        dist.destroy_process_group()
+
+
+@pytest.mark.parametrize("worlds", [(3, 2), (2, 4)])
+def test_checkpoint_written_per_rank_resumed_at_another_world_size(worlds, tmp_path):
+    """World size a trains 2 steps on flat blocks and each rank writes its own
+    shard file; world size b loads its shards from those files (resharded to
+    dim-0 rows per parameter) and trains 2 more steps.  The state gathered
+    from the b ranks equals 4 steps of unsharded AdamW whose gradient at each
+    step is the rank-ordered mean of that step's world's gradients (the
+    oracle), bit for bit ("ZeRO and FSDP sharding", Implementation notes)."""
+    import oracle
+    wa, wb = worlds
+    ck = tmp_path / "ck"
+    ck.mkdir()
+    mp.spawn(_ck_worker, args=(wa, _free_port(), str(ck), 0, 2, str(tmp_path)), nprocs=wa, join=True)
+    assert len(list(ck.glob("*.zck"))) == wa
+    mp.spawn(_ck_worker, args=(wb, _free_port(), str(ck), 1, 2, str(tmp_path)), nprocs=wb, join=True)
+    res = np.load(tmp_path / "resumed.npz")
+    numel, row_len, P = _ck_model()
+    B = z.zero_pack_rows(wb, numel, row_len)
+    full = z.zero_pack(1, [P])
+    h = H
+    w = np.random.default_rng(9).normal(0, 0.02, P).astype(np.float32)
+    m, v = np.zeros(P, np.float32), np.zeros(P, np.float32)
+    for t in range(1, 5):
+        n = wa if t <= 2 else wb
+        oracle.adamw_unsharded([_ck_grad(q, t, P) for q in range(n)], divisor=float(n), clip=1.0,
+                               w=w, m=m, v=v, t=t, lr=h["lr"], b1=h["b1"], b2=h["b2"], eps=h["eps"],
+                               wd=h["wd"])
+    for name, want in (("w", w), ("m", m), ("v", v)):
+        got = np.zeros(P, np.float32)
+        z.zero_reshard_host(B, [res[f"{name}{q}"] for q in range(wb)], full, 0, got)
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), name
