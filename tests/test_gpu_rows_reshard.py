@@ -327,6 +327,57 @@ def test_reshard_large_launch_group_table(dst_shift):
     assert bad == 0, f"{bad} elements differ"
 
 
+def fill_stream_positions16(L, q, buf):
+    """As fill_stream_positions for 2-byte elements: stream position mod 2^16."""
+    t = L.unit_table()
+    start = 0
+    buf.zero_()
+    for numel, padded, shard, offset, loff in t:
+        lo, hi = q * shard, min((q + 1) * shard, numel)
+        if hi > lo:
+            vals = torch.arange(start + lo, start + hi, dtype=torch.int64, device=DEV)
+            buf[loff:loff + hi - lo] = ((vals & 0xFFFF) - ((vals & 0x8000) << 1)).to(torch.int16)
+        start += numel
+
+
+@pytest.mark.parametrize("seed,kind", [(902, 0), (903, 1), (910, 2)])
+def test_reshard_large_random_plans(seed, kind):
+    """Random layouts of a few hundred million elements (launches whose group
+    table runs at 2^11 and 2^12 blocks per group), long units mixed with units
+    of a few elements, flat blocks or dim-0 rows on both sides, 4- and
+    2-byte elements, destinations at any 16-byte phase: every element of the
+    destination shard holds its stream position."""
+    rng = np.random.default_rng(seed)
+    big = [int(rng.integers(40_000_000, 150_000_000)) for _ in range(int(rng.integers(2, 6)))]
+    units = []
+    for b in big:
+        units += [b] + [int(rng.integers(1, 40)) for _ in range(int(rng.integers(0, 4)))]
+    rows = [1 if u < 40 or u % 7 else 7 for u in units]
+    n_a, n_b = int(rng.integers(1, 7)), int(rng.integers(1, 3))
+    A = z.zero_pack(n_a, units) if kind != 1 else z.zero_pack_rows(n_a, units, rows)
+    B = z.zero_pack_rows(n_b, units, rows) if kind != 2 else z.zero_pack(n_b, units)
+    r = int(rng.integers(0, n_b))
+    two = kind == 2
+    tdt = torch.int16 if two else torch.int32
+    fill = fill_stream_positions16 if two else fill_stream_positions
+    log(f"large random plan {seed}/{kind}: {len(units)} units, {sum(units)} elements, N {n_a} -> {n_b} "
+        f"rank {r}, {'bf16' if two else 'f32'}")
+    src = []
+    for q in range(n_a):
+        b = torch.empty(A.shard, dtype=tdt, device=DEV)
+        fill(A, q, b)
+        src.append(b.view(torch.bfloat16) if two else b.view(torch.float32))
+    dst = dev_buffer(B.shard, tdt, shift=int(rng.integers(0, 8)), fill=-1)
+    z.zero_reshard(A, src, B, r, dst.view(torch.bfloat16) if two else dst.view(torch.float32))
+    want = torch.empty(B.shard, dtype=tdt, device=DEV)
+    fill(B, r, want)
+    torch.cuda.synchronize()
+    bad = int((dst != want).sum().item())
+    assert bad == 0, f"{bad} elements differ"
+    del src, dst, want
+    torch.cuda.empty_cache()
+
+
 def test_reshard_with_prepared_source_pointers():
     """src_ptrs (sources marshalled once) gives the same bytes as passing
     the tensors, and a mismatched destination type is still refused."""
