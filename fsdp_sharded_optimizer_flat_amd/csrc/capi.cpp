@@ -203,39 +203,47 @@ int cap_for(int kind, const char *env, int dflt)
     return e[kind] >= 0 ? e[kind] : dflt;
 }
 
-// Streams a wave of the fused step keeps in flight: every gradient whose
-// quad it loads before the first add (all N for the compile-time rank
-// counts; two batches of 16 for the run-time kernel), plus master, m, v.
-int step_streams_in_flight(int n_grads)
-{
-    const bool compile_time = n_grads == 1 || n_grads == 2 || n_grads == 4 || n_grads == 8 ||
-                              n_grads == 16 || n_grads == 32 || n_grads == 64;
-    return (compile_time ? n_grads : (n_grads < 32 ? n_grads : 32)) + 3;
-}
 }  // namespace
 
-int step_waves_per_cu(int n_grads)
+int step_waves_per_cu(int n_grads, bool runtime_kernel)
 {
-    // Resident one-wave workgroups per CU of the fused step, falling as the
-    // number of streams a wave keeps in flight grows (fewer tiles in flight
-    // keep fewer DRAM rows competing per bank; too few starve the memory
-    // pipeline).  Measured on MI355X with interleaved sweeps in one process
-    // (bench.py --sweep-waves step:...), % of 8 TB/s at each cap:
+    // Resident one-wave workgroups per CU of the fused step.  A compiled
+    // rank count keeps all N gradient loads of a lane in flight beside
+    // master, m and v (N + 3 streams), and its best cap falls as the streams
+    // grow: fewer tiles in flight keep fewer DRAM rows competing per bank,
+    // too few starve the memory pipeline.  Measured on MI355X with
+    // interleaved sweeps in one process (bench.py --sweep-waves step:...),
+    // % of 8 TB/s at each cap:
     //    4 streams (N = 1): 10
     //    5 streams (N = 2):  5: 53.0  6: 62.8  7: 78.0  8: 82.9  10: 84.1
+    //    6 streams (N = 3):  6: 65.5  7: 79.0  8: 81.7  10: 82.0  12: 81.5
     //    7 streams (N = 4):  5: 58.8  6: 68.4  7: 80.8  8: 82.1  10: 82.4
+    //    8 streams (N = 5):  6: 69.2  7: 82.2  8: 83.8  10: 82.3
+    //    9 streams (N = 6):  6: 71.4  7: 83.8  8: 83.8  10: 82.4
+    //   10 streams (N = 7):  6: 73.4  7: 83.6  8: 82.4  10: 81.1
     //   11 streams (N = 8):  5: 66.0  6: 75.9  7: 84.0  8: 82.0  10: 80.9
+    //   15 streams (N = 12): 5: 71.6  6: 80.4  7: 80.0  8: 79.0
     //   19 streams (N = 16): 5: 76.3  6: 81.8  7: 78.9  8: 78.3  10: 77.3
+    //   23 streams (N = 20): 5: 78.6  6: 80.2  7: 76.7  8: 75.7
+    //   27 streams (N = 24): 4: 80.5  5: 80.5  6: 78.0  7: 75.5
+    //   31 streams (N = 28): 4: 78.1  5: 77.9  6: 76.2  7: 74.7
+    //   34 streams (N = 31): 4: 77.9  5: 78.0  6: 75.6  7: 73.5
     //   67 streams (N = 64): 4: 72.5  5: 72.6  6: 71.8  7: 71.3
-    // The run-time kernel (any other N) issues one batch of 16 ranks at a
-    // time, two batches in flight, and wants more waves than its stream
-    // count suggests: N = 48: 5: 63.9  6: 69.7  7: 73.7  8: 73.6  10: 72.8;
+    // The run-time kernel (bf16 gradients above 32 ranks but 64, fp32
+    // gradients above 1) issues the loads one batch of ranks at a time, two
+    // batches in flight, and wants more waves than its stream count
+    // suggests, the more the fewer ranks a batch holds (bf16):
+    // N = 3: 8: 57.7  10: 62.4  12: 70.6  16: 76.7;  N = 12: 8: 78.8
+    // 10: 81.2  12: 80.0;  N = 24: 7: 73.4  8: 75.3  10: 75.3  12: 74.2;
+    // N = 48: 5: 63.9  6: 69.7  7: 73.7  8: 73.6  10: 72.8;
     // N = 128: 5: 64.4  6: 69.3  7: 72.0  8: 71.6  10: 71.0.
-    const int streams = step_streams_in_flight(n_grads);
-    const bool runtime_kernel = streams == 35 && n_grads != 32;
-    int dflt = streams <= 7 ? 10 : streams <= 11 ? 7 : streams <= 19 ? 6 : 5;
-    if (runtime_kernel)
-        dflt = 7;
+    int dflt;
+    if (runtime_kernel) {
+        dflt = n_grads <= 8 ? 16 : n_grads <= 24 ? 10 : 7;
+    } else {
+        const int streams = n_grads + 3;
+        dflt = streams <= 7 ? 10 : streams == 8 ? 8 : streams <= 11 ? 7 : streams <= 23 ? 6 : 5;
+    }
     return cap_for(0, "ZERO_STEP_WAVES_PER_CU", dflt);
 }
 
@@ -250,19 +258,18 @@ int step1_waves_per_cu(bool staged_chunk)
     return cap_for(1, "ZERO_STEP1_WAVES_PER_CU", staged_chunk ? 12 : 10);
 }
 
-int norm_waves_per_cu(int n_grads)
+int norm_waves_per_cu(int n_grads, bool runtime_kernel)
 {
     // The norm pass and the staged step's reduction: N reads of 16 bytes per
     // lane and one write.  Measured (bench.py --sweep-waves norm:...):
-    // compile-time N = 64 (staged reduction) 4: 78.5  5: 78.6  6: 77.8
-    // 7: 76.4, and N = 32 like it (3 starves at 57 %); the run-time kernel,
-    // two batches of 16 ranks in flight, N = 48: 5: 72.1  6: 76.9  7: 76.3
+    // compiled N = 64 (staged reduction) 4: 78.5  5: 78.6  6: 77.8
+    // 7: 76.4, and N = 32 like it (3 starves at 57 %); compiled N = 24 best
+    // at 6 (5 % above 5 and 7), N = 12 at 7 (6: 5 % lower); the run-time kernel,
+    // two batches of 8 ranks in flight, N = 48: 5: 72.1  6: 76.9  7: 76.3
     // 8: 75.9; N = 128: 5: 74.8  6: 77.3  7: 77.8  8: 76.9; N = 256: 5: 74.7
     // 6: 76.7  7: 79.5  8: 78.9, so 7; fewer ranks keep less in flight and
     // take 7 as well.
-    const int streams = step_streams_in_flight(n_grads);
-    const bool runtime_kernel = streams == 35 && n_grads != 32;
-    const int dflt = !runtime_kernel && streams > 19 ? 5 : 7;
+    const int dflt = runtime_kernel || n_grads <= 16 ? 7 : n_grads <= 24 ? 6 : 5;
     return cap_for(2, "ZERO_NORM_WAVES_PER_CU", dflt);
 }
 
@@ -968,9 +975,11 @@ extern "C" zero_status zero_get_waves_per_cu(int32_t kind, int32_t n_grads, int3
     if (kind < ZERO_CAP_STEP || kind > ZERO_CAP_NORM || !waves || n_grads < 1 ||
         n_grads > ZERO_MAX_RANKS)
         return ZERO_EINVAL;
-    *waves = kind == ZERO_CAP_STEP ? step_waves_per_cu(n_grads)
+    // the kernels bf16 gradients take
+    const bool runtime = !compiled_ranks(n_grads);
+    *waves = kind == ZERO_CAP_STEP ? step_waves_per_cu(n_grads, runtime)
            : kind == ZERO_CAP_STEP1 ? step1_waves_per_cu(false)
-                                    : norm_waves_per_cu(n_grads);
+                                    : norm_waves_per_cu(n_grads, runtime);
     return ZERO_OK;
 }
 

@@ -53,6 +53,7 @@ __device__ __forceinline__ T ld_stream(const T *p)
 constexpr int kRawBufferWord3 = 0x00020000;  // raw (stride 0) buffer, 32-bit format
 constexpr int kSpanStorePolicy = 2 | 16;     // nt | sc1: streamed out, not read again
 constexpr int kKeepStorePolicy = 16;         // sc1: read back by the next kernel
+constexpr int kLoadStreamPolicy = 2;         // nt: the streaming loads' hint
 
 template <typename T, int POLICY = kSpanStorePolicy>
 __device__ __forceinline__ void st_span(T v, T *span, int lane)
@@ -79,11 +80,23 @@ __device__ __forceinline__ float bf_hi(unsigned x) { return __uint_as_float(x & 
 // wave instruction covers one contiguous span (the fp32 oct's two halves
 // interleave).
 struct Bf16Quad {
-    static constexpr int kN = 4;
+    static constexpr int kN = 4, kBytes = 8;
     u32x2 r;
     __device__ __forceinline__ void load(const void *base, int64_t i)
     {
         r = ld_stream(reinterpret_cast<const u32x2 *>(base) + i);
+    }
+    __device__ __forceinline__ void load_span(__amdgpu_buffer_rsrc_t rs, int lane)
+    {
+        r = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, lane * kBytes, 0,
+                                                                           kLoadStreamPolicy));
+    }
+    __device__ __forceinline__ void add_sel(float s[kN], bool on) const
+    {
+        const float e[kN] = {bf_lo(r.x), bf_hi(r.x), bf_lo(r.y), bf_hi(r.y)};
+#pragma unroll
+        for (int k = 0; k < kN; ++k)
+            s[k] = on ? s[k] + e[k] : s[k];
     }
     template <bool FIRST>
     __device__ __forceinline__ void add_to(float s[kN]) const
@@ -95,11 +108,23 @@ struct Bf16Quad {
     }
 };
 struct F32Quad {
-    static constexpr int kN = 4;
+    static constexpr int kN = 4, kBytes = 16;
     f32x4 a;
     __device__ __forceinline__ void load(const void *base, int64_t i)
     {
         a = ld_stream(reinterpret_cast<const f32x4 *>(base) + i);
+    }
+    __device__ __forceinline__ void load_span(__amdgpu_buffer_rsrc_t rs, int lane)
+    {
+        a = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, lane * kBytes, 0,
+                                                                            kLoadStreamPolicy));
+    }
+    __device__ __forceinline__ void add_sel(float s[kN], bool on) const
+    {
+        const float e[kN] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int k = 0; k < kN; ++k)
+            s[k] = on ? s[k] + e[k] : s[k];
     }
     template <bool FIRST>
     __device__ __forceinline__ void add_to(float s[kN]) const
@@ -111,11 +136,24 @@ struct F32Quad {
     }
 };
 struct Bf16Oct {
-    static constexpr int kN = 8;
+    static constexpr int kN = 8, kBytes = 16;
     u32x4 r;
     __device__ __forceinline__ void load(const void *base, int64_t i)
     {
         r = ld_stream(reinterpret_cast<const u32x4 *>(base) + i);
+    }
+    __device__ __forceinline__ void load_span(__amdgpu_buffer_rsrc_t rs, int lane)
+    {
+        r = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, lane * kBytes, 0,
+                                                                            kLoadStreamPolicy));
+    }
+    __device__ __forceinline__ void add_sel(float s[kN], bool on) const
+    {
+        const float e[kN] = {bf_lo(r.x), bf_hi(r.x), bf_lo(r.y), bf_hi(r.y),
+                             bf_lo(r.z), bf_hi(r.z), bf_lo(r.w), bf_hi(r.w)};
+#pragma unroll
+        for (int k = 0; k < kN; ++k)
+            s[k] = on ? s[k] + e[k] : s[k];
     }
     template <bool FIRST>
     __device__ __forceinline__ void add_to(float s[kN]) const
@@ -128,13 +166,27 @@ struct Bf16Oct {
     }
 };
 struct F32Oct {
-    static constexpr int kN = 8;
+    static constexpr int kN = 8, kBytes = 32;
     f32x4 a, b;
     __device__ __forceinline__ void load(const void *base, int64_t i)
     {
         const f32x4 *p = reinterpret_cast<const f32x4 *>(base) + 2 * i;
         a = ld_stream(p);
         b = ld_stream(p + 1);
+    }
+    __device__ __forceinline__ void load_span(__amdgpu_buffer_rsrc_t rs, int lane)
+    {
+        a = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, lane * kBytes, 0,
+                                                                            kLoadStreamPolicy));
+        b = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                          rs, lane * kBytes + 16, 0, kLoadStreamPolicy));
+    }
+    __device__ __forceinline__ void add_sel(float s[kN], bool on) const
+    {
+        const float e[kN] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int k = 0; k < kN; ++k)
+            s[k] = on ? s[k] + e[k] : s[k];
     }
     template <bool FIRST>
     __device__ __forceinline__ void add_to(float s[kN]) const
@@ -157,12 +209,16 @@ __device__ __forceinline__ void rank_sum(const GradSet<CAP> &gs, int n, int64_t 
         constexpr int B = NR < 16 ? NR : 16;
 #pragma unroll
         for (int q0 = 0; q0 < NR; q0 += B) {
+            const int nb = NR - q0 < B ? NR - q0 : B;  // known once unrolled
             QD c[B];
 #pragma unroll
             for (int b = 0; b < B; ++b)
-                c[b].load(gs.p[q0 + b], i);
+                if (b < nb)
+                    c[b].load(gs.p[q0 + b], i);
 #pragma unroll
             for (int b = 0; b < B; ++b) {
+                if (b >= nb)
+                    break;
                 if (q0 + b == 0)
                     c[b].template add_to<true>(s);
                 else
@@ -170,48 +226,55 @@ __device__ __forceinline__ void rank_sum(const GradSet<CAP> &gs, int n, int64_t 
             }
         }
     } else {
-        // Runtime rank count: batches of B ranks (128 bytes of loads per
-        // lane), software-pipelined -- batch k + 1's loads are issued before
-        // batch k is added -- so two batches stay in flight; the adds keep
-        // rank order, rank 0 starting the sum.
+        // Runtime rank count: ceil(n / B) batches of B ranks (128 bytes of
+        // loads per lane), the last one partial, software-pipelined -- batch
+        // k + 1's loads are issued before batch k is added -- so two batches
+        // stay in flight.  Each slot loads through a buffer resource confined
+        // to the wave's span of its rank's gradient; a slot past the rank
+        // count gets an empty resource, so its load is dropped by the range
+        // check (no memory access, zero returned) and its add is masked off.
+        // A partial batch therefore goes out at once like a full one, with
+        // no branch around any load (loaded one at a time, the ranks past the
+        // last full batch each cost a memory round trip: N = 17 to 31 ran at
+        // 27-49 % of the HBM peak).  The adds keep rank order, rank 0
+        // starting the sum.  Every call site gives lane l of a wave group
+        // i = i0 + l with i0 the same over the wave.
         constexpr int B = 128 / (int)sizeof(QD) < 4 ? 4 : 128 / (int)sizeof(QD);
-        const int nb = n / B;
-        int q = 0;
-        if (nb > 0) {
-            QD cur[B], nxt[B];
+        constexpr int W = QD::kBytes;
+        const int lane = (int)(threadIdx.x & (kWave - 1));
+        const uint64_t i0 = (uint64_t)(i - lane);
+        const int64_t base = (int64_t)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(i0 >> 32)) << 32) |
+                                       (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)i0)) * W;
+        auto rsrc = [&](int q) {
+            const bool on = q < n;
+            const char *p = static_cast<const char *>(gs.p[on ? q : 0]) + base;
+            return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(p), 0, on ? kWave * W : 0,
+                                                     kRawBufferWord3);
+        };
+        const int nbat = (n + B - 1) / B;
+        QD cur[B], nxt[B];
 #pragma unroll
-            for (int b = 0; b < B; ++b)
-                cur[b].load(gs.p[b], i);
-            for (int k = 1; k <= nb; ++k) {
-                if (k < nb) {
+        for (int b = 0; b < B; ++b)
+            cur[b].load_span(rsrc(b), lane);
+        for (int k = 0; k < nbat; ++k) {
+            const int q0 = k * B;
+            if (k + 1 < nbat) {
 #pragma unroll
-                    for (int b = 0; b < B; ++b)
-                        nxt[b].load(gs.p[k * B + b], i);
-                }
-                if (k == 1)
-                    cur[0].template add_to<true>(s);
-                else
-                    cur[0].template add_to<false>(s);
-#pragma unroll
-                for (int b = 1; b < B; ++b)
-                    cur[b].template add_to<false>(s);
-                if (k < nb) {
-#pragma unroll
-                    for (int b = 0; b < B; ++b)
-                        cur[b] = nxt[b];
-                }
+                for (int b = 0; b < B; ++b)
+                    nxt[b].load_span(rsrc(q0 + B + b), lane);
             }
-            q = nb * B;
-        } else {
-            QD c0;
-            c0.load(gs.p[0], i);
-            c0.template add_to<true>(s);
-            q = 1;
-        }
-        for (; q < n; ++q) {
-            QD c;
-            c.load(gs.p[q], i);
-            c.template add_to<false>(s);
+            if (k == 0)
+                cur[0].template add_to<true>(s);
+            else
+                cur[0].template add_to<false>(s);
+#pragma unroll
+            for (int b = 1; b < B; ++b)
+                cur[b].add_sel(s, q0 + b < n);
+            if (k + 1 < nbat) {
+#pragma unroll
+                for (int b = 0; b < B; ++b)
+                    cur[b] = nxt[b];
+            }
         }
     }
 }

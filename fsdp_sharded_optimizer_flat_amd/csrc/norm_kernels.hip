@@ -18,6 +18,8 @@
 #include <mutex>
 #include <vector>
 
+#include <utility>
+
 #include "device_common.h"
 
 // Partials of zero_gradnorm_async_noalloc: device memory that belongs to the
@@ -155,28 +157,41 @@ hipError_t launch_nr(const void *const *grads, int n, float *G, int64_t len, con
     GradSet<CAP> gs{};
     for (int q = 0; q < n; ++q)
         gs.p[q] = grads[q];
-    const size_t lds = occupancy_cap_lds(norm_waves_per_cu(n), 2 * kWave * sizeof(f32x4));
+    const size_t lds = occupancy_cap_lds(norm_waves_per_cu(n, NR == 0), 2 * kWave * sizeof(f32x4));
     hipLaunchKernelGGL((norm_kernel<NR, CAP, GT, OD, POW2, VEC>), dim3((unsigned)blocks),
                        dim3(kWave), lds, st, gs, n, G, len, c, partials);
     return hipGetLastError();
 }
 
+template <bool POW2, int... Ks>
+hipError_t bf16_vec_compiled(std::integer_sequence<int, Ks...>, const void *const *grads, int n,
+                             float *G, int64_t len, const StepConsts &c, double *partials,
+                             int64_t blocks, hipStream_t st)
+{
+    using T = uint16_t;
+    using QD = Bf16Oct;
+    hipError_t r = hipSuccess;
+    const bool hit =
+        ((n == Ks + 1
+              ? (r = launch_nr<Ks + 1, T, QD, POW2, true>(grads, n, G, len, c, partials, blocks, st),
+                 true)
+              : false) ||
+         ...);
+    if (hit)
+        return r;
+    if (n == 64)
+        return launch_nr<64, T, QD, POW2, true>(grads, n, G, len, c, partials, blocks, st);
+    return launch_nr<0, T, QD, POW2, true>(grads, n, G, len, c, partials, blocks, st);
+}
+
+// bf16 gradients, aligned: a kernel compiled for each rank count up to
+// kMaxCompiledRanks and for 64, the run-time kernel for any other N.
 template <bool POW2>
 hipError_t launch_bf16_vec(const void *const *grads, int n, float *G, int64_t len,
                            const StepConsts &c, double *partials, int64_t blocks, hipStream_t st)
 {
-    using T = uint16_t;
-    using QD = Bf16Oct;
-    switch (n) {
-    case 1: return launch_nr<1, T, QD, POW2, true>(grads, n, G, len, c, partials, blocks, st);
-    case 2: return launch_nr<2, T, QD, POW2, true>(grads, n, G, len, c, partials, blocks, st);
-    case 4: return launch_nr<4, T, QD, POW2, true>(grads, n, G, len, c, partials, blocks, st);
-    case 8: return launch_nr<8, T, QD, POW2, true>(grads, n, G, len, c, partials, blocks, st);
-    case 16: return launch_nr<16, T, QD, POW2, true>(grads, n, G, len, c, partials, blocks, st);
-    case 32: return launch_nr<32, T, QD, POW2, true>(grads, n, G, len, c, partials, blocks, st);
-    case 64: return launch_nr<64, T, QD, POW2, true>(grads, n, G, len, c, partials, blocks, st);
-    default: return launch_nr<0, T, QD, POW2, true>(grads, n, G, len, c, partials, blocks, st);
-    }
+    return bf16_vec_compiled<POW2>(std::make_integer_sequence<int, kMaxCompiledRanks>{}, grads, n,
+                                   G, len, c, partials, blocks, st);
 }
 
 }  // namespace

@@ -24,6 +24,8 @@
 // ranks up, 10 or 12 for one fp32 gradient, through a dynamic LDS
 // reservation the kernel never touches): fewer tiles in flight keep fewer
 // DRAM rows competing per bank across the N + 7 streams.
+#include <utility>
+
 #include "device_common.h"
 
 namespace zero {
@@ -125,7 +127,7 @@ hipError_t launch_quads_nr(const void *const *grads, int n, int gsize_quad, floa
                            hipStream_t st, int waves = -1)
 {
     constexpr int CAP = NR > 0 ? NR : ZERO_MAX_RANKS;
-    const size_t lds = occupancy_cap_lds(waves >= 0 ? waves : step_waves_per_cu(n), 0);
+    const size_t lds = occupancy_cap_lds(waves >= 0 ? waves : step_waves_per_cu(n, NR == 0), 0);
     for (int64_t q0 = 0; q0 < nquads; q0 += kMaxQuadsPerLaunch) {
         const int64_t nq = nquads - q0 < kMaxQuadsPerLaunch ? nquads - q0 : kMaxQuadsPerLaunch;
         GradSet<CAP> gs{};
@@ -142,22 +144,35 @@ hipError_t launch_quads_nr(const void *const *grads, int n, int gsize_quad, floa
     return hipSuccess;
 }
 
+// bf16 gradients: a kernel compiled for each rank count up to
+// kMaxCompiledRanks and for 64 (all N loads of a lane issued in batches of
+// 16, none predicated), the run-time kernel for any other N.
+template <bool POW2, int... Ks>
+hipError_t bf16_quads_compiled(std::integer_sequence<int, Ks...>, const void *const *grads, int n,
+                               float *w, float *m, float *v, uint16_t *o, int64_t nq,
+                               const StepConsts &c, hipStream_t st)
+{
+    using QD = Bf16Quad;
+    constexpr int B = 8;  // bytes of one bf16 quad
+    hipError_t r = hipSuccess;
+    const bool hit =
+        ((n == Ks + 1 ? (r = launch_quads_nr<Ks + 1, QD, POW2>(grads, n, B, w, m, v, o, nq, c, st),
+                         true)
+                      : false) ||
+         ...);
+    if (hit)
+        return r;
+    if (n == 64)
+        return launch_quads_nr<64, QD, POW2>(grads, n, B, w, m, v, o, nq, c, st);
+    return launch_quads_nr<0, QD, POW2>(grads, n, B, w, m, v, o, nq, c, st);
+}
+
 template <bool POW2>
 hipError_t launch_bf16_quads(const void *const *grads, int n, float *w, float *m, float *v,
                              uint16_t *o, int64_t nq, const StepConsts &c, hipStream_t st)
 {
-    using QD = Bf16Quad;
-    constexpr int B = 8;  // bytes of one bf16 quad
-    switch (n) {
-    case 1: return launch_quads_nr<1, QD, POW2>(grads, n, B, w, m, v, o, nq, c, st);
-    case 2: return launch_quads_nr<2, QD, POW2>(grads, n, B, w, m, v, o, nq, c, st);
-    case 4: return launch_quads_nr<4, QD, POW2>(grads, n, B, w, m, v, o, nq, c, st);
-    case 8: return launch_quads_nr<8, QD, POW2>(grads, n, B, w, m, v, o, nq, c, st);
-    case 16: return launch_quads_nr<16, QD, POW2>(grads, n, B, w, m, v, o, nq, c, st);
-    case 32: return launch_quads_nr<32, QD, POW2>(grads, n, B, w, m, v, o, nq, c, st);
-    case 64: return launch_quads_nr<64, QD, POW2>(grads, n, B, w, m, v, o, nq, c, st);
-    default: return launch_quads_nr<0, QD, POW2>(grads, n, B, w, m, v, o, nq, c, st);
-    }
+    return bf16_quads_compiled<POW2>(std::make_integer_sequence<int, kMaxCompiledRanks>{}, grads,
+                                     n, w, m, v, o, nq, c, st);
 }
 
 template <typename GT, bool POW2>

@@ -116,9 +116,16 @@ size_t occupancy_cap_lds(int waves_per_cu, size_t static_lds);
 // Target resident waves per CU of the streaming kernels (0 = no cap):
 // zero_set_waves_per_cu, else ZERO_STEP_WAVES_PER_CU / ZERO_STEP1_WAVES_PER_CU
 // / ZERO_NORM_WAVES_PER_CU, else the defaults measured on MI355X.
-int step_waves_per_cu(int n_grads);   // the fused step over N gradients
+// runtime_kernel: the kernel takes the rank count as an argument (loads in
+// batches of 128 bytes per lane) instead of having it compiled in.
+int step_waves_per_cu(int n_grads, bool runtime_kernel);  // the fused step over N gradients
 int step1_waves_per_cu(bool staged_chunk);  // the step on one fp32 gradient
-int norm_waves_per_cu(int n_grads);   // the norm pass and the staged reduction
+int norm_waves_per_cu(int n_grads, bool runtime_kernel);  // the norm pass and the staged reduction
+
+// Rank counts with a kernel of their own for bf16 gradients (fused step and
+// norm pass): every N up to kMaxCompiledRanks, and 64.
+constexpr int kMaxCompiledRanks = 32;
+constexpr bool compiled_ranks(int n) { return (n >= 1 && n <= kMaxCompiledRanks) || n == 64; }
 
 // Record a HIP error code for zero_last_hip_error(); returns ZERO_EHIP.
 zero_status hip_fail(int hip_error, const char *where);
@@ -155,7 +162,7 @@ zero_status validate_step_ext(const zero_layout *L, int32_t rank, const void *co
 // Launchers (defined in the .hip files).  Pointers are already offset to the
 // piece's first element.  Return a hipError_t value.
 // waves_per_cu (one fp32 gradient only): resident waves per CU; < 0 takes
-// step_waves_per_cu(n_grads).
+// step1_waves_per_cu(false).
 int launch_step_piece(const Piece &pc, const void *const *grads, int n_grads, int grad_dtype,
                       float *w, float *m, float *v, uint16_t *out, const StepConsts &c,
                       void *stream, int waves_per_cu = -1);

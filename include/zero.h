@@ -690,8 +690,8 @@ zero_status zero_gradnorm_traffic(const zero_layout *layout, int32_t rank, int32
  * other threads.  EINVAL: bad kind or value. */
 zero_status zero_set_waves_per_cu(int32_t kind, int32_t waves);
 
-/* The cap a launch of the family over n_grads gradients would use now (for
- * ZERO_CAP_STEP1 the clipped step's).  EINVAL: bad kind, n_grads out of
+/* The cap a launch of the family over n_grads bf16 gradients would use now
+ * (for ZERO_CAP_STEP1 the clipped step's).  EINVAL: bad kind, n_grads out of
  * 1..ZERO_MAX_RANKS, NULL. */
 zero_status zero_get_waves_per_cu(int32_t kind, int32_t n_grads, int32_t *waves);
 

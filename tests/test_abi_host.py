@@ -500,13 +500,15 @@ def test_occupancy_caps_table_and_setter():
     """The measured defaults per kernel family (from the streams a wave keeps
     in flight), the run-time setter, and its argument checks."""
     S, S1, NRM = z.ZERO_CAP_STEP, z.ZERO_CAP_STEP1, z.ZERO_CAP_NORM
-    want = {1: 10, 2: 10, 4: 10, 8: 7, 16: 6, 32: 5, 33: 7, 48: 7, 64: 5, 100: 7, 256: 7}
+    want = {1: 10, 2: 10, 3: 10, 4: 10, 5: 8, 6: 7, 7: 7, 8: 7, 12: 6, 16: 6, 20: 6, 21: 5,
+            24: 5, 31: 5, 32: 5, 33: 7, 48: 7, 64: 5, 100: 7, 256: 7}
     if any(os.environ.get(v) for v in ("ZERO_STEP_WAVES_PER_CU", "ZERO_STEP1_WAVES_PER_CU",
                                       "ZERO_NORM_WAVES_PER_CU")):
         pytest.skip("occupancy environment overrides set")
     assert {n: z.zero_get_waves_per_cu(S, n) for n in want} == want
     assert z.zero_get_waves_per_cu(S1, 1) == 10
-    assert [z.zero_get_waves_per_cu(NRM, n) for n in (8, 32, 48, 64, 128)] == [7, 5, 7, 5, 7]
+    assert [z.zero_get_waves_per_cu(NRM, n) for n in (8, 12, 17, 24, 25, 32, 48, 64, 128)] == \
+        [7, 7, 6, 6, 5, 5, 7, 5, 7]
     try:
         z.zero_set_waves_per_cu(S, 3)
         assert z.zero_get_waves_per_cu(S, 64) == 3 and z.zero_get_waves_per_cu(S, 8) == 3
