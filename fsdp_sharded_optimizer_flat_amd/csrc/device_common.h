@@ -229,16 +229,18 @@ __device__ __forceinline__ void rank_sum(const GradSet<CAP> &gs, int n, int64_t 
         // Runtime rank count: ceil(n / B) batches of B ranks (128 bytes of
         // loads per lane), the last one partial, software-pipelined -- batch
         // k + 1's loads are issued before batch k is added -- so two batches
-        // stay in flight.  Each slot loads through a buffer resource confined
-        // to the wave's span of its rank's gradient; a slot past the rank
-        // count gets an empty resource, so its load is dropped by the range
-        // check (no memory access, zero returned) and its add is masked off.
-        // A partial batch therefore goes out at once like a full one, with
-        // no branch around any load (loaded one at a time, the ranks past the
-        // last full batch each cost a memory round trip: N = 17 to 31 ran at
-        // 27-49 % of the HBM peak).  The adds keep rank order, rank 0
-        // starting the sum.  Every call site gives lane l of a wave group
-        // i = i0 + l with i0 the same over the wave.
+        // stay in flight.  Full batches use plain loads.  The partial batch
+        // loads each slot through a buffer resource confined to the wave's
+        // span of its rank's gradient; a slot past the rank count gets an
+        // empty resource, so its load is dropped by the range check (no
+        // memory access, zero returned) and its add is masked off.  It thus
+        // goes out at once like a full batch, with no branch around any load.
+        // (Loaded one at a time, the ranks past the last full batch each
+        // cost a memory round trip: N = 17 to 31 ran at 27-49 % of the HBM
+        // peak.  Building a resource for every rank of the full batches too
+        // cost 1 to 4 points at 128 and 256 ranks.)  The adds keep rank
+        // order, rank 0 starting the sum.  Every call site gives lane l of a
+        // wave group i = i0 + l with i0 the same over the wave.
         constexpr int B = 128 / (int)sizeof(QD) < 4 ? 4 : 128 / (int)sizeof(QD);
         constexpr int W = QD::kBytes;
         const int lane = (int)(threadIdx.x & (kWave - 1));
@@ -251,25 +253,41 @@ __device__ __forceinline__ void rank_sum(const GradSet<CAP> &gs, int n, int64_t 
             return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(p), 0, on ? kWave * W : 0,
                                                      kRawBufferWord3);
         };
-        const int nbat = (n + B - 1) / B;
-        QD cur[B], nxt[B];
-#pragma unroll
-        for (int b = 0; b < B; ++b)
-            cur[b].load_span(rsrc(b), lane);
-        for (int k = 0; k < nbat; ++k) {
+        const int nfull = n / B, nbat = (n + B - 1) / B;
+        // batch k's loads into x: plain loads for a full batch, the
+        // range-checked ones for the partial last batch (a uniform branch
+        // per batch)
+        auto load_batch = [&](QD (&x)[B], int k) {
             const int q0 = k * B;
-            if (k + 1 < nbat) {
+            if (k < nfull) {
 #pragma unroll
                 for (int b = 0; b < B; ++b)
-                    nxt[b].load_span(rsrc(q0 + B + b), lane);
+                    x[b].load(gs.p[q0 + b], i);
+            } else {
+#pragma unroll
+                for (int b = 0; b < B; ++b)
+                    x[b].load_span(rsrc(q0 + b), lane);
             }
+        };
+        QD cur[B], nxt[B];
+        load_batch(cur, 0);
+        for (int k = 0; k < nbat; ++k) {
+            const int q0 = k * B;
+            if (k + 1 < nbat)
+                load_batch(nxt, k + 1);
             if (k == 0)
                 cur[0].template add_to<true>(s);
             else
                 cur[0].template add_to<false>(s);
+            if (k < nfull) {
 #pragma unroll
-            for (int b = 1; b < B; ++b)
-                cur[b].add_sel(s, q0 + b < n);
+                for (int b = 1; b < B; ++b)
+                    cur[b].template add_to<false>(s);
+            } else {
+#pragma unroll
+                for (int b = 1; b < B; ++b)
+                    cur[b].add_sel(s, q0 + b < n);
+            }
             if (k + 1 < nbat) {
 #pragma unroll
                 for (int b = 0; b < B; ++b)
