@@ -91,6 +91,8 @@ def parse():
     ap.add_argument("--ranks", type=int, default=None,
                     help="simulated ranks N (default: the workload's); the same model at another N "
                          "(one rank's shard for the ZeRO-3 workloads)")
+    ap.add_argument("--grad-dtype", default="bf16", choices=["bf16", "f32"],
+                    help="gradient element type of the workload (f32: a reduce dtype of fp32)")
     ap.add_argument("--fused", action="store_true",
                     help="above 32 ranks, time the fused step instead of the staged one")
     ap.add_argument("--sweep-waves", default=None, metavar="FAMILY:CAPS",
@@ -566,7 +568,7 @@ def stagger_plan(sizes, step_bytes):
     return offs, at
 
 
-def setup_step(wl, fused=False, stage_chunk=None, stagger_kib=None, norm_only=None):
+def setup_step(wl, fused=False, stage_chunk=None, stagger_kib=None, norm_only=None, grad_dtype="bf16"):
     """The benchmark's resident inputs and its step, as bench.py times them:
     every streamed buffer in one allocation placed by zero_arena_plan, the
     workload's seeded gradients (the same every step) and master weights,
@@ -601,7 +603,8 @@ def setup_step(wl, fused=False, stage_chunk=None, stagger_kib=None, norm_only=No
     if ws_elems and stage_chunk:   # a chosen chunk (whole 512-element tiles) plus the spare
         ws_elems = stage_chunk + 4
     staged = ws_elems > 0
-    specs = [(ge, torch.bfloat16)] * n + [(se, torch.float32)] * 3 + [(oe, torch.int16)]
+    gdt = torch.float32 if grad_dtype == "f32" else torch.bfloat16
+    specs = [(ge, gdt)] * n + [(se, torch.float32)] * 3 + [(oe, torch.int16)]
     if clip:
         specs.append((se, torch.float32))
     if staged:
@@ -668,7 +671,7 @@ def setup_step(wl, fused=False, stage_chunk=None, stagger_kib=None, norm_only=No
     ns = types.SimpleNamespace(
         wl=wl, n=n, h=h, L=L, gidx=gidx, sidx=sidx, oidx=oidx, se=se, clip=clip, staged=staged,
         ws_elems=ws_elems, arena=arena, grads=grads, master=master, m=m, v=v, out=out,
-        stream=stream, one_step=one_step)
+        stream=stream, one_step=one_step, grad_dtype=z.ZERO_F32 if grad_dtype == "f32" else z.ZERO_BF16)
     if clip:
         ns.g_red, ns.ss_dev, ns.coef_dev = g_red, ss_dev, coef_dev
     if staged:
@@ -886,10 +889,10 @@ def sweep_waves(args, wl, S):
     n = S.n
     if S.clip:
         step_bytes, _ = z.zero_step_traffic(S.L, wl.rank, 1, z.ZERO_F32, True)
-        norm_bytes, _ = z.zero_gradnorm_traffic(S.L, wl.rank, n, z.ZERO_BF16, True)
+        norm_bytes, _ = z.zero_gradnorm_traffic(S.L, wl.rank, n, S.grad_dtype, True)
         job_bytes = step_bytes + norm_bytes
     else:
-        job_bytes, _ = z.zero_step_traffic(S.L, wl.rank, n, z.ZERO_BF16, True)
+        job_bytes, _ = z.zero_step_traffic(S.L, wl.rank, n, S.grad_dtype, True)
     t = 0
     for _ in range(args.warmup):
         t += 1
@@ -947,10 +950,14 @@ def main():
     from fsdp_sharded_optimizer_flat_amd.workloads import WORKLOADS
 
     wl = workload_from_args(args)
+    if args.grad_dtype != "bf16" and not args.no_cpu_baseline:
+        raise SystemExit("--grad-dtype f32 is a variant without the CPU leg: add --no-cpu-baseline")
     if args.norm_only and wl.clip_max_norm is None:
         raise SystemExit("--norm-only needs the clipped workload (llama8b_z3_clip)")
     S = setup_step(wl, fused=args.fused, stage_chunk=args.stage_chunk, stagger_kib=args.stagger_kib,
-                   norm_only=("no_g" if args.no_g else "g") if args.norm_only else None)
+                   norm_only=("no_g" if args.no_g else "g") if args.norm_only else None,
+                   grad_dtype=args.grad_dtype)
+    gdt = z.ZERO_F32 if args.grad_dtype == "f32" else z.ZERO_BF16
     if args.sweep_waves:
         sweep_waves(args, wl, S)
         return
@@ -990,16 +997,16 @@ def main():
         timing = ("HIP events on the launch stream at the two ends of the timed region; "
                   "average = span / steps")
     elements = se if wl.rank < 0 else L.shard
-    fused_bytes, _ = z.zero_step_traffic(L, wl.rank, n, z.ZERO_BF16, True)  # 2N + 26
+    fused_bytes, _ = z.zero_step_traffic(L, wl.rank, n, gdt, True)  # 2N + 26 (4N + 26 for fp32)
     if clip:
         step_bytes, _ = z.zero_step_traffic(L, wl.rank, 1, z.ZERO_F32, True)
-        norm_bytes, _ = z.zero_gradnorm_traffic(L, wl.rank, n, z.ZERO_BF16, not args.no_g)
+        norm_bytes, _ = z.zero_gradnorm_traffic(L, wl.rank, n, gdt, not args.no_g)
         if args.norm_only:
             step_bytes = 0.0
         job_bytes = step_bytes + norm_bytes   # 2N + 34: the bytes the two passes need
         dom_bytes, dom_name = norm_bytes, "norm_kernel (rank-sum + divide + fp32 g + binary64 sum of squares)"
     else:
-        step_bytes, _ = z.zero_step_traffic(L, wl.rank, n, z.ZERO_BF16, True)
+        step_bytes, _ = z.zero_step_traffic(L, wl.rank, n, gdt, True)
         job_bytes = step_bytes
         dom_bytes, dom_name = step_bytes, "step_quad_kernel (fused rank-sum + AdamW + bf16 cast)"
         if staged:
@@ -1024,6 +1031,7 @@ def main():
     per_ms = sorted(a.elapsed_time(b) for a, b in per_call)
 
     traffic = None if args.fused or args.norm_only or args.stage_chunk or args.stagger_kib is not None \
+        or args.grad_dtype != "bf16" \
         else measured_traffic(wl.name)
     box_copy = None if args.no_box_copy else box_copy_ceiling(z, torch, stream)
 
@@ -1047,7 +1055,7 @@ def main():
             "units": len(wl.unit_numel),
             "params": int(L.numel),
             "elements_per_step": int(elements),
-            "grad_dtype": "bf16",
+            "grad_dtype": args.grad_dtype,
             "state_dtype": "f32",
             "out_dtype": "bf16",
             "clip_max_norm": wl.clip_max_norm,
@@ -1055,7 +1063,8 @@ def main():
                 "fused step above 32 ranks" if args.fused else "",
                 ("norm pass only, " + ("g not written" if args.no_g else "g written")) if args.norm_only else "",
                 f"staged chunk {args.stage_chunk} elements" if args.stage_chunk else "",
-                f"buffers staggered by {args.stagger_kib} KiB" if args.stagger_kib is not None else "") if v)
+                f"buffers staggered by {args.stagger_kib} KiB" if args.stagger_kib is not None else "",
+                "fp32 gradients" if args.grad_dtype == "f32" else "") if v)
                 or None,
             "algorithmic_bytes_per_step": job_bytes,
             "bytes_per_element": job_bytes / elements,

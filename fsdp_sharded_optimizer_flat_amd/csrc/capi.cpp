@@ -205,44 +205,48 @@ int cap_for(int kind, const char *env, int dflt)
 
 }  // namespace
 
-int step_waves_per_cu(int n_grads, bool runtime_kernel)
+int step_waves_per_cu(int n_grads, bool runtime_kernel, int grad_bytes)
 {
     // Resident one-wave workgroups per CU of the fused step.  A compiled
-    // rank count keeps all N gradient loads of a lane in flight beside
-    // master, m and v (N + 3 streams), and its best cap falls as the streams
-    // grow: fewer tiles in flight keep fewer DRAM rows competing per bank,
-    // too few starve the memory pipeline.  Measured on MI355X with
-    // interleaved sweeps in one process (bench.py --sweep-waves step:...),
-    // % of 8 TB/s at each cap:
-    //    4 streams (N = 1): 10
-    //    5 streams (N = 2):  5: 53.0  6: 62.8  7: 78.0  8: 82.9  10: 84.1
-    //    6 streams (N = 3):  6: 65.5  7: 79.0  8: 81.7  10: 82.0  12: 81.5
-    //    7 streams (N = 4):  5: 58.8  6: 68.4  7: 80.8  8: 82.1  10: 82.4
-    //    8 streams (N = 5):  6: 69.2  7: 82.2  8: 83.8  10: 82.3
-    //    9 streams (N = 6):  6: 71.4  7: 83.8  8: 83.8  10: 82.4
-    //   10 streams (N = 7):  6: 73.4  7: 83.6  8: 82.4  10: 81.1
-    //   11 streams (N = 8):  5: 66.0  6: 75.9  7: 84.0  8: 82.0  10: 80.9
-    //   15 streams (N = 12): 5: 71.6  6: 80.4  7: 80.0  8: 79.0
-    //   19 streams (N = 16): 5: 76.3  6: 81.8  7: 78.9  8: 78.3  10: 77.3
-    //   23 streams (N = 20): 5: 78.6  6: 80.2  7: 76.7  8: 75.7
-    //   27 streams (N = 24): 4: 80.5  5: 80.5  6: 78.0  7: 75.5
-    //   31 streams (N = 28): 4: 78.1  5: 77.9  6: 76.2  7: 74.7
-    //   34 streams (N = 31): 4: 77.9  5: 78.0  6: 75.6  7: 73.5
-    //   67 streams (N = 64): 4: 72.5  5: 72.6  6: 71.8  7: 71.3
-    // The run-time kernel (bf16 gradients above 32 ranks but 64, fp32
-    // gradients above 1) issues the loads one batch of ranks at a time, two
-    // batches in flight, and wants more waves than its stream count
-    // suggests, the more the fewer ranks a batch holds (bf16):
-    // N = 3: 8: 57.7  10: 62.4  12: 70.6  16: 76.7;  N = 12: 8: 78.8
-    // 10: 81.2  12: 80.0;  N = 24: 7: 73.4  8: 75.3  10: 75.3  12: 74.2;
-    // N = 48: 5: 63.9  6: 69.7  7: 73.7  8: 73.6  10: 72.8;
-    // N = 128: 5: 64.4  6: 69.3  7: 72.0  8: 71.6  10: 71.0.
+    // rank count keeps all N gradient quads of a lane in flight beside
+    // master, m and v (4 * grad_bytes * N + 48 bytes per lane), and its best
+    // cap falls as those bytes grow: fewer tiles in flight keep fewer DRAM
+    // rows competing per bank, too few starve the memory pipeline.  Measured
+    // on MI355X with interleaved sweeps in one process (bench.py
+    // --sweep-waves step:..., the 8B shard at N ranks), % of 8 TB/s:
+    //   bf16 N = 2   (64 B):  5: 53.0  6: 62.8  7: 78.0  8: 82.9  10: 84.1
+    //   bf16 N = 3   (72 B):  6: 65.5  7: 79.0  8: 81.7  10: 82.0  12: 81.5
+    //   bf16 N = 4   (80 B):  5: 58.8  6: 68.4  7: 80.8  8: 82.1  10: 82.4
+    //   fp32 N = 2   (80 B):  6: 69.8  7: 83.0  8: 84.0  10: 82.4
+    //   bf16 N = 5   (88 B):  6: 69.2  7: 82.2  8: 83.8  10: 82.3
+    //   bf16 N = 6   (96 B):  6: 71.4  7: 83.8  8: 83.8  10: 82.4
+    //   bf16 N = 7  (104 B):  6: 73.4  7: 83.6  8: 82.4  10: 81.1
+    //   bf16 N = 8  (112 B):  5: 66.0  6: 75.9  7: 84.0  8: 82.0  10: 80.9
+    //   fp32 N = 4  (112 B):  6: 77.7  7: 82.3  8: 81.1  10: 80.2
+    //   bf16 N = 12 (144 B):  5: 71.6  6: 80.4  7: 80.0  8: 79.0
+    //   bf16 N = 16 (176 B):  5: 76.3  6: 81.8  7: 78.9  8: 78.3  10: 77.3
+    //   fp32 N = 8  (176 B):  5: 81.0  6: 81.7  7: 78.2  8: 78.0
+    //   bf16 N = 20 (208 B):  5: 78.6  6: 80.2  7: 76.7  8: 75.7
+    //   bf16 N = 24 (240 B):  4: 80.5  5: 80.5  6: 78.0  7: 75.5
+    //   bf16 N = 28 (272 B):  4: 78.1  5: 77.9  6: 76.2  7: 74.7
+    //   fp32 N = 16 (304 B):  4: 79.3  5: 79.4  6: 77.0  7: 75.7
+    //   bf16 N = 31 (296 B):  4: 77.9  5: 78.0  6: 75.6  7: 73.5
+    //   fp32 N = 32 (560 B):  4: 74.1  5: 74.2  6: 72.4  7: 70.3
+    //   bf16 N = 64 (560 B):  4: 72.5  5: 72.6  6: 71.8  7: 71.3
+    // The run-time kernel issues the loads one batch of 128 bytes per lane
+    // at a time, two batches in flight: bf16 takes it only above 32 ranks
+    // (N = 48: 5: 63.9  6: 69.7  7: 73.7  8: 73.6  10: 72.8;  N = 128: 5:
+    // 64.4  6: 69.3  7: 72.0  8: 71.6  10: 71.0), fp32 at the rank counts
+    // without a kernel of their own (N = 3: 8: 77.5  10: 82.2  12: 84.6
+    // 16: 80.5;  N = 12: 6: 77.2  7: 79.6  8: 78.4;  N = 24: 4: 76.4
+    // 5: 76.4  6: 75.2  7: 73.0).
     int dflt;
     if (runtime_kernel) {
-        dflt = n_grads <= 8 ? 16 : n_grads <= 24 ? 10 : 7;
+        dflt = grad_bytes == 2 ? 7 : n_grads <= 4 ? 12 : n_grads <= 12 ? 7 : 5;
     } else {
-        const int streams = n_grads + 3;
-        dflt = streams <= 7 ? 10 : streams == 8 ? 8 : streams <= 11 ? 7 : streams <= 23 ? 6 : 5;
+        const int lane_bytes = 4 * grad_bytes * n_grads + 48;
+        dflt = lane_bytes <= 72 ? 10 : lane_bytes <= 88 ? 8 : lane_bytes <= 112 ? 7
+             : lane_bytes <= 208 ? 6 : 5;
     }
     return cap_for(0, "ZERO_STEP_WAVES_PER_CU", dflt);
 }
@@ -977,7 +981,7 @@ extern "C" zero_status zero_get_waves_per_cu(int32_t kind, int32_t n_grads, int3
         return ZERO_EINVAL;
     // the kernels bf16 gradients take
     const bool runtime = !compiled_ranks(n_grads);
-    *waves = kind == ZERO_CAP_STEP ? step_waves_per_cu(n_grads, runtime)
+    *waves = kind == ZERO_CAP_STEP ? step_waves_per_cu(n_grads, runtime, 2)
            : kind == ZERO_CAP_STEP1 ? step1_waves_per_cu(false)
                                     : norm_waves_per_cu(n_grads, runtime);
     return ZERO_OK;

@@ -127,7 +127,8 @@ hipError_t launch_quads_nr(const void *const *grads, int n, int gsize_quad, floa
                            hipStream_t st, int waves = -1)
 {
     constexpr int CAP = NR > 0 ? NR : ZERO_MAX_RANKS;
-    const size_t lds = occupancy_cap_lds(waves >= 0 ? waves : step_waves_per_cu(n, NR == 0), 0);
+    const size_t lds =
+        occupancy_cap_lds(waves >= 0 ? waves : step_waves_per_cu(n, NR == 0, gsize_quad / kQuad), 0);
     for (int64_t q0 = 0; q0 < nquads; q0 += kMaxQuadsPerLaunch) {
         const int64_t nq = nquads - q0 < kMaxQuadsPerLaunch ? nquads - q0 : kMaxQuadsPerLaunch;
         GradSet<CAP> gs{};
@@ -175,6 +176,24 @@ hipError_t launch_bf16_quads(const void *const *grads, int n, float *w, float *m
                                      n, w, m, v, o, nq, c, st);
 }
 
+// fp32 gradients (a reduce dtype of fp32): kernels compiled for the
+// power-of-two rank counts up to 32, the run-time kernel for any other N.
+template <bool POW2>
+hipError_t launch_f32_quads(const void *const *grads, int n, float *w, float *m, float *v,
+                            uint16_t *o, int64_t nq, const StepConsts &c, hipStream_t st)
+{
+    using QD = F32Quad;
+    constexpr int B = 16;  // bytes of one fp32 quad
+    switch (n) {
+    case 2: return launch_quads_nr<2, QD, POW2>(grads, n, B, w, m, v, o, nq, c, st);
+    case 4: return launch_quads_nr<4, QD, POW2>(grads, n, B, w, m, v, o, nq, c, st);
+    case 8: return launch_quads_nr<8, QD, POW2>(grads, n, B, w, m, v, o, nq, c, st);
+    case 16: return launch_quads_nr<16, QD, POW2>(grads, n, B, w, m, v, o, nq, c, st);
+    case 32: return launch_quads_nr<32, QD, POW2>(grads, n, B, w, m, v, o, nq, c, st);
+    default: return launch_quads_nr<0, QD, POW2>(grads, n, B, w, m, v, o, nq, c, st);
+    }
+}
+
 template <typename GT, bool POW2>
 hipError_t launch_scalar(const void *const *grads, int n, float *w, float *m, float *v,
                          uint16_t *o, int64_t len, const StepConsts &c, hipStream_t st)
@@ -208,8 +227,8 @@ int launch_step_piece(const Piece &pc, const void *const *grads, int n_grads, in
                       : launch_quads_nr<1, F32Quad, false>(grads, n_grads, 16, w, m, v, out, nq, c,
                                                            st, wv);
         }
-        return p2 ? launch_quads_nr<0, F32Quad, true>(grads, n_grads, 16, w, m, v, out, nq, c, st)
-                  : launch_quads_nr<0, F32Quad, false>(grads, n_grads, 16, w, m, v, out, nq, c, st);
+        return p2 ? launch_f32_quads<true>(grads, n_grads, w, m, v, out, nq, c, st)
+                  : launch_f32_quads<false>(grads, n_grads, w, m, v, out, nq, c, st);
     }
     if (bf)
         return p2 ? launch_scalar<uint16_t, true>(grads, n_grads, w, m, v, out, pc.len, c, st)

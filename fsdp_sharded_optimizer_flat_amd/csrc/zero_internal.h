@@ -118,7 +118,7 @@ size_t occupancy_cap_lds(int waves_per_cu, size_t static_lds);
 // / ZERO_NORM_WAVES_PER_CU, else the defaults measured on MI355X.
 // runtime_kernel: the kernel takes the rank count as an argument (loads in
 // batches of 128 bytes per lane) instead of having it compiled in.
-int step_waves_per_cu(int n_grads, bool runtime_kernel);  // the fused step over N gradients
+int step_waves_per_cu(int n_grads, bool runtime_kernel, int grad_bytes);  // the fused step
 int step1_waves_per_cu(bool staged_chunk);  // the step on one fp32 gradient
 int norm_waves_per_cu(int n_grads, bool runtime_kernel);  // the norm pass and the staged reduction
 

@@ -500,7 +500,7 @@ def test_occupancy_caps_table_and_setter():
     """The measured defaults per kernel family (from the streams a wave keeps
     in flight), the run-time setter, and its argument checks."""
     S, S1, NRM = z.ZERO_CAP_STEP, z.ZERO_CAP_STEP1, z.ZERO_CAP_NORM
-    want = {1: 10, 2: 10, 3: 10, 4: 10, 5: 8, 6: 7, 7: 7, 8: 7, 12: 6, 16: 6, 20: 6, 21: 5,
+    want = {1: 10, 2: 10, 3: 10, 4: 8, 5: 8, 6: 7, 7: 7, 8: 7, 12: 6, 16: 6, 20: 6, 21: 5,
             24: 5, 31: 5, 32: 5, 33: 7, 48: 7, 64: 5, 100: 7, 256: 7}
     if any(os.environ.get(v) for v in ("ZERO_STEP_WAVES_PER_CU", "ZERO_STEP1_WAVES_PER_CU",
                                       "ZERO_NORM_WAVES_PER_CU")):

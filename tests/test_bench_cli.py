@@ -27,6 +27,15 @@ def test_help_lists_the_modes():
         assert flag in res.stdout
 
 
+def test_fp32_gradient_variant_needs_no_cpu_leg():
+    """The fp32-gradient variant has no oracle leg of its own: it must be
+    asked for without one (refused before any device work)."""
+    res = subprocess.run([sys.executable, BENCH, "--grad-dtype", "f32"], capture_output=True, text=True,
+                         timeout=120)
+    assert res.returncode != 0 and "--no-cpu-baseline" in res.stderr, res.stderr
+    assert res.stdout == ""
+
+
 def test_cpu_baseline_one_thread_and_all_cores():
     """The oracle leg of bench.py on CPU: one thread, then every available
     thread on its own copy of the sample; the clipped workload's sample runs
