@@ -91,6 +91,9 @@ def parse():
     ap.add_argument("--ranks", type=int, default=None,
                     help="simulated ranks N (default: the workload's); the same model at another N "
                          "(one rank's shard for the ZeRO-3 workloads)")
+    ap.add_argument("--rank", type=int, default=None,
+                    help="step this rank's shard only (its slice of every unit) instead of the "
+                         "workload's selection (gpt2l: every rank's shards)")
     ap.add_argument("--grad-dtype", default="bf16", choices=["bf16", "f32"],
                     help="gradient element type of the workload (f32: a reduce dtype of fp32)")
     ap.add_argument("--fused", action="store_true",
@@ -551,6 +554,12 @@ def workload_from_args(args):
     if args.ranks and args.ranks != wl.n_ranks:
         wl = dataclasses.replace(wl, n_ranks=args.ranks, name=f"{wl.name}_n{args.ranks}",
                                  description=wl.description + f" (at N = {args.ranks})")
+    rank = getattr(args, "rank", None)
+    if rank is not None and rank != wl.rank:
+        if not 0 <= rank < wl.n_ranks:
+            raise SystemExit(f"--rank must be in 0..{wl.n_ranks - 1}")
+        wl = dataclasses.replace(wl, rank=rank, name=f"{wl.name}_r{rank}",
+                                 description=wl.description + f" (rank {rank}'s shard only)")
     return wl
 
 

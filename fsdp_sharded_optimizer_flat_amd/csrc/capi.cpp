@@ -370,7 +370,28 @@ static zero_status step_launch(const zero_layout *L, int32_t rank, const void *c
     rq.out_ptr = out;
     const std::vector<Piece> pieces = build_pieces(
         build_segments(L, rank, grad_index, state_index, out_index, u0, u1, from_range), rq);
+    // Two or more vector pieces (one rank's slice of several units) go out in
+    // shared launches when every base is quad-aligned; otherwise, and for the
+    // heads, tails and unaligned runs, one launch per piece.
+    std::vector<Piece> vec;
+    bool aligned = (uintptr_t)master % 16 == 0 && (uintptr_t)exp_avg % 16 == 0 &&
+                   (uintptr_t)exp_avg_sq % 16 == 0 && (!out || (uintptr_t)out % 8 == 0);
+    for (int32_t q = 0; q < n_grads && aligned; ++q)
+        aligned = (uintptr_t)grads[q] % (uintptr_t)(kQuad * gsize) == 0;
+    for (const Piece &pc : pieces)
+        if (pc.vec && aligned)
+            vec.push_back(pc);
+    bool batched = false;
+    if (vec.size() >= 2) {
+        const int err = launch_step_batch(vec.data(), (int)vec.size(), grads, n_grads, grad_dtype,
+                                          master, exp_avg, exp_avg_sq, out, c, stream);
+        if (err != hipSuccess && err != hipErrorNotSupported)
+            return hip_fail(err, "zero_step launch");
+        batched = err == hipSuccess;
+    }
     for (const Piece &pc : pieces) {
+        if (batched && pc.vec)
+            continue;
         const std::vector<const void *> gp = offset_grads(grads, n_grads, pc.g_off, gsize);
         const int err = launch_step_piece(pc, gp.data(), n_grads, grad_dtype, master + pc.s_off,
                                           exp_avg + pc.s_off, exp_avg_sq + pc.s_off,

@@ -166,6 +166,13 @@ zero_status validate_step_ext(const zero_layout *L, int32_t rank, const void *co
 int launch_step_piece(const Piece &pc, const void *const *grads, int n_grads, int grad_dtype,
                       float *w, float *m, float *v, uint16_t *out, const StepConsts &c,
                       void *stream, int waves_per_cu = -1);
+// The vector pieces pcs[0..count) in as few launches as possible (several
+// pieces per launch).  Every base pointer must be quad-aligned (then every
+// vector piece's offsets are whole quads).  hipErrorNotSupported when the
+// rank count has no compiled kernel (the caller launches piece by piece).
+int launch_step_batch(const Piece *pcs, int count, const void *const *grads, int n_grads,
+                      int grad_dtype, float *w, float *m, float *v, uint16_t *out,
+                      const StepConsts &c, void *stream, int waves_per_cu = -1);
 int launch_norm_segment(int64_t len, bool vec, const void *const *grads, int n_grads,
                         int grad_dtype, float *g_out, const StepConsts &c, double *partials,
                         void *stream);

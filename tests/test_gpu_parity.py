@@ -337,6 +337,48 @@ def test_reduced_gradient_input():
     _run_case(rng, 8, [4096 + 3], 2, z.ZERO_F32, Lc, Lc, Lc, shift=0, n_grads=1)
 
 
+@pytest.mark.parametrize("n,gdt", [(8, z.ZERO_BF16), (5, z.ZERO_BF16), (64, z.ZERO_BF16),
+                                   (48, z.ZERO_BF16), (8, z.ZERO_F32), (3, z.ZERO_F32)])
+def test_many_units_one_rank(n, gdt):
+    """One rank's slice of 81 units with quad-aligned bases: the vector
+    pieces go out several per launch (more than one launch carries), the
+    heads and tails one by one; rank counts with a compiled kernel and
+    without (48, fp32 at 3: one launch per piece)."""
+    rng = np.random.default_rng(600 + n)
+    numel = [1000 + 37 * k for k in range(80)] + [4096 * n + 5]
+    for rank, (gidx, sidx, oidx) in ((n - 1, (G, Lc, G)), (n // 2, (G, G, Lc)), (0, (Lc, Lc, Lc))):
+        _run_case(rng, n, numel, rank, gdt, gidx, sidx, oidx, shift=0)
+
+
+def test_one_rank_piece_longer_than_a_launch():
+    """A rank slice of more than 2^24 quads (2^18 workgroups) is cut across
+    launches of the batched step: rank 1 of N = 2 over a 134M-element unit
+    and a small one, GLOBAL gradients, LOCAL state and output."""
+    rng = np.random.default_rng(601)
+    n, numel, rank = 2, [2 * (1 << 26) + 24, 1000], 1
+    h = dict(lr=1e-3, b1=0.9, b2=0.95, eps=1e-8, wd=0.1)
+    L = z.zero_pack(n, numel)
+    log(f"one rank, long piece: {L.shard} elements of rank {rank}")
+    gnp = [(rng.standard_normal(L.padded, dtype=np.float32) * 1e-3) for _ in range(n)]
+    grads = [torch.from_numpy(g).to(DEV).to(torch.bfloat16) for g in gnp]
+    gnp = [np.ascontiguousarray(to_np(g)) for g in grads]
+    init = rng.normal(0, 0.02, L.shard).astype(np.float32)
+    master = torch.from_numpy(init).to(DEV)
+    m, v = torch.zeros_like(master), torch.zeros_like(master)
+    out = torch.zeros(L.shard, dtype=torch.int16, device=DEV)
+    z.zero_step(L, rank, grads, G, float(n), master, m, v, Lc, out, Lc, scalars(1, h))
+    om, omm, ov = init.copy(), np.zeros(L.shard, np.float32), np.zeros(L.shard, np.float32)
+    oout = np.zeros(L.shard, np.uint16)
+    oracle.zero_step_rank(n, numel, rank, gnp, grad_local=False, divisor=float(n), clip=1.0,
+                          master=om, m=omm, v=ov, state_global=False, out=oout, out_gather=False,
+                          t=1, **hyper_args(h))
+    torch.cuda.synchronize()
+    assert_same_f32(to_np(master), om, "master")
+    assert_same_f32(to_np(m), omm, "m")
+    assert_same_f32(to_np(v), ov, "v")
+    assert_same_bf16(to_np(out), oout, "bf16 out")
+
+
 def test_rank_by_rank_equals_all_at_once_and_unsharded():
     """The pages' invariant on the GPU: every rank stepping its own shard
     (LOCAL state) reproduces the all-ranks step and plain AdamW."""
