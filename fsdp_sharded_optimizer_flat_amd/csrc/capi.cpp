@@ -370,9 +370,10 @@ static zero_status step_launch(const zero_layout *L, int32_t rank, const void *c
     rq.out_ptr = out;
     const std::vector<Piece> pieces = build_pieces(
         build_segments(L, rank, grad_index, state_index, out_index, u0, u1, from_range), rq);
-    // Two or more vector pieces (one rank's slice of several units) go out in
-    // shared launches when every base is quad-aligned; otherwise, and for the
-    // heads, tails and unaligned runs, one launch per piece.
+    // Two or more vector pieces (one rank's slice of several units), or a
+    // piece whose wave grid is shifted to cache lines, go out through the
+    // shared-launch kernel when every base is quad-aligned; otherwise, and
+    // for the heads, tails and unaligned runs, one launch per piece.
     std::vector<Piece> vec;
     bool aligned = (uintptr_t)master % 16 == 0 && (uintptr_t)exp_avg % 16 == 0 &&
                    (uintptr_t)exp_avg_sq % 16 == 0 && (!out || (uintptr_t)out % 8 == 0);
@@ -382,7 +383,10 @@ static zero_status step_launch(const zero_layout *L, int32_t rank, const void *c
         if (pc.vec && aligned)
             vec.push_back(pc);
     bool batched = false;
-    if (vec.size() >= 2) {
+    bool shifted = false;  // a grid phase only the shared-launch kernel applies
+    for (const Piece &pc : vec)
+        shifted = shifted || pc.phase != 0;
+    if (vec.size() >= 2 || shifted) {
         const int err = launch_step_batch(vec.data(), (int)vec.size(), grads, n_grads, grad_dtype,
                                           master, exp_avg, exp_avg_sq, out, c, stream);
         if (err != hipSuccess && err != hipErrorNotSupported)

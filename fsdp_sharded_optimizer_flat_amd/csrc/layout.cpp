@@ -111,6 +111,38 @@ static inline int64_t quad_need(const void *p, int elem, int64_t off)
     return need_mod(p, elem, off, mult);
 }
 
+// The wave grid's phase for a vector body that starts at element offsets
+// (g, s, o): the p in 0..15 quads that puts the most streamed bytes at a
+// 128-byte line when each wave's span starts, counting each gradient's read,
+// each state array's read and write, and the bf16 output's write, writes
+// twice (a store covering part of a line costs more than a load).  A wave
+// span is 64 quads, a whole number of lines for every element size, so only
+// the span starts matter; any p keeps quad alignment.
+static int line_phase(const Request &rq, int gsize, int64_t g, int64_t s, int64_t o)
+{
+    auto at_line = [](const void *base, int elem, int64_t off, int p, int shift_elems) {
+        const uintptr_t a = (uintptr_t)base + (uintptr_t)(off * elem);
+        return (a - (uintptr_t)(shift_elems * p) * (uintptr_t)elem) % 128u == 0;
+    };
+    int best = 0, best_score = -1;
+    for (int p = 0; p < 16; ++p) {
+        int score = 0;
+        for (int q = 0; q < rq.n_grads; ++q)
+            if (at_line(rq.grads[q], gsize, g, p, kQuad))
+                score += gsize;
+        for (int i = 0; i < rq.n_state_ptrs; ++i)
+            if (rq.state_ptrs[i] && at_line(rq.state_ptrs[i], 4, s, p, kQuad))
+                score += 4 + 2 * 4;
+        if (rq.out_ptr && at_line(rq.out_ptr, 2, o, p, kQuad))
+            score += 2 * 2;
+        if (score > best_score) {
+            best_score = score;
+            best = p;
+        }
+    }
+    return best;
+}
+
 std::vector<Piece> build_pieces(const std::vector<Segment> &segs, const Request &rq)
 {
     std::vector<Piece> pieces;
@@ -138,8 +170,11 @@ std::vector<Piece> build_pieces(const std::vector<Segment> &segs, const Request 
         const int64_t body = (s.len - head) / kQuad * kQuad;
         if (head > 0)
             pieces.push_back({s.g_off, s.s_off, s.o_off, head, false});
-        if (body > 0)
-            pieces.push_back({s.g_off + head, s.s_off + head, s.o_off + head, body, true});
+        if (body > 0) {
+            Piece pc{s.g_off + head, s.s_off + head, s.o_off + head, body, true};
+            pc.phase = line_phase(rq, gsize, pc.g_off, pc.s_off, pc.o_off);
+            pieces.push_back(pc);
+        }
         const int64_t tail_at = head + body;
         if (tail_at < s.len)
             pieces.push_back({s.g_off + tail_at, s.s_off + tail_at, s.o_off + tail_at,

@@ -107,8 +107,9 @@ constexpr int kStepGroupShift = 9;  // blocks per group
 constexpr int64_t kStepBatchBlocks = int64_t(kStepGroups) << kStepGroupShift;
 
 struct QuadPiece {
-    int64_t g, s, o;     // quad offsets from the gradient, state and output bases
-    uint32_t nq, first;  // quads; the launch's first block of this piece
+    int64_t g, s, o;         // quad offsets from the gradient, state and output bases
+    uint32_t nq_phase;       // quads (low 24 bits, < 2^24) | the grid phase << 24
+    uint32_t first;          // the launch's first block of this piece
 };
 
 struct StepBatch {
@@ -136,9 +137,11 @@ __global__ __launch_bounds__(kWave) void step_batch_kernel(GradSet<CAP> gs, int 
         while (blk >= b.end[i])  // the last piece ends at the grid size: the walk stops there
             ++i;
     const QuadPiece pc = b.p[i];
-    const int64_t t0 = (int64_t)(blk - pc.first) * kWave;
+    // the piece's waves start `phase` quads before it (lanes before the
+    // piece, like lanes past its end, do nothing)
+    const int64_t t0 = (int64_t)(blk - pc.first) * kWave - (int64_t)(pc.nq_phase >> 24);
     const int lane = threadIdx.x;
-    if (t0 + lane >= (int64_t)pc.nq)
+    if (t0 + lane < 0 || t0 + lane >= (int64_t)(pc.nq_phase & 0xffffffu))
         return;
     step_tile<NR, CAP, QD, POW2>(gs, n, W + kQuad * pc.s, M + kQuad * pc.s, V + kQuad * pc.s,
                                  O ? O + kQuad * pc.o : nullptr, pc.g + t0 + lane, t0, lane, c);
@@ -313,19 +316,21 @@ std::vector<std::pair<StepBatch, uint32_t>> step_batches(const Piece *pcs, int c
         b = StepBatch{};
         blocks = 0;
     };
-    constexpr int64_t kMaxQuads = kStepBatchBlocks * kWave;
+    constexpr int64_t kMaxQuads = (kStepBatchBlocks - 1) * kWave;  // < 2^24
     for (int k = 0; k < count; ++k) {
         int64_t g = pcs[k].g_off / kQuad, st = pcs[k].s_off / kQuad, o = pcs[k].o_off / kQuad;
+        int phase = pcs[k].phase;
         for (int64_t left = pcs[k].len / kQuad; left > 0;) {
-            const int64_t nq = std::min(left, kMaxQuads);
-            const uint32_t nb = (uint32_t)((nq + kWave - 1) / kWave);
+            // a cut leaves the next part on the same wave grid, at phase 0
+            const int64_t nq = std::min(left, kMaxQuads - phase);
+            const uint32_t nb = (uint32_t)((nq + phase + kWave - 1) / kWave);
             if (b.n_pieces == kStepPieces || (int64_t)blocks + nb > kStepBatchBlocks)
                 flush();
             QuadPiece &q = b.p[b.n_pieces];
             q.g = g;
             q.s = st;
             q.o = o;
-            q.nq = (uint32_t)nq;
+            q.nq_phase = (uint32_t)nq | ((uint32_t)phase << 24);
             q.first = blocks;
             blocks += nb;
             b.end[b.n_pieces] = blocks;
@@ -334,6 +339,7 @@ std::vector<std::pair<StepBatch, uint32_t>> step_batches(const Piece *pcs, int c
             st += nq;
             o += nq;
             left -= nq;
+            phase = 0;
         }
     }
     flush();

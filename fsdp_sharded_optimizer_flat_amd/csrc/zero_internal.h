@@ -42,6 +42,10 @@ struct Segment {
 struct Piece {
     int64_t g_off, s_off, o_off, len;
     bool vec;
+    // Vector pieces: how many quads (0..15) before the piece the wave grid
+    // starts, chosen so that the most streamed bytes begin each wave's span
+    // at a 128-byte cache line (line_phase in layout.cpp).
+    int32_t phase = 0;
 };
 
 // Validated step / norm request, pointers already checked.
