@@ -91,6 +91,9 @@ def parse():
     ap.add_argument("--ranks", type=int, default=None,
                     help="simulated ranks N (default: the workload's); the same model at another N "
                          "(one rank's shard for the ZeRO-3 workloads)")
+    ap.add_argument("--clip", type=float, default=None, metavar="MAX_NORM",
+                    help="clip the workload's gradients to this global norm (the norm pass, the "
+                         "coefficient and the step on g, as llama8b_z3_clip does)")
     ap.add_argument("--rank", type=int, default=None,
                     help="step this rank's shard only (its slice of every unit) instead of the "
                          "workload's selection (gpt2l: every rank's shards)")
@@ -554,6 +557,10 @@ def workload_from_args(args):
     if args.ranks and args.ranks != wl.n_ranks:
         wl = dataclasses.replace(wl, n_ranks=args.ranks, name=f"{wl.name}_n{args.ranks}",
                                  description=wl.description + f" (at N = {args.ranks})")
+    clip = getattr(args, "clip", None)
+    if clip is not None and clip != wl.clip_max_norm:
+        wl = dataclasses.replace(wl, clip_max_norm=clip, name=f"{wl.name}_clip{clip:g}",
+                                 description=wl.description + f" (clipped at {clip:g})")
     rank = getattr(args, "rank", None)
     if rank is not None and rank != wl.rank:
         if not 0 <= rank < wl.n_ranks:

@@ -740,14 +740,43 @@ zero_status gradnorm_launch(const zero_layout *L, int32_t rank, const void *cons
     double *partials = static_cast<double *>(workspace);
     double *tree = partials + norm_partials_bound(L, rank) + 1;
     const std::vector<Segment> segs = build_segments(L, rank, grad_index, g_index, ZERO_LOCAL);
+    // Two or more aligned segments (one rank's slice of several units) share
+    // launches when every base is 16-byte aligned; each segment's tiles and
+    // partial slots are the same either way.
+    bool aligned = !g_out || (uintptr_t)g_out % 16 == 0;
+    for (int32_t q = 0; q < n_grads && aligned; ++q)
+        aligned = (uintptr_t)grads[q] % 16 == 0;
+    std::vector<NormSegment> batch;
+    std::vector<bool> in_batch(segs.size(), false);
     int64_t total = 0;
-    for (const Segment &sg : segs) {
-        const std::vector<const void *> gp = offset_grads(grads, n_grads, sg.g_off, gsize);
-        const int err = launch_norm_segment(sg.len, segment_vec_aligned(sg, rq), gp.data(), n_grads,
-                                            grad_dtype, g_out ? g_out + sg.s_off : nullptr, c,
-                                            partials + total, stream);
-        if (err != hipSuccess)
+    for (size_t k = 0; k < segs.size(); ++k) {
+        const Segment &sg = segs[k];
+        if (aligned && sg.g_off % kOct == 0 && segment_vec_aligned(sg, rq)) {
+            batch.push_back(NormSegment{sg.g_off, sg.s_off, sg.len, total});
+            in_batch[k] = true;
+        }
+        total += norm_segment_blocks(sg.len);
+    }
+    bool batched = false;
+    if (batch.size() >= 2) {
+        const int err = launch_norm_batch(batch.data(), (int)batch.size(), grads, n_grads,
+                                          grad_dtype, g_out, c, partials, stream);
+        if (err != hipSuccess && err != hipErrorNotSupported)
             return hip_fail(err, "zero_gradnorm stage 1");
+        batched = err == hipSuccess;
+    }
+    total = 0;
+    for (size_t k = 0; k < segs.size(); ++k) {
+        const Segment &sg = segs[k];
+        if (!(batched && in_batch[k])) {
+            const std::vector<const void *> gp = offset_grads(grads, n_grads, sg.g_off, gsize);
+            const int err = launch_norm_segment(sg.len, segment_vec_aligned(sg, rq), gp.data(),
+                                                n_grads, grad_dtype,
+                                                g_out ? g_out + sg.s_off : nullptr, c,
+                                                partials + total, stream);
+            if (err != hipSuccess)
+                return hip_fail(err, "zero_gradnorm stage 1");
+        }
         total += norm_segment_blocks(sg.len);
     }
     *n_partials = total;

@@ -15,6 +15,7 @@
 // layout, the rank and the index spaces -- never on the device, the
 // pointers' alignment or whether g is written -- so the result is bitwise
 // reproducible.
+#include <algorithm>
 #include <mutex>
 #include <vector>
 
@@ -52,21 +53,21 @@ using namespace dev;
 // alignment nor on whether g_out is written.  One tile per workgroup (a
 // non-persistent grid) keeps the tiles in flight in one compact window, as in
 // the step kernel.
+// Tile `tile` of a segment whose gradient elements start g8 octs (8 * g8
+// elements) past every rank's gradient base; G (may be null) is the
+// segment's g_out.
 template <int NR, int CAP, typename GT, typename OD, bool POW2, bool VEC>
-__global__ __launch_bounds__(kWave) void norm_kernel(GradSet<CAP> gs, int n,
-                                                    float *__restrict__ G, int64_t len,
-                                                    StepConsts c,
-                                                    double *__restrict__ partials)
+__device__ __forceinline__ void norm_tile(const GradSet<CAP> &gs, int n, float *__restrict__ G,
+                                          int64_t len, int64_t g8, int64_t tile, int lane,
+                                          const StepConsts &c, double *__restrict__ partial,
+                                          f32x4 *xg)
 {
     static_assert(OD::kN == kOct, "one oct per lane");
-    __shared__ f32x4 xg[2 * kWave];  // the tile's g in element order
-    const int64_t tile = blockIdx.x;
-    const int lane = threadIdx.x;
     const int64_t e0 = tile * kNormSpan + (int64_t)lane * kOct;  // first element of the oct
     float g[kOct];
     if (VEC && (tile + 1) * kNormSpan <= len) {  // uniform over the workgroup
         float s[kOct];
-        rank_sum<NR, CAP, OD>(gs, n, tile * kWave + lane, s);
+        rank_sum<NR, CAP, OD>(gs, n, g8 + tile * kWave + lane, s);
 #pragma unroll
         for (int k = 0; k < kOct; ++k)
             g[k] = average<POW2>(s[k], c);
@@ -79,13 +80,14 @@ __global__ __launch_bounds__(kWave) void norm_kernel(GradSet<CAP> gs, int n,
             st_span(xg[kWave + lane], t4 + kWave, lane);
         }
     } else {
+        const int64_t gb = g8 * kOct;
 #pragma unroll
         for (int k = 0; k < kOct; ++k) {
             g[k] = 0.0f;
             if (e0 + k < len) {
-                float s = grad_at<GT>(gs.p[0], e0 + k);
+                float s = grad_at<GT>(gs.p[0], gb + e0 + k);
                 for (int q = 1; q < n; ++q)
-                    s = s + grad_at<GT>(gs.p[q], e0 + k);
+                    s = s + grad_at<GT>(gs.p[q], gb + e0 + k);
                 g[k] = average<POW2>(s, c);
                 if (G)
                     G[e0 + k] = g[k];
@@ -100,7 +102,71 @@ __global__ __launch_bounds__(kWave) void norm_kernel(GradSet<CAP> gs, int n,
     }
     const double t = wave_sum(acc);
     if (lane == 0)
-        partials[tile] = t;
+        *partial = t;
+}
+
+template <int NR, int CAP, typename GT, typename OD, bool POW2, bool VEC>
+__global__ __launch_bounds__(kWave) void norm_kernel(GradSet<CAP> gs, int n,
+                                                    float *__restrict__ G, int64_t len,
+                                                    StepConsts c,
+                                                    double *__restrict__ partials)
+{
+    __shared__ f32x4 xg[2 * kWave];  // the tile's g in element order
+    const int64_t tile = blockIdx.x;
+    norm_tile<NR, CAP, GT, OD, POW2, VEC>(gs, n, G, len, 0, tile, threadIdx.x, c, partials + tile,
+                                          xg);
+}
+
+// Several aligned segments in one launch -- one rank's slice of every unit --
+// instead of a launch per segment (each launch's drain and refill is worth
+// tens of MB of streaming: one rank's GPT-2 Large norm pass, 36 segments,
+// ran at 36-40 % of the HBM peak).  Each segment keeps its own tiles and
+// partial slots, so the partition -- and the sum's bits -- are those of the
+// launch per segment.  A workgroup finds its segment as the step's shared
+// launches do: a byte per group of 512 tiles naming the segment that holds
+// the group's first tile (bit 7: the whole group lies in it), a walk over
+// segment ends only in a group that holds a boundary.
+constexpr int kNormPieces = 48;
+constexpr int kNormGroups = 512;
+constexpr int kNormGroupShift = 9;
+constexpr int64_t kNormBatchTiles = int64_t(kNormGroups) << kNormGroupShift;
+
+struct NormPiece {
+    int64_t g8;     // octs from every gradient base to the segment's first element
+    int64_t s;      // g_out elements to the segment's first g
+    int64_t len;    // elements
+    int64_t pbase;  // the segment's first partial
+    uint32_t first; // the launch's first tile of this segment
+    uint32_t pad;
+};
+
+struct NormBatch {
+    NormPiece p[kNormPieces];
+    uint32_t end[kNormPieces];        // segment i covers tiles [p[i].first, end[i])
+    uint32_t group[kNormGroups / 4];  // byte per group, as described above
+    int32_t n_pieces, pad;
+};
+static_assert(sizeof(NormBatch) + sizeof(GradSet<64>) + sizeof(StepConsts) + 64 <= 4096,
+              "kernel arguments are limited to 4 KB");
+
+template <int NR, int CAP, typename GT, typename OD, bool POW2>
+__global__ __launch_bounds__(kWave) void norm_batch_kernel(GradSet<CAP> gs, int n,
+                                                          float *__restrict__ G, const NormBatch b,
+                                                          StepConsts c,
+                                                          double *__restrict__ partials)
+{
+    __shared__ f32x4 xg[2 * kWave];
+    const uint32_t blk = blockIdx.x;
+    const uint32_t g = blk >> kNormGroupShift;
+    const uint32_t entry = (b.group[g >> 2] >> ((g & 3u) * 8u)) & 0xffu;
+    int i = (int)(entry & 0x7fu);
+    if (!(entry & 0x80u))
+        while (blk >= b.end[i])  // the last segment ends at the grid size: the walk stops there
+            ++i;
+    const NormPiece pc = b.p[i];
+    const int64_t tile = blk - pc.first;
+    norm_tile<NR, CAP, GT, OD, POW2, true>(gs, n, G ? G + pc.s : nullptr, pc.len, pc.g8, tile,
+                                           threadIdx.x, c, partials + pc.pbase + tile, xg);
 }
 
 // One level of the fixed-order reduction of the partials: workgroup b sums
@@ -194,6 +260,106 @@ hipError_t launch_bf16_vec(const void *const *grads, int n, float *G, int64_t le
                                    G, len, c, partials, blocks, st);
 }
 
+// ---- several segments per launch ---------------------------------------
+
+void fill_norm_groups(NormBatch &b, uint32_t total)
+{
+    int first_piece = 0, last_piece = 0;
+    for (uint32_t g = 0; g < (uint32_t)kNormGroups; ++g) {
+        const uint32_t a = g << kNormGroupShift;
+        if (a >= total)
+            break;
+        const uint32_t z =
+            std::min<uint64_t>((uint64_t)a + (1u << kNormGroupShift) - 1u, total - 1u);
+        while (b.end[first_piece] <= a)
+            ++first_piece;
+        if (last_piece < first_piece)
+            last_piece = first_piece;
+        while (b.end[last_piece] <= z)
+            ++last_piece;
+        const uint32_t entry = (uint32_t)first_piece | (first_piece == last_piece ? 0x80u : 0u);
+        b.group[g >> 2] |= entry << ((g & 3u) * 8u);
+    }
+}
+
+// Batches of the segments, in order: at most kNormPieces segments and
+// kNormBatchTiles tiles each, a longer segment cut at a whole tile (its
+// later tiles keep their elements and partial slots).
+std::vector<std::pair<NormBatch, uint32_t>> norm_batches(const NormSegment *segs, int count)
+{
+    std::vector<std::pair<NormBatch, uint32_t>> out;
+    NormBatch b{};
+    uint32_t tiles = 0;
+    auto flush = [&]() {
+        if (b.n_pieces == 0)
+            return;
+        fill_norm_groups(b, tiles);
+        out.emplace_back(b, tiles);
+        b = NormBatch{};
+        tiles = 0;
+    };
+    for (int k = 0; k < count; ++k) {
+        int64_t g8 = segs[k].g_off / kOct, sg = segs[k].g_out_off, len = segs[k].len,
+                pbase = segs[k].partial;
+        while (len > 0) {
+            const int64_t nt = std::min((len + kNormSpan - 1) / kNormSpan, kNormBatchTiles);
+            const int64_t part = std::min(len, nt * kNormSpan);
+            if (b.n_pieces == kNormPieces || (int64_t)tiles + nt > kNormBatchTiles)
+                flush();
+            NormPiece &q = b.p[b.n_pieces];
+            q.g8 = g8;
+            q.s = sg;
+            q.len = part;
+            q.pbase = pbase;
+            q.first = tiles;
+            tiles += (uint32_t)nt;
+            b.end[b.n_pieces] = tiles;
+            ++b.n_pieces;
+            g8 += nt * kWave;
+            sg += nt * kNormSpan;
+            pbase += nt;
+            len -= part;
+        }
+    }
+    flush();
+    return out;
+}
+
+template <int NR, bool POW2>
+hipError_t launch_norm_batch_nr(const NormSegment *segs, int count, const void *const *grads, int n,
+                                float *G, const StepConsts &c, double *partials, hipStream_t st)
+{
+    GradSet<NR> gs{};
+    for (int q = 0; q < n; ++q)
+        gs.p[q] = grads[q];
+    const size_t lds = occupancy_cap_lds(norm_waves_per_cu(n, false), 2 * kWave * sizeof(f32x4));
+    for (const auto &bb : norm_batches(segs, count)) {
+        hipLaunchKernelGGL((norm_batch_kernel<NR, NR, uint16_t, Bf16Oct, POW2>), dim3(bb.second),
+                           dim3(kWave), lds, st, gs, n, G, bb.first, c, partials);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
+}
+
+template <bool POW2, int... Ks>
+hipError_t norm_batch_compiled(std::integer_sequence<int, Ks...>, const NormSegment *segs,
+                               int count, const void *const *grads, int n, float *G,
+                               const StepConsts &c, double *partials, hipStream_t st)
+{
+    hipError_t r = hipErrorNotSupported;
+    const bool hit =
+        ((n == Ks + 1
+              ? (r = launch_norm_batch_nr<Ks + 1, POW2>(segs, count, grads, n, G, c, partials, st),
+                 true)
+              : false) ||
+         ...);
+    if (!hit && n == 64)
+        r = launch_norm_batch_nr<64, POW2>(segs, count, grads, n, G, c, partials, st);
+    return r;
+}
+
 }  // namespace
 
 int64_t norm_segment_blocks(int64_t len)
@@ -224,6 +390,20 @@ int launch_norm_segment(int64_t len, bool vec, const void *const *grads, int n_g
                   : launch_nr<0, float, F32Oct, false, true>(grads, n_grads, g_out, len, c, partials, blocks, st);
     return p2 ? launch_nr<0, float, F32Oct, true, false>(grads, n_grads, g_out, len, c, partials, blocks, st)
               : launch_nr<0, float, F32Oct, false, false>(grads, n_grads, g_out, len, c, partials, blocks, st);
+}
+
+int launch_norm_batch(const NormSegment *segs, int count, const void *const *grads, int n_grads,
+                      int grad_dtype, float *g_out, const StepConsts &c, double *partials,
+                      void *stream)
+{
+    if (grad_dtype != ZERO_BF16)
+        return hipErrorNotSupported;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const auto seq = std::make_integer_sequence<int, kMaxCompiledRanks>{};
+    return c.div_pow2 ? norm_batch_compiled<true>(seq, segs, count, grads, n_grads, g_out, c,
+                                                  partials, st)
+                      : norm_batch_compiled<false>(seq, segs, count, grads, n_grads, g_out, c,
+                                                   partials, st);
 }
 
 int noalloc_scratch(void **ptr)

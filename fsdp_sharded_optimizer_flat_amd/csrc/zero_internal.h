@@ -177,6 +177,18 @@ int launch_step_piece(const Piece &pc, const void *const *grads, int n_grads, in
 int launch_step_batch(const Piece *pcs, int count, const void *const *grads, int n_grads,
                       int grad_dtype, float *w, float *m, float *v, uint16_t *out,
                       const StepConsts &c, void *stream, int waves_per_cu = -1);
+// One aligned segment of a norm pass: gradient elements from g_off (a
+// multiple of 8) past every gradient base, g at g_out_off past g_out, its
+// tiles' partials from `partial`.
+struct NormSegment {
+    int64_t g_off, g_out_off, len, partial;
+};
+// The segments in as few launches as possible, each tile's partial where a
+// launch per segment puts it.  Every gradient base 16-byte aligned (g_out's
+// too).  hipErrorNotSupported without a compiled bf16 kernel for n_grads.
+int launch_norm_batch(const NormSegment *segs, int count, const void *const *grads, int n_grads,
+                      int grad_dtype, float *g_out, const StepConsts &c, double *partials,
+                      void *stream);
 int launch_norm_segment(int64_t len, bool vec, const void *const *grads, int n_grads,
                         int grad_dtype, float *g_out, const StepConsts &c, double *partials,
                         void *stream);
