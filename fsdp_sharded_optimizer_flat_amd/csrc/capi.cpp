@@ -262,18 +262,33 @@ int step1_waves_per_cu(bool staged_chunk)
     return cap_for(1, "ZERO_STEP1_WAVES_PER_CU", staged_chunk ? 12 : 10);
 }
 
-int norm_waves_per_cu(int n_grads, bool runtime_kernel)
+int norm_waves_per_cu(int n_grads, bool runtime_kernel, int grad_bytes)
 {
     // The norm pass and the staged step's reduction: N reads of 16 bytes per
-    // lane and one write.  Measured (bench.py --sweep-waves norm:...):
+    // lane and one write.  Measured (bench.py --sweep-waves norm:..., the 8B
+    // shard at N ranks, three interleaved rounds; % of 8 TB/s):
     // compiled N = 64 (staged reduction) 4: 78.5  5: 78.6  6: 77.8
     // 7: 76.4, and N = 32 like it (3 starves at 57 %); compiled N = 24 best
-    // at 6 (5 % above 5 and 7), N = 12 at 7 (6: 5 % lower); the run-time kernel,
-    // two batches of 8 ranks in flight, N = 48: 5: 72.1  6: 76.9  7: 76.3
-    // 8: 75.9; N = 128: 5: 74.8  6: 77.3  7: 77.8  8: 76.9; N = 256: 5: 74.7
-    // 6: 76.7  7: 79.5  8: 78.9, so 7; fewer ranks keep less in flight and
-    // take 7 as well.
-    const int dflt = runtime_kernel || n_grads <= 16 ? 7 : n_grads <= 24 ? 6 : 5;
+    // at 6 (5 % above 5 and 7), N = 12 at 7 (6: 5 % lower).  The run-time
+    // kernel (two batches of 128 bytes per lane in flight; bf16 above 32
+    // ranks, fp32 at every N), as the staged step / the clipped workload's
+    // norm pass:
+    //   bf16 N = 40   5: 74.6 / 77.8  6: 77.0 / 80.5  7: 76.2 / 78.7  8: 75.6 / 77.8
+    //   bf16 N = 48   5: 75.3 / 77.8  6: 77.1 / 80.6  7: 76.3 / 78.9  8: 75.4 / 77.9
+    //   bf16 N = 96   5: 73.6 / 75.0  6: 75.1 / 77.7  7: 74.4 / 76.4  8: 74.3 / 75.9
+    //   bf16 N = 128  5: 77.0 / 77.4  6: 77.9 / 79.6  7: 78.1 / 79.0  8: 77.3 / 78.1
+    //   bf16 N = 192  5: 77.3 / 77.6  6: 77.4 / 79.7  7: 76.3 / 79.8  8: 75.7 / 78.9
+    //   bf16 N = 256  5: 76.2 / 76.3  6: 78.4 / 78.4  7: 80.2 / 80.1  8: 79.5 / 79.4
+    //   fp32 N = 48   5: 69.8 / 71.8  6: 69.1 / 70.8  7: 66.7 / 68.2  8: 65.8 / 67.3
+    //   fp32 N = 64   5: 68.3 / 68.1  6: 68.7 / 66.5  7: 67.6 / 64.8  8: 66.7 / 64.5
+    //   fp32 N = 128  5: 72.5 / 73.0  6: 71.9 / 72.1  7: 70.7 / 70.8  8: 70.1 / 70.3
+    // so 6 for bf16 up to 192 ranks and 7 above, 5 for fp32 above 32 ranks;
+    // fewer fp32 ranks keep less in flight and take 7.
+    int dflt;
+    if (runtime_kernel)
+        dflt = grad_bytes == 2 ? (n_grads <= 192 ? 6 : 7) : (n_grads <= 32 ? 7 : 5);
+    else
+        dflt = n_grads <= 16 ? 7 : n_grads <= 24 ? 6 : 5;
     return cap_for(2, "ZERO_NORM_WAVES_PER_CU", dflt);
 }
 
@@ -1037,7 +1052,7 @@ extern "C" zero_status zero_get_waves_per_cu(int32_t kind, int32_t n_grads, int3
     const bool runtime = !compiled_ranks(n_grads);
     *waves = kind == ZERO_CAP_STEP ? step_waves_per_cu(n_grads, runtime, 2)
            : kind == ZERO_CAP_STEP1 ? step1_waves_per_cu(false)
-                                    : norm_waves_per_cu(n_grads, runtime);
+                                    : norm_waves_per_cu(n_grads, runtime, 2);
     return ZERO_OK;
 }
 

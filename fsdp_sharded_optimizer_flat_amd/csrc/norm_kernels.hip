@@ -223,7 +223,8 @@ hipError_t launch_nr(const void *const *grads, int n, float *G, int64_t len, con
     GradSet<CAP> gs{};
     for (int q = 0; q < n; ++q)
         gs.p[q] = grads[q];
-    const size_t lds = occupancy_cap_lds(norm_waves_per_cu(n, NR == 0), 2 * kWave * sizeof(f32x4));
+    const size_t lds = occupancy_cap_lds(norm_waves_per_cu(n, NR == 0, (int)sizeof(GT)),
+                                         2 * kWave * sizeof(f32x4));
     hipLaunchKernelGGL((norm_kernel<NR, CAP, GT, OD, POW2, VEC>), dim3((unsigned)blocks),
                        dim3(kWave), lds, st, gs, n, G, len, c, partials);
     return hipGetLastError();
@@ -332,7 +333,7 @@ hipError_t launch_norm_batch_nr(const NormSegment *segs, int count, const void *
     GradSet<NR> gs{};
     for (int q = 0; q < n; ++q)
         gs.p[q] = grads[q];
-    const size_t lds = occupancy_cap_lds(norm_waves_per_cu(n, false), 2 * kWave * sizeof(f32x4));
+    const size_t lds = occupancy_cap_lds(norm_waves_per_cu(n, false, 2), 2 * kWave * sizeof(f32x4));
     for (const auto &bb : norm_batches(segs, count)) {
         hipLaunchKernelGGL((norm_batch_kernel<NR, NR, uint16_t, Bf16Oct, POW2>), dim3(bb.second),
                            dim3(kWave), lds, st, gs, n, G, bb.first, c, partials);

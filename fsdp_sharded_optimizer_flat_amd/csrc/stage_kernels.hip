@@ -80,7 +80,8 @@ hipError_t launch_nr(const void *const *grads, int n, float *G, int64_t len, con
     for (int q = 0; q < n; ++q)
         gs.p[q] = grads[q];
     const int64_t blocks = (len + kNormSpan - 1) / kNormSpan;
-    const size_t lds = occupancy_cap_lds(norm_waves_per_cu(n, NR == 0), 2 * kWave * sizeof(f32x4));
+    const size_t lds = occupancy_cap_lds(norm_waves_per_cu(n, NR == 0, (int)sizeof(GT)),
+                                         2 * kWave * sizeof(f32x4));
     hipLaunchKernelGGL((stage_reduce_kernel<NR, CAP, GT, OD, POW2, VEC>), dim3((unsigned)blocks),
                        dim3(kWave), lds, st, gs, n, G, len, c);
     return hipGetLastError();

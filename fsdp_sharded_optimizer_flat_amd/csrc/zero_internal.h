@@ -124,7 +124,8 @@ size_t occupancy_cap_lds(int waves_per_cu, size_t static_lds);
 // batches of 128 bytes per lane) instead of having it compiled in.
 int step_waves_per_cu(int n_grads, bool runtime_kernel, int grad_bytes);  // the fused step
 int step1_waves_per_cu(bool staged_chunk);  // the step on one fp32 gradient
-int norm_waves_per_cu(int n_grads, bool runtime_kernel);  // the norm pass and the staged reduction
+int norm_waves_per_cu(int n_grads, bool runtime_kernel,
+                      int grad_bytes);  // the norm pass and the staged reduction
 
 // Rank counts with a kernel of their own for bf16 gradients (fused step and
 // norm pass): every N up to kMaxCompiledRanks, and 64.

@@ -507,8 +507,9 @@ def test_occupancy_caps_table_and_setter():
         pytest.skip("occupancy environment overrides set")
     assert {n: z.zero_get_waves_per_cu(S, n) for n in want} == want
     assert z.zero_get_waves_per_cu(S1, 1) == 10
-    assert [z.zero_get_waves_per_cu(NRM, n) for n in (8, 12, 17, 24, 25, 32, 48, 64, 128)] == \
-        [7, 7, 6, 6, 5, 5, 7, 5, 7]
+    assert [z.zero_get_waves_per_cu(NRM, n) for n in (8, 12, 17, 24, 25, 32, 48, 64, 128, 192,
+                                                       193, 256)] == \
+        [7, 7, 6, 6, 5, 5, 6, 5, 6, 6, 7, 7]
     try:
         z.zero_set_waves_per_cu(S, 3)
         assert z.zero_get_waves_per_cu(S, 64) == 3 and z.zero_get_waves_per_cu(S, 8) == 3
