@@ -766,11 +766,12 @@ zero_status gradnorm_launch(const zero_layout *L, int32_t rank, const void *cons
     int64_t total = 0;
     for (size_t k = 0; k < segs.size(); ++k) {
         const Segment &sg = segs[k];
+        const int phase = norm_segment_phase(sg.g_off, gsize);
         if (aligned && sg.g_off % kOct == 0 && segment_vec_aligned(sg, rq)) {
-            batch.push_back(NormSegment{sg.g_off, sg.s_off, sg.len, total});
+            batch.push_back(NormSegment{sg.g_off, sg.s_off, sg.len, total, phase});
             in_batch[k] = true;
         }
-        total += norm_segment_blocks(sg.len);
+        total += norm_segment_blocks(sg.len, phase);
     }
     bool batched = false;
     if (batch.size() >= 2) {
@@ -783,16 +784,17 @@ zero_status gradnorm_launch(const zero_layout *L, int32_t rank, const void *cons
     total = 0;
     for (size_t k = 0; k < segs.size(); ++k) {
         const Segment &sg = segs[k];
+        const int phase = norm_segment_phase(sg.g_off, gsize);
         if (!(batched && in_batch[k])) {
             const std::vector<const void *> gp = offset_grads(grads, n_grads, sg.g_off, gsize);
-            const int err = launch_norm_segment(sg.len, segment_vec_aligned(sg, rq), gp.data(),
-                                                n_grads, grad_dtype,
+            const int err = launch_norm_segment(sg.len, phase, segment_vec_aligned(sg, rq),
+                                                gp.data(), n_grads, grad_dtype,
                                                 g_out ? g_out + sg.s_off : nullptr, c,
                                                 partials + total, stream);
             if (err != hipSuccess)
                 return hip_fail(err, "zero_gradnorm stage 1");
         }
-        total += norm_segment_blocks(sg.len);
+        total += norm_segment_blocks(sg.len, phase);
     }
     *n_partials = total;
     if (total == 0)

@@ -199,10 +199,12 @@ bool segment_vec_aligned(const Segment &s, const Request &rq)
 
 int64_t norm_partials_bound(const zero_layout *L, int32_t rank)
 {
-    // One partial per started kNormSpan elements of each segment; at most one
-    // segment per unit (one in total for rank < 0).
+    // One partial per kNormSpan-element tile of each segment, whose first
+    // tile starts up to 56 elements before it: ceil((len + phase) / 512) <=
+    // len / 512 + 2 per segment; at most one segment per unit (one in total
+    // for rank < 0).
     const int64_t segs = rank < 0 ? 1 : (L->n_units > 0 ? L->n_units : 1);
-    return selected_elements(L, rank) / kNormSpan + segs;
+    return selected_elements(L, rank) / kNormSpan + 2 * segs;
 }
 
 bool layouts_match(const zero_layout *from, const zero_layout *to)

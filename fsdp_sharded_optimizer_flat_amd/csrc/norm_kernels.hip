@@ -36,38 +36,44 @@ namespace {
 using namespace dev;
 
 // Stage 1 over one segment of `len` elements, cut into tiles of kNormSpan =
-// 512 elements; workgroup b (one wave64) owns tile b and lane l the oct of
-// elements 8l .. 8l+7 of it.  The lane adds its oct's squares in element
-// order, the wave sums its lanes by a fixed butterfly, and lane 0 writes the
-// tile's partial.  Elements past `len` contribute +0.0, which leaves a
-// binary64 sum unchanged.
+// 512 elements that start `phase` elements before the segment (0 to 56, a
+// whole number of octs: the segment's first gradient element modulo a
+// 128-byte line, so that the tiles' gradient spans start on lines when the
+// gradient bases do).  Workgroup b (one wave64) owns tile b and lane l the
+// oct of elements 8l .. 8l+7 of it.  The lane adds its oct's squares in
+// element order, the wave sums its lanes by a fixed butterfly, and lane 0
+// writes the tile's partial.  Elements before the segment or past `len`
+// contribute +0.0, which leaves a binary64 sum unchanged.
 //
 // VEC: every gradient is 16-byte aligned at the segment start (and g_out
 // too), so whole tiles load each rank's oct with one 16-byte access -- a 1 KiB
 // span per wave instruction for bf16, the access width that streams N = 64
 // ranks best on MI355X -- and g goes through LDS so that lane l then stores
-// quads l and 64 + l of the tile: two contiguous 1 KiB stores per wave.  The
-// last, partial tile of a segment, and every tile without VEC, reads the
-// same octs element by element.  Either way every value and every addition
-// happen in the same order, so the result depends on neither pointer
-// alignment nor on whether g_out is written.  One tile per workgroup (a
-// non-persistent grid) keeps the tiles in flight in one compact window, as in
-// the step kernel.
+// quads l and 64 + l of the tile: two contiguous 1 KiB stores per wave.  In
+// the first tile the lanes before the segment load in-bounds data (the
+// phase never exceeds the segment's offset in its buffers) and discard it,
+// and their quads of g are not stored.  The last, partial tile of a segment,
+// and every tile without VEC, reads the same octs element by element.
+// Either way every value and every addition happen in the same order, so
+// the result depends on neither pointer alignment nor on whether g_out is
+// written.  One tile per workgroup (a non-persistent grid) keeps the tiles
+// in flight in one compact window, as in the step kernel.
 // Tile `tile` of a segment whose gradient elements start g8 octs (8 * g8
 // elements) past every rank's gradient base; G (may be null) is the
 // segment's g_out.
 template <int NR, int CAP, typename GT, typename OD, bool POW2, bool VEC>
 __device__ __forceinline__ void norm_tile(const GradSet<CAP> &gs, int n, float *__restrict__ G,
-                                          int64_t len, int64_t g8, int64_t tile, int lane,
-                                          const StepConsts &c, double *__restrict__ partial,
-                                          f32x4 *xg)
+                                          int64_t len, int64_t g8, int phase, int64_t tile,
+                                          int lane, const StepConsts &c,
+                                          double *__restrict__ partial, f32x4 *xg)
 {
     static_assert(OD::kN == kOct, "one oct per lane");
-    const int64_t e0 = tile * kNormSpan + (int64_t)lane * kOct;  // first element of the oct
+    const int64_t t0 = tile * kNormSpan - phase;      // the tile's first element
+    const int64_t e0 = t0 + (int64_t)lane * kOct;     // first element of the lane's oct
     float g[kOct];
-    if (VEC && (tile + 1) * kNormSpan <= len) {  // uniform over the workgroup
+    if (VEC && t0 >= 0 && t0 + kNormSpan <= len) {  // a whole tile (uniform over the workgroup)
         float s[kOct];
-        rank_sum<NR, CAP, OD>(gs, n, g8 + tile * kWave + lane, s);
+        rank_sum<NR, CAP, OD>(gs, n, g8 + t0 / kOct + lane, s);
 #pragma unroll
         for (int k = 0; k < kOct; ++k)
             g[k] = average<POW2>(s[k], c);
@@ -75,16 +81,31 @@ __device__ __forceinline__ void norm_tile(const GradSet<CAP> &gs, int n, float *
             xg[2 * lane] = f32x4{g[0], g[1], g[2], g[3]};
             xg[2 * lane + 1] = f32x4{g[4], g[5], g[6], g[7]};
             __syncthreads();
-            f32x4 *t4 = reinterpret_cast<f32x4 *>(G) + tile * (2 * kWave);
+            f32x4 *t4 = reinterpret_cast<f32x4 *>(G + t0);
             st_span(xg[lane], t4, lane);
             st_span(xg[kWave + lane], t4 + kWave, lane);
+        }
+    } else if (VEC && t0 < 0 && t0 + kNormSpan <= len) {  // a phased first tile
+        float s[kOct];
+        rank_sum<NR, CAP, OD>(gs, n, g8 + t0 / kOct + lane, s);
+#pragma unroll
+        for (int k = 0; k < kOct; ++k)
+            g[k] = e0 >= 0 ? average<POW2>(s[k], c) : 0.0f;
+        if (G) {
+            xg[2 * lane] = f32x4{g[0], g[1], g[2], g[3]};
+            xg[2 * lane + 1] = f32x4{g[4], g[5], g[6], g[7]};
+            __syncthreads();
+            f32x4 *t4 = reinterpret_cast<f32x4 *>(G + t0);
+            if (t0 + 4 * (int64_t)lane >= 0)  // quad `lane` lies in the segment
+                st_span(xg[lane], t4, lane);
+            st_span(xg[kWave + lane], t4 + kWave, lane);  // quads 64.. always do
         }
     } else {
         const int64_t gb = g8 * kOct;
 #pragma unroll
         for (int k = 0; k < kOct; ++k) {
             g[k] = 0.0f;
-            if (e0 + k < len) {
+            if (e0 + k >= 0 && e0 + k < len) {
                 float s = grad_at<GT>(gs.p[0], gb + e0 + k);
                 for (int q = 1; q < n; ++q)
                     s = s + grad_at<GT>(gs.p[q], gb + e0 + k);
@@ -108,13 +129,13 @@ __device__ __forceinline__ void norm_tile(const GradSet<CAP> &gs, int n, float *
 template <int NR, int CAP, typename GT, typename OD, bool POW2, bool VEC>
 __global__ __launch_bounds__(kWave) void norm_kernel(GradSet<CAP> gs, int n,
                                                     float *__restrict__ G, int64_t len,
-                                                    StepConsts c,
+                                                    int phase, StepConsts c,
                                                     double *__restrict__ partials)
 {
     __shared__ f32x4 xg[2 * kWave];  // the tile's g in element order
     const int64_t tile = blockIdx.x;
-    norm_tile<NR, CAP, GT, OD, POW2, VEC>(gs, n, G, len, 0, tile, threadIdx.x, c, partials + tile,
-                                          xg);
+    norm_tile<NR, CAP, GT, OD, POW2, VEC>(gs, n, G, len, 0, phase, tile, threadIdx.x, c,
+                                          partials + tile, xg);
 }
 
 // Several aligned segments in one launch -- one rank's slice of every unit --
@@ -137,7 +158,7 @@ struct NormPiece {
     int64_t len;    // elements
     int64_t pbase;  // the segment's first partial
     uint32_t first; // the launch's first tile of this segment
-    uint32_t pad;
+    int32_t phase;  // elements the segment's first tile starts before it
 };
 
 struct NormBatch {
@@ -165,8 +186,8 @@ __global__ __launch_bounds__(kWave) void norm_batch_kernel(GradSet<CAP> gs, int 
             ++i;
     const NormPiece pc = b.p[i];
     const int64_t tile = blk - pc.first;
-    norm_tile<NR, CAP, GT, OD, POW2, true>(gs, n, G ? G + pc.s : nullptr, pc.len, pc.g8, tile,
-                                           threadIdx.x, c, partials + pc.pbase + tile, xg);
+    norm_tile<NR, CAP, GT, OD, POW2, true>(gs, n, G ? G + pc.s : nullptr, pc.len, pc.g8, pc.phase,
+                                           tile, threadIdx.x, c, partials + pc.pbase + tile, xg);
 }
 
 // One level of the fixed-order reduction of the partials: workgroup b sums
@@ -216,8 +237,8 @@ __global__ void clip_coef_kernel(const double *__restrict__ sums, int n, double 
 }
 
 template <int NR, typename GT, typename OD, bool POW2, bool VEC>
-hipError_t launch_nr(const void *const *grads, int n, float *G, int64_t len, const StepConsts &c,
-                     double *partials, int64_t blocks, hipStream_t st)
+hipError_t launch_nr(const void *const *grads, int n, float *G, int64_t len, int phase,
+                     const StepConsts &c, double *partials, int64_t blocks, hipStream_t st)
 {
     constexpr int CAP = NR > 0 ? NR : ZERO_MAX_RANKS;
     GradSet<CAP> gs{};
@@ -226,39 +247,40 @@ hipError_t launch_nr(const void *const *grads, int n, float *G, int64_t len, con
     const size_t lds = occupancy_cap_lds(norm_waves_per_cu(n, NR == 0, (int)sizeof(GT)),
                                          2 * kWave * sizeof(f32x4));
     hipLaunchKernelGGL((norm_kernel<NR, CAP, GT, OD, POW2, VEC>), dim3((unsigned)blocks),
-                       dim3(kWave), lds, st, gs, n, G, len, c, partials);
+                       dim3(kWave), lds, st, gs, n, G, len, phase, c, partials);
     return hipGetLastError();
 }
 
 template <bool POW2, int... Ks>
 hipError_t bf16_vec_compiled(std::integer_sequence<int, Ks...>, const void *const *grads, int n,
-                             float *G, int64_t len, const StepConsts &c, double *partials,
-                             int64_t blocks, hipStream_t st)
+                             float *G, int64_t len, int phase, const StepConsts &c,
+                             double *partials, int64_t blocks, hipStream_t st)
 {
     using T = uint16_t;
     using QD = Bf16Oct;
     hipError_t r = hipSuccess;
     const bool hit =
         ((n == Ks + 1
-              ? (r = launch_nr<Ks + 1, T, QD, POW2, true>(grads, n, G, len, c, partials, blocks, st),
+              ? (r = launch_nr<Ks + 1, T, QD, POW2, true>(grads, n, G, len, phase, c, partials,
+                                                          blocks, st),
                  true)
               : false) ||
          ...);
     if (hit)
         return r;
     if (n == 64)
-        return launch_nr<64, T, QD, POW2, true>(grads, n, G, len, c, partials, blocks, st);
-    return launch_nr<0, T, QD, POW2, true>(grads, n, G, len, c, partials, blocks, st);
+        return launch_nr<64, T, QD, POW2, true>(grads, n, G, len, phase, c, partials, blocks, st);
+    return launch_nr<0, T, QD, POW2, true>(grads, n, G, len, phase, c, partials, blocks, st);
 }
 
 // bf16 gradients, aligned: a kernel compiled for each rank count up to
 // kMaxCompiledRanks and for 64, the run-time kernel for any other N.
 template <bool POW2>
-hipError_t launch_bf16_vec(const void *const *grads, int n, float *G, int64_t len,
+hipError_t launch_bf16_vec(const void *const *grads, int n, float *G, int64_t len, int phase,
                            const StepConsts &c, double *partials, int64_t blocks, hipStream_t st)
 {
     return bf16_vec_compiled<POW2>(std::make_integer_sequence<int, kMaxCompiledRanks>{}, grads, n,
-                                   G, len, c, partials, blocks, st);
+                                   G, len, phase, c, partials, blocks, st);
 }
 
 // ---- several segments per launch ---------------------------------------
@@ -285,7 +307,8 @@ void fill_norm_groups(NormBatch &b, uint32_t total)
 
 // Batches of the segments, in order: at most kNormPieces segments and
 // kNormBatchTiles tiles each, a longer segment cut at a whole tile (its
-// later tiles keep their elements and partial slots).
+// later tiles keep their elements and partial slots; the part after a cut
+// starts on a tile boundary, with no phase).
 std::vector<std::pair<NormBatch, uint32_t>> norm_batches(const NormSegment *segs, int count)
 {
     std::vector<std::pair<NormBatch, uint32_t>> out;
@@ -302,9 +325,11 @@ std::vector<std::pair<NormBatch, uint32_t>> norm_batches(const NormSegment *segs
     for (int k = 0; k < count; ++k) {
         int64_t g8 = segs[k].g_off / kOct, sg = segs[k].g_out_off, len = segs[k].len,
                 pbase = segs[k].partial;
+        int phase = segs[k].phase;
         while (len > 0) {
-            const int64_t nt = std::min((len + kNormSpan - 1) / kNormSpan, kNormBatchTiles);
-            const int64_t part = std::min(len, nt * kNormSpan);
+            const int64_t nt =
+                std::min((len + phase + kNormSpan - 1) / kNormSpan, kNormBatchTiles);
+            const int64_t part = std::min(len, nt * kNormSpan - phase);  // elements covered
             if (b.n_pieces == kNormPieces || (int64_t)tiles + nt > kNormBatchTiles)
                 flush();
             NormPiece &q = b.p[b.n_pieces];
@@ -313,13 +338,15 @@ std::vector<std::pair<NormBatch, uint32_t>> norm_batches(const NormSegment *segs
             q.len = part;
             q.pbase = pbase;
             q.first = tiles;
+            q.phase = phase;
             tiles += (uint32_t)nt;
             b.end[b.n_pieces] = tiles;
             ++b.n_pieces;
-            g8 += nt * kWave;
-            sg += nt * kNormSpan;
+            g8 += part / kOct;  // a cut part is whole tiles less the phase: whole octs
+            sg += part;
             pbase += nt;
             len -= part;
+            phase = 0;
         }
     }
     flush();
@@ -363,34 +390,49 @@ hipError_t norm_batch_compiled(std::integer_sequence<int, Ks...>, const NormSegm
 
 }  // namespace
 
-int64_t norm_segment_blocks(int64_t len)
+int64_t norm_segment_blocks(int64_t len, int phase)
 {
-    return (len + kNormSpan - 1) / kNormSpan;
+    return len > 0 ? (len + phase + kNormSpan - 1) / kNormSpan : 0;
 }
 
-int launch_norm_segment(int64_t len, bool vec, const void *const *grads, int n_grads,
+int norm_segment_phase(int64_t g_off, int grad_bytes)
+{
+    // the segment's first gradient element modulo a 128-byte line, in whole
+    // octs (never more than g_off, so the first tile stays in the buffers)
+    const int64_t line = 128 / grad_bytes;
+    return (int)(g_off % line) / kOct * kOct;
+}
+
+int launch_norm_segment(int64_t len, int phase, bool vec, const void *const *grads, int n_grads,
                         int grad_dtype, float *g_out, const StepConsts &c, double *partials,
                         void *stream)
 {
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    const int64_t blocks = norm_segment_blocks(len);
+    const int64_t blocks = norm_segment_blocks(len, phase);
     if (blocks <= 0)
         return hipSuccess;
     if (blocks > 0xffffffffLL / kWave)
         return hipErrorInvalidValue;  // larger than one dispatch can address
     const bool bf = grad_dtype == ZERO_BF16;
     const bool p2 = c.div_pow2 != 0;
+    const int ph = phase;
     if (bf && vec)
-        return p2 ? launch_bf16_vec<true>(grads, n_grads, g_out, len, c, partials, blocks, st)
-                  : launch_bf16_vec<false>(grads, n_grads, g_out, len, c, partials, blocks, st);
+        return p2 ? launch_bf16_vec<true>(grads, n_grads, g_out, len, ph, c, partials, blocks, st)
+                  : launch_bf16_vec<false>(grads, n_grads, g_out, len, ph, c, partials, blocks, st);
     if (bf)
-        return p2 ? launch_nr<0, uint16_t, Bf16Oct, true, false>(grads, n_grads, g_out, len, c, partials, blocks, st)
-                  : launch_nr<0, uint16_t, Bf16Oct, false, false>(grads, n_grads, g_out, len, c, partials, blocks, st);
+        return p2 ? launch_nr<0, uint16_t, Bf16Oct, true, false>(grads, n_grads, g_out, len, ph, c,
+                                                                  partials, blocks, st)
+                  : launch_nr<0, uint16_t, Bf16Oct, false, false>(grads, n_grads, g_out, len, ph, c,
+                                                                   partials, blocks, st);
     if (vec)
-        return p2 ? launch_nr<0, float, F32Oct, true, true>(grads, n_grads, g_out, len, c, partials, blocks, st)
-                  : launch_nr<0, float, F32Oct, false, true>(grads, n_grads, g_out, len, c, partials, blocks, st);
-    return p2 ? launch_nr<0, float, F32Oct, true, false>(grads, n_grads, g_out, len, c, partials, blocks, st)
-              : launch_nr<0, float, F32Oct, false, false>(grads, n_grads, g_out, len, c, partials, blocks, st);
+        return p2 ? launch_nr<0, float, F32Oct, true, true>(grads, n_grads, g_out, len, ph, c,
+                                                             partials, blocks, st)
+                  : launch_nr<0, float, F32Oct, false, true>(grads, n_grads, g_out, len, ph, c,
+                                                              partials, blocks, st);
+    return p2 ? launch_nr<0, float, F32Oct, true, false>(grads, n_grads, g_out, len, ph, c, partials,
+                                                          blocks, st)
+              : launch_nr<0, float, F32Oct, false, false>(grads, n_grads, g_out, len, ph, c, partials,
+                                                           blocks, st);
 }
 
 int launch_norm_batch(const NormSegment *segs, int count, const void *const *grads, int n_grads,

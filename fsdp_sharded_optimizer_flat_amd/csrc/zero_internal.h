@@ -180,9 +180,11 @@ int launch_step_batch(const Piece *pcs, int count, const void *const *grads, int
                       const StepConsts &c, void *stream, int waves_per_cu = -1);
 // One aligned segment of a norm pass: gradient elements from g_off (a
 // multiple of 8) past every gradient base, g at g_out_off past g_out, its
-// tiles' partials from `partial`.
+// tiles' partials from `partial`, its first tile starting `phase` elements
+// before it (norm_segment_phase).
 struct NormSegment {
     int64_t g_off, g_out_off, len, partial;
+    int phase;
 };
 // The segments in as few launches as possible, each tile's partial where a
 // launch per segment puts it.  Every gradient base 16-byte aligned (g_out's
@@ -190,10 +192,19 @@ struct NormSegment {
 int launch_norm_batch(const NormSegment *segs, int count, const void *const *grads, int n_grads,
                       int grad_dtype, float *g_out, const StepConsts &c, double *partials,
                       void *stream);
-int launch_norm_segment(int64_t len, bool vec, const void *const *grads, int n_grads,
+// One segment of `len` elements: grads and g_out already point at its first
+// element, which lies at least `phase` elements into every gradient buffer.
+int launch_norm_segment(int64_t len, int phase, bool vec, const void *const *grads, int n_grads,
                         int grad_dtype, float *g_out, const StepConsts &c, double *partials,
                         void *stream);
-int64_t norm_segment_blocks(int64_t len);
+// The tiles (partials) of a segment of `len` elements whose first tile starts
+// `phase` elements before it.
+int64_t norm_segment_blocks(int64_t len, int phase);
+// The phase of a segment whose gradients start g_off elements into their
+// buffers: g_off modulo a 128-byte line of gradients, rounded down to whole
+// octs.  A function of the layout, rank and index spaces only, so the
+// partition (and the sum's bits) never depends on the pointers.
+int norm_segment_phase(int64_t g_off, int grad_bytes);
 // The staged step's first half over len elements: g = (rank-ordered sum) /
 // divisor written to g_out (fp32), 16-byte gradient loads when vec.
 int launch_stage_reduce(int64_t len, bool vec, const void *const *grads, int n_grads,

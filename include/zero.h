@@ -434,10 +434,13 @@ zero_status zero_offload_step(const zero_layout *layout, int32_t rank,
  * index rules as zero_step).  Two stages: one wave of the first reduces each
  * 512-element tile of a contiguous run to one binary64 partial (each lane
  * sums the squares of 8 consecutive elements in order, the wave adds its
- * lanes in a fixed butterfly); the second adds the partials in a fixed-order
- * tree of 1024-way workgroups.  The partition depends only on the layout, the
- * rank and the index spaces (not on the device, pointer alignment or whether
- * g_out is written), so the result is bitwise reproducible.
+ * lanes in a fixed butterfly); a run's tiles start 0 to 56 elements before
+ * it (its first gradient element's index modulo a 128-byte line, in whole
+ * 8-element groups), and elements outside the run add nothing.  The second
+ * stage adds the partials in a fixed-order tree of 1024-way workgroups.  The
+ * partition depends only on the layout, the rank and the index spaces (not
+ * on the device, pointer alignment or whether g_out is written), so the
+ * result is bitwise reproducible.
  *   g_out:      if not NULL, g is also written (fp32, g_index space), so the
  *               step can read one reduced gradient instead of N.
  *   workspace:  caller device memory of at least zero_gradnorm_workspace_bytes.

@@ -341,7 +341,8 @@ def test_gradnorm_argument_errors():
     L = z.zero_pack(4, [1000])
     lib = z.raw_library()
     need = z.zero_gradnorm_workspace_bytes(L, -1)
-    np_ = 1000 // 512 + 1                 # partials: one per 512-element tile, per segment
+    np_ = 1000 // 512 + 2                 # partials: one per 512-element tile, the first of a
+                                          # segment starting up to 56 elements before it
     tree = 1                              # one 1024-way level reduces them to the result
     assert need == 8 * (np_ + 1 + tree)
     arr = (C.c_void_p * 1)(0x1000)

@@ -666,6 +666,47 @@ def test_norm_partition_independent_of_alignment(n, gdt):
     assert abs(s0 - osum) <= 1e-12 * osum
 
 
+def test_norm_phased_tiles_shared_launch_cut():
+    """One rank's slice of two units from full (GLOBAL) gradient buffers, each
+    starting off a 128-byte line (40 and 16 elements past one), so the norm's
+    first tile of each starts that far before its segment; the first slice
+    is longer than one shared launch holds (2^18 tiles), so it is cut.  The
+    reduced gradient and the sum equal the same pass on buffers shifted by
+    one element (every tile element by element, one launch per segment) bit
+    for bit, g_out's neighbours stay untouched, and both match the oracle."""
+    n, rank = 2, 1
+    numel = [2 * ((1 << 27) + 40), 2 * 1024]
+    L = z.zero_pack(n, numel)
+    log(f"norm phased tiles: rank {rank} slice of {L.shard} elements")
+    gen = torch.Generator(device=DEV).manual_seed(616)
+    vals = [(torch.randn(L.padded, device=DEV, generator=gen) * 2e-3).to(torch.bfloat16) for _ in range(n)]
+    ws = torch.zeros(z.zero_gradnorm_workspace_bytes(L, rank) // 8, dtype=torch.float64, device=DEV)
+    guard = 96
+    res = {}
+    for shift in (0, 1):
+        grads = [dev_buffer(L.padded, torch.bfloat16, shift=shift) for _ in range(n)]
+        for q in range(n):
+            grads[q].copy_(vals[q])
+        base = torch.full((L.shard + 2 * guard + shift,), float("nan"), device=DEV)
+        g_out = base[guard + shift:guard + shift + L.shard]
+        s = z.zero_gradnorm(L, rank, grads, G, float(n), g_out, Lc, ws)
+        torch.cuda.synchronize()
+        assert torch.isnan(base[:guard + shift]).all() and torch.isnan(base[guard + shift + L.shard:]).all(), \
+            f"shift {shift}: the pass wrote outside g_out"
+        res[shift] = (s, to_np(g_out).copy())
+        del grads, base, g_out
+    (s0, g0), (s1, g1) = res[0], res[1]
+    assert s0 == s1, (s0, s1)
+    assert_same_f32(g1, g0, "reduced gradient, shifted buffers")
+    gnp = [np.ascontiguousarray(to_np(v)) for v in vals]
+    og = oracle.reduced_grad(n, numel, rank, gnp, grad_local=False, divisor=float(n))
+    assert_same_f32(g0, og, "reduced gradient vs oracle")
+    serial = oracle.sumsq(og)
+    pair = float(np.sum(og.astype(np.float64) ** 2))
+    assert abs(s0 - serial) <= og.size * 2.0 ** -53 * serial, (s0, serial)
+    assert abs(s0 - pair) <= 1e-12 * pair, (s0, pair)
+
+
 def test_norm_closed_form():
     """Every rank's gradient equal to c: the average is c exactly and the sum
     of squares is (elements) * c^2 exactly in binary64."""
