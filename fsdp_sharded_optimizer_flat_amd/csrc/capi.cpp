@@ -279,14 +279,24 @@ int norm_waves_per_cu(int n_grads, bool runtime_kernel, int grad_bytes)
     //   bf16 N = 128  5: 77.0 / 77.4  6: 77.9 / 79.6  7: 78.1 / 79.0  8: 77.3 / 78.1
     //   bf16 N = 192  5: 77.3 / 77.6  6: 77.4 / 79.7  7: 76.3 / 79.8  8: 75.7 / 78.9
     //   bf16 N = 256  5: 76.2 / 76.3  6: 78.4 / 78.4  7: 80.2 / 80.1  8: 79.5 / 79.4
-    //   fp32 N = 48   5: 69.8 / 71.8  6: 69.1 / 70.8  7: 66.7 / 68.2  8: 65.8 / 67.3
-    //   fp32 N = 64   5: 68.3 / 68.1  6: 68.7 / 66.5  7: 67.6 / 64.8  8: 66.7 / 64.5
-    //   fp32 N = 128  5: 72.5 / 73.0  6: 71.9 / 72.1  7: 70.7 / 70.8  8: 70.1 / 70.3
-    // so 6 for bf16 up to 192 ranks and 7 above, 5 for fp32 above 32 ranks;
-    // fewer fp32 ranks keep less in flight and take 7.
+    // fp32 gradients (the staged step from 33 ranks, the clipped workload's
+    // norm pass at every N; the staged step only where measured):
+    //   fp32 N = 8    4:   — / 77.8  5:   — / 77.9  6:   — / 76.5  7:   — / 75.8
+    //   fp32 N = 16   4:   — / 83.1  5:   — / 81.8  6:   — / 81.2  7:   — / 80.8
+    //   fp32 N = 32   4:   — / 81.8  5:   — / 80.7  6:   — / 79.7  7:   — / 78.2
+    //   fp32 N = 48   4: 81.3 / 85.9  5: 81.1 / 85.0  6: 80.4 / 84.7  7: 79.7 / 84.6
+    //   fp32 N = 64   4: 71.8 /   —   5: 72.7 /   —   6: 74.3 /   —   7: 74.8 /   —
+    //   fp32 N = 128  4: 82.5 / 83.8  5: 82.7 / 82.9  6: 82.2 / 82.1  7: 81.6 / 81.2
+    //   fp32 N = 256  4: 82.9 /   —   5: 84.5 /   —   6: 84.0 /   —   7: 83.7 /   —
+    // so 6 for bf16 up to 192 ranks and 7 above; 4 for fp32 up to 128 ranks
+    // and 5 above (an fp32 lane's two batches hold as many bytes as bf16's
+    // over half the ranks).  The staged step at 64 fp32 ranks prefers 7 and
+    // stays 7 to 9 points below its neighbours at any cap: its gradient
+    // buffers lie 32 MiB + 256 KiB apart modulo 64 MiB, as at the bf16 rank
+    // counts whose placement dips (96 and 160).
     int dflt;
     if (runtime_kernel)
-        dflt = grad_bytes == 2 ? (n_grads <= 192 ? 6 : 7) : (n_grads <= 32 ? 7 : 5);
+        dflt = grad_bytes == 2 ? (n_grads <= 192 ? 6 : 7) : (n_grads <= 128 ? 4 : 5);
     else
         dflt = n_grads <= 16 ? 7 : n_grads <= 24 ? 6 : 5;
     return cap_for(2, "ZERO_NORM_WAVES_PER_CU", dflt);

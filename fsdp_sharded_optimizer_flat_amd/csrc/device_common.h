@@ -73,12 +73,16 @@ __device__ __forceinline__ void st_span(T v, T *span, int lane)
 __device__ __forceinline__ float bf_lo(unsigned x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bf_hi(unsigned x) { return __uint_as_float(x & 0xffff0000u); }
 
-// Loads of one lane's group of consecutive gradient elements: a quad
-// (4 elements: 8 bytes of bf16, 16 of fp32) or an oct (8 elements: 16 bytes
-// of bf16, two 16-byte halves of fp32).  Group i covers elements
-// kN*i .. kN*i + kN-1; lane l of a wave reads group (tile * 64 + l), so each
-// wave instruction covers one contiguous span (the fp32 oct's two halves
-// interleave).
+// Loads of one lane's group of gradient elements: a quad (4 elements: 8
+// bytes of bf16, 16 of fp32) or an oct (8 elements: 16 bytes of bf16, two
+// 16-byte quads of fp32).  Lane l of a wave reads group i = i0 + l (i0 the
+// same over the wave), and each wave instruction covers one contiguous span.
+// A quad and a bf16 oct are the consecutive elements kN*i .. kN*i + kN-1.
+// An fp32 oct is two quads 256 elements apart: elements 8*i0 + 4l .. +3 and
+// 8*i0 + 256 + 4l .. +3, so that each of its two loads is a whole 1 KiB span
+// (reading the oct's 32 consecutive bytes per lane instead, every load
+// instruction touched half of each of 16 cache lines: the staged step on
+// fp32 gradients ran 10-13 points slower at 48 and 128 ranks).
 struct Bf16Quad {
     static constexpr int kN = 4, kBytes = 8;
     u32x2 r;
@@ -138,6 +142,8 @@ struct F32Quad {
 struct Bf16Oct {
     static constexpr int kN = 8, kBytes = 16;
     u32x4 r;
+    // element offset of the lane's k-th value from the wave's first element
+    static __device__ __forceinline__ int elem(int lane, int k) { return 8 * lane + k; }
     __device__ __forceinline__ void load(const void *base, int64_t i)
     {
         r = ld_stream(reinterpret_cast<const u32x4 *>(base) + i);
@@ -168,18 +174,24 @@ struct Bf16Oct {
 struct F32Oct {
     static constexpr int kN = 8, kBytes = 32;
     f32x4 a, b;
+    // element offset of the lane's k-th value from the wave's first element
+    static __device__ __forceinline__ int elem(int lane, int k)
+    {
+        return k < 4 ? 4 * lane + k : 4 * kWave + 4 * lane + (k - 4);
+    }
     __device__ __forceinline__ void load(const void *base, int64_t i)
     {
-        const f32x4 *p = reinterpret_cast<const f32x4 *>(base) + 2 * i;
+        const int64_t lane = threadIdx.x & (kWave - 1);
+        const f32x4 *p = reinterpret_cast<const f32x4 *>(base) + (2 * i - lane);
         a = ld_stream(p);
-        b = ld_stream(p + 1);
+        b = ld_stream(p + kWave);
     }
     __device__ __forceinline__ void load_span(__amdgpu_buffer_rsrc_t rs, int lane)
     {
-        a = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, lane * kBytes, 0,
+        a = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16, 0,
                                                                             kLoadStreamPolicy));
         b = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                          rs, lane * kBytes + 16, 0, kLoadStreamPolicy));
+                                          rs, kWave * 16 + lane * 16, 0, kLoadStreamPolicy));
     }
     __device__ __forceinline__ void add_sel(float s[kN], bool on) const
     {

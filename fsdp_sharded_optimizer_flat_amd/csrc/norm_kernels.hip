@@ -39,28 +39,51 @@ using namespace dev;
 // 512 elements that start `phase` elements before the segment (0 to 56, a
 // whole number of octs: the segment's first gradient element modulo a
 // 128-byte line, so that the tiles' gradient spans start on lines when the
-// gradient bases do).  Workgroup b (one wave64) owns tile b and lane l the
-// oct of elements 8l .. 8l+7 of it.  The lane adds its oct's squares in
-// element order, the wave sums its lanes by a fixed butterfly, and lane 0
-// writes the tile's partial.  Elements before the segment or past `len`
-// contribute +0.0, which leaves a binary64 sum unchanged.
+// gradient bases do).  Workgroup b (one wave64) owns tile b and lane l an
+// oct of it: elements 8l .. 8l+7 for bf16 gradients, 4l .. 4l+3 and
+// 256+4l .. +3 for fp32 (the loaders' layouts, OD::elem).  The lane adds its
+// oct's squares in that order, the wave sums its lanes by a fixed butterfly,
+// and lane 0 writes the tile's partial.  Elements before the segment or
+// past `len` contribute +0.0, which leaves a binary64 sum unchanged.
 //
 // VEC: every gradient is 16-byte aligned at the segment start (and g_out
-// too), so whole tiles load each rank's oct with one 16-byte access -- a 1 KiB
-// span per wave instruction for bf16, the access width that streams N = 64
-// ranks best on MI355X -- and g goes through LDS so that lane l then stores
-// quads l and 64 + l of the tile: two contiguous 1 KiB stores per wave.  In
-// the first tile the lanes before the segment load in-bounds data (the
-// phase never exceeds the segment's offset in its buffers) and discard it,
-// and their quads of g are not stored.  The last, partial tile of a segment,
-// and every tile without VEC, reads the same octs element by element.
-// Either way every value and every addition happen in the same order, so
-// the result depends on neither pointer alignment nor on whether g_out is
-// written.  One tile per workgroup (a non-persistent grid) keeps the tiles
-// in flight in one compact window, as in the step kernel.
+// too), so whole tiles load each rank's oct as whole 1 KiB spans per wave
+// instruction (one for bf16, the access width that streams N = 64 ranks best
+// on MI355X, two for fp32), and the wave stores g as two contiguous 1 KiB
+// spans, quads l and 64 + l of the tile (bf16's octs go through LDS to get
+// there; fp32's already are).  In the first tile the lanes before the
+// segment load in-bounds data (the phase never exceeds the segment's offset
+// in its buffers) and discard it, and their quads of g are not stored.  The
+// last, partial tile of a segment, and every tile without VEC, reads the same
+// elements one by one.  Either way every value and every addition happen in
+// the same order, so the result depends on neither pointer alignment nor on
+// whether g_out is written.  One tile per workgroup (a non-persistent grid)
+// keeps the tiles in flight in one compact window, as in the step kernel.
 // Tile `tile` of a segment whose gradient elements start g8 octs (8 * g8
 // elements) past every rank's gradient base; G (may be null) is the
 // segment's g_out.
+
+// A vector tile's g to G + t0 (quads l and 64 + l from lane l); in a phased
+// first tile (PHASED, t0 < 0) the first store only where quad l lies in the
+// segment.
+template <typename OD, bool PHASED>
+__device__ __forceinline__ void store_tile_g(const float g[kOct], float *Gt, int64_t t0,
+                                             int lane, f32x4 *xg)
+{
+    f32x4 q0 = f32x4{g[0], g[1], g[2], g[3]}, q1 = f32x4{g[4], g[5], g[6], g[7]};
+    if constexpr (OD::kBytes != 32) {  // bf16: lane l holds quads 2l and 2l + 1
+        xg[2 * lane] = q0;
+        xg[2 * lane + 1] = q1;
+        __syncthreads();
+        q0 = xg[lane];
+        q1 = xg[kWave + lane];
+    }
+    f32x4 *t4 = reinterpret_cast<f32x4 *>(Gt);
+    if (!PHASED || t0 + 4 * (int64_t)lane >= 0)
+        st_span(q0, t4, lane);
+    st_span(q1, t4 + kWave, lane);  // quads 64.. lie in the segment (phase < 256)
+}
+
 template <int NR, int CAP, typename GT, typename OD, bool POW2, bool VEC>
 __device__ __forceinline__ void norm_tile(const GradSet<CAP> &gs, int n, float *__restrict__ G,
                                           int64_t len, int64_t g8, int phase, int64_t tile,
@@ -68,8 +91,7 @@ __device__ __forceinline__ void norm_tile(const GradSet<CAP> &gs, int n, float *
                                           double *__restrict__ partial, f32x4 *xg)
 {
     static_assert(OD::kN == kOct, "one oct per lane");
-    const int64_t t0 = tile * kNormSpan - phase;      // the tile's first element
-    const int64_t e0 = t0 + (int64_t)lane * kOct;     // first element of the lane's oct
+    const int64_t t0 = tile * kNormSpan - phase;  // the tile's first element
     float g[kOct];
     if (VEC && t0 >= 0 && t0 + kNormSpan <= len) {  // a whole tile (uniform over the workgroup)
         float s[kOct];
@@ -77,41 +99,29 @@ __device__ __forceinline__ void norm_tile(const GradSet<CAP> &gs, int n, float *
 #pragma unroll
         for (int k = 0; k < kOct; ++k)
             g[k] = average<POW2>(s[k], c);
-        if (G) {
-            xg[2 * lane] = f32x4{g[0], g[1], g[2], g[3]};
-            xg[2 * lane + 1] = f32x4{g[4], g[5], g[6], g[7]};
-            __syncthreads();
-            f32x4 *t4 = reinterpret_cast<f32x4 *>(G + t0);
-            st_span(xg[lane], t4, lane);
-            st_span(xg[kWave + lane], t4 + kWave, lane);
-        }
+        if (G)
+            store_tile_g<OD, false>(g, G + t0, t0, lane, xg);
     } else if (VEC && t0 < 0 && t0 + kNormSpan <= len) {  // a phased first tile
         float s[kOct];
         rank_sum<NR, CAP, OD>(gs, n, g8 + t0 / kOct + lane, s);
 #pragma unroll
         for (int k = 0; k < kOct; ++k)
-            g[k] = e0 >= 0 ? average<POW2>(s[k], c) : 0.0f;
-        if (G) {
-            xg[2 * lane] = f32x4{g[0], g[1], g[2], g[3]};
-            xg[2 * lane + 1] = f32x4{g[4], g[5], g[6], g[7]};
-            __syncthreads();
-            f32x4 *t4 = reinterpret_cast<f32x4 *>(G + t0);
-            if (t0 + 4 * (int64_t)lane >= 0)  // quad `lane` lies in the segment
-                st_span(xg[lane], t4, lane);
-            st_span(xg[kWave + lane], t4 + kWave, lane);  // quads 64.. always do
-        }
+            g[k] = t0 + OD::elem(lane, k) >= 0 ? average<POW2>(s[k], c) : 0.0f;
+        if (G)
+            store_tile_g<OD, true>(g, G + t0, t0, lane, xg);
     } else {
         const int64_t gb = g8 * kOct;
 #pragma unroll
         for (int k = 0; k < kOct; ++k) {
+            const int64_t e = t0 + OD::elem(lane, k);
             g[k] = 0.0f;
-            if (e0 + k >= 0 && e0 + k < len) {
-                float s = grad_at<GT>(gs.p[0], gb + e0 + k);
+            if (e >= 0 && e < len) {
+                float s = grad_at<GT>(gs.p[0], gb + e);
                 for (int q = 1; q < n; ++q)
-                    s = s + grad_at<GT>(gs.p[q], gb + e0 + k);
+                    s = s + grad_at<GT>(gs.p[q], gb + e);
                 g[k] = average<POW2>(s, c);
                 if (G)
-                    G[e0 + k] = g[k];
+                    G[e] = g[k];
             }
         }
     }

@@ -29,10 +29,11 @@ namespace {
 
 using namespace dev;
 
-// One 512-element tile per wave64 workgroup, lane l owning elements
-// 8l .. 8l+7 (16-byte gradient loads for bf16, as in the norm pass); the
-// tile's g goes through LDS so the wave stores it as two contiguous 1 KiB
-// spans.  VEC: the gradients are 16-byte aligned at the chunk start (the
+// One 512-element tile per wave64 workgroup, lane l owning one oct of it, as
+// in the norm pass: elements 8l .. 8l+7 for bf16 gradients (one 16-byte
+// load per rank), whose g goes through LDS so the wave stores it as two
+// contiguous 1 KiB spans; elements 4l .. 4l+3 and 256+4l .. +3 for fp32
+// gradients (two 1 KiB loads per rank), whose g the wave stores as it is.  VEC: the gradients are 16-byte aligned at the chunk start (the
 // workspace always is); the last, partial tile and unaligned chunks go
 // element by element.
 template <int NR, int CAP, typename GT, typename OD, bool POW2, bool VEC>
@@ -51,12 +52,17 @@ __global__ __launch_bounds__(kWave) void stage_reduce_kernel(GradSet<CAP> gs, in
 #pragma unroll
         for (int k = 0; k < kOct; ++k)
             g[k] = average<POW2>(s[k], c);
-        xg[2 * lane] = f32x4{g[0], g[1], g[2], g[3]};
-        xg[2 * lane + 1] = f32x4{g[4], g[5], g[6], g[7]};
-        __syncthreads();
         f32x4 *t4 = reinterpret_cast<f32x4 *>(G) + tile * (2 * kWave);
-        st_span<f32x4, kKeepStorePolicy>(xg[lane], t4, lane);
-        st_span<f32x4, kKeepStorePolicy>(xg[kWave + lane], t4 + kWave, lane);
+        if constexpr (OD::kBytes == 32) {  // fp32: the lane holds quads l and 64 + l
+            st_span<f32x4, kKeepStorePolicy>(f32x4{g[0], g[1], g[2], g[3]}, t4, lane);
+            st_span<f32x4, kKeepStorePolicy>(f32x4{g[4], g[5], g[6], g[7]}, t4 + kWave, lane);
+        } else {
+            xg[2 * lane] = f32x4{g[0], g[1], g[2], g[3]};
+            xg[2 * lane + 1] = f32x4{g[4], g[5], g[6], g[7]};
+            __syncthreads();
+            st_span<f32x4, kKeepStorePolicy>(xg[lane], t4, lane);
+            st_span<f32x4, kKeepStorePolicy>(xg[kWave + lane], t4 + kWave, lane);
+        }
     } else {
         const int64_t e0 = tile * kNormSpan + (int64_t)lane * kOct;
 #pragma unroll
