@@ -613,9 +613,11 @@ def setup_step(wl, fused=False, stage_chunk=None, stagger_kib=None, norm_only=No
     # -- inputs, resident before the timed region --------------------------------------
     # Every streamed buffer in one allocation, placed by zero_arena_plan
     # (gradients, master, m, v, out, and the reduced gradient when clipping).
-    # Unclipped at 32+ ranks: the staged step, through a workspace chunk the
-    # memory-side cache holds (zero_step_staged).
-    ws_elems = 0 if clip or fused else z.zero_step_staged_workspace_bytes(L, wl.rank, n) // 4
+    # Unclipped above 32 bf16 / 24 fp32 ranks: the staged step, through a
+    # workspace chunk the memory-side cache holds (zero_step_staged).
+    stages = n > 32 or (grad_dtype == "f32" and n > 24)
+    ws_elems = 0 if clip or fused or not stages else \
+        z.zero_step_staged_workspace_bytes(L, wl.rank, n) // 4
     if ws_elems and stage_chunk:   # a chosen chunk (whole 512-element tiles) plus the spare
         ws_elems = stage_chunk + 4
     staged = ws_elems > 0

@@ -528,8 +528,8 @@ def zero_step_staged(layout: Layout, rank: int, grads, grad_index: int, divisor:
                      master, exp_avg, exp_avg_sq, state_index: int, out, out_index: int,
                      scalars: ZeroAdamwScalars, workspace, stream=None, *, grad_ptrs=None):
     """Enqueue the staged step (zero_step's result, two kernels per chunk
-    through ``workspace``, a device tensor; None when fewer than 32
-    gradients)."""
+    through ``workspace``, a device tensor; None where the fused step runs:
+    up to 32 bf16 or 24 fp32 gradients)."""
     arr, gdt = grad_ptrs if grad_ptrs is not None else _grad_ptrs(grads)
     _need_step(layout, grads if grad_ptrs is None else (), grad_index, master, exp_avg, exp_avg_sq,
                state_index, out, out_index)
@@ -558,7 +558,7 @@ def zero_step_units(layout: Layout, rank: int, unit_begin: int, unit_end: int, g
     """Enqueue the step of units [unit_begin, unit_end) from gradient buckets
     that hold only those units (see zero.h); state and out are the whole
     buffers.  ``workspace`` (device tensor) selects the staged path above 32
-    gradients."""
+    bf16 or 24 fp32 gradients."""
     arr, gdt = grad_ptrs if grad_ptrs is not None else _grad_ptrs(grads)
     if not (0 <= unit_begin <= unit_end <= layout.n_units):
         raise ValueError("unit range outside the layout")

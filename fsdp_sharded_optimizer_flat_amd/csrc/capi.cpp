@@ -513,7 +513,7 @@ extern "C" zero_status zero_step_staged_workspace_bytes(const zero_layout *L, in
         return ZERO_EINVAL;
     if (n_grads < 1 || n_grads > ZERO_MAX_RANKS)
         return ZERO_ERANGE;
-    if (n_grads < kStageMinRanks) {
+    if (n_grads < kStageMinRanksF32) {  // the smaller threshold: the dtype is not known here
         *bytes = 0;
         return ZERO_OK;
     }
@@ -530,7 +530,7 @@ extern "C" zero_status zero_step_staged_workspace_bytes(const zero_layout *L, in
 
 // The staged step over units [u0, u1) (from_range: gradient buckets of
 // grad_extent elements holding only those units); step arguments validated,
-// n_grads >= kStageMinRanks.
+// n_grads >= stage_min_ranks(grad_dtype).
 static zero_status staged_launch(const zero_layout *L, int32_t rank, const void *const *grads,
                                  int32_t n_grads, int32_t grad_dtype, int32_t grad_index,
                                  float divisor, float *master, float *exp_avg, float *exp_avg_sq,
@@ -661,7 +661,7 @@ extern "C" zero_status zero_step_staged(const zero_layout *L, int32_t rank,
                                    master, exp_avg, exp_avg_sq, state_index, out, out_index, sc);
     if (st != ZERO_OK)
         return st;
-    if (n_grads < kStageMinRanks)  // few streams: the fused step is the faster one
+    if (n_grads < stage_min_ranks(grad_dtype))  // few streams: the fused step is the faster one
         return step_launch(L, rank, grads, n_grads, grad_dtype, grad_index, divisor, master,
                            exp_avg, exp_avg_sq, state_index, out, out_index, sc, nullptr, stream,
                            0, -1, false);
@@ -690,7 +690,7 @@ extern "C" zero_status zero_step_units(const zero_layout *L, int32_t rank, int32
                                        sc, ge);
     if (st != ZERO_OK)
         return st;
-    if (workspace && n_grads >= kStageMinRanks)
+    if (workspace && n_grads >= stage_min_ranks(grad_dtype))
         return staged_launch(L, rank, grads, n_grads, grad_dtype, grad_index, divisor, master,
                              exp_avg, exp_avg_sq, state_index, out, out_index, sc, workspace,
                              workspace_bytes, stream, unit_begin, unit_end, true, ge);

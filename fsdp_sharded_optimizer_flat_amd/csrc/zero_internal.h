@@ -23,9 +23,17 @@ constexpr int kNormFanIn = 1024;           // partials one reduction workgroup c
 constexpr int64_t kMaxQuadsPerLaunch = int64_t(1) << 30;  // 32-bit dispatch grid size
 // The staged step: from this many gradients on, reduce chunks of at most
 // kStageMaxChunk elements (128 MB of fp32, half the memory-side cache) into
-// a workspace and step each chunk from it.  Measured on MI355X: the fused
-// step is 0.6 points faster at N = 32, the staged one 5 points faster at 64.
-constexpr int32_t kStageMinRanks = 33;
+// a workspace and step each chunk from it.  Measured on MI355X: with bf16
+// gradients the fused step is 0.6 points faster at N = 32, the staged one 5
+// points faster at 64; with fp32 gradients (twice the bytes per rank) the
+// fused step is 2 points faster at 24, the staged one 4-5 points faster at
+// 28 and 32.
+constexpr int32_t kStageMinRanks = 33;     // bf16 gradients
+constexpr int32_t kStageMinRanksF32 = 25;  // fp32 gradients
+inline int32_t stage_min_ranks(int32_t grad_dtype)
+{
+    return grad_dtype == ZERO_F32 ? kStageMinRanksF32 : kStageMinRanks;
+}
 constexpr int64_t kStageMaxChunk = int64_t(1) << 25;
 constexpr int64_t kStageSlack = 4;  // elements to place a chunk at the state's 16-byte phase
 

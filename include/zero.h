@@ -338,11 +338,14 @@ zero_status zero_step_device_clip(const zero_layout *layout, int32_t rank,
  *               the state share a phase (as the fused step needs too).
  *               zero_step_staged_workspace_bytes gives the size that needs a
  *               single chunk up to that limit, spare bytes included.
- * For n_grads <= 32 the fused step is as fast or faster and runs instead;
- * the workspace is then not used and may be NULL (its size query returns 0).
- * Async on `stream`.  Errors as zero_step, plus for n_grads > 32: EINVAL
- * (NULL workspace, workspace overlapping another buffer), EALIGN (workspace
- * not 16-byte aligned), ENOSPC (workspace_bytes < 2048). */
+ * For n_grads <= 32 with bf16 gradients, and n_grads <= 24 with fp32
+ * gradients (twice the bytes per rank), the fused step is as fast or faster
+ * and runs instead; the workspace is then not used and may be NULL.  The size
+ * query does not know the gradient type: it returns 0 up to 24 gradients and
+ * one chunk's size from 25 on.  Async on `stream`.  Errors as zero_step,
+ * plus, where the staged step runs: EINVAL (NULL workspace, workspace
+ * overlapping another buffer), EALIGN (workspace not 16-byte aligned),
+ * ENOSPC (workspace_bytes < 2048). */
 zero_status zero_step_staged_workspace_bytes(const zero_layout *layout, int32_t rank,
                                              int32_t n_grads, size_t *bytes);
 zero_status zero_step_staged(const zero_layout *layout, int32_t rank,
@@ -369,8 +372,8 @@ zero_status zero_step_staged(const zero_layout *layout, int32_t rank,
  * disjoint unit ranges that together cover every unit, in any order and on any
  * streams, give the bits of one zero_step call, so a caller can step unit k
  * on a side stream while backward still writes the buckets of the next units.
- * workspace: as zero_step_staged, used when n_grads > 32 (NULL: the fused
- * step at any N).  Async on `stream`.  Errors as zero_step / zero_step_staged,
+ * workspace: as zero_step_staged, used where that call stages (bf16
+ * gradients above 32, fp32 above 24; NULL: the fused step at any N).  Async on `stream`.  Errors as zero_step / zero_step_staged,
  * plus EINVAL for a unit range outside 0 <= unit_begin <= unit_end <= U. */
 zero_status zero_step_units(const zero_layout *layout, int32_t rank, int32_t unit_begin,
                             int32_t unit_end, const void *const *grads, int32_t n_grads,

@@ -459,15 +459,17 @@ def test_arena_plan():
 
 
 def test_staged_step_workspace_and_errors():
-    """zero_step_staged_workspace_bytes: 0 up to 32 gradients, else one
-    chunk's fp32 elements (the selection rounded up to whole 512-element
-    tiles, at most 32M); the staged step's workspace errors, raised before
-    any device work."""
+    """zero_step_staged_workspace_bytes: 0 up to 24 gradients (the fused
+    step runs below 25 fp32 / 33 bf16 gradients), else one chunk's fp32
+    elements (the selection rounded up to whole 512-element tiles, at most
+    32M); the staged step's workspace errors, raised before any device
+    work."""
     _no_gpu()
     L = z.zero_pack(64, [64 * 1000 + 5, 64 * 3])
     assert z.zero_step_staged_workspace_bytes(L, 0, 8) == 0
-    assert z.zero_step_staged_workspace_bytes(L, 0, 32) == 0
-    assert z.zero_step_staged_workspace_bytes(L, 0, 33) > 0
+    assert z.zero_step_staged_workspace_bytes(L, 0, 24) == 0
+    assert z.zero_step_staged_workspace_bytes(L, 0, 25) > 0
+    assert z.zero_step_staged_workspace_bytes(L, 0, 32) == z.zero_step_staged_workspace_bytes(L, 0, 33) > 0
     # one chunk of whole 512-element tiles, plus 4 elements to place it at the
     # state's 16-byte phase
     assert z.zero_step_staged_workspace_bytes(L, 0, 64) == 4 * ((L.shard + 511) // 512 * 512 + 4)

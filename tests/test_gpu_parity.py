@@ -225,13 +225,14 @@ def test_rank_order_visible(n, gdt, dist):
     _run_case(rng, n, numel, n // 2, gdt, Lc, Lc, Lc, shift=1, dist=dist, check_order=True)
 
 
-@pytest.mark.parametrize("n", [33, 48, 64, 100, 256, 32, 8])
+@pytest.mark.parametrize("n", [33, 48, 64, 100, 256, 32, 25, 24, 8])
 def test_staged_step(n):
     """zero_step_staged against the oracle, bit for bit: the workspace size
     sets the chunk, so small workspaces give many chunks with ragged ends
     inside every contiguous run; every index mode, both gradient types,
     pointers that are not 16-byte aligned (element path of the reduction,
-    scalar heads of the step).  Up to 32 ranks the fused step runs."""
+    scalar heads of the step).  The fused step runs up to 32 bf16 and 24
+    fp32 ranks."""
     log(f"staged n={n}")
     rng = np.random.default_rng(300 + n)
     numel = [n * 512 * 3 + 11, 3 * n + 1] if n <= 64 else [n * 64 * 9 + 5]

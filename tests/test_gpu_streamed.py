@@ -128,7 +128,7 @@ def test_step_units_random_splits():
         rank = -1 if rng.random() < 0.35 else int(rng.integers(0, n))
         modes = [(G, G, G)] if rank < 0 else [(Lc, Lc, Lc), (G, Lc, G), (Lc, G, Lc)]
         gidx, sidx, oidx = modes[int(rng.integers(0, len(modes)))]
-        staged = int(rng.choice([512, 2048])) if n > 32 and rng.random() < 0.7 else None
+        staged = int(rng.choice([512, 2048])) if n > 24 and rng.random() < 0.7 else None
         _case(rng, n, numel, rank, gdt, gidx, sidx, oidx, staged)
         cases += 1
     log(f"unit-range cases: {cases}")
