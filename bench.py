@@ -111,6 +111,12 @@ def parse():
                     help="with --norm-only: the norm pass without writing the reduced gradient")
     ap.add_argument("--stage-chunk", type=int, default=None,
                     help="elements per chunk of the staged step (default: the largest, 32M)")
+    ap.add_argument("--toggle", action="store_true",
+                    help="with --stagger-kib: one 2 MiB page more wherever consecutive buffers would "
+                         "start a multiple of 4 MiB (plus the step) apart")
+    ap.add_argument("--gap-mib", type=int, default=0,
+                    help="with --stagger-kib: leave this many more MiB (a multiple of 2) between "
+                         "consecutive buffers, to move their bases modulo larger powers of two")
     ap.add_argument("--stagger-kib", type=int, default=None,
                     help="place buffer i at phase (i * KiB) mod 2 MiB instead of zero_arena_plan's "
                          "256 KiB step (0: all at phase 0)")
@@ -570,21 +576,29 @@ def workload_from_args(args):
     return wl
 
 
-def stagger_plan(sizes, step_bytes):
+def stagger_plan(sizes, step_bytes, gap_bytes=0, toggle=False):
     """Buffer offsets in one allocation with buffer i at phase (i * step) mod
-    2 MiB (step 0: every buffer at phase 0); the library's zero_arena_plan is
-    this rule with a 256 KiB step.  For sweeping the step."""
+    2 MiB (step 0: every buffer at phase 0), and gap_bytes (whole 2 MiB pages)
+    more between consecutive buffers; toggle: one 2 MiB page more wherever a
+    buffer would start a multiple of 4 MiB (plus the phase step) after the
+    one before.  The library's zero_arena_plan is this rule with a 256 KiB
+    step, no gap and no toggle.  For sweeping the placement."""
     page = 2 << 20
     offs, at = [], 0
     for i, b in enumerate(sizes):
+        if i:
+            at += gap_bytes
         want = (i * step_bytes) % page
         at += (want - at % page) % page
+        if toggle and i and (at - offs[-1]) % (2 * page) < page:
+            at += page
         offs.append(at)
         at += b
     return offs, at
 
 
-def setup_step(wl, fused=False, stage_chunk=None, stagger_kib=None, norm_only=None, grad_dtype="bf16"):
+def setup_step(wl, fused=False, stage_chunk=None, stagger_kib=None, norm_only=None, grad_dtype="bf16",
+               gap_mib=0, toggle=False):
     """The benchmark's resident inputs and its step, as bench.py times them:
     every streamed buffer in one allocation placed by zero_arena_plan, the
     workload's seeded gradients (the same every step) and master weights,
@@ -631,7 +645,7 @@ def setup_step(wl, fused=False, stage_chunk=None, stagger_kib=None, norm_only=No
     if stagger_kib is None:
         offs, total = z.zero_arena_plan(sizes)
     else:
-        offs, total = stagger_plan(sizes, stagger_kib << 10)
+        offs, total = stagger_plan(sizes, stagger_kib << 10, gap_mib << 20, toggle)
     arena = torch.empty(total, dtype=torch.uint8, device=dev)
     views = [arena[o:o + b].view(dt) for o, b, (_, dt) in zip(offs, sizes, specs)]
     grads, (master, m, v, out) = views[:n], views[n:n + 4]
@@ -972,9 +986,13 @@ def main():
         raise SystemExit("--grad-dtype f32 is a variant without the CPU leg: add --no-cpu-baseline")
     if args.norm_only and wl.clip_max_norm is None:
         raise SystemExit("--norm-only needs the clipped workload (llama8b_z3_clip)")
+    if args.gap_mib and (args.stagger_kib is None or args.gap_mib < 0 or args.gap_mib % 2):
+        raise SystemExit("--gap-mib takes a non-negative multiple of 2, with --stagger-kib")
+    if args.toggle and args.stagger_kib is None:
+        raise SystemExit("--toggle goes with --stagger-kib")
     S = setup_step(wl, fused=args.fused, stage_chunk=args.stage_chunk, stagger_kib=args.stagger_kib,
                    norm_only=("no_g" if args.no_g else "g") if args.norm_only else None,
-                   grad_dtype=args.grad_dtype)
+                   grad_dtype=args.grad_dtype, gap_mib=args.gap_mib, toggle=args.toggle)
     gdt = z.ZERO_F32 if args.grad_dtype == "f32" else z.ZERO_BF16
     if args.sweep_waves:
         sweep_waves(args, wl, S)
@@ -1082,6 +1100,8 @@ def main():
                 ("norm pass only, " + ("g not written" if args.no_g else "g written")) if args.norm_only else "",
                 f"staged chunk {args.stage_chunk} elements" if args.stage_chunk else "",
                 f"buffers staggered by {args.stagger_kib} KiB" if args.stagger_kib is not None else "",
+                f"{args.gap_mib} MiB more between buffers" if args.gap_mib else "",
+                "bases toggled off 4 MiB multiples" if args.toggle else "",
                 "fp32 gradients" if args.grad_dtype == "f32" else "") if v)
                 or None,
             "algorithmic_bytes_per_step": job_bytes,
