@@ -214,9 +214,13 @@ zero_status zero_reshard_traffic(const zero_layout *from, const zero_layout *to,
  * device memory is mapped in 2 MiB pages, so a buffer's phase inside its
  * page is the same physically as virtually, and buffers that start at the
  * same phase are streamed through the same HBM channels at the same moment.
- * Measured with the N = 64 step (65 streamed buffers): 67 % of the 8 TB/s peak
- * with every buffer 2 MiB-aligned (what one allocation per buffer gives),
- * 73-74 % with staggered phases; the N = 8 step gains about 1 point.
+ * Measured with the N = 64 step (the fused kernel, 65 streamed buffers): 67 %
+ * of the 8 TB/s peak with every buffer 2 MiB-aligned (what one allocation per
+ * buffer gives), 73-74 % with staggered phases; the staged N = 64 step 75.2 /
+ * 78.0 % and the N = 8 step 82.2 / 83.4 % without / with the stagger.  The
+ * rule was chosen on those two rank counts; at some others (96 and 160
+ * bf16 gradients, 64 fp32) a placement 2 MiB further apart measured 1 to 6
+ * points faster, and no single rule measured won at every N.
  *
  * Lays out n_buffers buffers of bytes[i] bytes, in the given order, in one
  * allocation: buffer i starts at the first offset at or after the end of
