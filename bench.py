@@ -576,21 +576,32 @@ def workload_from_args(args):
     return wl
 
 
-def stagger_plan(sizes, step_bytes, gap_bytes=0, toggle=False):
+def stagger_plan(sizes, step_bytes, gap_bytes=0, toggle=False, alias_fix=False):
     """Buffer offsets in one allocation with buffer i at phase (i * step) mod
     2 MiB (step 0: every buffer at phase 0), and gap_bytes (whole 2 MiB pages)
     more between consecutive buffers; toggle: one 2 MiB page more wherever a
     buffer would start a multiple of 4 MiB (plus the phase step) after the
-    one before.  The library's zero_arena_plan is this rule with a 256 KiB
-    step, no gap and no toggle.  For sweeping the placement."""
+    one before; alias_fix: the library's exception (one page more where a
+    buffer of a run of more than 32 equal sizes would start a multiple of
+    2 MiB plus 32 MiB, modulo 64 MiB, after the one before).  The library's
+    zero_arena_plan is this rule with a 256 KiB step, no gap, no toggle and
+    the exception.  For sweeping the placement."""
     page = 2 << 20
     offs, at = [], 0
+    run_begin = run_end = 0
     for i, b in enumerate(sizes):
+        if i >= run_end:
+            run_begin, run_end = i, i + 1
+            while run_end < len(sizes) and sizes[run_end] == b:
+                run_end += 1
         if i:
             at += gap_bytes
         want = (i * step_bytes) % page
         at += (want - at % page) % page
         if toggle and i and (at - offs[-1]) % (2 * page) < page:
+            at += page
+        if alias_fix and i > run_begin and run_end - run_begin > 32 and \
+                ((at - offs[-1]) // page) % 32 == 16:
             at += page
         offs.append(at)
         at += b

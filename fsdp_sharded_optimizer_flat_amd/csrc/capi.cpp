@@ -290,10 +290,10 @@ int norm_waves_per_cu(int n_grads, bool runtime_kernel, int grad_bytes)
     //   fp32 N = 256  4: 82.9 /   —   5: 84.5 /   —   6: 84.0 /   —   7: 83.7 /   —
     // so 6 for bf16 up to 192 ranks and 7 above; 4 for fp32 up to 128 ranks
     // and 5 above (an fp32 lane's two batches hold as many bytes as bf16's
-    // over half the ranks).  The staged step at 64 fp32 ranks prefers 7 and
-    // stays 7 to 9 points below its neighbours at any cap: its gradient
-    // buffers lie 32 MiB + 256 KiB apart modulo 64 MiB, as at the bf16 rank
-    // counts whose placement dips (96 and 160).
+    // over half the ranks).  The staged step at 64 fp32 ranks was swept on
+    // buffers 32 MiB + 256 KiB apart modulo 64 MiB, a placement that cost it
+    // 7 to 9 points at any cap; zero_arena_plan now moves such runs (79 %
+    // at the cap above).
     int dflt;
     if (runtime_kernel)
         dflt = grad_bytes == 2 ? (n_grads <= 192 ? 6 : 7) : (n_grads <= 128 ? 4 : 5);

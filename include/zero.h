@@ -218,14 +218,19 @@ zero_status zero_reshard_traffic(const zero_layout *from, const zero_layout *to,
  * of the 8 TB/s peak with every buffer 2 MiB-aligned (what one allocation per
  * buffer gives), 73-74 % with staggered phases; the staged N = 64 step 75.2 /
  * 78.0 % and the N = 8 step 82.2 / 83.4 % without / with the stagger.  The
- * rule was chosen on those two rank counts; at some others (96 and 160
- * bf16 gradients, 64 fp32) a placement 2 MiB further apart measured 1 to 6
- * points faster, and no single rule measured won at every N.
+ * stagger was chosen on those two rank counts; no single rule measured won
+ * at every N (the exception below covers the largest dips found).
  *
  * Lays out n_buffers buffers of bytes[i] bytes, in the given order, in one
  * allocation: buffer i starts at the first offset at or after the end of
- * buffer i - 1 whose remainder modulo 2 MiB is (i * 256 KiB) mod 2 MiB.
- * offsets[i] receives the byte offset of buffer i (every offset is a
+ * buffer i - 1 whose remainder modulo 2 MiB is (i * 256 KiB) mod 2 MiB, with
+ * one exception: in a run of more than 32 consecutive buffers of one size,
+ * a buffer whose start would lie a multiple of 2 MiB plus 32 MiB (modulo 64
+ * MiB) past the previous one's, beyond the stagger, starts 2 MiB later (the
+ * staged step at the rank counts with that spacing, 96 and 160 bf16 or 64
+ * and 192 fp32 gradients, measured 1.2 to 7.2 points faster; any extra space
+ * cost the fused 32-rank step 1 to 3 points, hence only for runs longer than
+ * 32).  offsets[i] receives the byte offset of buffer i (every offset is a
  * multiple of 256 KiB), *total_bytes the size to allocate (the end of the
  * last buffer).  Order the buffers as the step reads them: the gradients,
  * then master, exp_avg, exp_avg_sq, then the output.  EINVAL: n_buffers < 0,

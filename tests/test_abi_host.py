@@ -431,8 +431,10 @@ def test_clip_coef_across_ranks():
 
 def test_arena_plan():
     """zero_arena_plan: buffers in order, non-overlapping, buffer i at phase
-    (i * 256 KiB) mod 2 MiB, no more than one 2 MiB page of slack per buffer;
-    argument errors."""
+    (i * 256 KiB) mod 2 MiB, no more than one 2 MiB page of slack per buffer
+    (sizes drawn at random: no run of more than 32 equal sizes, where one
+    more page is taken -- tests/test_bench_cli.py checks that case against
+    its own statement of the rule); argument errors."""
     rng = np.random.default_rng(3)
     page, stag = 2 << 20, 256 << 10
     cases = [[], [0], [1], [page], [page + 1] * 9, [0, 0, 0]]

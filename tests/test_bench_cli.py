@@ -66,8 +66,27 @@ def test_stagger_plan_reproduces_the_arena_plan():
     rng = np.random.default_rng(4)
     for _ in range(50):
         sizes = [int(x) for x in rng.integers(0, 40 << 20, int(rng.integers(1, 70)))]
-        offs, total = bench.stagger_plan(sizes, 256 << 10)
+        offs, total = bench.stagger_plan(sizes, 256 << 10, alias_fix=True)
         lib_offs, lib_total = z.zero_arena_plan(sizes)
         assert list(offs) == list(lib_offs) and total == lib_total
         offs, total = bench.stagger_plan(sizes, 0)
         assert all(o % (2 << 20) == 0 for o in offs) and total == offs[-1] + sizes[-1]
+    # runs of equal sizes (gradient buffers of the 8B model's shard at N ranks):
+    # more than 32 whose stagger leaves them 32 MiB apart modulo 64 MiB (plus
+    # whole pages and the stagger) start one 2 MiB page later; shorter runs
+    # and other spacings are the plain stagger
+    page, mib = 2 << 20, 1 << 20
+    for n, size, moved in ((160, 100_378_268, True), (96, 167_297_110, True),
+                           (64, 501_891_328, True), (32, 501_891_328, False),
+                           (64, 250_945_664, False), (256, 62_736_416, False)):
+        sizes = [size] * n + [size * 2] * 3 + [size // 2]
+        offs, total = bench.stagger_plan(sizes, 256 << 10, alias_fix=True)
+        lib_offs, lib_total = z.zero_arena_plan(sizes)
+        assert list(offs) == list(lib_offs) and total == lib_total
+        plain, _ = bench.stagger_plan(sizes, 256 << 10)
+        assert (list(offs) != list(plain)) == moved, (n, size)
+        def spacings(o):
+            return {((o[i] - o[i - 1]) // page * page) % (64 * mib) for i in range(1, n)}
+        assert (n > 32 and 32 * mib in spacings(plain)) == moved, (n, size, spacings(plain))
+        assert 32 * mib not in spacings(offs) or n <= 32, (n, size, spacings(offs))
+        assert all(o % page == (i * (256 << 10)) % page for i, o in enumerate(offs))
