@@ -5,7 +5,8 @@ two steps, and so is the clipped workload (the norm pass's reduced gradient,
 its sum of squares and coefficient, and the clipped step, through the
 benchmark's sync-free chain).  A step of 2^32 + 17 elements (more than one
 dispatch) is checked on sampled elements the oracle recomputes one by one,
-which is exact because the step is elementwise."""
+which is exact because the step is elementwise; so is the staged step on a
+shard past 2^31 elements, whose norm pass is compared on every element."""
 import concurrent.futures as cf
 import os
 
@@ -221,3 +222,92 @@ def test_step_beyond_one_launch():
     assert_same_f32(gather_np(v, idx_t), vv, "max-size v")
     assert_same_bf16(gather_np(out, idx_t), oo, "max-size out")
     del g, master, m, v, out
+
+
+def test_norm_and_staged_step_past_2_31_elements():
+    """One rank's shard of 2^31 + 3 * 2^20 + 17 elements (element indices past
+    int32, byte offsets past 2^33, a ragged last tile) under 33 gradients that
+    alternate between two buffers.  The norm pass: its reduced gradient on
+    every element bit for bit against orc_reduced_grad (in chunks, on host
+    threads) and its binary64 sum of squares within n 2^-53 of the oracle's
+    (the chunks' sums added in order) and within 1e-12 of a pairwise binary64
+    sum of the oracle's gradient.  The staged step (many workspace
+    chunks): two steps on sampled elements around 2^31, the chunk boundaries
+    and the tail, recomputed by the oracle one by one."""
+    n, E = 33, (1 << 31) + 3 * (1 << 20) + 17
+    h = WORKLOADS["llama8b_z3"].hyper
+    L = z.zero_pack(n, [E * n])
+    assert L.shard == E
+    log(f"past 2^31: N={n}, S={E}")
+    g0 = torch.empty(E, dtype=torch.bfloat16, device=DEV)
+    g1 = torch.empty(E, dtype=torch.bfloat16, device=DEV)
+    synth.fill_normal_(g0, 1e-3, 71)
+    synth.fill_normal_(g1, 3e-3, 72)
+    grads = [g0 if q % 2 == 0 else g1 for q in range(n)]
+
+    # the norm pass
+    g_out = torch.empty(E, dtype=torch.float32, device=DEV)
+    ws = torch.zeros(z.zero_gradnorm_workspace_bytes(L, 0) // 8, dtype=torch.float64, device=DEV)
+    sumsq = torch.zeros(1, dtype=torch.float64, device=DEV)
+    z.zero_gradnorm_async(L, 0, grads, Lc, float(n), g_out, Lc, ws, sumsq)
+    torch.cuda.synchronize()
+    dev_sum = float(sumsq.item())
+    del ws
+    h0, h1, gh = to_np(g0), to_np(g1), to_np(g_out)
+    del g_out
+    log("past 2^31: norm pass done, host copies taken")
+    CH = 1 << 26
+    bounds = [(a, min(a + CH, E)) for a in range(0, E, CH)]
+
+    def chunk(b):
+        a, e = b
+        gs = [h0[a:e] if q % 2 == 0 else h1[a:e] for q in range(n)]
+        og = oracle.reduced_grad(n, [(e - a) * n], 0, gs, grad_local=True, divisor=float(n))
+        same = bool(np.array_equal(og.view(np.uint32), gh[a:e].view(np.uint32)))
+        return same, oracle.sumsq(og), float(np.sum(og.astype(np.float64) ** 2))
+
+    with cf.ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+        res = list(ex.map(chunk, bounds))
+    bad = [b for b, (same, _, _) in zip(bounds, res) if not same]
+    assert not bad, f"reduced gradient differs from the oracle in chunks {bad[:4]}"
+    orc_sum = pair = 0.0
+    for _, s, p in res:
+        orc_sum += s
+        pair += p
+    assert abs(dev_sum - orc_sum) <= E * 2.0 ** -53 * orc_sum, (dev_sum, orc_sum)
+    assert abs(dev_sum - pair) <= 1e-12 * pair, (dev_sum, pair)
+    log(f"past 2^31: g bit-exact on all {E} elements; sumsq device {dev_sum:.12e} oracle {orc_sum:.12e} "
+        f"pairwise {pair:.12e}")
+    del gh
+
+    # the staged step, two steps on the same gradients
+    master = torch.empty(E, dtype=torch.float32, device=DEV)
+    synth.fill_normal_(master, 0.02, 73)
+    m, v = torch.zeros_like(master), torch.zeros_like(master)
+    out = torch.zeros(E, dtype=torch.int16, device=DEV)
+    wsb = z.zero_step_staged_workspace_bytes(L, 0, n)
+    stage_ws = torch.empty(wsb // 4, dtype=torch.float32, device=DEV)
+    chunk_elems = wsb // 4 - 4
+    rng = np.random.default_rng(6)
+    picks = set(int(x) for x in rng.integers(0, E, 4096))
+    picks.update(range(0, 8))
+    picks.update(range((1 << 31) - 8, (1 << 31) + 8))
+    for k in (1, 2, E // chunk_elems):
+        picks.update(x for x in range(k * chunk_elems - 8, k * chunk_elems + 8) if 0 <= x < E)
+    picks.update(range(E - 24, E))
+    idx = np.array(sorted(picks), np.int64)
+    idx_t = torch.from_numpy(idx).to(DEV)
+    master0 = gather_np(master, idx_t)
+    s0, s1 = h0[idx], h1[idx]
+    gs = [s0 if q % 2 == 0 else s1 for q in range(n)]
+    del h0, h1
+    for t in (1, 2):
+        z.zero_step_staged(L, 0, grads, Lc, float(n), master, m, v, Lc, out, Lc, scalars(t, h), stage_ws)
+    torch.cuda.synchronize()
+    w, mm, vv, oo = oracle_on_samples(n, [gs, gs], master0, 2, h, divisor=float(n))
+    assert_same_f32(gather_np(master, idx_t), w, "past 2^31 staged master")
+    assert_same_f32(gather_np(m, idx_t), mm, "past 2^31 staged m")
+    assert_same_f32(gather_np(v, idx_t), vv, "past 2^31 staged v")
+    assert_same_bf16(gather_np(out, idx_t), oo, "past 2^31 staged out")
+    log(f"past 2^31: staged step bit-exact on {idx.size} sampled elements after 2 steps "
+        f"({-(-E // chunk_elems)} chunks of {chunk_elems})")
