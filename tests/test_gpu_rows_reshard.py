@@ -327,6 +327,27 @@ def test_reshard_large_launch_group_table(dst_shift):
     assert bad == 0, f"{bad} elements differ"
 
 
+
+@pytest.mark.parametrize("dst_shift", [0, 1])
+def test_reshard_run_past_2_31_bytes(dst_shift):
+    """One unit of 2^31 + 24,692 fp32 elements from N = 1 to rank 1 of N = 2:
+    a single run of 2^30 + 12,346 elements (4.3 GB, longer than one copy
+    piece addresses, so it is cut into pieces of one launch) read from source
+    byte offsets past 2^32; the destination at the source's 16-byte phase, or
+    one element off it."""
+    P = (1 << 31) + 2 * 12_345 + 2
+    A, B = z.zero_pack(1, [P]), z.zero_pack(2, [P])
+    log(f"run past 2^31 bytes: 1 x {A.shard} -> rank 1 of 2: {B.shard}, destination shifted by {dst_shift}")
+    src = torch.empty(A.shard, dtype=torch.int32, device=DEV)
+    fill_stream_positions(A, 0, src)
+    dst = dev_buffer(B.shard, torch.int32, shift=dst_shift, fill=-1)
+    z.zero_reshard(A, [src.view(torch.float32)], B, 1, dst.view(torch.float32))
+    want = torch.empty(B.shard, dtype=torch.int32, device=DEV)
+    fill_stream_positions(B, 1, want)
+    torch.cuda.synchronize()
+    bad = int((dst != want).sum().item())
+    assert bad == 0, f"{bad} elements differ"
+
 def fill_stream_positions16(L, q, buf):
     """As fill_stream_positions for 2-byte elements: stream position mod 2^16."""
     t = L.unit_table()
