@@ -22,9 +22,10 @@ def test_c_program_against_header(tmp_path):
 
 @pytest.mark.gpu
 def test_c_program_on_the_gpu():
-    """tests/c/gpu_step_check.c (built by __graft_entry__.build()): the step
-    and the norm driven from plain C with HIP's C runtime API, checked against
-    the oracle's C library, with no Python in the process."""
+    """tests/c/gpu_step_check.c (built by __graft_entry__.build()): the step,
+    the norm, the clipped step with no host synchronization and the staged
+    step at 40 ranks driven from plain C with HIP's C runtime API, checked
+    against the oracle's C library, with no Python in the process."""
     import torch
     if torch.cuda.device_count() == 0:
         pytest.skip("needs a GPU")
