@@ -229,10 +229,11 @@ def test_rank_order_visible(n, gdt, dist):
 def test_staged_step(n):
     """zero_step_staged against the oracle, bit for bit: the workspace size
     sets the chunk, so small workspaces give many chunks with ragged ends
-    inside every contiguous run; every index mode, both gradient types,
-    pointers that are not 16-byte aligned (element path of the reduction,
-    scalar heads of the step).  The fused step runs up to 32 bf16 and 24
-    fp32 ranks."""
+    inside every contiguous run; every index mode, both gradient types (each
+    on aligned pointers, where the reduction loads whole spans, and on
+    pointers that are not 16-byte aligned: the element path of the
+    reduction, scalar heads of the step).  The fused step runs up to 32 bf16
+    and 24 fp32 ranks."""
     log(f"staged n={n}")
     rng = np.random.default_rng(300 + n)
     numel = [n * 512 * 3 + 11, 3 * n + 1] if n <= 64 else [n * 64 * 9 + 5]
@@ -240,6 +241,7 @@ def test_staged_step(n):
         _run_case(rng, n, numel, -1, z.ZERO_BF16, G, G, G, shift=0, staged=ws)
         _run_case(rng, n, numel, n - 1, z.ZERO_BF16, Lc, Lc, Lc, shift=0, staged=ws)
         _run_case(rng, n, numel, 0, z.ZERO_F32, G, Lc, G, shift=2, staged=ws)
+        _run_case(rng, n, numel, n - 1, z.ZERO_F32, Lc, Lc, Lc, shift=0, staged=ws)
         _run_case(rng, n, numel, n // 2, z.ZERO_BF16, Lc, G, Lc, shift=1, staged=ws, with_out=False)
 
 
