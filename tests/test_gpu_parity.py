@@ -669,10 +669,12 @@ def test_norm_partition_independent_of_alignment(n, gdt):
     assert abs(s0 - osum) <= 1e-12 * osum
 
 
-def test_norm_phased_tiles_shared_launch_cut():
+@pytest.mark.parametrize("tdt", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_norm_phased_tiles_shared_launch_cut(tdt):
     """One rank's slice of two units from full (GLOBAL) gradient buffers, each
-    starting off a 128-byte line (40 and 16 elements past one), so the norm's
-    first tile of each starts that far before its segment; the first slice
+    starting off a 128-byte line (bf16: 40 and 16 elements past one; fp32: 8
+    and 16), so the norm's first tile of each starts that far before its
+    segment; the first slice
     is longer than one shared launch holds (2^18 tiles), so it is cut.  The
     reduced gradient and the sum equal the same pass on buffers shifted by
     one element (every tile element by element, one launch per segment) bit
@@ -680,14 +682,14 @@ def test_norm_phased_tiles_shared_launch_cut():
     n, rank = 2, 1
     numel = [2 * ((1 << 27) + 40), 2 * 1024]
     L = z.zero_pack(n, numel)
-    log(f"norm phased tiles: rank {rank} slice of {L.shard} elements")
+    log(f"norm phased tiles: rank {rank} slice of {L.shard} elements, {tdt}")
     gen = torch.Generator(device=DEV).manual_seed(616)
-    vals = [(torch.randn(L.padded, device=DEV, generator=gen) * 2e-3).to(torch.bfloat16) for _ in range(n)]
+    vals = [(torch.randn(L.padded, device=DEV, generator=gen) * 2e-3).to(tdt) for _ in range(n)]
     ws = torch.zeros(z.zero_gradnorm_workspace_bytes(L, rank) // 8, dtype=torch.float64, device=DEV)
     guard = 96
     res = {}
     for shift in (0, 1):
-        grads = [dev_buffer(L.padded, torch.bfloat16, shift=shift) for _ in range(n)]
+        grads = [dev_buffer(L.padded, tdt, shift=shift) for _ in range(n)]
         for q in range(n):
             grads[q].copy_(vals[q])
         base = torch.full((L.shard + 2 * guard + shift,), float("nan"), device=DEV)
