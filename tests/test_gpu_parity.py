@@ -120,7 +120,8 @@ def _order_sensitive(gnp, gdt):
 def _run_case(rng, n, numel, rank, gdt, gidx, sidx, oidx, shift, steps=2, with_out=True, n_grads=None,
               dist="normal", check_order=False, staged=None):
     """staged: None for zero_step; otherwise zero_step_staged with a
-    workspace of that many fp32 elements (0: the size the library asks for)."""
+    workspace of that many fp32 elements (0: the size the library asks for),
+    followed by sentinels the call must leave untouched."""
     h = dict(lr=1e-3, b1=0.9, b2=0.95, eps=1e-8, wd=0.1)
     L = z.zero_pack(n, numel)
     O = oracle.Layout(n, numel)
@@ -136,11 +137,13 @@ def _run_case(rng, n, numel, rank, gdt, gidx, sidx, oidx, shift, steps=2, with_o
     master.copy_(torch.from_numpy(init))
     om, omm, ov = init.copy(), np.zeros(se, np.float32), np.zeros(se, np.float32)
     oout = np.zeros(oe, np.uint16)
-    ws = None
+    ws = ws_guard = None
     if staged is not None:
         want = z.zero_step_staged_workspace_bytes(L, rank, ng) // 4
         elems = want if staged == 0 else staged
-        ws = torch.empty(max(elems, 1), dtype=torch.float32, device=DEV) if want else None
+        if want:   # a guard of 64 sentinels past the workspace, which the call must not touch
+            ws_full = torch.full((max(elems, 1) + 64,), -99.0, dtype=torch.float32, device=DEV)
+            ws, ws_guard = ws_full[:max(elems, 1)], ws_full[max(elems, 1):]
     for t in range(1, steps + 1):
         for g in grads:
             vals = rng.standard_normal(ge) * 1e-3
@@ -165,6 +168,8 @@ def _run_case(rng, n, numel, rank, gdt, gidx, sidx, oidx, shift, steps=2, with_o
                                   **hyper_args(h))
     torch.cuda.synchronize()
     tag = f"n={n} numel={numel} rank={rank} gdt={gdt} idx={gidx}{sidx}{oidx} shift={shift} staged={staged}"
+    if ws_guard is not None:
+        assert bool((ws_guard == -99.0).all()), f"{tag}: the staged step wrote past its workspace"
     # compare only the elements the selection owns (others stay as initialised)
     if rank < 0:
         sel_s = np.arange(se)
@@ -1033,7 +1038,8 @@ def test_norm_random_sweep():
     gradient types, pointers shifted off 16-byte alignment, with and without
     writing g.  The written g must equal the oracle's reduced gradient bit
     for bit, the sum of squares must agree with the oracle's to 1e-12 and be
-    the same bits with or without g."""
+    the same bits with or without g, and nothing past the workspace the size
+    query gives may be written."""
     rng = np.random.default_rng(77)
     for case in range(80):
         n = int(rng.choice([1, 2, 3, 7, 8, 16, 32, 33, 64, 100, 256]))
@@ -1059,12 +1065,14 @@ def test_norm_random_sweep():
             g.copy_(torch.from_numpy(vals[q]).to(tdt))
             grads.append(g)
         gnp = [np.ascontiguousarray(to_np(g)) for g in grads]
-        ws = torch.zeros(max(z.zero_gradnorm_workspace_bytes(L, rank) // 8, 1), dtype=torch.float64,
-                         device=DEV)
+        need = max(z.zero_gradnorm_workspace_bytes(L, rank) // 8, 1)
+        ws_full = torch.full((need + 64,), -99.0, dtype=torch.float64, device=DEV)
+        ws = ws_full[:need]   # 64 sentinels past it, which the pass must not touch
         g_out = dev_buffer(se, torch.float32, shift=int(rng.integers(0, 4)), fill=-7.0)
         s1 = z.zero_gradnorm(L, rank, grads, gidx, float(n), g_out, sidx, ws)
         s2 = z.zero_gradnorm(L, rank, grads, gidx, float(n), None, sidx, ws)
         assert s1 == s2, "the sum must not depend on whether g is written"
+        assert bool((ws_full[need:] == -99.0).all()), f"case {case}: the norm pass wrote past its workspace"
         if rank < 0:
             og = np.zeros(se, np.float32)
             for r in range(n):
