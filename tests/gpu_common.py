@@ -28,6 +28,22 @@ def dev_buffer(n, dtype, shift=0, fill=0.0):
     return base[shift:shift + n]
 
 
+def dev_buffer_guarded(n, dtype, shift=0, fill=0.0, guard=64, sentinel=-99):
+    """dev_buffer with `sentinel` in the `shift` elements before the view and
+    in `guard` elements after it.  Returns (view, check) where check(what)
+    asserts that both guards still hold the sentinel."""
+    base = torch.full((shift + n + guard,), fill, dtype=dtype, device=DEV)
+    base[:shift] = sentinel
+    base[shift + n:] = sentinel
+    view = base[shift:shift + n]
+
+    def check(what):
+        head, tail = base[:shift], base[shift + n:]
+        assert bool((head == sentinel).all()) and bool((tail == sentinel).all()), \
+            f"{what}: written outside its {n} elements"
+    return view, check
+
+
 def to_np(t):
     t = t.detach()
     if t.dtype == torch.bfloat16:

@@ -19,9 +19,9 @@ import oracle  # noqa: E402
 import fsdp_sharded_optimizer_flat_amd as z  # noqa: E402
 from fsdp_sharded_optimizer_flat_amd import synth  # noqa: E402
 from fsdp_sharded_optimizer_flat_amd.workloads import WORKLOADS, GPT_HYPER, TOY_HYPER  # noqa: E402
-from gpu_common import (DEV, assert_same_bf16, assert_same_f32, dev_buffer, extent,  # noqa: E402
-                        gather_np, hyper_args, oracle_on_samples, sampled_indices, scalars,
-                        to_np)
+from gpu_common import (DEV, assert_same_bf16, assert_same_f32, dev_buffer,  # noqa: E402
+                        dev_buffer_guarded, extent, gather_np, hyper_args, oracle_on_samples,
+                        sampled_indices, scalars, to_np)
 
 G, Lc = z.ZERO_GLOBAL, z.ZERO_LOCAL
 
@@ -129,10 +129,11 @@ def _run_case(rng, n, numel, rank, gdt, gidx, sidx, oidx, shift, steps=2, with_o
     tdt = torch.bfloat16 if gdt == z.ZERO_BF16 else torch.float32
     ge, se, oe = extent(L, gidx), extent(L, sidx), extent(L, oidx)
     grads = [dev_buffer(ge, tdt, shift=(shift * (q + 1)) % 8) for q in range(ng)]
-    master = dev_buffer(se, torch.float32, shift=shift)
-    m = dev_buffer(se, torch.float32, shift=shift)
-    v = dev_buffer(se, torch.float32, shift=shift)
-    out = dev_buffer(oe, torch.int16, shift=(shift * 3) % 8) if with_out else None
+    # the written buffers carry sentinels before and after them
+    master, cw = dev_buffer_guarded(se, torch.float32, shift=shift)
+    m, cm = dev_buffer_guarded(se, torch.float32, shift=shift)
+    v, cv = dev_buffer_guarded(se, torch.float32, shift=shift)
+    out, co = dev_buffer_guarded(oe, torch.int16, shift=(shift * 3) % 8) if with_out else (None, None)
     init = rng.normal(0, 0.02, se).astype(np.float32)
     master.copy_(torch.from_numpy(init))
     om, omm, ov = init.copy(), np.zeros(se, np.float32), np.zeros(se, np.float32)
@@ -182,10 +183,17 @@ def _run_case(rng, n, numel, rank, gdt, gidx, sidx, oidx, shift, steps=2, with_o
     assert_same_f32(to_np(master)[sel_s], om[sel_s], "master " + tag)
     assert_same_f32(to_np(m)[sel_s], omm[sel_s], "m " + tag)
     assert_same_f32(to_np(v)[sel_s], ov[sel_s], "v " + tag)
+    rest = np.setdiff1d(np.arange(se), sel_s)   # state outside the selection: as initialised
+    assert_same_f32(to_np(master)[rest], init[rest], "master outside the selection " + tag)
+    assert np.all(to_np(m)[rest] == 0) and np.all(to_np(v)[rest] == 0), \
+        "m / v outside the selection were written " + tag
+    for check, what in ((cw, "master"), (cm, "m"), (cv, "v")):
+        check(f"{what} {tag}")
     if with_out:
         assert_same_bf16(to_np(out)[sel_o], oout[sel_o], "out " + tag)
         untouched = np.setdiff1d(np.arange(oe), sel_o)
         assert np.all(to_np(out)[untouched] == 0), "elements outside the selection were written"
+        co(f"out {tag}")
 
 
 def test_index_modes_bruteforce():
