@@ -1076,11 +1076,12 @@ def test_norm_random_sweep():
         need = max(z.zero_gradnorm_workspace_bytes(L, rank) // 8, 1)
         ws_full = torch.full((need + 64,), -99.0, dtype=torch.float64, device=DEV)
         ws = ws_full[:need]   # 64 sentinels past it, which the pass must not touch
-        g_out = dev_buffer(se, torch.float32, shift=int(rng.integers(0, 4)), fill=-7.0)
+        g_out, cg = dev_buffer_guarded(se, torch.float32, shift=int(rng.integers(0, 4)), fill=-7.0)
         s1 = z.zero_gradnorm(L, rank, grads, gidx, float(n), g_out, sidx, ws)
         s2 = z.zero_gradnorm(L, rank, grads, gidx, float(n), None, sidx, ws)
         assert s1 == s2, "the sum must not depend on whether g is written"
         assert bool((ws_full[need:] == -99.0).all()), f"case {case}: the norm pass wrote past its workspace"
+        cg(f"g, case {case}")
         if rank < 0:
             og = np.zeros(se, np.float32)
             for r in range(n):
