@@ -961,7 +961,7 @@ def sweep_waves(args, wl, S):
                       "staged": S.staged, "clip": S.clip, "steps_per_point": args.steps,
                       "rounds": args.rounds, "pct_of_8TBps": res, "median": med,
                       "best": max(med, key=med.get),
-                      "default": z.zero_get_waves_per_cu(kind, n)}))
+                      "default": z.zero_get_waves_per_cu_for(kind, n, S.grad_dtype, S.staged)}))
 
 
 def main():

@@ -162,6 +162,7 @@ _zero_ckpt_inspect = _sig("zero_ckpt_inspect", i32, C.c_char_p, i32, C.POINTER(Z
 _zero_ckpt_load = _sig("zero_ckpt_load", i32, vp, i32, vp, i32, i32, C.POINTER(i32), vp, vp, vp)
 _zero_set_waves_per_cu = _sig("zero_set_waves_per_cu", i32, i32, i32)
 _zero_get_waves_per_cu = _sig("zero_get_waves_per_cu", i32, i32, i32, C.POINTER(i32))
+_zero_get_waves_per_cu_for = _sig("zero_get_waves_per_cu_for", i32, i32, i32, i32, i32, C.POINTER(i32))
 _zero_strerror = _sig("zero_strerror", C.c_char_p, i32)
 _zero_last_hip_error = _sig("zero_last_hip_error", C.c_char_p)
 _zero_abi_version = _sig("zero_abi_version", i32)
@@ -178,7 +179,7 @@ EXPORTED = ["zero_layout_bytes", "zero_pack", "zero_pack_rows", "zero_reshard",
             "zero_clip_coef", "zero_ledger", "zero_sim_footprint",
             "zero_gather_buffer_bytes", "zero_arena_plan", "zero_step_traffic",
             "zero_gradnorm_traffic", "zero_ckpt_save", "zero_ckpt_inspect", "zero_ckpt_load",
-            "zero_set_waves_per_cu", "zero_get_waves_per_cu",
+            "zero_set_waves_per_cu", "zero_get_waves_per_cu", "zero_get_waves_per_cu_for",
             "zero_strerror", "zero_last_hip_error", "zero_abi_version"]
 
 
@@ -896,6 +897,14 @@ def zero_set_waves_per_cu(kind: int, waves: int):
 def zero_get_waves_per_cu(kind: int, n_grads: int = 1) -> int:
     w = i32()
     _check(_zero_get_waves_per_cu(kind, n_grads, C.byref(w)), "zero_get_waves_per_cu")
+    return w.value
+
+
+def zero_get_waves_per_cu_for(kind: int, n_grads: int, grad_dtype: int = ZERO_BF16,
+                              staged: bool = False) -> int:
+    w = i32()
+    _check(_zero_get_waves_per_cu_for(kind, n_grads, grad_dtype, int(staged), C.byref(w)),
+           "zero_get_waves_per_cu_for")
     return w.value
 
 

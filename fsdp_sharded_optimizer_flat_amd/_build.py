@@ -24,7 +24,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libzero.so")
 
-SOURCES = ["layout.cpp", "scalars.cpp", "ledger.cpp", "capi.cpp", "offload.cpp", "reshard.cpp",
+SOURCES = ["layout.cpp", "scalars.cpp", "ledger.cpp", "capi.cpp", "caps.cpp", "offload.cpp", "reshard.cpp",
            "step_kernels.hip", "norm_kernels.hip", "stage_kernels.hip", "pack_kernels.hip",
            "reshard_kernels.hip"]
 # Host-only C++ built with g++: the offload step's AVX2 code (no FMA, no

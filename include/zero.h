@@ -710,6 +710,17 @@ zero_status zero_set_waves_per_cu(int32_t kind, int32_t waves);
  * 1..ZERO_MAX_RANKS, NULL. */
 zero_status zero_get_waves_per_cu(int32_t kind, int32_t n_grads, int32_t *waves);
 
+/* The same for n_grads gradients of grad_dtype (ZERO_BF16 or ZERO_F32) and,
+ * when staged is nonzero, for the staged step's kernels: ZERO_CAP_STEP1 its
+ * second half (whose default differs from the clipped step's), ZERO_CAP_NORM
+ * its reduction (compiled for fewer rank counts than the norm pass); staged
+ * does not change ZERO_CAP_STEP.  For 16-byte aligned buffers (the vector
+ * kernels).  zero_get_waves_per_cu(kind, n, w) equals
+ * zero_get_waves_per_cu_for(kind, n, ZERO_BF16, 0, w).  EINVAL: as
+ * zero_get_waves_per_cu, or a bad grad_dtype. */
+zero_status zero_get_waves_per_cu_for(int32_t kind, int32_t n_grads, int32_t grad_dtype,
+                                      int32_t staged, int32_t *waves);
+
 /* ------------------------------------------------------------------------
  * Diagnostics.
  * ------------------------------------------------------------------------ */

@@ -530,3 +530,32 @@ def test_occupancy_caps_table_and_setter():
             z.zero_set_waves_per_cu(kind, waves)
     with pytest.raises(z.ZeroError):
         z.zero_get_waves_per_cu(S, 0)
+
+
+def test_occupancy_caps_by_gradient_type_and_staged():
+    """zero_get_waves_per_cu_for: equal to zero_get_waves_per_cu for bf16
+    gradients outside the staged step; fp32 gradients on their own kernels
+    (compiled for 2, 4, 8, 16, 32 ranks: caps from the bytes a lane keeps in
+    flight; the run-time kernel at other N) and on the run-time reduction;
+    the staged step's second half and its reduction (compiled for 32 and 64
+    bf16 ranks only)."""
+    S, S1, NRM = z.ZERO_CAP_STEP, z.ZERO_CAP_STEP1, z.ZERO_CAP_NORM
+    BF, F32 = z.ZERO_BF16, z.ZERO_F32
+    if any(os.environ.get(v) for v in ("ZERO_STEP_WAVES_PER_CU", "ZERO_STEP1_WAVES_PER_CU",
+                                      "ZERO_NORM_WAVES_PER_CU")):
+        pytest.skip("occupancy environment overrides set")
+    for kind in (S, S1, NRM):
+        for n in range(1, 257):
+            assert z.zero_get_waves_per_cu_for(kind, n, BF) == z.zero_get_waves_per_cu(kind, n), (kind, n)
+    assert {n: z.zero_get_waves_per_cu_for(S, n, F32) for n in (2, 4, 8, 16, 32, 3, 12, 24, 48)} == \
+        {2: 8, 4: 7, 8: 6, 16: 5, 32: 5, 3: 12, 12: 7, 24: 5, 48: 5}
+    assert z.zero_get_waves_per_cu_for(S, 64, BF, True) == z.zero_get_waves_per_cu(S, 64)
+    assert z.zero_get_waves_per_cu_for(S1, 64, BF, True) == 12
+    assert z.zero_get_waves_per_cu_for(S1, 64, F32, False) == 10
+    assert [z.zero_get_waves_per_cu_for(NRM, n, F32) for n in (8, 48, 128, 129, 256)] == [4, 4, 4, 5, 5]
+    assert [z.zero_get_waves_per_cu_for(NRM, n, F32, True) for n in (25, 64, 128, 192)] == [4, 4, 4, 5]
+    assert [z.zero_get_waves_per_cu_for(NRM, n, BF, True) for n in (32, 33, 48, 64, 100, 192, 193, 256)] == \
+        [5, 6, 6, 5, 6, 6, 7, 7]
+    for args in ((3, 8, BF, 0), (S, 0, BF, 0), (S, 257, BF, 0), (S, 8, 2, 0), (S, 8, -1, 0)):
+        with pytest.raises(z.ZeroError):
+            z.zero_get_waves_per_cu_for(*args)
